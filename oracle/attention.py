@@ -1,0 +1,297 @@
+"""fp64 CPU oracle: the plain definition of what the HIP path computes.
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring for who may import it.
+Shares no code with the HIP path.  Page tags ([BLT], [ORT], [FLEX], [NANO],
+[VLLM]) are defined in ``oracle/__init__.py``.
+
+Everything here is float64 numpy with explicit per-sequence / per-head loops.
+A library primitive (a matrix product, ``np.exp``, ``np.max``) serves as a
+step; there is no tiling, no online softmax and no reordering beyond the
+definition, so each function can be compared with the pages by eye.
+
+Readings where the pages are silent (each is also listed in the design doc):
+  * causal alignment when q_len != kv_len is bottom-right: query i of a
+    sequence sits at absolute position kv_len - q_len + i, so it sees key j
+    iff j <= i + kv_len - q_len.  The pages only show ``q_idx >= kv_idx`` at
+    equal lengths ([FLEX] test diff; [NANO] "Note on impact": is_causal at
+    Tq == Tk), where both alignments agree.
+  * GQA maps q head h to kv head h // (Hq // Hkv) ([FLEX] flex_attention
+    docstring: Hq query heads over Hkv key/value heads; [ORT] Implementation,
+    step 2: "GQA head expansion").
+  * paged cache layout is [num_blocks, block_size, num_kv_heads, head_size]
+    ([ORT] Scratch allocation: the size formula multiplies blocks x block_size
+    x num_heads x head_size) and block_table is int32 [batch, max_blocks].
+  * a query row with no visible key outputs O = 0 and LSE = -inf ([BLT]
+    kernel options: ROWS_GUARANTEED_SAFE is False, so such rows may occur; the
+    value they take is not printed).
+  * LSE is the natural-log logsumexp of the scaled, masked scores ([BLT]
+    kernel options: OUTPUT_LOGSUMEXP True, PRESCALE_QK False).
+  * fp8 is OCP e4m3fn ([FLEX] _enforce_mem_layouts names torch.float8_e4m3fn);
+    a tensor's real value is descale * decoded code.
+"""
+
+import math
+
+import numpy as np
+
+MASK_CAUSAL = 1
+MASK_DOCUMENT = 2
+MASK_PATCH = 4
+
+# Which pin covers which function (test names in tests/test_oracle_pins.py).
+PIN_STATUS = {
+    "cu_seqlens": "pinned: numpy.cumsum special case, hand-written golden example",
+    "reshape_and_cache": "pinned: hand-written golden placement example, gather round trip",
+    "gather_paged": "pinned: identity table equals packed layout; permuted tables agree",
+    "visibility": "pinned: np.tril closed forms, page predicate q_idx >= kv_idx, brute-force counts",
+    "attention_varlen": "pinned: torch CPU fp64 SDPA (dense, GQA), closed forms, invariants",
+    "paged_attention": "pinned: equals attention_varlen on gathered K/V; block-table permutation invariance",
+    "paged_decode": "pinned: equals the last row of a causal prefill over the same cache",
+    "e4m3_decode": "pinned: all 256 codes against torch.float8_e4m3fn; closed-form extremes",
+    "fp8_attention": "pinned: equals attention_varlen on decoded values; hand-derived two-key example",
+    "default_scale": "pinned: golden value 0.0625 at E=256 from [BLT]",
+}
+
+
+def default_scale(head_size):
+    """Softmax scale when the caller gives none: 1/sqrt(E).
+
+    [FLEX] flex_attention docstring, argument ``scale``; the [BLT] lowering
+    arguments show the instance 0.0625 for E = 256.
+    """
+    return 1.0 / math.sqrt(head_size)
+
+
+def cu_seqlens(seqlens):
+    """Cumulative sequence lengths: cu[0] = 0, cu[b + 1] = cu[b] + seqlens[b].
+
+    [ORT] Implementation, steps 1 and 3: the cumulative-seqlens buffer is the
+    varlen ``seqstart`` array and its last element is the token total.
+    Returns int32 [batch + 1]; raises if the total does not fit int32.
+    """
+    out = [0]
+    for n in seqlens:
+        n = int(n)
+        if n < 0:
+            raise ValueError("negative sequence length")
+        out.append(out[-1] + n)
+    if out[-1] >= 2**31:
+        raise OverflowError("total length does not fit int32")
+    return np.asarray(out, dtype=np.int32)
+
+
+def reshape_and_cache(k_new, v_new, k_cache, v_cache, block_table, cu_new, cu_kv, block_size):
+    """Write new K/V tokens into the paged cache (returns updated copies).
+
+    [ORT] Implementation, step 1 (ReshapeAndCache runs before attention) and
+    step 2 (block_table maps a sequence's logical blocks to physical blocks).
+    Sequence b appends ``n_new = cu_new[b+1] - cu_new[b]`` tokens; after the
+    write it holds ``kv_len = cu_kv[b+1] - cu_kv[b]`` tokens, so new token i
+    lands at position ``pos = kv_len - n_new + i``, i.e. in physical block
+    ``block_table[b][pos // block_size]`` at slot ``pos % block_size``.
+
+    Works on any dtype (the tests pass raw integer views so the copy is
+    checked bit for bit).  k_new, v_new: [total_new, Hkv, D];
+    caches: [num_blocks, block_size, Hkv, D].
+    """
+    k_out = np.array(k_cache, copy=True)
+    v_out = np.array(v_cache, copy=True)
+    batch = len(cu_new) - 1
+    for b in range(batch):
+        n_new = int(cu_new[b + 1]) - int(cu_new[b])
+        kv_len = int(cu_kv[b + 1]) - int(cu_kv[b])
+        if n_new > kv_len:
+            raise ValueError("sequence has more new tokens than total tokens")
+        for i in range(n_new):
+            pos = kv_len - n_new + i
+            blk = int(block_table[b][pos // block_size])
+            slot = pos % block_size
+            k_out[blk, slot] = k_new[int(cu_new[b]) + i]
+            v_out[blk, slot] = v_new[int(cu_new[b]) + i]
+    return k_out, v_out
+
+
+def gather_paged(cache, table_row, kv_len, block_size):
+    """Logical token j of one sequence is ``cache[table_row[j // bs], j % bs]``.
+
+    [ORT] Implementation, step 2: GatherAndExpandPagedKVCache walks block_table
+    to build the packed [total_kv_tokens, num_heads, head_size] K/V.
+    Returns [kv_len, Hkv, D] (GQA expansion happens in attention_varlen).
+    """
+    out = np.empty((kv_len,) + tuple(cache.shape[2:]), dtype=cache.dtype)
+    for j in range(kv_len):
+        out[j] = cache[int(table_row[j // block_size]), j % block_size]
+    return out
+
+
+def visibility(q_len, kv_len, flags, q_ids=None, kv_ids=None):
+    """Boolean [q_len, kv_len]: may query i of a sequence attend to key j.
+
+    Conjunction of
+      * CAUSAL:   j <= i + (kv_len - q_len)   ([FLEX] test diff: mask_mod
+                  ``q_idx >= kv_idx``; bottom-right when lengths differ)
+      * DOCUMENT: q_ids[i] == kv_ids[j]      (document ids; packing several
+                  documents into one sequence)
+      * PATCH:    j <= q_ids[i]              ([BLT] CrossAttention: byte
+                  queries see their own and earlier patch keys; q_ids holds
+                  each byte's patch index within its sequence)
+    Every key index j < kv_len exists; there is no other bound.
+    """
+    if flags & MASK_DOCUMENT and flags & MASK_PATCH:
+        raise ValueError("DOCUMENT and PATCH masks are exclusive")
+    i = np.arange(q_len)[:, None]
+    j = np.arange(kv_len)[None, :]
+    vis = np.ones((q_len, kv_len), dtype=bool)
+    if flags & MASK_CAUSAL:
+        vis &= j <= i + (kv_len - q_len)
+    if flags & MASK_DOCUMENT:
+        vis &= np.asarray(q_ids)[:q_len, None] == np.asarray(kv_ids)[None, :kv_len]
+    if flags & MASK_PATCH:
+        vis &= j <= np.asarray(q_ids)[:q_len, None]
+    return vis
+
+
+def _softmax_rows(s, vis, v):
+    """O = softmax(s restricted to vis) @ v and LSE, row by row (fp64).
+
+    A row with no visible key gives O = 0 and LSE = -inf (reading of [BLT]
+    ROWS_GUARANTEED_SAFE False).
+    """
+    q_len = s.shape[0]
+    out = np.zeros((q_len, v.shape[1]), dtype=np.float64)
+    lse = np.full(q_len, -np.inf, dtype=np.float64)
+    for i in range(q_len):
+        idx = np.nonzero(vis[i])[0]
+        if idx.size == 0:
+            continue
+        row = s[i, idx]
+        m = row.max()
+        w = np.exp(row - m)
+        total = w.sum()
+        out[i] = (w @ v[idx]) / total
+        lse[i] = m + math.log(total)
+    return out, lse
+
+
+def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, rows=None):
+    """Varlen attention over packed (non-paged) K/V, fp64.
+
+    q: [total_q, Hq, D]; k: [total_kv, Hkv, D]; v: [total_kv, Hkv, Dv];
+    cu_q, cu_kv: [batch + 1] cumulative lengths ([ORT] Implementation, step 3:
+    seqstart_q / seqstart_k, no padding, BSNH strides).
+    s[i, j] = scale * <q_i, k_j> with the scale applied to the product
+    ([BLT] kernel options: PRESCALE_QK False), masked by ``visibility``, then
+    softmax over visible j and the weighted sum of V ([FLEX] flex_attention:
+    softmax(scale * QK^T + mask) V).
+    q_ids / kv_ids are indexed by global token ([total_q] / [total_kv]).
+    rows: optional global query indices to compute (others stay 0 / -inf);
+    used to sample outputs of full-size workloads.
+    Returns (out [total_q, Hq, Dv], lse [total_q, Hq]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    total_q, hq, _ = q.shape
+    hkv = k.shape[1]
+    if hq % hkv:
+        raise ValueError("num_heads must be a multiple of num_kv_heads")
+    group = hq // hkv
+    out = np.zeros((total_q, hq, v.shape[2]), dtype=np.float64)
+    lse = np.full((total_q, hq), -np.inf, dtype=np.float64)
+    want = None if rows is None else np.zeros(total_q, dtype=bool)
+    if want is not None:
+        want[np.asarray(rows)] = True
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
+        q_len, kv_len = q1 - q0, k1 - k0
+        sel = np.arange(q_len) if want is None else np.nonzero(want[q0:q1])[0]
+        if sel.size == 0:
+            continue
+        qi = None if q_ids is None else np.asarray(q_ids)[q0:q1]
+        ki = None if kv_ids is None else np.asarray(kv_ids)[k0:k1]
+        vis = visibility(q_len, kv_len, flags, qi, ki)[sel]
+        for h in range(hq):
+            kvh = h // group
+            s = scale * (q[q0 + sel, h, :] @ k[k0:k1, kvh, :].T)
+            o, l = _softmax_rows(s, vis, v[k0:k1, kvh, :])
+            out[q0 + sel, h] = o
+            lse[q0 + sel, h] = l
+    return out, lse
+
+
+def paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, scale,
+                    flags=0, q_ids=None, kv_ids=None, rows=None):
+    """Attention whose K/V live in a paged cache ([ORT] Implementation, step 2
+    then step 3): gather each sequence's K/V through block_table into a packed
+    buffer, then run ``attention_varlen`` on it.  Returns (out, lse) in fp64.
+    """
+    batch = len(cu_kv) - 1
+    ks, vs = [], []
+    for b in range(batch):
+        kv_len = int(cu_kv[b + 1]) - int(cu_kv[b])
+        ks.append(gather_paged(k_cache, block_table[b], kv_len, block_size))
+        vs.append(gather_paged(v_cache, block_table[b], kv_len, block_size))
+    k = np.concatenate(ks, axis=0) if ks else np.zeros((0,) + tuple(k_cache.shape[2:]))
+    v = np.concatenate(vs, axis=0) if vs else np.zeros((0,) + tuple(v_cache.shape[2:]))
+    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows)
+
+
+def paged_decode(q, k_cache, v_cache, block_table, cu_kv, block_size, scale, batches=None):
+    """One new query per sequence (q: [batch, Hq, D]) against its paged cache.
+
+    This is paged_attention with q_len = 1; under bottom-right causal
+    alignment the single query sits at the last position and sees every key,
+    so no mask applies.  ``batches`` optionally restricts the sequences
+    computed.  Returns (out [batch, Hq, Dv], lse [batch, Hq]).
+    """
+    batch = len(cu_kv) - 1
+    cu_q = np.arange(batch + 1, dtype=np.int64)
+    rows = None if batches is None else np.asarray(batches)
+    return paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, scale,
+                           MASK_CAUSAL, rows=rows)
+
+
+def e4m3_decode(codes):
+    """Decode OCP FP8 E4M3 ("fn": finite, no infinities) bytes to float64.
+
+    [FLEX] _enforce_mem_layouts lists torch.float8_e4m3fn among the fp8 dtypes.
+    Bit layout s eeee mmm, exponent bias 7.  e = 0 is subnormal:
+    m / 8 * 2**-6.  Otherwise (1 + m / 8) * 2**(e - 7), except e = 15, m = 7
+    which is NaN.  Largest finite magnitude: 1.75 * 2**8 = 448.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    flat_c = codes.reshape(-1)
+    flat_o = out.reshape(-1)
+    table = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            table[c] = np.nan
+        elif e == 0:
+            table[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            table[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    flat_o[:] = table[flat_c]
+    return out
+
+
+def fp8_attention(q8, k8, v8_colmajor, descale, cu_q, cu_kv, scale, flags=0,
+                  q_ids=None, kv_ids=None, rows=None):
+    """fp8 e4m3 attention: decode, apply per-tensor descales, then attend.
+
+    q8: uint8 codes [total_q, Hq, D]; k8: [total_kv, Hkv, D];
+    v8_colmajor: [Hkv, D, total_kv] -- V is column-major, i.e. token-contiguous
+    for each (head, feature), as [FLEX] _enforce_mem_layouts requires for the
+    right operand of ``softmax_scores @ V``.
+    descale = (dq, dk, dv): the real tensor is descale * decoded code.
+    The result is the exact attention of those real values (fp64).
+    """
+    dq, dk, dv = (float(x) for x in descale)
+    q = dq * e4m3_decode(q8)
+    k = dk * e4m3_decode(k8)
+    v = dv * np.transpose(e4m3_decode(v8_colmajor), (2, 0, 1))
+    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows)

@@ -1,0 +1,559 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+Each ``check_*`` function takes the oracle module and raises AssertionError on
+a mismatch.  The tests run them on the real oracle; ``test_planted_mistakes``
+plants plausible mistakes into the oracle (on the CPU) and requires that at
+least one check catches each of them.
+
+Sources of truth used here (none of them is the oracle's own formula):
+  * values the pages print (tests/golden/*.json, each with its citation);
+  * hand-derived closed forms (tests/golden/two_key_example.json, uniform
+    scores give the mean of the visible V rows, LSE = ln(count));
+  * library routines for special cases: numpy.cumsum, numpy.tril, torch CPU
+    float64 scaled_dot_product_attention (dense, GQA, explicit masks),
+    torch.logsumexp, torch.float8_e4m3fn decoding;
+  * invariants: block-table permutation, score shifts, GQA head expansion,
+    varlen packing, decode = last causal row.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle.attention as ORC
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sdpa(q, k, v, scale, is_causal=False, attn_mask=None, enable_gqa=False):
+    """torch CPU float64 SDPA on one sequence; q [L, Hq, D], k/v [S, Hkv, D]."""
+    Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None]
+    K = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None]
+    V = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None]
+    m = None if attn_mask is None else torch.from_numpy(attn_mask)
+    o = F.scaled_dot_product_attention(Q, K, V, attn_mask=m, is_causal=is_causal, scale=scale,
+                                       enable_gqa=enable_gqa)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------
+# check functions (each raises AssertionError on mismatch)
+# ----------------------------------------------------------------------------
+
+def check_default_scale(A):
+    g = _golden("flex_lowering_args.json")
+    E = g["query_shape_BHLE"][-1]
+    assert A.default_scale(E) == g["scale"]
+
+
+def check_cu_seqlens_golden(A):
+    for case in _golden("cu_seqlens_examples.json")["cases"]:
+        got = A.cu_seqlens(case["lens"])
+        assert got.dtype == np.int32
+        assert got.tolist() == case["cu"], (case, got)
+
+
+def check_cu_seqlens_cumsum(A):
+    rng = np.random.default_rng(7)
+    for n in (1, 2, 17, 300):
+        lens = rng.integers(0, 5000, n)
+        ref = np.concatenate([[0], np.cumsum(lens)])
+        assert np.array_equal(A.cu_seqlens(lens), ref)
+
+
+def check_reshape_and_cache_golden(A):
+    g = _golden("reshape_and_cache_example.json")
+    bs, nb = g["block_size"], g["num_blocks"]
+    table = np.asarray(g["block_table"], dtype=np.int32)
+    kv_lens, new_lens = g["kv_lens"], g["new_lens"]
+    vals = np.asarray(g["new_token_values"], dtype=np.int64)
+    k_new = vals.reshape(-1, 1, 1)
+    cache = np.full((nb, bs, 1, 1), g["untouched_value"], dtype=np.int64)
+    cu_new = np.concatenate([[0], np.cumsum(new_lens)])
+    cu_kv = np.concatenate([[0], np.cumsum(kv_lens)])
+    kc, vc = A.reshape_and_cache(k_new, -k_new, cache, cache, table, cu_new, cu_kv, bs)
+    exp = np.asarray(g["expected_cache"], dtype=np.int64)
+    assert np.array_equal(kc[:, :, 0, 0], exp), kc[:, :, 0, 0]
+    expv = np.where(exp == g["untouched_value"], exp, -exp)
+    assert np.array_equal(vc[:, :, 0, 0], expv)
+
+
+def check_reshape_gather_roundtrip(A):
+    """Scatter then gather returns the new tokens bit for bit; other slots keep their poison."""
+    rng = np.random.default_rng(11)
+    bs, hkv, d = 4, 2, 3
+    kv_lens = np.array([5, 0, 9, 4])
+    new_lens = np.array([2, 0, 9, 1])
+    need = [(n + bs - 1) // bs for n in kv_lens]
+    nb = sum(need) + 2
+    perm = rng.permutation(nb)
+    table = np.full((4, max(need)), nb - 1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    poison = np.int64(-(2**40))
+    cache = np.full((nb, bs, hkv, d), poison, dtype=np.int64)
+    total_new = int(new_lens.sum())
+    k_new = rng.integers(0, 2**30, (total_new, hkv, d))
+    v_new = rng.integers(0, 2**30, (total_new, hkv, d))
+    cu_new = np.concatenate([[0], np.cumsum(new_lens)])
+    cu_kv = np.concatenate([[0], np.cumsum(kv_lens)])
+    kc, vc = A.reshape_and_cache(k_new, v_new, cache, cache, table, cu_new, cu_kv, bs)
+    written = 0
+    for b in range(4):
+        gk = A.gather_paged(kc, table[b], int(kv_lens[b]), bs)
+        gv = A.gather_paged(vc, table[b], int(kv_lens[b]), bs)
+        n, L = int(new_lens[b]), int(kv_lens[b])
+        assert np.array_equal(gk[L - n:], k_new[cu_new[b]:cu_new[b + 1]])
+        assert np.array_equal(gv[L - n:], v_new[cu_new[b]:cu_new[b + 1]])
+        assert np.all(gk[:L - n] == poison)
+        written += n
+    assert int(np.sum(kc != poison)) == written * hkv * d
+
+
+def check_gather_identity_and_permutation(A):
+    """Identity placement equals the packed layout; any placement gathers the same tokens."""
+    rng = np.random.default_rng(3)
+    bs, hkv, d, L = 4, 2, 3, 13
+    packed = _rand(rng, L, hkv, d)
+    nb = (L + bs - 1) // bs
+    cache = np.full((nb, bs, hkv, d), np.nan)
+    for j in range(L):
+        cache[j // bs, j % bs] = packed[j]
+    ident = np.arange(nb)
+    assert np.array_equal(A.gather_paged(cache, ident, L, bs), packed)
+    perm = rng.permutation(nb)
+    cache2 = np.full_like(cache, np.nan)
+    cache2[perm] = cache
+    assert np.array_equal(A.gather_paged(cache2, perm, L, bs), packed)
+
+
+def check_visibility_page_predicate(A):
+    g = _golden("causal_mask_predicate.json")
+    L = g["shape_BHLE"][2]
+    vis = A.visibility(L, L, ORC.MASK_CAUSAL)
+    brute = np.array([[q_idx >= kv_idx for kv_idx in range(L)] for q_idx in range(L)])
+    assert np.array_equal(vis, brute)
+    assert int(vis.sum()) == g["visible_pairs_per_head"]
+
+
+def check_visibility_closed_forms(A):
+    # bottom-right causal with q_len != kv_len is a shifted lower triangle
+    for q_len, kv_len in ((5, 9), (9, 5), (1, 7), (7, 7), (3, 0)):
+        vis = A.visibility(q_len, kv_len, ORC.MASK_CAUSAL)
+        assert np.array_equal(vis, np.tril(np.ones((q_len, kv_len), bool), k=kv_len - q_len))
+    # PATCH with patch index = byte index and equal lengths is causal
+    n = 11
+    assert np.array_equal(A.visibility(n, n, ORC.MASK_PATCH, np.arange(n)),
+                          np.tril(np.ones((n, n), bool)))
+    # PATCH: each byte sees keys 0..patch(byte)
+    pid = np.array([0, 0, 1, 1, 1, 2, 4, 4])
+    vis = A.visibility(len(pid), 6, ORC.MASK_PATCH, pid)
+    assert vis.sum(axis=1).tolist() == [1, 1, 2, 2, 2, 3, 5, 5]
+    # DOCUMENT is block diagonal over runs of equal ids
+    docs = np.array([0, 0, 0, 1, 1, 2, 2, 2, 2])
+    blocks = [np.ones((3, 3)), np.ones((2, 2)), np.ones((4, 4))]
+    bd = np.zeros((9, 9), bool)
+    o = 0
+    for blk in blocks:
+        n_ = blk.shape[0]
+        bd[o:o + n_, o:o + n_] = True
+        o += n_
+    assert np.array_equal(A.visibility(9, 9, ORC.MASK_DOCUMENT, docs, docs), bd)
+    assert np.array_equal(A.visibility(9, 9, ORC.MASK_DOCUMENT | ORC.MASK_CAUSAL, docs, docs),
+                          bd & np.tril(np.ones((9, 9), bool)))
+
+
+def check_two_key_golden(A):
+    g = _golden("two_key_example.json")
+    q = np.asarray(g["q"])[:, None, :]
+    k = np.asarray(g["k"])[:, None, :]
+    v = np.asarray(g["v"])[:, None, :]
+    out, lse = A.attention_varlen(q, k, v, [0, 1], [0, 2], g["scale"])
+    assert np.allclose(out[0, 0], g["out"], rtol=0, atol=1e-15), out
+    assert abs(lse[0, 0] - g["lse"]) < 1e-15
+
+
+def check_dense_vs_sdpa(A):
+    """Dense single sequence, no GQA: causal and full, against torch SDPA fp64."""
+    rng = np.random.default_rng(5)
+    L, H, D = 23, 3, 8
+    q, k, v = _rand(rng, L, H, D), _rand(rng, L, H, D), _rand(rng, L, H, D)
+    for flags, causal in ((0, False), (ORC.MASK_CAUSAL, True)):
+        out, _ = A.attention_varlen(q, k, v, [0, L], [0, L], 0.37, flags)
+        ref = _sdpa(q, k, v, 0.37, is_causal=causal)
+        assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_gqa_vs_sdpa(A):
+    rng = np.random.default_rng(6)
+    L, HQ, HKV, D = 17, 8, 2, 4
+    q, k, v = _rand(rng, L, HQ, D), _rand(rng, L, HKV, D), _rand(rng, L, HKV, D)
+    out, _ = A.attention_varlen(q, k, v, [0, L], [0, L], 0.5, ORC.MASK_CAUSAL)
+    ref = _sdpa(q, k, v, 0.5, is_causal=True, enable_gqa=True)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+    # explicit expansion gives the same answer through the oracle itself
+    kx = np.repeat(k, HQ // HKV, axis=1)
+    vx = np.repeat(v, HQ // HKV, axis=1)
+    out2, _ = A.attention_varlen(q, kx, vx, [0, L], [0, L], 0.5, ORC.MASK_CAUSAL)
+    assert np.allclose(out, out2, rtol=1e-13, atol=1e-13)
+
+
+def check_varlen_bottom_right_vs_sdpa(A):
+    """Packed varlen with q_len != kv_len: each sequence equals SDPA with the shifted-tril mask."""
+    rng = np.random.default_rng(8)
+    q_lens, kv_lens = [3, 7, 1, 6], [8, 7, 5, 6]
+    HQ, HKV, D = 4, 2, 5
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)])
+    cu_k = np.concatenate([[0], np.cumsum(kv_lens)])
+    q = _rand(rng, cu_q[-1], HQ, D)
+    k = _rand(rng, cu_k[-1], HKV, D)
+    v = _rand(rng, cu_k[-1], HKV, D)
+    out, lse = A.attention_varlen(q, k, v, cu_q, cu_k, 0.3, ORC.MASK_CAUSAL)
+    for b in range(4):
+        ql, kl = q_lens[b], kv_lens[b]
+        mask = np.tril(np.ones((ql, kl), bool), k=kl - ql)
+        qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        ref = _sdpa(q[qs], k[ks], v[ks], 0.3, attn_mask=mask, enable_gqa=True)
+        assert np.allclose(out[qs], ref, rtol=1e-12, atol=1e-12), b
+        # LSE against torch.logsumexp of the masked, scaled scores
+        kx = np.repeat(k[ks], HQ // HKV, axis=1)
+        s = 0.3 * np.einsum("ihd,jhd->hij", q[qs], kx)
+        s = np.where(mask[None], s, -np.inf)
+        ref_lse = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy().T
+        assert np.allclose(lse[qs], ref_lse, rtol=1e-12, atol=1e-12), b
+
+
+def check_uniform_scores_mean(A):
+    """scale = 0: every visible key gets the same weight, O = mean of visible V, LSE = ln(count)."""
+    rng = np.random.default_rng(9)
+    L, H, D = 12, 2, 6
+    q, k, v = _rand(rng, L, H, D), _rand(rng, L, H, D), _rand(rng, L, H, D)
+    out, lse = A.attention_varlen(q, k, v, [0, L], [0, L], 0.0, ORC.MASK_CAUSAL)
+    for i in range(L):
+        assert np.allclose(out[i], v[:i + 1].mean(axis=0), rtol=1e-13, atol=1e-13)
+        assert abs(lse[i, 0] - math.log(i + 1)) < 1e-13
+
+
+def check_single_key_rows(A):
+    """Causal row 0 sees only key 0: its output is V[0] exactly."""
+    rng = np.random.default_rng(10)
+    q_lens = [4, 9]
+    cu = np.concatenate([[0], np.cumsum(q_lens)])
+    q, k, v = _rand(rng, 13, 2, 4), _rand(rng, 13, 1, 4), _rand(rng, 13, 1, 4)
+    out, lse = A.attention_varlen(q, k, v, cu, cu, 0.8, ORC.MASK_CAUSAL)
+    for b in range(2):
+        r = cu[b]
+        for h in range(2):
+            assert np.array_equal(out[r, h], v[r, 0])
+            assert math.isclose(lse[r, h], 0.8 * float(q[r, h] @ k[r, 0]), rel_tol=1e-14,
+                                abs_tol=1e-15)
+
+
+def check_shift_invariance(A):
+    """Adding a per-row constant to every score leaves O unchanged and shifts LSE by it."""
+    rng = np.random.default_rng(12)
+    L, H, D = 10, 2, 4
+    q, k, v = _rand(rng, L, H, D), _rand(rng, L, H, D), _rand(rng, L, H, D)
+    c = rng.standard_normal((L, H, 1))
+    q2 = np.concatenate([q, c], axis=2)
+    k2 = np.concatenate([k, np.ones((L, H, 1))], axis=2)
+    out1, lse1 = A.attention_varlen(q, k, v, [0, L], [0, L], 0.6, ORC.MASK_CAUSAL)
+    out2, lse2 = A.attention_varlen(q2, k2, v, [0, L], [0, L], 0.6, ORC.MASK_CAUSAL)
+    assert np.allclose(out1, out2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse2 - lse1, 0.6 * c[:, :, 0], rtol=1e-12, atol=1e-12)
+
+
+def check_fully_masked_rows(A):
+    """No visible key: O = 0 and LSE = -inf, never NaN (empty sequence and unmatched document)."""
+    rng = np.random.default_rng(13)
+    q, k, v = _rand(rng, 5, 1, 3), _rand(rng, 4, 1, 3), _rand(rng, 4, 1, 3)
+    out, lse = A.attention_varlen(q, k, v, [0, 2, 5], [0, 0, 4], 1.0, ORC.MASK_DOCUMENT,
+                                  q_ids=np.array([0, 0, 1, 9, 2]), kv_ids=np.array([1, 1, 2, 2]))
+    assert np.all(out[0:2] == 0) and np.all(np.isneginf(lse[0:2]))   # kv_len = 0
+    assert np.all(out[3] == 0) and np.isneginf(lse[3, 0])              # doc 9 has no key
+    assert np.allclose(out[2], _sdpa(q[2:3], k[0:2], v[0:2], 1.0)[0], rtol=1e-12, atol=1e-12)
+    assert np.allclose(out[4], _sdpa(q[4:5], k[2:4], v[2:4], 1.0)[0], rtol=1e-12, atol=1e-12)
+    assert not np.any(np.isnan(out))
+
+
+def check_paged_equals_packed(A):
+    """Paged attention over a permuted pool equals packed attention on the same tokens."""
+    rng = np.random.default_rng(14)
+    bs, HQ, HKV, D = 4, 4, 2, 3
+    lens = np.array([6, 1, 11])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    k = _rand(rng, cu[-1], HKV, D)
+    v = _rand(rng, cu[-1], HKV, D)
+    q = _rand(rng, cu[-1], HQ, D)
+    need = [(n + bs - 1) // bs for n in lens]
+    nb = sum(need) + 1
+    perm = rng.permutation(nb - 1)
+    table = np.full((3, max(need)), nb - 1, dtype=np.int32)
+    kc = np.full((nb, bs, HKV, D), np.nan)
+    vc = np.full((nb, bs, HKV, D), np.nan)
+    off = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[off:off + n]
+        off += n
+        for j in range(lens[b]):
+            kc[table[b, j // bs], j % bs] = k[cu[b] + j]
+            vc[table[b, j // bs], j % bs] = v[cu[b] + j]
+    out_p, lse_p = A.paged_attention(q, kc, vc, table, cu, cu, bs, 0.4, ORC.MASK_CAUSAL)
+    out_r, lse_r = A.attention_varlen(q, k, v, cu, cu, 0.4, ORC.MASK_CAUSAL)
+    assert np.array_equal(out_p, out_r) and np.array_equal(lse_p, lse_r)
+    assert not np.any(np.isnan(out_p))
+    for b in range(3):
+        L = lens[b]
+        ref = _sdpa(q[cu[b]:cu[b + 1]], k[cu[b]:cu[b + 1]], v[cu[b]:cu[b + 1]], 0.4,
+                    is_causal=True, enable_gqa=True)
+        assert np.allclose(out_p[cu[b]:cu[b + 1]], ref, rtol=1e-12, atol=1e-12), L
+
+
+def check_decode_is_last_causal_row(A):
+    rng = np.random.default_rng(15)
+    bs, HQ, HKV, D = 8, 4, 1, 5
+    lens = np.array([9, 17, 1])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    need = [(n + bs - 1) // bs for n in lens]
+    nb = sum(need)
+    table = np.zeros((3, max(need)), dtype=np.int32)
+    kc = np.zeros((nb, bs, HKV, D))
+    vc = np.zeros((nb, bs, HKV, D))
+    perm = rng.permutation(nb)
+    off = 0
+    k = _rand(rng, cu[-1], HKV, D)
+    v = _rand(rng, cu[-1], HKV, D)
+    for b, n in enumerate(need):
+        table[b, :n] = perm[off:off + n]
+        off += n
+        for j in range(lens[b]):
+            kc[table[b, j // bs], j % bs] = k[cu[b] + j]
+            vc[table[b, j // bs], j % bs] = v[cu[b] + j]
+    q_full = _rand(rng, cu[-1], HQ, D)
+    last = cu[1:] - 1
+    out_d, lse_d = A.paged_decode(q_full[last], kc, vc, table, cu, bs, 0.45)
+    for b in range(3):
+        ref = _sdpa(q_full[cu[b]:cu[b + 1]], k[cu[b]:cu[b + 1]], v[cu[b]:cu[b + 1]], 0.45,
+                    is_causal=True, enable_gqa=True)
+        assert np.allclose(out_d[b], ref[-1], rtol=1e-12, atol=1e-12)
+
+
+def check_e4m3_table(A):
+    codes = np.arange(256, dtype=np.uint8)
+    got = A.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    g = _golden("e4m3_values.json")
+    for code, val in g["values"].items():
+        x = A.e4m3_decode(np.array([int(code, 16)], dtype=np.uint8))[0]
+        assert x == val and np.signbit(x) == np.signbit(val), (code, x, val)
+    for code in g["nan_codes"]:
+        assert np.isnan(A.e4m3_decode(np.array([int(code, 16)], dtype=np.uint8))[0])
+
+
+def check_fp8_attention(A):
+    """fp8: the two-key example through e4m3 codes and descales, and a random case
+    against SDPA on the values torch decodes from the same codes."""
+    # two keys: k0 = 0, k1 = (1,0,...) with descale 1; q = (ln2-ish): use scale = ln 2
+    one, zero = 0x38, 0x00
+    q8 = np.array([[[one, zero, zero, zero]]], dtype=np.uint8)             # q = (1,0,0,0)
+    k8 = np.array([[[zero] * 4], [[one, zero, zero, zero]]], dtype=np.uint8)
+    three = 0x44  # 1.5 * 2^1 = 3
+    v_rows = np.array([[three, zero, zero, zero], [zero, three, zero, zero]], dtype=np.uint8)
+    v8 = v_rows.T[None]                                                      # [1, 4, 2]
+    out, lse = A.fp8_attention(q8, k8, v8, (1.0, 1.0, 1.0), [0, 1], [0, 2], math.log(2.0))
+    assert np.allclose(out[0, 0], [1.0, 2.0, 0.0, 0.0], rtol=0, atol=1e-15)
+    assert abs(lse[0, 0] - math.log(3.0)) < 1e-15
+    # random, descaled, GQA, causal
+    rng = np.random.default_rng(16)
+    L, HQ, HKV, D = 9, 4, 2, 8
+    codes = lambda *s: rng.integers(0, 256, s, dtype=np.uint8) & np.uint8(0xF7)  # no NaN codes
+    q8, k8, vr = codes(L, HQ, D), codes(L, HKV, D), codes(L, HKV, D)
+    ds = (0.5, 0.25, 2.0)
+    v8 = np.ascontiguousarray(vr.transpose(1, 2, 0))
+    out, _ = A.fp8_attention(q8, k8, v8, ds, [0, L], [0, L], 0.1, ORC.MASK_CAUSAL)
+    dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = _sdpa(ds[0] * dec(q8), ds[1] * dec(k8), ds[2] * dec(vr), 0.1, is_causal=True,
+                enable_gqa=True)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]
+
+
+@pytest.mark.parametrize("check", CHECKS, ids=lambda f: f.__name__[len("check_"):])
+def test_oracle_pin(check):
+    check(ORC)
+
+
+def test_pin_status_covers_exports():
+    import oracle
+    for name in ("cu_seqlens", "reshape_and_cache", "gather_paged", "visibility",
+                 "attention_varlen", "paged_attention", "paged_decode", "e4m3_decode",
+                 "fp8_attention", "default_scale"):
+        assert hasattr(oracle, name)
+        assert "pinned" in ORC.PIN_STATUS[name]
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must make at least one check fail
+# ----------------------------------------------------------------------------
+
+def _mut_visibility_off_by_one(orig):
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None):
+        vis = orig(q_len, kv_len, flags & ~ORC.MASK_CAUSAL, q_ids, kv_ids)
+        if flags & ORC.MASK_CAUSAL:
+            i = np.arange(q_len)[:, None]
+            j = np.arange(kv_len)[None, :]
+            vis &= j < i + (kv_len - q_len)
+        return vis
+    return f
+
+
+def _mut_visibility_top_left(orig):
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None):
+        vis = orig(q_len, kv_len, flags & ~ORC.MASK_CAUSAL, q_ids, kv_ids)
+        if flags & ORC.MASK_CAUSAL:
+            vis &= np.arange(kv_len)[None, :] <= np.arange(q_len)[:, None]
+        return vis
+    return f
+
+
+def _mut_visibility_patch_strict(orig):
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None):
+        vis = orig(q_len, kv_len, flags, q_ids, kv_ids)
+        if flags & ORC.MASK_PATCH:
+            vis &= np.arange(kv_len)[None, :] < np.asarray(q_ids)[:q_len, None]
+        return vis
+    return f
+
+
+def _mut_attention_scale_dropped(orig):
+    def f(q, k, v, cu_q, cu_kv, scale, *a, **kw):
+        return orig(q, k, v, cu_q, cu_kv, 1.0, *a, **kw)
+    return f
+
+
+def _mut_attention_gqa_modulo(orig):
+    # q head h reads kv head h % Hkv instead of h // G: permute the q heads going in and out
+    def f(q, k, v, cu_q, cu_kv, scale, *a, **kw):
+        q = np.asarray(q, dtype=np.float64)
+        hq, hkv = q.shape[1], np.asarray(k).shape[1]
+        g = hq // hkv
+        perm = np.array([(h % hkv) * g + h // hkv for h in range(hq)])
+        out, lse = orig(q[:, perm], k, v, cu_q, cu_kv, scale, *a, **kw)
+        inv = np.argsort(perm)
+        return out[:, inv], lse[:, inv]
+    return f
+
+
+def _mut_softmax_no_normalise(orig):
+    def f(s, vis, v):
+        out, lse = orig(s, vis, v)
+        counts = vis.sum(axis=1)
+        return out * np.maximum(counts, 1)[:, None], lse
+    return f
+
+
+def _mut_softmax_log2_lse(orig):
+    def f(s, vis, v):
+        out, lse = orig(s, vis, v)
+        return out, lse / math.log(2.0)
+    return f
+
+
+def _mut_softmax_kv_swapped(orig):
+    def f(s, vis, v):
+        return orig(s.T[:s.shape[0]] if s.shape[0] == s.shape[1] else s * 0.5, vis, v)
+    return f
+
+
+def _mut_gather_slot_reversed(orig):
+    def f(cache, table_row, kv_len, block_size):
+        out = np.empty((kv_len,) + tuple(cache.shape[2:]), dtype=cache.dtype)
+        for j in range(kv_len):
+            out[j] = cache[int(table_row[j // block_size]), block_size - 1 - j % block_size]
+        return out
+    return f
+
+
+def _mut_reshape_from_start(orig):
+    def f(k_new, v_new, k_cache, v_cache, table, cu_new, cu_kv, bs):
+        return orig(k_new, v_new, k_cache, v_cache, table, cu_new, cu_new, bs)
+    return f
+
+
+def _mut_e4m3_bias8(orig):
+    def f(codes):
+        return orig(codes) * 0.5
+    return f
+
+
+def _mut_cu_inclusive(orig):
+    def f(lens):
+        out = orig(lens)
+        return np.concatenate([out[1:], out[-1:]]).astype(np.int32)
+    return f
+
+
+def _mut_fp8_v_rowmajor(orig):
+    def f(q8, k8, v8, descale, *a, **kw):
+        h, d, t = v8.shape
+        return orig(q8, k8, np.ascontiguousarray(v8).reshape(h, t, d).transpose(0, 2, 1), descale,
+                    *a, **kw)
+    return f
+
+
+def _mut_default_scale_inverse(orig):
+    return lambda e: math.sqrt(e)
+
+
+MUTATIONS = {
+    "causal_off_by_one": ("visibility", _mut_visibility_off_by_one),
+    "causal_top_left": ("visibility", _mut_visibility_top_left),
+    "patch_strict": ("visibility", _mut_visibility_patch_strict),
+    "scale_dropped": ("attention_varlen", _mut_attention_scale_dropped),
+    "gqa_modulo_map": ("attention_varlen", _mut_attention_gqa_modulo),
+    "no_normalisation": ("_softmax_rows", _mut_softmax_no_normalise),
+    "lse_in_log2": ("_softmax_rows", _mut_softmax_log2_lse),
+    "scores_perturbed": ("_softmax_rows", _mut_softmax_kv_swapped),
+    "gather_slot_reversed": ("gather_paged", _mut_gather_slot_reversed),
+    "reshape_positions_from_start": ("reshape_and_cache", _mut_reshape_from_start),
+    "e4m3_wrong_bias": ("e4m3_decode", _mut_e4m3_bias8),
+    "cu_seqlens_inclusive": ("cu_seqlens", _mut_cu_inclusive),
+    "fp8_v_read_row_major": ("fp8_attention", _mut_fp8_v_rowmajor),
+    "default_scale_inverted": ("default_scale", _mut_default_scale_inverse),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes(name, monkeypatch):
+    attr, make = MUTATIONS[name]
+    monkeypatch.setattr(ORC, attr, make(getattr(ORC, attr)))
+    caught = []
+    for check in CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(ORC)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(check.__name__)
+    assert caught, f"planted mistake {name} passed every pin"

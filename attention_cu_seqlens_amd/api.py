@@ -1,0 +1,197 @@
+"""torch-facing wrappers of the C ABI: argument marshalling only.
+
+Each function checks that the tensors are contiguous device tensors of the
+expected dtype, reads sizes from their shapes, allocates outputs with torch
+when the caller gives none, and calls the C entry point of the same name on
+torch's current stream.  Every step of the computation runs in the HIP
+kernels; nothing here computes on the CPU.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16}
+
+
+def library_path():
+    return _lib.LIB_PATH
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _u8(t):
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def attn_cu_seqlens(seqlens, out=None):
+    """int32 [batch] lengths -> int32 [batch + 1] cumulative lengths (device)."""
+    _need(seqlens, "seqlens", torch.int32)
+    batch = seqlens.numel()
+    if out is None:
+        out = torch.zeros(batch + 1, dtype=torch.int32, device=seqlens.device)
+    _need(out, "out", torch.int32, seqlens.device)
+    if out.numel() != batch + 1:
+        raise ValueError("out must hold batch + 1 elements")
+    lib = _lib.load()
+    with torch.cuda.device(seqlens.device):
+        _lib.check("attn_cu_seqlens",
+                   lib.attn_cu_seqlens(_ptr(seqlens), _ptr(out), batch, _stream(seqlens.device)))
+    return out
+
+
+def attn_reshape_and_cache(k, v, k_cache, v_cache, block_table, cu_seqlens_new, cu_seqlens_kv):
+    """Write k, v [total_new, Hkv, D] into the paged caches [NB, bs, Hkv, D] in place."""
+    dev = k.device
+    for name, t in (("k", k), ("v", v), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, device=dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_new", cu_seqlens_new),
+                    ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    if not (k.dtype == v.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("k, v and the caches must share a dtype")
+    dtype = _DT.get(k.dtype, _lib.ATTN_FP8_E4M3 if k.element_size() == 1 else None)
+    if dtype is None:
+        raise TypeError(f"unsupported dtype {k.dtype}")
+    total_new, hkv, d = k.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[1]
+    if tuple(k_cache.shape[2:]) != (hkv, d) or v_cache.shape != k_cache.shape or v.shape != k.shape:
+        raise ValueError("cache / token shapes disagree")
+    batch = cu_seqlens_new.numel() - 1
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_reshape_and_cache", lib.attn_reshape_and_cache(
+            _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            block_table.shape[1], _ptr(cu_seqlens_new), _ptr(cu_seqlens_kv), batch, total_new,
+            hkv, d, bs, nb, dtype, _stream(dev)))
+
+
+def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seqlens_kv,
+                           max_seqlen_q, max_seqlen_kv, scale=None, mask_flags=0, q_ids=None,
+                           kv_ids=None, out=None, return_lse=False):
+    """Paged varlen attention; returns out (and lse [total_q, Hq] fp32 if asked)."""
+    dev = q.device
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype, dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    for name, t in (("q_ids", q_ids), ("kv_ids", kv_ids)):
+        if t is not None:
+            _need(t, name, torch.int32, dev)
+    total_q, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    if dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes disagree with q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    batch = cu_seqlens_q.numel() - 1
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_paged_prefill_fwd", lib.attn_paged_prefill_fwd(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+            _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), batch, total_q, int(max_seqlen_q),
+            int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale), int(mask_flags), _ptr(q_ids),
+            _ptr(kv_ids), _DT[q.dtype], _ptr(out), _ptr(lse), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def attn_paged_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_size, max_seqlen_kv,
+                                      split_tokens=0):
+    return int(_lib.load().attn_paged_decode_workspace_bytes(
+        batch, num_heads, num_kv_heads, head_size, int(max_seqlen_kv), int(split_tokens)))
+
+
+def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_seqlen_kv,
+                          scale=None, split_tokens=0, out=None, return_lse=False, workspace=None):
+    """One query per sequence (q [batch, Hq, D]) against the paged cache."""
+    dev = q.device
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype, dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    batch, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_paged_decode_workspace_bytes(batch, hq, hkv, d, max_seqlen_kv, split_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_paged_decode_fwd", lib.attn_paged_decode_fwd(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+            _ptr(cu_seqlens_kv), batch, int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale),
+            int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel(), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
+                 max_seqlen_kv, scale=None, mask_flags=0, q_ids=None, kv_ids=None, out=None,
+                 return_lse=False):
+    """fp8 e4m3 attention: q8 [total_q, Hq, D], k8 [total_kv, Hkv, D],
+    v8_colmajor [Hkv, D, total_kv] (uint8 codes or float8_e4m3fn), descale fp32 [3]."""
+    dev = q8.device
+    q8, k8, v8 = _u8(q8), _u8(k8), _u8(v8_colmajor)
+    for name, t in (("q8", q8), ("k8", k8), ("v8_colmajor", v8)):
+        _need(t, name, torch.uint8, dev)
+    _need(descale, "descale", torch.float32, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    for name, t in (("q_ids", q_ids), ("kv_ids", kv_ids)):
+        if t is not None:
+            _need(t, name, torch.int32, dev)
+    total_q, hq, d = q8.shape
+    total_kv, hkv, _ = k8.shape
+    if tuple(v8.shape) != (hkv, d, total_kv):
+        raise ValueError("v8_colmajor must be [Hkv, D, total_kv]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((total_q, hq, d), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, dev)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    batch = cu_seqlens_q.numel() - 1
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_fp8_fwd", lib.attn_fp8_fwd(
+            _ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
+            batch, total_q, total_kv, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d,
+            float(scale), int(mask_flags), _ptr(q_ids), _ptr(kv_ids), _ptr(out), _ptr(lse),
+            _stream(dev)))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,287 @@
+// C ABI of the attention library: host-side argument checks, a cached gfx950
+// device check and launch planning.  No entry point allocates, frees,
+// synchronises or copies device memory to the host.
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/attn_cu_seqlens.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+attn_status check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known == 1) return ATTN_OK;
+        if (known == 2) return ATTN_ERR_UNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? ATTN_OK : ATTN_ERR_UNSUPPORTED;
+}
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+// Largest power of two dividing g, at most 8: how many query heads of one
+// GQA group share a workgroup's rows.
+int pack_log2_for_group(int g) {
+    int r = 0;
+    while (r < 3 && (g % (2 << r)) == 0) ++r;
+    return r;
+}
+
+attn_status check_mask(uint32_t mask, const int32_t* q_ids, const int32_t* kv_ids) {
+    if (mask & ~(ATTN_MASK_CAUSAL | ATTN_MASK_DOCUMENT | ATTN_MASK_PATCH))
+        return ATTN_ERR_UNSUPPORTED;
+    if ((mask & ATTN_MASK_DOCUMENT) && (mask & ATTN_MASK_PATCH)) return ATTN_ERR_UNSUPPORTED;
+    if ((mask & ATTN_MASK_DOCUMENT) && (q_ids == nullptr || kv_ids == nullptr))
+        return ATTN_ERR_NULL_ARG;
+    if ((mask & ATTN_MASK_PATCH) && q_ids == nullptr) return ATTN_ERR_NULL_ARG;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_status_string(attn_status status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL_ARG: return "a required pointer is NULL";
+        case ATTN_ERR_BAD_SHAPE: return "sizes are inconsistent or out of range";
+        case ATTN_ERR_UNSUPPORTED: return "unsupported dtype, head size, mask or device";
+        case ATTN_ERR_DEVICE: return "HIP could not report the current device";
+        case ATTN_ERR_LAUNCH: return "kernel launch failed";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+attn_status attn_cu_seqlens(const int32_t* seqlens, int32_t* cu_seqlens, int32_t batch,
+                            void* stream) {
+    if (batch < 0) return ATTN_ERR_BAD_SHAPE;
+    if (seqlens == nullptr || cu_seqlens == nullptr) return ATTN_ERR_NULL_ARG;
+    if (batch == 0) return ATTN_OK;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+    return from_hip(attn::launch_cu_seqlens(seqlens, cu_seqlens, batch,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* cu_seqlens_new, const int32_t* cu_seqlens_kv,
+                                   int32_t batch, int32_t total_new, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   attn_dtype dtype, void* stream) {
+    int esize;
+    switch (dtype) {
+        case ATTN_F16:
+        case ATTN_BF16: esize = 2; break;
+        case ATTN_FP8_E4M3: esize = 1; break;
+        default: return ATTN_ERR_UNSUPPORTED;
+    }
+    if (batch < 0 || total_new < 0) return ATTN_ERR_BAD_SHAPE;
+    if (num_kv_heads <= 0 || head_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (!is_pow2(block_size)) return ATTN_ERR_BAD_SHAPE;
+    const int64_t row_bytes = (int64_t)num_kv_heads * head_size * esize;
+    if (row_bytes % 16 != 0 || row_bytes > (1 << 24)) return ATTN_ERR_BAD_SHAPE;
+    if (k == nullptr || v == nullptr || k_cache == nullptr || v_cache == nullptr ||
+        block_table == nullptr || cu_seqlens_new == nullptr || cu_seqlens_kv == nullptr)
+        return ATTN_ERR_NULL_ARG;
+    if (batch == 0 || total_new == 0) return ATTN_OK;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+    return from_hip(attn::launch_reshape_and_cache(
+        k, v, k_cache, v_cache, block_table, max_blocks_per_seq, cu_seqlens_new, cu_seqlens_kv,
+        batch, total_new, (int)row_bytes, ilog2(block_size), static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                   int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   float scale, uint32_t mask_flags, const int32_t* q_ids,
+                                   const int32_t* kv_ids, attn_dtype dtype, void* out, float* lse,
+                                   void* stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
+    if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0) return ATTN_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size < max_seqlen_kv) return ATTN_ERR_BAD_SHAPE;
+    if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+    const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
+    if (m != ATTN_OK) return m;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+        cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || out == nullptr)
+        return ATTN_ERR_NULL_ARG;
+    if (batch == 0 || total_q == 0) return ATTN_OK;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+
+    attn::PrefillParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k_cache = static_cast<const uint16_t*>(k_cache);
+    p.v_cache = static_cast<const uint16_t*>(v_cache);
+    p.block_table = block_table;
+    p.cu_q = cu_seqlens_q;
+    p.cu_kv = cu_seqlens_kv;
+    p.q_ids = q_ids;
+    p.kv_ids = kv_ids;
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.mbps = max_blocks_per_seq;
+    p.batch = batch;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.pack_log2 = pack_log2_for_group(p.group);
+    p.n_head_groups = num_heads >> p.pack_log2;
+    p.bs_log2 = ilog2(block_size);
+    p.mask = mask_flags;
+    p.c = scale * 1.4426950408889634f;
+    return from_hip(attn::launch_paged_prefill(p, head_size, dtype == ATTN_BF16, max_seqlen_q,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_size, int32_t max_seqlen_kv,
+                                         int32_t split_tokens) {
+    if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_seqlen_kv < 0)
+        return 0;
+    if (split_tokens < 0 || split_tokens % 256 != 0) return 0;
+    const int st = attn::decode_split_tokens(batch, num_kv_heads, max_seqlen_kv, split_tokens);
+    return attn::decode_workspace_bytes(batch, num_heads, head_size, max_seqlen_kv, st);
+}
+
+attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_seqlens_kv, int32_t batch,
+                                  int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                  float scale, int32_t split_tokens, attn_dtype dtype, void* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
+    if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
+    if (batch < 0 || max_seqlen_kv < 0) return ATTN_ERR_BAD_SHAPE;
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (num_heads / num_kv_heads > 32) return ATTN_ERR_UNSUPPORTED;
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0) return ATTN_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size < max_seqlen_kv) return ATTN_ERR_BAD_SHAPE;
+    if (split_tokens < 0 || split_tokens % 256 != 0) return ATTN_ERR_BAD_SHAPE;
+    if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+    if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+        cu_seqlens_kv == nullptr || out == nullptr)
+        return ATTN_ERR_NULL_ARG;
+    if (batch == 0) return ATTN_OK;
+    const int st = attn::decode_split_tokens(batch, num_kv_heads, max_seqlen_kv, split_tokens);
+    const size_t need = attn::decode_workspace_bytes(batch, num_heads, head_size, max_seqlen_kv, st);
+    if (workspace == nullptr || workspace_bytes < need ||
+        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return ATTN_ERR_WORKSPACE;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+
+    attn::DecodeParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k_cache = static_cast<const uint16_t*>(k_cache);
+    p.v_cache = static_cast<const uint16_t*>(v_cache);
+    p.block_table = block_table;
+    p.cu_kv = cu_seqlens_kv;
+    p.max_splits = max_seqlen_kv > 0 ? (max_seqlen_kv + st - 1) / st : 1;
+    const int64_t rows = (int64_t)batch * num_heads * p.max_splits;
+    const int64_t o_bytes = ((rows * head_size * 4 + 255) / 256) * 256;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    p.out = static_cast<uint16_t*>(out);
+    p.lse = lse;
+    p.mbps = max_blocks_per_seq;
+    p.batch = batch;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.bs_log2 = ilog2(block_size);
+    p.split_tokens = st;
+    p.c = scale * 1.4426950408889634f;
+    return from_hip(attn::launch_paged_decode(p, head_size, dtype == ATTN_BF16,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor,
+                         const float* descale_qkv, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, int32_t batch, int32_t total_q,
+                         int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size, float scale,
+                         uint32_t mask_flags, const int32_t* q_ids, const int32_t* kv_ids,
+                         void* out_bf16, float* lse, void* stream) {
+    if (head_size != 128) return ATTN_ERR_UNSUPPORTED;
+    if (batch < 0 || total_q < 0 || total_kv < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+    const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
+    if (m != ATTN_OK) return m;
+    if (q8 == nullptr || k8 == nullptr || v8_colmajor == nullptr || descale_qkv == nullptr ||
+        cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || out_bf16 == nullptr)
+        return ATTN_ERR_NULL_ARG;
+    if (batch == 0 || total_q == 0) return ATTN_OK;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+
+    attn::Fp8Params p{};
+    p.q = static_cast<const uint8_t*>(q8);
+    p.k = static_cast<const uint8_t*>(k8);
+    p.vt = static_cast<const uint8_t*>(v8_colmajor);
+    p.descale = descale_qkv;
+    p.cu_q = cu_seqlens_q;
+    p.cu_kv = cu_seqlens_kv;
+    p.q_ids = q_ids;
+    p.kv_ids = kv_ids;
+    p.out = static_cast<uint16_t*>(out_bf16);
+    p.lse = lse;
+    p.batch = batch;
+    p.total_kv = total_kv;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.pack_log2 = pack_log2_for_group(p.group);
+    p.n_head_groups = num_heads >> p.pack_log2;
+    p.mask = mask_flags;
+    p.scale = scale;
+    return from_hip(attn::launch_fp8_prefill(p, head_size, max_seqlen_q,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

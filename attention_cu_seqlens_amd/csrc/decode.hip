@@ -1,0 +1,209 @@
+// Paged GQA decode (one query token per sequence) for 16-bit dtypes on gfx950.
+//
+// Split-KV: workgroup (sequence b, kv head hk, split s) streams keys
+// [s*split_tokens, (s+1)*split_tokens) of the paged cache.  Its NW waves take
+// interleaved 32-key blocks of each BN = 32*NW key tile, each with its own
+// online-softmax state for the G = Hq/Hkv query heads of the group (the 32
+// query columns of the MFMA, G of them live).  The waves merge in LDS at the
+// end and the workgroup writes one partial (unnormalised O, running max m,
+// sum l) per query head.  A second kernel merges the splits with the same
+// logsumexp rule; its LSE output is the "OUTPUT_LOGSUMEXP" quantity of the
+// FlexAttention kernel options shown in the blt issue "Cross Attention does
+// not work on CPU and older GPUs".
+//
+// The grid is sized from max_seqlen_kv on the host (no device->host sync);
+// splits past a sequence's end exit at once and the merge kernel derives
+// each sequence's split count from its own length.
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace attn {
+
+template <int D, int NW, bool BF16>
+__global__ __launch_bounds__(NW * 64) void k_paged_decode(DecodeParams p) {
+    constexpr int NT = NW * 64;
+    constexpr int BN = NW * 32;
+    using Tile = PagedTile16<D, BN, NT>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    int u = blockIdx.x;
+    const int s = u % p.max_splits;
+    u /= p.max_splits;
+    const int hk = u % p.num_kv_heads;
+    const int b = u / p.num_kv_heads;
+    const int kv_start = p.cu_kv[b];
+    const int kv_len = p.cu_kv[b + 1] - kv_start;
+    const int k0 = s * p.split_tokens;
+    if (k0 >= kv_len) return;
+    const int k1 = min(kv_len, k0 + p.split_tokens);
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id(), w = wave_id();
+    const int col = lane & 31, g = lane >> 5;
+    const int G = p.group;
+    const bool valid = col < G;
+    const int head = hk * G + col;
+
+    RowsState<D, 1> st;
+    st.init();
+    {
+        const uint16_t* qp = p.q + ((int64_t)b * p.num_heads + head) * D + 8 * g;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            u32x4_t v = {0u, 0u, 0u, 0u};
+            if (valid) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
+            st.q[0][t] = v;
+        }
+    }
+    st.lo[0] = 0;
+    st.hi[0] = k1;
+
+    const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+    const int tok_stride = p.num_kv_heads * D;
+    const int head_off = hk * D;
+    const int n_tiles = (k1 - k0 + BN - 1) / BN;
+
+    Tile ld;
+    ld.load(p.k_cache, p.v_cache, table, k0, k1, p.bs_log2, tok_stride, head_off, tid);
+    ld.store(smem, tid);
+    __syncthreads();
+    for (int it = 0; it < n_tiles; ++it) {
+        const int j = k0 + it * BN;
+        const bool has_next = it + 1 < n_tiles;
+        if (has_next)
+            ld.load(p.k_cache, p.v_cache, table, j + BN, k1, p.bs_log2, tok_stride, head_off,
+                    tid);
+        const int kb_start = j + 32 * w;
+        if (kb_start < k1) {
+            if (kb_start + 32 <= k1)
+                tile_step<D, BN, 1, 1, BF16, false>(st, smem, j, w, p.c);
+            else
+                tile_step<D, BN, 1, 1, BF16, true>(st, smem, j, w, p.c);
+        }
+        __syncthreads();
+        if (has_next) {
+            ld.store(smem, tid);
+            __syncthreads();
+        }
+    }
+
+    // merge the NW wave states of this split
+    float* red_o = reinterpret_cast<float*>(smem);   // [NW][G][D]
+    float* red_m = red_o + NW * G * D;               // [NW][G]
+    float* red_l = red_m + NW * G;
+    if (valid) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int d = db * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                red_o[(w * G + col) * D + d] = st.o[db][0][r];
+            }
+        if (g == 0) {
+            red_m[w * G + col] = st.m[0];
+            red_l[w * G + col] = st.l[0];
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += NT) {
+        const int c = idx / D, d = idx % D;
+        float mstar = kNegInf;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) mstar = fmaxf(mstar, red_m[i * G + c]);
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const float mi = red_m[i * G + c];
+            const float wgt = (mi == kNegInf) ? 0.f : fast_exp2(mi - mstar);
+            lsum += red_l[i * G + c] * wgt;
+            osum += red_o[(i * G + c) * D + d] * wgt;
+        }
+        const int64_t slot = ((int64_t)b * p.num_heads + hk * G + c) * p.max_splits + s;
+        p.part_o[slot * D + d] = osum;
+        if (d == 0) {
+            p.part_ml[slot * 2 + 0] = mstar;
+            p.part_ml[slot * 2 + 1] = lsum;
+        }
+    }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
+    const int bh = blockIdx.x;
+    const int b = bh / p.num_heads;
+    const int kv_len = p.cu_kv[b + 1] - p.cu_kv[b];
+    const int n_s = (kv_len + p.split_tokens - 1) / p.split_tokens;
+    const int d = threadIdx.x;
+    const int64_t base = (int64_t)bh * p.max_splits;
+    float mstar = kNegInf;
+    for (int s = 0; s < n_s; ++s) mstar = fmaxf(mstar, p.part_ml[(base + s) * 2]);
+    float lsum = 0.f, osum = 0.f;
+    for (int s = 0; s < n_s; ++s) {
+        const float ms = p.part_ml[(base + s) * 2];
+        const float wgt = (ms == kNegInf) ? 0.f : fast_exp2(ms - mstar);
+        lsum += p.part_ml[(base + s) * 2 + 1] * wgt;
+        osum += p.part_o[(base + s) * D + d] * wgt;
+    }
+    const float val = lsum > 0.f ? osum / lsum : 0.f;
+    f32x2_t v2 = {val, 0.f};
+    uint32_t packed;
+    if constexpr (BF16) packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, bf16x2_t));
+    else packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, f16x2_t));
+    p.out[(int64_t)bh * D + d] = (uint16_t)(packed & 0xffffu);
+    if (d == 0 && p.lse != nullptr)
+        p.lse[bh] = lsum > 0.f ? (mstar + __builtin_log2f(lsum)) * kLn2 : kNegInf;
+}
+
+int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested) {
+    if (requested > 0) return requested;
+    const int64_t units = (int64_t)batch * num_kv_heads;
+    int st = 256;
+    while (st < 8192 && units * ((max_seqlen_kv + st - 1) / st) > 8192) st *= 2;
+    return st;
+}
+
+size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_seqlen_kv,
+                              int split_tokens) {
+    const int64_t splits = max_seqlen_kv > 0 ? (max_seqlen_kv + split_tokens - 1) / split_tokens : 1;
+    const int64_t rows = (int64_t)batch * num_heads * splits;
+    const int64_t o_bytes = ((rows * head_size * 4 + 255) / 256) * 256;
+    return (size_t)(o_bytes + rows * 2 * 4);
+}
+
+namespace {
+
+template <int D, int NW, bool BF16>
+hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
+    constexpr int BN = NW * 32;
+    const size_t tile = (size_t)BN * D * 4;
+    const size_t red = (size_t)NW * p.group * (D + 2) * 4;
+    const size_t lds = tile > red ? tile : red;
+    // the largest request over every supported group size (G <= 32)
+    const size_t red_max = (size_t)NW * 32 * (D + 2) * 4;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(tile > red_max ? tile : red_max));
+    if (attr != hipSuccess) return attr;
+    const int64_t grid = (int64_t)p.batch * p.num_kv_heads * p.max_splits;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16>), dim3((unsigned)grid), dim3(NW * 64), lds, s,
+                       p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_decode_combine<D, BF16>), dim3((unsigned)(p.batch * p.num_heads)),
+                       dim3(D), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s) {
+    if (head_size == 128)
+        return bf16 ? launch_decode_cfg<128, 4, true>(p, s) : launch_decode_cfg<128, 4, false>(p, s);
+    if (head_size == 64)
+        return bf16 ? launch_decode_cfg<64, 4, true>(p, s) : launch_decode_cfg<64, 4, false>(p, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

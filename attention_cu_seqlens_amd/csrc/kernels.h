@@ -1,0 +1,99 @@
+// Kernel parameter blocks and launchers (internal; the public ABI is
+// include/attn_cu_seqlens.h).  Launchers return a hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+enum : uint32_t { kMaskCausal = 1u, kMaskDocument = 2u, kMaskPatch = 4u };
+
+// Paged varlen prefill (16-bit dtypes).
+struct PrefillParams {
+    const uint16_t* q;          // [total_q, Hq, D]
+    const uint16_t* k_cache;    // [num_blocks, bs, Hkv, D]
+    const uint16_t* v_cache;
+    const int32_t* block_table; // [batch, mbps]
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    const int32_t* q_ids;
+    const int32_t* kv_ids;
+    uint16_t* out;              // [total_q, Hq, D]
+    float* lse;                 // [total_q, Hq] or null
+    int mbps;
+    int batch;
+    int num_heads;
+    int num_kv_heads;
+    int group;                  // num_heads / num_kv_heads
+    int pack_log2;              // log2 of q heads packed per workgroup
+    int n_head_groups;          // num_heads >> pack_log2
+    int n_qtiles;               // tiles per sequence at max_seqlen_q
+    int bs_log2;
+    uint32_t mask;
+    float c;                    // scale * log2(e)
+};
+
+// Paged decode (16-bit dtypes): split kernel + combine kernel.
+struct DecodeParams {
+    const uint16_t* q;          // [batch, Hq, D]
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* cu_kv;
+    float* part_o;              // [batch*Hq, max_splits, D]
+    float* part_ml;             // [batch*Hq, max_splits, 2]
+    uint16_t* out;              // [batch, Hq, D]
+    float* lse;                 // [batch, Hq] or null
+    int mbps;
+    int batch;
+    int num_heads;
+    int num_kv_heads;
+    int group;
+    int bs_log2;
+    int split_tokens;
+    int max_splits;
+    float c;
+};
+
+// Dense varlen fp8 prefill.
+struct Fp8Params {
+    const uint8_t* q;           // [total_q, Hq, D]
+    const uint8_t* k;           // [total_kv, Hkv, D]
+    const uint8_t* vt;          // [Hkv, D, total_kv]
+    const float* descale;       // [3] device
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    const int32_t* q_ids;
+    const int32_t* kv_ids;
+    uint16_t* out;              // bf16 [total_q, Hq, D]
+    float* lse;
+    int batch;
+    int total_kv;
+    int num_heads;
+    int num_kv_heads;
+    int group;
+    int pack_log2;
+    int n_head_groups;
+    int n_qtiles;
+    uint32_t mask;
+    float scale;
+};
+
+hipError_t launch_cu_seqlens(const int32_t* seqlens, int32_t* cu, int batch, hipStream_t s);
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int32_t* block_table, int mbps, const int32_t* cu_new,
+                                    const int32_t* cu_kv, int batch, int total_new,
+                                    int row_bytes, int bs_log2, hipStream_t s);
+hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16,
+                                int max_seqlen_q, hipStream_t s);
+hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s);
+hipError_t launch_fp8_prefill(const Fp8Params& p, int head_size, int max_seqlen_q, hipStream_t s);
+
+// Decode planning shared by the workspace query and the launch.
+int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested);
+size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_seqlen_kv,
+                              int split_tokens);
+
+}  // namespace attn

@@ -1,0 +1,303 @@
+"""Benchmark of the varlen paged GQA attention hot path on one MI355X.
+
+A step is one pass of the prefill hot path over the varlen workload
+(16 sequences, lengths uniform on [256, 4096] drawn with seed 1002, 32 query
+heads over 8 kv heads, head size 128, block size 16, bf16, causal):
+cu_seqlens of the query and kv lengths, reshape_and_cache of every K/V token
+into a randomly permuted paged pool, then the fused paged prefill.  Inputs are
+resident in HBM before the timed region.  `value` is causal-adjusted
+TFLOP/s of the whole step: 4 * D * Hq * sum_b L_b (L_b + 1) / 2 flops (the
+visible query-key pairs, each needing a D-long dot product and a D-long
+weighted sum) divided by the step time.
+
+The same JSON line carries the prefill kernel's roofline figure, the fp64 CPU
+oracle timed on a bounded sample of the same workload, and three more
+single-GPU measurements: paged decode (HBM GB/s), byte->patch cross attention
+and dense causal fp8 (TFLOP/s).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extra] [--no-cpu]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def causal_pairs(q_lens, kv_lens):
+    tot = 0
+    for ql, kl in zip(q_lens, kv_lens):
+        ql, kl = int(ql), int(kl)
+        off = kl - ql
+        for_rows = np.minimum(np.arange(ql) + off + 1, kl)
+        tot += int(np.clip(for_rows, 0, None).sum())
+    return tot
+
+
+def patch_pairs(w):
+    cu = np.concatenate([[0], np.cumsum(w.q_lens)])
+    tot = 0
+    for b in range(w.batch):
+        pid = w.q_ids[cu[b]:cu[b + 1]].astype(np.int64)
+        tot += int(np.minimum(pid + 1, int(w.kv_lens[b])).sum())
+    return tot
+
+
+def timed(fn, iters, torch):
+    """Mean ms per call measured with events on the current stream."""
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(s)
+    for _ in range(iters):
+        fn()
+    ev[1].record(s)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / iters
+
+
+def i32(a, torch, dev):
+    return torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
+
+
+def paged_inputs(w, A, torch, dev):
+    lens_q = i32(w.q_lens, torch, dev)
+    lens_kv = i32(w.kv_lens, torch, dev)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
+    kc = torch.full(shape, float("nan"), dtype=w.k_new.dtype, device=dev)
+    vc = torch.full(shape, float("nan"), dtype=w.k_new.dtype, device=dev)
+    bt = i32(w.block_table, torch, dev)
+    return lens_q, lens_kv, kc, vc, bt
+
+
+def cpu_baseline(w, n_heads):
+    """The fp64 oracle on sequence 0 of the workload, n_heads query heads."""
+    import oracle as ORC
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        cores = int(max(blas)) if blas else 1
+    except Exception:
+        cores = 1
+    L = int(w.q_lens[0])
+    hkv = w.num_kv_heads
+    g = w.num_heads // hkv
+    q = w.q[:L, :n_heads].double().cpu().numpy()
+    k = w.k_new[:L, :max(1, n_heads // g)].double().cpu().numpy()
+    v = w.v_new[:L, :max(1, n_heads // g)].double().cpu().numpy()
+    bs = w.block_size
+    nblk = (L + bs - 1) // bs
+    kc = np.zeros((nblk, bs) + k.shape[1:])
+    vc = np.zeros_like(kc)
+    table = np.arange(nblk, dtype=np.int32)[None]
+    cu = ORC.cu_seqlens([L])
+    t0 = time.perf_counter()
+    kc, vc = ORC.reshape_and_cache(k, v, kc, vc, table, cu, cu, bs)
+    ORC.paged_attention(q, kc, vc, table, cu, cu, bs, w.scale, w.mask_flags)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.head_size * n_heads * L * (L + 1) / 2
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"sequence 0 (length {L}) x {n_heads} of {w.num_heads} query heads, "
+                      f"cache fill + paged causal attention in fp64 numpy, {dt:.1f} s"}
+
+
+def bench_decode(A, W, torch, dev, iters=20):
+    w = W.paged_gqa_decode_bf16(device=dev)
+    lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
+    cu_kv = A.attn_cu_seqlens(lens_kv)
+    A.attn_reshape_and_cache(w.k_new, w.v_new, kc, vc, bt, cu_kv, cu_kv)
+    del w.k_new, w.v_new
+    maxkv = int(w.kv_lens.max())
+    need = A.attn_paged_decode_workspace_bytes(w.batch, w.num_heads, w.num_kv_heads, w.head_size,
+                                               maxkv)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(w.q)
+
+    def run():
+        A.attn_paged_decode_fwd(w.q, kc, vc, bt, cu_kv, maxkv, scale=w.scale, out=out,
+                                workspace=ws)
+
+    for _ in range(3):
+        run()
+    ms = timed(run, iters, torch)
+    tokens = int(w.kv_lens.sum())
+    used_blocks = int(sum(math.ceil(int(n) / w.block_size) for n in w.kv_lens))
+    nbytes = (2 * tokens * w.num_kv_heads * w.head_size * 2 + 2 * w.q.numel() * 2
+              + used_blocks * 4)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_prefill_generic(A, W, torch, dev, w, flops, iters=20):
+    lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
+    cu_q = A.attn_cu_seqlens(lens_q)
+    cu_kv = A.attn_cu_seqlens(lens_kv)
+    A.attn_reshape_and_cache(w.k_new, w.v_new, kc, vc, bt, cu_kv, cu_kv)
+    q_ids = None if w.q_ids is None else i32(w.q_ids, torch, dev)
+    out = torch.empty_like(w.q)
+
+    def run():
+        A.attn_paged_prefill_fwd(w.q, kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max()),
+                                 int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags,
+                                 q_ids=q_ids, out=out)
+
+    for _ in range(3):
+        run()
+    ms = timed(run, iters, torch)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": flops}
+
+
+def bench_fp8(A, W, torch, dev, iters=20):
+    w = W.dense_causal_fp8(device=dev)
+    cu_q = A.attn_cu_seqlens(i32(w.q_lens, torch, dev))
+    ds = torch.as_tensor(w.descale, dtype=torch.float32, device=dev)
+    out = torch.empty((w.total_q, w.num_heads, w.head_size), dtype=torch.bfloat16, device=dev)
+    flops = 4.0 * w.head_size * w.num_heads * causal_pairs(w.q_lens, w.kv_lens)
+
+    def run():
+        A.attn_fp8_fwd(w.q, w.k_new, w.v8_colmajor, ds, cu_q, cu_q, int(w.q_lens.max()),
+                       int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags, out=out)
+
+    for _ in range(3):
+        run()
+    ms = timed(run, iters, torch)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "flops": flops}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="skip decode / cross / fp8 lines")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this attention hot path has no multi-GPU "
+              "code (each GPU would run its own heads or sequences); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_cu_seqlens_amd as A
+    import workloads as W
+
+    A._lib.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating the varlen prefill workload")
+    w = W.varlen_gqa_causal_bf16(device=dev)
+    lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
+    cu_q = torch.empty(w.batch + 1, dtype=torch.int32, device=dev)
+    cu_kv = torch.empty(w.batch + 1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(w.q)
+    max_q, max_kv = int(w.q_lens.max()), int(w.kv_lens.max())
+    pairs = causal_pairs(w.q_lens, w.kv_lens)
+    flops = 4.0 * w.head_size * w.num_heads * pairs
+    stream = torch.cuda.current_stream()
+    k_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+
+    def step(i=None):
+        A.attn_cu_seqlens(lens_q, out=cu_q)
+        A.attn_cu_seqlens(lens_kv, out=cu_kv)
+        A.attn_reshape_and_cache(w.k_new, w.v_new, kc, vc, bt, cu_kv, cu_kv)
+        if i is not None:
+            k_ev[i][0].record(stream)
+        A.attn_paged_prefill_fwd(w.q, kc, vc, bt, cu_q, cu_kv, max_q, max_kv, scale=w.scale,
+                                 mask_flags=w.mask_flags, out=out)
+        if i is not None:
+            k_ev[i][1].record(stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in k_ev]))
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (k_ms * 1e-3) / 1e12
+    log(f"step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms), prefill kernel {k_ms:.4f} ms")
+
+    line = {
+        "metric": "prefill attn TFLOP/s (causal-adjusted) + decode HBM GB/s, % of MI355X peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "total_tokens": w.total_q,
+                   "max_seqlen": max_q, "num_heads": w.num_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_size": w.head_size,
+                   "block_size": w.block_size, "mask": "causal", "seed": 1002,
+                   "step": "cu_seqlens x2 + reshape_and_cache + paged prefill",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "k_paged_prefill", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(k_ms, 5), "flops_per_launch": flops},
+    }
+    del kc, vc, out
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        log("decode")
+        line["decode"] = bench_decode(A, W, torch, dev)
+        torch.cuda.empty_cache()
+        log("byte->patch cross attention")
+        wc = W.byte_patch_cross_bf16(device=dev)
+        line["cross_attention"] = bench_prefill_generic(
+            A, W, torch, dev, wc, 4.0 * wc.head_size * wc.num_heads * patch_pairs(wc))
+        del wc
+        torch.cuda.empty_cache()
+        log("fp8")
+        line["fp8"] = bench_fp8(A, W, torch, dev)
+
+    if not args.no_cpu:
+        log("cpu oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * attn_cu_seqlens -- varlen, paged, GQA attention forward for AMD MI355X (gfx950).
+ *
+ * C ABI.  Every pointer argument is caller-owned DEVICE memory unless stated
+ * otherwise; the library never allocates, frees, synchronises or copies device
+ * memory to the host.  Each call enqueues its kernels on `stream` (a
+ * hipStream_t; NULL is the default stream) and returns at once.  Argument
+ * checks run on the host before any HIP call; a failed check returns an error
+ * code and launches nothing.  No function aborts the process.
+ *
+ * Conventions shared by all entry points
+ *   - Packed varlen ("BSNH") tensors: token-major, [total_tokens, heads,
+ *     head_size], contiguous.  Sequence b owns tokens cu[b] .. cu[b+1]-1 of a
+ *     cumulative-length array cu[batch+1] with cu[0] = 0 (the cumulative
+ *     seqlens of the onnxruntime PR "[CUDA] PagedAttention: add SM<80 fp16
+ *     fallback via memory-efficient attention", section Implementation,
+ *     steps 1 and 3).
+ *   - Paged K/V cache: [num_blocks, block_size, num_kv_heads, head_size];
+ *     block_table is int32 [batch, max_blocks_per_seq] and maps logical block
+ *     i of sequence b to physical block block_table[b*max_blocks_per_seq + i]
+ *     (same PR, Implementation step 2 and the size formula under "Scratch
+ *     allocation").  Token j of sequence b lives in physical block
+ *     block_table[b][j / block_size] at slot j % block_size.  Entries past
+ *     ceil(kv_len / block_size) are never read; cache slots past kv_len are
+ *     never read into a result (they may hold any bits, NaN included).
+ *   - GQA: query head h reads kv head h / (num_heads / num_kv_heads).
+ *   - Scores are scale * <q, k> (the scale multiplies the product, not q:
+ *     "PRESCALE_QK: False" among the FlexAttention kernel options in the blt
+ *     issue "Cross Attention does not work on CPU and older GPUs").  Callers
+ *     wanting the usual default pass 1/sqrt(head_size) (flex_attention
+ *     docstring in the pytorch commit "[FlexAttention] Enforce Q,K,V memory
+ *     layouts for fp8 flex attention to avoid perf degradation").
+ *   - Masks (mask_flags): ATTN_MASK_CAUSAL keeps key j for query i iff
+ *     j <= i + kv_len - q_len (bottom-right alignment; equals the page's
+ *     q_idx >= kv_idx when lengths match).  ATTN_MASK_DOCUMENT keeps j iff
+ *     q_ids[q] == kv_ids[k] (document ids, non-decreasing within each
+ *     sequence).  ATTN_MASK_PATCH keeps j iff j <= q_ids[q], where q_ids is
+ *     each query byte's patch index within its sequence (non-decreasing) --
+ *     the byte->patch cross-attention of the blt issue.  CAUSAL combines with
+ *     either; DOCUMENT and PATCH are exclusive.  q_ids / kv_ids are indexed by
+ *     global token (q_ids[total_q], kv_ids[total_kv]).
+ *   - A query row with no visible key outputs zeros and LSE = -inf (rows may
+ *     be fully masked: "ROWS_GUARANTEED_SAFE: False" in the same kernel
+ *     options).
+ *   - lse (optional, may be NULL): float32 [total_q, num_heads], natural-log
+ *     logsumexp of the scaled, masked scores ("OUTPUT_LOGSUMEXP: True").
+ *   - Accumulation is fp32 whatever the input dtype; outputs are rounded to
+ *     nearest even.
+ *   - Device-resident metadata (cu_seqlens, block_table, ids) is trusted:
+ *     cu arrays must be non-decreasing with cu[batch] equal to the stated
+ *     total, used table entries must lie in [0, num_blocks), and no sequence
+ *     may be longer than the max_seqlen arguments.
+ *   - The device must be gfx950; otherwise ATTN_ERR_UNSUPPORTED.  The check
+ *     runs on the first call on each device and is cached.
+ *   - Calls with nothing to compute (batch == 0, total == 0) return ATTN_OK
+ *     without touching the GPU.
+ */
+#ifndef ATTN_CU_SEQLENS_H
+#define ATTN_CU_SEQLENS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+    ATTN_ERR_BAD_SHAPE = 2,    /* sizes inconsistent or out of range */
+    ATTN_ERR_UNSUPPORTED = 3,  /* dtype / head_size / mask / device not supported */
+    ATTN_ERR_DEVICE = 4,       /* HIP could not report the current device */
+    ATTN_ERR_LAUNCH = 5,       /* a kernel launch failed (hipGetLastError) */
+    ATTN_ERR_WORKSPACE = 6     /* workspace missing or too small */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_F16 = 0,
+    ATTN_BF16 = 1,
+    ATTN_FP8_E4M3 = 2          /* OCP e4m3fn */
+} attn_dtype;
+
+#define ATTN_MASK_NONE 0u
+#define ATTN_MASK_CAUSAL 1u
+#define ATTN_MASK_DOCUMENT 2u
+#define ATTN_MASK_PATCH 4u
+
+/* Version of this ABI (ATTN_ABI_VERSION). */
+int attn_abi_version(void);
+
+/* Static text for a status code (never NULL). */
+const char* attn_status_string(attn_status status);
+
+/*
+ * attn_cu_seqlens -- cumulative sequence lengths.
+ * The cumulative-seqlens buffer of the onnxruntime PR (section
+ * Implementation: LaunchGetCumulativeSeqlensKV, whose element [batch_size]
+ * is the token total).
+ *   seqlens     int32 [batch], each >= 0 (device)
+ *   cu_seqlens  int32 [batch + 1] output (device): cu[0] = 0,
+ *               cu[b+1] = cu[b] + seqlens[b].  Must not alias seqlens.
+ * The caller guarantees the total fits int32.  batch == 0 writes nothing.
+ * Errors: NULL pointer, batch < 0.
+ */
+attn_status attn_cu_seqlens(const int32_t* seqlens, int32_t* cu_seqlens, int32_t batch,
+                            void* stream);
+
+/*
+ * attn_reshape_and_cache -- append new K/V tokens to the paged cache.
+ * ReshapeAndCache of the onnxruntime PR (section Implementation, step 1).
+ * Sequence b appends n = cu_seqlens_new[b+1] - cu_seqlens_new[b] tokens and
+ * afterwards holds kv_len = cu_seqlens_kv[b+1] - cu_seqlens_kv[b] tokens
+ * (n <= kv_len), so new token i goes to position kv_len - n + i.
+ *   k, v              [total_new, num_kv_heads, head_size] (device)
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_size], written
+ *   block_table       int32 [batch, max_blocks_per_seq]
+ *   dtype             any attn_dtype (the copy is bitwise)
+ * Only the addressed slots are written.  Errors: NULL pointer, non-positive
+ * sizes, head_size not a multiple of 16 bytes / element size, block_size not
+ * a power of two, unsupported dtype.
+ */
+attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* cu_seqlens_new, const int32_t* cu_seqlens_kv,
+                                   int32_t batch, int32_t total_new, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   attn_dtype dtype, void* stream);
+
+/*
+ * attn_paged_prefill_fwd -- varlen attention of packed queries against the
+ * paged cache: out = softmax(scale * q k^T + mask) v per sequence and head.
+ * The fused form of the onnxruntime PR's gather-then-varlen-attention path
+ * (section Implementation, steps 2-3), with the masks of the blt issue and
+ * the FlexAttention commit.
+ *   q            [total_q, num_heads, head_size], dtype ATTN_F16 or ATTN_BF16
+ *   k_cache, v_cache, block_table, max_blocks_per_seq, block_size, num_blocks:
+ *                the paged cache as above (same dtype as q)
+ *   cu_seqlens_q, cu_seqlens_kv  int32 [batch + 1]
+ *   max_seqlen_q, max_seqlen_kv  upper bounds of the per-sequence lengths
+ *                (host values; they size the launch, no device sync is made)
+ *   mask_flags, q_ids, kv_ids    see Conventions (ids may be NULL unless the
+ *                matching flag is set)
+ *   out          [total_q, num_heads, head_size], same dtype as q
+ *   lse          float32 [total_q, num_heads] or NULL
+ * Supported: head_size 64 or 128; block_size 16, 32 or 64;
+ * num_heads % num_kv_heads == 0.  Errors: NULL pointer, bad shape,
+ * unsupported dtype/head_size/block_size/mask, launch failure.
+ */
+attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                   int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   float scale, uint32_t mask_flags, const int32_t* q_ids,
+                                   const int32_t* kv_ids, attn_dtype dtype, void* out, float* lse,
+                                   void* stream);
+
+/*
+ * attn_paged_decode_workspace_bytes -- workspace size attn_paged_decode_fwd
+ * needs for these sizes (same split_tokens argument).  Host only, no HIP call.
+ * Returns 0 for invalid sizes.
+ */
+size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_size, int32_t max_seqlen_kv,
+                                         int32_t split_tokens);
+
+/*
+ * attn_paged_decode_fwd -- one query token per sequence against its paged
+ * cache (q_len = 1; under bottom-right alignment the query sees all kv_len
+ * keys).  Split-KV: each sequence's keys are cut into chunks of split_tokens
+ * keys processed in parallel; a second kernel merges the partial results
+ * with their logsumexp (the LSE output of the blt issue's kernel options).
+ *   q            [batch, num_heads, head_size], ATTN_F16 or ATTN_BF16
+ *   cu_seqlens_kv int32 [batch + 1]; max_seqlen_kv bounds every kv length
+ *   split_tokens keys per split, a multiple of 256, or 0 to let the library
+ *                choose from (batch, num_kv_heads, max_seqlen_kv)
+ *   out          [batch, num_heads, head_size], same dtype as q
+ *   lse          float32 [batch, num_heads] or NULL
+ *   workspace    device scratch of at least
+ *                attn_paged_decode_workspace_bytes(...) bytes, 256-byte aligned,
+ *                owned by the caller; its contents need no initialisation.
+ *                Calls that share a workspace must not overlap in time.
+ * Errors: as prefill, plus ATTN_ERR_WORKSPACE.
+ */
+attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_seqlens_kv, int32_t batch,
+                                  int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                  float scale, int32_t split_tokens, attn_dtype dtype, void* out,
+                                  float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * attn_fp8_fwd -- dense varlen fp8 e4m3 attention with a column-major V.
+ * The fp8 path of the FlexAttention commit: Q and K row-major, V column-major
+ * so that the fp8 product softmax_scores @ V reads V contiguously along the
+ * key dimension (commit message, Context and Fix summary;
+ * _enforce_mem_layouts).
+ *   q8           uint8 e4m3 codes [total_q, num_heads, head_size]
+ *   k8           uint8 e4m3 codes [total_kv, num_kv_heads, head_size]
+ *   v8_colmajor  uint8 e4m3 codes [num_kv_heads, head_size, total_kv]
+ *   descale_qkv  float32 [3] (device): real value = descale * decoded code
+ *   cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, masks: as prefill
+ *   out_bf16     bf16 [total_q, num_heads, head_size]
+ *   lse          float32 [total_q, num_heads] or NULL
+ * Scores and the softmax run in fp32.  The probabilities are rounded to e4m3
+ * (nearest even) for the P.V product, and each row's normaliser is summed
+ * from those rounded values.  Supported: head_size 128.
+ */
+attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor,
+                         const float* descale_qkv, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_kv, int32_t batch, int32_t total_q,
+                         int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size, float scale,
+                         uint32_t mask_flags, const int32_t* q_ids, const int32_t* kv_ids,
+                         void* out_bf16, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_CU_SEQLENS_H */

@@ -1,0 +1,164 @@
+"""Helpers for the GPU parity tests: run a workload through the C ABI (via the
+binding) and through the oracle, and compare.
+
+The oracle side and the HIP side each compute their own cu_seqlens and fill
+their own paged cache from the same generated tokens.
+"""
+
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as ORC
+
+ATOL_16 = 2e-2     # max-abs bound for fp16 / bf16 outputs against the fp64 oracle
+REL_16 = 1e-2      # relative L2 bound
+ATOL_FP8 = 6e-2    # max-abs bound for fp8 outputs
+LSE_ATOL = 2e-3    # fp32 logsumexp of exactly the same inputs
+
+DEV = "cuda"
+
+
+def gpu_available():
+    try:
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+def lib_module():
+    import attention_cu_seqlens_amd as A
+    A._lib.load()
+    return A
+
+
+def banner(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------- oracle side
+
+def oracle_prefill(w, rows=None):
+    cu_q = ORC.cu_seqlens(w.q_lens)
+    cu_kv = ORC.cu_seqlens(w.kv_lens)
+    cu_new = ORC.cu_seqlens(w.new_lens)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
+    kc = np.full(shape, np.nan)
+    vc = np.full(shape, np.nan)
+    k = w.k_new.double().cpu().numpy()
+    v = w.v_new.double().cpu().numpy()
+    kc, vc = ORC.reshape_and_cache(k, v, kc, vc, w.block_table, cu_new, cu_kv, w.block_size)
+    q = w.q.double().cpu().numpy()
+    return ORC.paged_attention(q, kc, vc, w.block_table, cu_q, cu_kv, w.block_size, w.scale,
+                               w.mask_flags, w.q_ids, w.kv_ids, rows)
+
+
+def oracle_decode(w, batches=None):
+    cu_kv = ORC.cu_seqlens(w.kv_lens)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
+    kc = np.full(shape, np.nan)
+    vc = np.full(shape, np.nan)
+    k = w.k_new.double().cpu().numpy()
+    v = w.v_new.double().cpu().numpy()
+    kc, vc = ORC.reshape_and_cache(k, v, kc, vc, w.block_table, cu_kv, cu_kv, w.block_size)
+    q = w.q.double().cpu().numpy()
+    return ORC.paged_decode(q, kc, vc, w.block_table, cu_kv, w.block_size, w.scale, batches)
+
+
+def oracle_fp8(w, rows=None):
+    cu_q = ORC.cu_seqlens(w.q_lens)
+    cu_kv = ORC.cu_seqlens(w.kv_lens)
+    return ORC.fp8_attention(w.q.cpu().numpy(), w.k_new.cpu().numpy(),
+                             w.v8_colmajor.cpu().numpy(), w.descale, cu_q, cu_kv, w.scale,
+                             w.mask_flags, w.q_ids, w.kv_ids, rows)
+
+
+# ------------------------------------------------------------------- GPU side
+
+def _i32(a):
+    return torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32).to(DEV)
+
+
+def gpu_cache(w, A, poison=float("nan")):
+    """Cu-seqlens and a NaN-poisoned paged cache filled through the library."""
+    cu_kv = A.attn_cu_seqlens(_i32(w.kv_lens))
+    cu_new = A.attn_cu_seqlens(_i32(w.new_lens))
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
+    dt = w.k_new.dtype
+    kc = torch.full(shape, poison, dtype=dt, device=DEV)
+    vc = torch.full(shape, poison, dtype=dt, device=DEV)
+    bt = _i32(w.block_table)
+    A.attn_reshape_and_cache(w.k_new.to(DEV).contiguous(), w.v_new.to(DEV).contiguous(), kc, vc,
+                             bt, cu_new, cu_kv)
+    return kc, vc, bt, cu_kv
+
+
+def gpu_prefill(w, A, cache=None, scale=None, block_table=None):
+    kc, vc, bt, cu_kv = cache if cache is not None else gpu_cache(w, A)
+    if block_table is not None:
+        bt = _i32(block_table)
+    cu_q = A.attn_cu_seqlens(_i32(w.q_lens))
+    q_ids = None if w.q_ids is None else _i32(w.q_ids)
+    kv_ids = None if w.kv_ids is None else _i32(w.kv_ids)
+    out, lse = A.attn_paged_prefill_fwd(
+        w.q.to(DEV).contiguous(), kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max(initial=0)),
+        int(w.kv_lens.max(initial=0)), scale=w.scale if scale is None else scale,
+        mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def gpu_decode(w, A, split_tokens=0, cache=None):
+    kc, vc, bt, cu_kv = cache if cache is not None else gpu_cache(w, A)
+    out, lse = A.attn_paged_decode_fwd(w.q.to(DEV).contiguous(), kc, vc, bt, cu_kv,
+                                       int(w.kv_lens.max(initial=0)), scale=w.scale,
+                                       split_tokens=split_tokens, return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def gpu_fp8(w, A):
+    cu_q = A.attn_cu_seqlens(_i32(w.q_lens))
+    cu_kv = A.attn_cu_seqlens(_i32(w.kv_lens))
+    q_ids = None if w.q_ids is None else _i32(w.q_ids)
+    kv_ids = None if w.kv_ids is None else _i32(w.kv_ids)
+    out, lse = A.attn_fp8_fwd(w.q.to(DEV), w.k_new.to(DEV), w.v8_colmajor.to(DEV),
+                              torch.as_tensor(w.descale, dtype=torch.float32).to(DEV), cu_q,
+                              cu_kv, int(w.q_lens.max()), int(w.kv_lens.max()), scale=w.scale,
+                              mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids,
+                              return_lse=True)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+# ----------------------------------------------------------------- comparison
+
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, atol, rel=None, rows=None, what=""):
+    """Element-wise comparison on (optionally) sampled rows; returns error stats."""
+    o = out_gpu.float().cpu().double().numpy()
+    l = lse_gpu.cpu().double().numpy()
+    if rows is not None:
+        o, l, out_ref, lse_ref = o[rows], l[rows], out_ref[rows], lse_ref[rows]
+    assert not np.any(np.isnan(o)), f"{what}: NaN in GPU output"
+    diff = np.abs(o - out_ref)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    denom = float(np.linalg.norm(out_ref))
+    rel_l2 = float(np.linalg.norm(o - out_ref) / denom) if denom > 0 else 0.0
+    inf_ref = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(l), inf_ref), f"{what}: fully-masked rows differ"
+    lse_err = float(np.max(np.abs(l[~inf_ref] - lse_ref[~inf_ref]))) if (~inf_ref).any() else 0.0
+    stats = dict(max_abs=max_abs, rel_l2=rel_l2, lse_err=lse_err)
+    print(f"[parity] {what}: {stats}", flush=True)
+    assert max_abs <= atol, f"{what}: max-abs {max_abs} > {atol}"
+    if rel is not None:
+        assert rel_l2 <= rel, f"{what}: rel-L2 {rel_l2} > {rel}"
+    assert lse_err <= LSE_ATOL, f"{what}: LSE error {lse_err}"
+    return stats
+
+
+requires_gpu = pytest.mark.skipif(not gpu_available(), reason="needs a GPU")

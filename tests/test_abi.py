@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_cu_seqlens_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_cu_seqlens.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libattn_cu_seqlens.so is not built (python -m attention_cu_seqlens_amd.build_lib)")
+    return _lib.load()
+
+
+def test_header_declares_the_five_entry_points():
+    names = _declared()
+    for n in ("attn_cu_seqlens", "attn_reshape_and_cache", "attn_paged_prefill_fwd",
+              "attn_paged_decode_fwd", "attn_fp8_fwd"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(_declared()) == set(_lib.SIGNATURES), "binding signatures out of sync with header"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.attn_abi_version() == 1
+    for code in range(7):
+        assert lib.attn_status_string(code)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p(16)   # never dereferenced: every call below fails its host checks
+
+
+def test_cu_seqlens_host_checks(lib):
+    assert lib.attn_cu_seqlens(None, P, 3, None) == 1
+    assert lib.attn_cu_seqlens(P, P, -1, None) == 2
+    assert lib.attn_cu_seqlens(P, P, 0, None) == 0     # nothing to do, no GPU touched
+
+
+def test_reshape_and_cache_host_checks(lib):
+    f = lib.attn_reshape_and_cache
+    ok = [P, P, P, P, P, 4, P, P, 2, 10, 2, 64, 16, 8, 1, None]
+    bad = list(ok); bad[0] = None
+    assert f(*bad) == 1
+    bad = list(ok); bad[12] = 24                        # block_size not a power of two
+    assert f(*bad) == 2
+    bad = list(ok); bad[10], bad[11], bad[14] = 1, 4, 2  # 4 fp8 bytes per row: not 16-byte rows
+    assert f(*bad) == 2
+    bad = list(ok); bad[14] = 7
+    assert f(*bad) == 3
+    bad = list(ok); bad[9] = 0                          # no tokens: no-op
+    assert f(*bad) == 0
+
+
+def _prefill_args(**kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, mbps=8, cuq=P, cukv=P, batch=2, total_q=100, msq=64, mskv=64,
+             hq=8, hkv=2, d=128, bs=16, nb=32, scale=0.1, mask=1, qids=None, kvids=None, dtype=1,
+             out=P, lse=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def test_prefill_host_checks(lib):
+    f = lib.attn_paged_prefill_fwd
+    assert f(*_prefill_args(q=None)) == 1
+    assert f(*_prefill_args(d=96)) == 3
+    assert f(*_prefill_args(hq=6, hkv=4)) == 2
+    assert f(*_prefill_args(bs=8)) == 3
+    assert f(*_prefill_args(dtype=2)) == 3
+    assert f(*_prefill_args(mask=2)) == 1               # DOCUMENT needs both id arrays
+    assert f(*_prefill_args(mask=4)) == 1               # PATCH needs q_ids
+    assert f(*_prefill_args(mask=6, qids=P, kvids=P)) == 3
+    assert f(*_prefill_args(mask=8)) == 3
+    assert f(*_prefill_args(mskv=129)) == 2             # table too narrow for the longest kv
+    assert f(*_prefill_args(scale=float("nan"))) == 2
+    assert f(*_prefill_args(batch=0)) == 0
+    assert f(*_prefill_args(total_q=0)) == 0
+
+
+def test_decode_host_checks(lib):
+    ws = lib.attn_paged_decode_workspace_bytes
+    assert ws(64, 32, 8, 128, 32768, 0) > 0
+    assert ws(64, 32, 8, 128, 32768, 100) == 0          # split not a multiple of 256
+    assert ws(0, 32, 8, 128, 1, 0) == 0
+    need = ws(4, 8, 2, 128, 1000, 256)
+    assert need == 4 * 8 * 4 * 128 * 4 + 4 * 8 * 4 * 2 * 4
+
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, bt=P, mbps=64, cukv=P, batch=4, mskv=1000, hq=8, hkv=2, d=128,
+                 bs=16, nb=300, scale=0.1, split=256, dtype=1, out=P, lse=None,
+                 ws=ctypes.c_void_p(256), wsb=need, stream=None)
+        a.update(kw)
+        return lib.attn_paged_decode_fwd(*a.values())
+
+    assert call(q=None) == 1
+    assert call(wsb=need - 1) == 6
+    assert call(ws=None) == 6
+    assert call(ws=ctypes.c_void_p(128)) == 6             # not 256-byte aligned
+    assert call(hq=66, hkv=1) == 3                      # group above 32
+    assert call(split=300) == 2
+    assert call(batch=0) == 0
+
+
+def test_fp8_host_checks(lib):
+    f = lib.attn_fp8_fwd
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, ds=P, cuq=P, cukv=P, batch=2, tq=10, tkv=10, msq=5, mskv=5, hq=4,
+                 hkv=4, d=128, scale=0.1, mask=1, qids=None, kvids=None, out=P, lse=None,
+                 stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(d=64) == 3
+    assert call(ds=None) == 1
+    assert call(hq=6) == 2
+    assert call(tq=0) == 0

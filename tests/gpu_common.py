@@ -19,6 +19,10 @@ ATOL_16 = 2e-2     # max-abs bound for fp16 / bf16 outputs against the fp64 orac
 REL_16 = 1e-2      # relative L2 bound
 ATOL_FP8 = 6e-2    # max-abs bound for fp8 outputs
 LSE_ATOL = 2e-3    # fp32 logsumexp of exactly the same inputs
+# fp8: the row normaliser is summed from probabilities rounded to e4m3, whose
+# round-to-nearest-even relative error is at most 2^-4 (3 mantissa bits), so
+# ln(l) -- and the LSE -- may move by up to ln(1 + 2^-4) < 2^-4.
+LSE_ATOL_FP8 = 2.0 ** -4
 
 DEV = "cuda"
 
@@ -138,7 +142,8 @@ def gpu_fp8(w, A):
 
 # ----------------------------------------------------------------- comparison
 
-def compare(out_gpu, lse_gpu, out_ref, lse_ref, atol, rel=None, rows=None, what=""):
+def compare(out_gpu, lse_gpu, out_ref, lse_ref, atol, rel=None, rows=None, what="",
+            lse_atol=LSE_ATOL):
     """Element-wise comparison on (optionally) sampled rows; returns error stats."""
     o = out_gpu.float().cpu().double().numpy()
     l = lse_gpu.cpu().double().numpy()
@@ -157,7 +162,7 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, atol, rel=None, rows=None, what=
     assert max_abs <= atol, f"{what}: max-abs {max_abs} > {atol}"
     if rel is not None:
         assert rel_l2 <= rel, f"{what}: rel-L2 {rel_l2} > {rel}"
-    assert lse_err <= LSE_ATOL, f"{what}: LSE error {lse_err}"
+    assert lse_err <= lse_atol, f"{what}: LSE error {lse_err}"
     return stats
 
 

@@ -177,7 +177,7 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
                                          int32_t split_tokens) {
     if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_seqlen_kv < 0)
         return 0;
-    if (split_tokens < 0 || split_tokens % 256 != 0) return 0;
+    if (split_tokens < 0 || split_tokens % 256 != 0 || split_tokens > 8192) return 0;
     const int st = attn::decode_split_tokens(batch, num_kv_heads, max_seqlen_kv, split_tokens);
     return attn::decode_workspace_bytes(batch, num_heads, head_size, max_seqlen_kv, st);
 }
@@ -199,7 +199,8 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     if (num_heads / num_kv_heads > 32) return ATTN_ERR_UNSUPPORTED;
     if (max_blocks_per_seq <= 0 || num_blocks <= 0) return ATTN_ERR_BAD_SHAPE;
     if ((int64_t)max_blocks_per_seq * block_size < max_seqlen_kv) return ATTN_ERR_BAD_SHAPE;
-    if (split_tokens < 0 || split_tokens % 256 != 0) return ATTN_ERR_BAD_SHAPE;
+    if (split_tokens < 0 || split_tokens % 256 != 0 || split_tokens > 8192)
+        return ATTN_ERR_BAD_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
     if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
         cu_seqlens_kv == nullptr || out == nullptr)

@@ -21,11 +21,20 @@
 namespace attn {
 
 template <int D, int NW, bool BF16>
-__global__ __launch_bounds__(NW * 64) void k_paged_decode(DecodeParams p) {
-    constexpr int NT = NW * 64;
-    constexpr int BN = NW * 32;
-    using Tile = PagedTile16<D, BN, NT>;
+struct DecodeLayout {
+    using Tile = PagedTile16<D, 32, 64, true>;            // one wave, 32 keys
+    static constexpr int WIN_OFF = NW * Tile::BYTES;
+    static constexpr int TILE_BYTES = WIN_OFF + (PAGE_WIN + 1) * 4;
+    static constexpr int RED_BYTES = NW * 32 * (D + 2) * 4;   // merge space, G <= 32
+    static constexpr int LDS_BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
+};
+
+template <int D, int NW, bool BF16>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_decode(DecodeParams p) {
+    using L = DecodeLayout<D, NW, BF16>;
+    using Tile = typename L::Tile;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int* win = reinterpret_cast<int*>(smem + L::WIN_OFF);
 
     int u = blockIdx.x;
     const int s = u % p.max_splits;
@@ -37,6 +46,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_decode(DecodeParams p) {
     const int k0 = s * p.split_tokens;
     if (k0 >= kv_len) return;
     const int k1 = min(kv_len, k0 + p.split_tokens);
+    const bool neg = p.c < 0.f;
+    const float c = fabsf(p.c);
 
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
@@ -53,40 +64,42 @@ __global__ __launch_bounds__(NW * 64) void k_paged_decode(DecodeParams p) {
         for (int t = 0; t < D / 16; ++t) {
             u32x4_t v = {0u, 0u, 0u, 0u};
             if (valid) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-            st.q[0][t] = v;
+            st.q[0][t] = neg ? neg16x8(v) : v;
         }
     }
     st.lo[0] = 0;
     st.hi[0] = k1;
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
+    const int first = k0 >> p.bs_log2;
+    fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+    __syncthreads();
+
+    // Each wave streams 32-key tiles w, w + NW, ... of the split through its
+    // own LDS slot, with its next tile's loads in flight while it computes.
     const int tok_stride = p.num_kv_heads * D;
     const int head_off = hk * D;
-    const int n_tiles = (k1 - k0 + BN - 1) / BN;
-
+    const int n_t = (k1 - k0 + 31) >> 5;
+    uint8_t* mine = smem + w * Tile::BYTES;
     Tile ld;
-    ld.load(p.k_cache, p.v_cache, table, k0, k1, p.bs_log2, tok_stride, head_off, tid);
-    ld.store(smem, tid);
-    __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-        const int j = k0 + it * BN;
-        const bool has_next = it + 1 < n_tiles;
-        if (has_next)
-            ld.load(p.k_cache, p.v_cache, table, j + BN, k1, p.bs_log2, tok_stride, head_off,
-                    tid);
-        const int kb_start = j + 32 * w;
-        if (kb_start < k1) {
-            if (kb_start + 32 <= k1)
-                tile_step<D, BN, 1, 1, BF16, false>(st, smem, j, w, p.c);
-            else
-                tile_step<D, BN, 1, 1, BF16, true>(st, smem, j, w, p.c);
-        }
-        __syncthreads();
-        if (has_next) {
-            ld.store(smem, tid);
-            __syncthreads();
-        }
+    if (w < n_t)
+        ld.load(p.k_cache, p.v_cache, win, first, k0 + 32 * w, k1, p.bs_log2, tok_stride,
+                head_off, lane);
+    for (int t = w; t < n_t; t += NW) {
+        const int j = k0 + 32 * t;
+        ld.store(mine, j, k1, lane);
+        __builtin_amdgcn_wave_barrier();
+        if (t + NW < n_t)
+            ld.load(p.k_cache, p.v_cache, win, first, j + 32 * NW, k1, p.bs_log2, tok_stride,
+                    head_off, lane);
+        if (j + 32 <= k1)
+            tile_step<D, 32, 1, 1, BF16, false>(st, mine, j, 0, c);
+        else
+            tile_step<D, 32, 1, 1, BF16, true>(st, mine, j, 0, c);
+        __builtin_amdgcn_wave_barrier();
     }
+    __syncthreads();
 
     // merge the NW wave states of this split
     float* red_o = reinterpret_cast<float*>(smem);   // [NW][G][D]
@@ -106,20 +119,20 @@ __global__ __launch_bounds__(NW * 64) void k_paged_decode(DecodeParams p) {
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < G * D; idx += NT) {
-        const int c = idx / D, d = idx % D;
+    for (int idx = tid; idx < G * D; idx += NW * 64) {
+        const int cc = idx / D, d = idx % D;
         float mstar = kNegInf;
 #pragma unroll
-        for (int i = 0; i < NW; ++i) mstar = fmaxf(mstar, red_m[i * G + c]);
+        for (int i = 0; i < NW; ++i) mstar = fmaxf(mstar, red_m[i * G + cc]);
         float lsum = 0.f, osum = 0.f;
 #pragma unroll
         for (int i = 0; i < NW; ++i) {
-            const float mi = red_m[i * G + c];
+            const float mi = red_m[i * G + cc];
             const float wgt = (mi == kNegInf) ? 0.f : fast_exp2(mi - mstar);
-            lsum += red_l[i * G + c] * wgt;
-            osum += red_o[(i * G + c) * D + d] * wgt;
+            lsum += red_l[i * G + cc] * wgt;
+            osum += red_o[(i * G + cc) * D + d] * wgt;
         }
-        const int64_t slot = ((int64_t)b * p.num_heads + hk * G + c) * p.max_splits + s;
+        const int64_t slot = ((int64_t)b * p.num_heads + hk * G + cc) * p.max_splits + s;
         p.part_o[slot * D + d] = osum;
         if (d == 0) {
             p.part_ml[slot * 2 + 0] = mstar;
@@ -175,15 +188,10 @@ namespace {
 
 template <int D, int NW, bool BF16>
 hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
-    constexpr int BN = NW * 32;
-    const size_t tile = (size_t)BN * D * 4;
-    const size_t red = (size_t)NW * p.group * (D + 2) * 4;
-    const size_t lds = tile > red ? tile : red;
-    // the largest request over every supported group size (G <= 32)
-    const size_t red_max = (size_t)NW * 32 * (D + 2) * 4;
+    constexpr int lds = DecodeLayout<D, NW, BF16>::LDS_BYTES;
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)(tile > red_max ? tile : red_max));
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     const int64_t grid = (int64_t)p.batch * p.num_kv_heads * p.max_splits;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;

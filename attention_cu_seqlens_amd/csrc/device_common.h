@@ -92,104 +92,158 @@ __device__ __forceinline__ int swap23(int k) {
     return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-// 16-byte chunk swizzles for the LDS tiles (bank-conflict avoidance).
-__device__ __forceinline__ int k_swz(int row) { return row & 7; }
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+// LDS row pitches: one extra 16-byte chunk per row shifts consecutive rows by
+// one bank group, so the 8 (or 16) lanes that read one 16-byte chunk of 8
+// (16) consecutive rows hit distinct banks, and every fragment read is a
+// per-lane base plus a compile-time offset.
+template <int D> constexpr int k_pitch() { return D * 2 + 16; }
+template <int BN> constexpr int vt_pitch() { return BN * 2 + 16; }
+
+// ---------------------------------------------------------------------------
+// Block-table window.  The physical block ids of a key range are staged in
+// LDS once (all loads in flight together), so the K/V loads of every tile
+// find their page with an LDS read instead of a dependent global load.
+// A window holds PAGE_WIN + 1 ids starting at logical block `first`; a key
+// range of PAGE_WIN * block_size keys starting anywhere fits in it.
+// ---------------------------------------------------------------------------
+constexpr int PAGE_WIN = 512;
+
+template <bool STREAM>
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
+    if constexpr (STREAM)
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    else
+        return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+__device__ __forceinline__ void fill_page_window(int* win, const int32_t* __restrict__ table,
+                                                 int first, int n_blocks, int tid, int nt) {
+    for (int i = tid; i <= PAGE_WIN; i += nt) {
+        const int p = first + i;
+        win[i] = p < n_blocks ? table[p] : 0;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Paged K/V tile loader for 16-bit dtypes.
 //
 // A tile is BN consecutive keys of one sequence and one kv head.  LDS gets
-//   K  [BN][D]   16-bit, row = key, 16-byte chunk c stored at c ^ k_swz(row)
-//   Vt [D][BN]   16-bit, row = dim, key k at slot swap23(k); 16-byte chunk c
-//                stored at c ^ vt_swz(d)
+//   K  [BN][D]  16-bit, row = key, pitch k_pitch<D>()
+//   Vt [D][BN]  16-bit, row = dim, key k at slot swap23(k), pitch vt_pitch<BN>()
 // Keys at or past kv_len are zero-filled (the cache may hold NaN there).
-// Each thread owns KPT 16-byte K chunks and VPT V units of 4 keys x 8 dims;
-// a V unit is transposed in registers (4 rows x 4 dwords -> 8 dim rows x 2
-// dwords) and written as eight 8-byte LDS stores.
+// Loads are unconditional: a row past kv_len is read from a valid row of the
+// same sequence and zeroed when stored, so a tile's loads issue back to back.
+// K is moved in 16-byte chunks (16 lanes cover one 256-byte row).  V moves in
+// units of 4 keys x 8 dims, transposed in registers (4 rows x 4 dwords -> 8
+// dim rows x 2 dwords) and written as eight 8-byte stores; units are numbered
+// key-quad fastest so the 8-byte stores of neighbouring lanes are contiguous.
+// STREAM marks the loads non-temporal (decode reads each byte once; prefill
+// re-reads K/V across query tiles and keeps them cacheable).
 // ---------------------------------------------------------------------------
-template <int D, int BN, int NT>
+template <int D, int BN, int NT, bool STREAM>
 struct PagedTile16 {
     static constexpr int CPR = D / 8;                 // 16-byte chunks per key row
-    static constexpr int NV = (BN / 4) * CPR;         // V units per tile
-    static constexpr int VPT = NV / NT;
-    static constexpr int KPT = BN * CPR / NT;
-    static_assert(VPT >= 1 && NV % NT == 0, "V units must divide evenly");
-    static_assert(KPT >= 1 && (BN * CPR) % NT == 0, "K chunks must divide evenly");
-    static constexpr int K_BYTES = BN * D * 2;
-    static constexpr int V_BYTES = D * BN * 2;
+    static constexpr int QPT = BN / 4;                // key quads per tile
+    static constexpr int NV = QPT * CPR;              // V units per tile
+    static constexpr int NK = BN * CPR;               // K chunks per tile
+    // SPLIT: fewer V units than threads -- threads [0, NV) take one V unit
+    // each and the others share the K chunks; otherwise every thread takes
+    // NV/NT V units and NK/NT K chunks.  Either way each thread issues the
+    // same number of 16-byte loads.
+    static constexpr bool SPLIT = NV < NT;
+    static constexpr int KT = SPLIT ? NT - NV : NT;   // threads loading K
+    static constexpr int VPT = SPLIT ? 1 : NV / NT;
+    static constexpr int KPT = NK / KT;
+    static_assert(SPLIT ? (NV % 64 == 0 && NK % KT == 0) : (NV % NT == 0 && NK % NT == 0),
+                  "tile does not divide over the workgroup");
+    static_assert(!SPLIT || KPT == 4 * VPT, "unbalanced split");
+    static constexpr int KP = k_pitch<D>();
+    static constexpr int VP = vt_pitch<BN>();
+    static constexpr int K_BYTES = BN * KP;
+    static constexpr int V_BYTES = D * VP;
     static constexpr int BYTES = K_BYTES + V_BYTES;
 
     u32x4_t kreg[KPT];
     u32x4_t vreg[VPT][4];
 
-    // Issue the global loads for keys [j0, j0 + BN) of one sequence.
-    //   cache_k/v: element base of the caches; table: this sequence's
-    //   block_table row; tok_stride = Hkv*D; head_off = hk*D (elements).
+    __device__ __forceinline__ bool does_k(int tid) const { return !SPLIT || tid >= NV; }
+    __device__ __forceinline__ bool does_v(int tid) const { return !SPLIT || tid < NV; }
+    __device__ __forceinline__ int k_index(int tid, int i) const {
+        return (SPLIT ? tid - NV : tid) + i * KT;
+    }
+
+    // Issue the global loads for keys [j0, j0 + BN) of one sequence
+    // (kv_len >= 1).  win/first: the block-table window; cache_k/v: element
+    // base of the caches; tok_stride = Hkv*D; head_off = hk*D (elements).
     __device__ __forceinline__ void load(const uint16_t* __restrict__ cache_k,
-                                         const uint16_t* __restrict__ cache_v,
-                                         const int32_t* __restrict__ table, int j0, int kv_len,
-                                         int bs_log2, int tok_stride, int head_off, int tid) {
+                                         const uint16_t* __restrict__ cache_v, const int* win,
+                                         int first, int j0, int kv_len, int bs_log2,
+                                         int tok_stride, int head_off, int tid) {
         const int bs_mask = (1 << bs_log2) - 1;
+        const int last = kv_len - 1;
+        const int64_t page_stride = (int64_t)tok_stride << bs_log2;
+        if (does_k(tid)) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            const int row = idx / CPR, c = idx % CPR;
-            const int tok = j0 + row;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (tok < kv_len) {
-                const int64_t page = table[tok >> bs_log2];
-                const int64_t off = ((page << bs_log2) + (tok & bs_mask)) * tok_stride + head_off +
-                                    c * 8;
-                v = *reinterpret_cast<const u32x4_t*>(cache_k + off);
+            for (int i = 0; i < KPT; ++i) {
+                const int idx = k_index(tid, i);
+                const int row = idx / CPR, c = idx % CPR;
+                const int tok = min(j0 + row, last);
+                const int page = win[(tok >> bs_log2) - first];
+                const uint16_t* src = cache_k + page * page_stride +
+                                      ((tok & bs_mask) * tok_stride + head_off + c * 8);
+                kreg[i] = ld16<STREAM>(src);
             }
-            kreg[i] = v;
         }
+        if (does_v(tid)) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = tid + i * NT;
-            const int dc = u % CPR, quad = u / CPR;
-            const int key0 = swap23(quad * 4);           // 4 consecutive keys key0..key0+3
-            const int tok0 = j0 + key0;
-            int64_t base = 0;
-            if (tok0 < kv_len) {
-                const int64_t page = table[tok0 >> bs_log2];
-                base = ((page << bs_log2) + (tok0 & bs_mask)) * tok_stride + head_off + dc * 8;
-            }
+            for (int i = 0; i < VPT; ++i) {
+                const int u = tid + i * NT;
+                const int quad = u % QPT, dc = u / QPT;
+                const int tok0 = min(j0 + swap23(quad * 4), last);   // keys tok0 .. tok0+3
+                const int page = win[(tok0 >> bs_log2) - first];
+                const uint16_t* src = cache_v + page * page_stride +
+                                      ((tok0 & bs_mask) * tok_stride + head_off + dc * 8);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u32x4_t v = {0u, 0u, 0u, 0u};
-                if (tok0 + e < kv_len)
-                    v = *reinterpret_cast<const u32x4_t*>(cache_v + base + (int64_t)e * tok_stride);
-                vreg[i][e] = v;
+                for (int e = 0; e < 4; ++e) {
+                    const int step = (tok0 + e <= last) ? e : 0;
+                    vreg[i][e] = ld16<STREAM>(src + step * tok_stride);
+                }
             }
         }
     }
 
-    __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+    __device__ __forceinline__ void store(uint8_t* lds, int j0, int kv_len, int tid) const {
         uint8_t* lk = lds;
         uint8_t* lv = lds + K_BYTES;
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+        if (does_k(tid)) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            const int row = idx / CPR, c = idx % CPR;
-            *reinterpret_cast<u32x4_t*>(lk + row * (D * 2) + ((c ^ k_swz(row)) << 4)) = kreg[i];
+            for (int i = 0; i < KPT; ++i) {
+                const int idx = k_index(tid, i);
+                const int row = idx / CPR, c = idx % CPR;
+                const u32x4_t v = (j0 + row < kv_len) ? kreg[i] : zero;
+                *reinterpret_cast<u32x4_t*>(lk + row * KP + c * 16) = v;
+            }
         }
+        if (does_v(tid)) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int u = tid + i * NT;
-            const int dc = u % CPR, quad = u / CPR;
-            const int chunk = quad >> 1, half = quad & 1;   // slots quad*4 .. quad*4+3
+            for (int i = 0; i < VPT; ++i) {
+                const int u = tid + i * NT;
+                const int quad = u % QPT, dc = u / QPT;
+                const int tok0 = j0 + swap23(quad * 4);
+                u32x4_t rows[4];
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                const int d = dc * 8 + x;
-                const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
-                const int w = x >> 1;
-                u32x2_t out;
-                out.x = __builtin_amdgcn_perm(vreg[i][1][w], vreg[i][0][w], sel);
-                out.y = __builtin_amdgcn_perm(vreg[i][3][w], vreg[i][2][w], sel);
-                *reinterpret_cast<u32x2_t*>(lv + d * (BN * 2) + ((chunk ^ vt_swz(d)) << 4) +
-                                            half * 8) = out;
+                for (int e = 0; e < 4; ++e) rows[e] = (tok0 + e < kv_len) ? vreg[i][e] : zero;
+                uint8_t* dst = lv + (dc * 8) * VP + quad * 8;   // slots quad*4 .. quad*4+3
+#pragma unroll
+                for (int x = 0; x < 8; ++x) {
+                    const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+                    const int w = x >> 1;
+                    u32x2_t out;
+                    out.x = __builtin_amdgcn_perm(rows[1][w], rows[0][w], sel);
+                    out.y = __builtin_amdgcn_perm(rows[3][w], rows[2][w], sel);
+                    *reinterpret_cast<u32x2_t*>(dst + x * VP) = out;
+                }
             }
         }
     }
@@ -198,13 +252,22 @@ struct PagedTile16 {
 // ---------------------------------------------------------------------------
 // Per-wave attention state for QB blocks of 32 query rows (one row per lane
 // column) and the tile step.
+//
+// Online softmax with a lazily updated running max: m only moves when some
+// row's tile max exceeds it by more than kRescaleSlack (log2 units), so the
+// O^T rescale -- D/32 x 16 multiplies per row block -- runs on a handful of
+// tiles instead of every tile.  Between updates the probabilities
+// exp2(s*c - m) may reach 2^kRescaleSlack; the final O/l and LSE are
+// unchanged by the choice of m, which cancels exactly.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, int QB>
 struct RowsState {
     u32x4_t q[QB][D / 16];    // Q^T operand: 8 dims (16t + 8g ..) per lane-half
     f32x16_t o[D / 32][QB];   // O^T accumulators (unnormalised)
-    float m[QB];              // running max of scores * scale * log2(e)
-    float l[QB];              // running sum of exp2(score - m)
+    float m[QB];              // running max of score * scale * log2(e) (may lag)
+    float l[QB];              // running sum of exp2(score * c - m)
     int lo[QB], hi[QB];       // visible key interval [lo, hi) of the lane's row
 
     __device__ __forceinline__ void init() {
@@ -218,18 +281,27 @@ struct RowsState {
     }
 };
 
+// Flip the sign of every 16-bit element of a Q operand (a negative scale is
+// applied as |scale| on -q, which keeps the running max a max).
+__device__ __forceinline__ u32x4_t neg16x8(u32x4_t v) {
+    const uint32_t s = 0x80008000u;
+    return u32x4_t{v.x ^ s, v.y ^ s, v.z ^ s, v.w ^ s};
+}
+
 // One key tile against the wave's rows, reading K and Vt from LDS.  The LDS
 // tile is BN keys wide (starting at key j0); this wave processes the NKB
-// 32-key blocks kb0 .. kb0+NKB-1 of it.  c = scale * log2(e).  MASKED
+// 32-key blocks kb0 .. kb0+NKB-1 of it.  c = |scale| * log2(e) >= 0.  MASKED
 // evaluates each row's visible interval [lo, hi); otherwise every key of the
 // processed blocks is visible to every row.
 template <int D, int BN, int NKB, int QB, bool BF16, bool MASKED>
 __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* lds, int j0,
                                           int kb0, float c) {
-    const uint8_t* lk = lds;
-    const uint8_t* lv = lds + BN * D * 2;
+    constexpr int KP = k_pitch<D>();
+    constexpr int VP = vt_pitch<BN>();
     const int lane = lane_id();
     const int col = lane & 31, g = lane >> 5;
+    const uint8_t* lk = lds + col * KP + g * 16;                 // + row block, + 32 t
+    const uint8_t* lv = lds + BN * KP + col * VP + g * 16;       // + 32 VP db, + 16 chunk
 
     f32x16_t s[NKB][QB];
 #pragma unroll
@@ -241,15 +313,14 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
     for (int t = 0; t < D / 16; ++t) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const int row = (kb0 + kb) * 32 + col;
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                lk + row * (D * 2) + (((2 * t + g) ^ k_swz(row)) << 4));
+                lk + (kb0 + kb) * 32 * KP + t * 32);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32<BF16>(a, st.q[qb][t], s[kb][qb]);
         }
     }
 
-    // scale, mask, row max
+    // mask (select) and raw row max
     float mx[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mx[qb] = kNegInf;
@@ -259,38 +330,47 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = s[kb][qb][r] * c;
                 if constexpr (MASKED) {
                     const int key = j0 + (kb0 + kb) * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                    x = (key >= st.lo[qb] && key < st.hi[qb]) ? x : kNegInf;
+                    if (!(key >= st.lo[qb] && key < st.hi[qb])) s[kb][qb][r] = kNegInf;
                 }
-                s[kb][qb][r] = x;
-                mx[qb] = fmaxf(mx[qb], x);
+                mx[qb] = fmaxf(mx[qb], s[kb][qb][r]);
             }
 
-    float alpha[QB], msub[QB];
+    bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         mx[qb] = fmaxf(mx[qb], xor32(mx[qb]));
-        const float mnew = fmaxf(st.m[qb], mx[qb]);
-        msub[qb] = (mnew == kNegInf) ? 0.f : mnew;
-        alpha[qb] = fast_exp2(st.m[qb] - msub[qb]);
-        st.m[qb] = mnew;
+        mx[qb] = (mx[qb] == kNegInf) ? kNegInf : mx[qb] * c;
+        need |= mx[qb] > st.m[qb] + kRescaleSlack;
+    }
+    if (__any(need)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mnew = fmaxf(st.m[qb], mx[qb]);
+            const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(st.m[qb] - mnew);
+            st.m[qb] = mnew;
+            st.l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) st.o[db][qb] *= alpha;
+        }
     }
 
     // probabilities, row sums, packed P^T operands
     float rs[QB];
     u32x4_t pb[NKB][2][QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+        rs[qb] = 0.f;
+        const float nm = (st.m[qb] == kNegInf) ? 0.f : -st.m[qb];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        for (int kb = 0; kb < NKB; ++kb) {
             float p[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = fast_exp2(s[kb][qb][r] - msub[qb]);
+                // masked scores are -inf; with c == 0 the product would be NaN
+                p[r] = fast_exp2(__builtin_fmaf(s[kb][qb][r], c, nm));
+                if constexpr (MASKED) p[r] = (s[kb][qb][r] == kNegInf) ? 0.f : p[r];
                 rs[qb] += p[r];
             }
 #pragma unroll
@@ -303,13 +383,7 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
                 pb[kb][tp][qb] = w;
             }
         }
-
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        rs[qb] += xor32(rs[qb]);
-        st.l[qb] = st.l[qb] * alpha[qb] + rs[qb];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) st.o[db][qb] *= alpha[qb];
+        st.l[qb] += rs[qb] + xor32(rs[qb]);
     }
 
     // O^T += V^T P^T
@@ -319,10 +393,8 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
         for (int tp = 0; tp < 2; ++tp)
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
-                const int d = db * 32 + col;
-                const int chunk = 4 * (kb0 + kb) + 2 * tp + g;
                 const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                    lv + d * (BN * 2) + ((chunk ^ vt_swz(d)) << 4));
+                    lv + db * 32 * VP + (4 * (kb0 + kb) + 2 * tp) * 16);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
                     st.o[db][qb] = mfma32<BF16>(a, pb[kb][tp][qb], st.o[db][qb]);

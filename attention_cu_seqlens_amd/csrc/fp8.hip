@@ -72,66 +72,74 @@ struct DenseTile8 {
     u32x4_t kreg[KPT];
     u32x4_t vreg[VPT];
 
-    // keys [j0, j0 + BN8) of a sequence starting at global key kv_start.
+    // keys [j0, j0 + BN8) of a sequence starting at global key kv_start
+    // (kv_len >= 1).  Loads past kv_len read a valid row / chunk of the same
+    // sequence and are zeroed by store(), so the loads issue back to back.
     __device__ __forceinline__ void load(const uint8_t* __restrict__ k, const uint8_t* __restrict__ vt,
                                          int64_t total_kv, int kv_start, int j0, int kv_len,
                                          int k_tok_stride, int k_head_off, int64_t v_head_base,
                                          bool v_aligned, int tid) {
+        const int last = kv_len - 1;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * NT;
             const int row = idx >> 3, c = idx & 7;
-            const int key = j0 + row;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (key < kv_len)
-                v = *reinterpret_cast<const u32x4_t*>(
-                    k + (int64_t)(kv_start + key) * k_tok_stride + k_head_off + c * 16);
-            kreg[i] = v;
+            const int key = min(j0 + row, last);
+            kreg[i] = *reinterpret_cast<const u32x4_t*>(
+                k + (int64_t)(kv_start + key) * k_tok_stride + k_head_off + c * 16);
         }
+        if (v_aligned) {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * NT;
-            const int d = idx >> 3, c = idx & 7;
-            const int key0 = j0 + c * 16;
-            const uint8_t* src = vt + v_head_base + (int64_t)d * total_kv + kv_start + key0;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            const int n = kv_len - key0;   // valid keys in this chunk
-            if (n > 0) {
-                if (v_aligned) {
-                    v = *reinterpret_cast<const u32x4_t*>(src);
-                    if (n < 16) {
-#pragma unroll
-                        for (int wd = 0; wd < 4; ++wd) {
-                            const int keep = n - 4 * wd;   // bytes of this dword to keep
-                            const uint32_t msk = keep >= 4 ? 0xffffffffu
-                                               : keep <= 0 ? 0u
-                                                           : (0xffffffffu >> (32 - 8 * keep));
-                            v[wd] &= msk;
-                        }
-                    }
-                } else {
-                    uint32_t wds[4] = {0u, 0u, 0u, 0u};
-                    for (int bI = 0; bI < 16 && bI < n; ++bI)
-                        wds[bI >> 2] |= (uint32_t)src[bI] << (8 * (bI & 3));
-                    v = u32x4_t{wds[0], wds[1], wds[2], wds[3]};
-                }
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = tid + i * NT;
+                const int d = idx >> 3, c = idx & 7;
+                const int key0 = min(j0 + c * 16, last & ~15);
+                vreg[i] = *reinterpret_cast<const u32x4_t*>(
+                    vt + v_head_base + (int64_t)d * total_kv + kv_start + key0);
             }
-            vreg[i] = v;
+        } else {
+            // unaligned varlen layout: byte loads of the valid keys only
+#pragma unroll
+            for (int i = 0; i < VPT; ++i) {
+                const int idx = tid + i * NT;
+                const int d = idx >> 3, c = idx & 7;
+                const int key0 = j0 + c * 16;
+                const uint8_t* src = vt + v_head_base + (int64_t)d * total_kv + kv_start + key0;
+                uint32_t wds[4] = {0u, 0u, 0u, 0u};
+                const int n = kv_len - key0;
+                for (int bI = 0; bI < 16 && bI < n; ++bI)
+                    wds[bI >> 2] |= (uint32_t)src[bI] << (8 * (bI & 3));
+                vreg[i] = u32x4_t{wds[0], wds[1], wds[2], wds[3]};
+            }
         }
     }
 
-    __device__ __forceinline__ void store(uint8_t* lds, int tid) const {
+    __device__ __forceinline__ void store(uint8_t* lds, int j0, int kv_len, int tid) const {
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int idx = tid + i * NT;
             const int row = idx >> 3, c = idx & 7;
-            *reinterpret_cast<u32x4_t*>(lds + row * D8 + ((c ^ fp8_kswz(row)) << 4)) = kreg[i];
+            const u32x4_t v = (j0 + row < kv_len) ? kreg[i] : zero;
+            *reinterpret_cast<u32x4_t*>(lds + row * D8 + ((c ^ fp8_kswz(row)) << 4)) = v;
         }
 #pragma unroll
         for (int i = 0; i < VPT; ++i) {
             const int idx = tid + i * NT;
             const int d = idx >> 3, c = idx & 7;
-            *reinterpret_cast<u32x4_t*>(lds + K_BYTES + d * BN8 + ((c ^ (d & 7)) << 4)) = vreg[i];
+            const int n = kv_len - (j0 + c * 16);   // valid keys in this 16-key chunk
+            u32x4_t v = vreg[i];
+            if (n < 16) {
+#pragma unroll
+                for (int wd = 0; wd < 4; ++wd) {
+                    const int keep = n - 4 * wd;
+                    const uint32_t msk = keep >= 4 ? 0xffffffffu
+                                       : keep <= 0 ? 0u
+                                                   : (0xffffffffu >> (32 - 8 * keep));
+                    v[wd] &= msk;
+                }
+            }
+            *reinterpret_cast<u32x4_t*>(lds + K_BYTES + d * BN8 + ((c ^ (d & 7)) << 4)) = v;
         }
     }
 };
@@ -182,57 +190,61 @@ __device__ __forceinline__ void fp8_tile_step(Fp8Rows<QB>& st, const uint8_t* ld
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float x = s[kb][qb][r] * c;
                 if constexpr (MASKED) {
                     // key held by register r of block kb for this lane
                     const int key = j0 + 64 * (kb >> 1) + 32 * g + 16 * (kb & 1) + r;
-                    x = (key >= st.lo[qb] && key < st.hi[qb]) ? x : kNegInf;
+                    if (!(key >= st.lo[qb] && key < st.hi[qb])) s[kb][qb][r] = kNegInf;
                 }
-                s[kb][qb][r] = x;
-                mx[qb] = fmaxf(mx[qb], x);
+                mx[qb] = fmaxf(mx[qb], s[kb][qb][r]);
             }
 
-    float alpha[QB], msub[QB];
+    bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         mx[qb] = fmaxf(mx[qb], xor32(mx[qb]));
-        const float mnew = fmaxf(st.m[qb], mx[qb]);
-        msub[qb] = (mnew == kNegInf) ? 0.f : mnew;
-        alpha[qb] = fast_exp2(st.m[qb] - msub[qb]);
-        st.m[qb] = mnew;
+        mx[qb] = (mx[qb] == kNegInf) ? kNegInf : mx[qb] * c;
+        need |= mx[qb] > st.m[qb] + kRescaleSlack;
+    }
+    if (__any(need)) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float mnew = fmaxf(st.m[qb], mx[qb]);
+            const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(st.m[qb] - mnew);
+            st.m[qb] = mnew;
+            st.l[qb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db) st.o[db][qb] *= alpha;
+        }
     }
 
     float rs[QB];
     i32x8_t pb[2][QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) rs[qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+        rs[qb] = 0.f;
+        const float nm = (st.m[qb] == kNegInf) ? 0.f : -st.m[qb];
 #pragma unroll
-    for (int gp = 0; gp < 2; ++gp)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        for (int gp = 0; gp < 2; ++gp) {
 #pragma unroll
             for (int wd = 0; wd < 8; ++wd) {
                 const int kb = 2 * gp + (wd >> 2);
                 const int r0 = 4 * (wd & 3);
-                const float p0 = fast_exp2(s[kb][qb][r0 + 0] - msub[qb]);
-                const float p1 = fast_exp2(s[kb][qb][r0 + 1] - msub[qb]);
-                const float p2 = fast_exp2(s[kb][qb][r0 + 2] - msub[qb]);
-                const float p3 = fast_exp2(s[kb][qb][r0 + 3] - msub[qb]);
-                int packed = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-                packed = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, packed, true);
+                float pv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float sv = s[kb][qb][r0 + e];
+                    pv[e] = fast_exp2(__builtin_fmaf(sv, c, nm));
+                    if constexpr (MASKED) pv[e] = (sv == kNegInf) ? 0.f : pv[e];
+                }
+                int packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+                packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], packed, true);
                 pb[gp][qb][wd] = packed;
                 const f32x2_t back_lo = __builtin_amdgcn_cvt_pk_f32_fp8(packed, false);
                 const f32x2_t back_hi = __builtin_amdgcn_cvt_pk_f32_fp8(packed, true);
                 rs[qb] += (back_lo.x + back_lo.y) + (back_hi.x + back_hi.y);
             }
         }
-
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        rs[qb] += xor32(rs[qb]);
-        st.l[qb] = st.l[qb] * alpha[qb] + rs[qb];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) st.o[db][qb] *= alpha[qb];
+        st.l[qb] += rs[qb] + xor32(rs[qb]);
     }
 
 #pragma unroll
@@ -275,7 +287,9 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     const int h0 = hg << p.pack_log2;
     const int hk = h0 / p.group;
     const float dq = p.descale[0], dk = p.descale[1], dv = p.descale[2];
-    const float c = p.scale * dq * dk * kLog2e;
+    const float c_signed = p.scale * dq * dk * kLog2e;
+    const bool neg = c_signed < 0.f;
+    const float c = fabsf(c_signed);
 
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
@@ -304,6 +318,7 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
                 const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t + 16);
                 v = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
                             (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                if (neg) v ^= (int)0x80808080u;   // apply a negative scale to -q
             }
             st.q[qb][t] = v;
         }
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     if (n_tiles > 0) {
         ld.load(p.k, p.vt, p.total_kv, kv_start, kv_begin, kv_len, k_tok_stride, k_head_off,
                 v_head_base, v_aligned, tid);
-        ld.store(smem, tid);
+        ld.store(smem, kv_begin, kv_len, tid);
     }
     __syncthreads();
     for (int it = 0; it < n_tiles; ++it) {
@@ -369,7 +384,7 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             else
                 fp8_tile_step<QB, true>(st, cur, j, c);
         }
-        if (has_next) ld.store(smem + ((it + 1) & 1) * Tile::BYTES, tid);
+        if (has_next) ld.store(smem + ((it + 1) & 1) * Tile::BYTES, j + BN8, kv_len, tid);
         __syncthreads();
     }
 

@@ -53,9 +53,10 @@ template <int D, int BN, int QB, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     constexpr int NT = NW * 64;
     constexpr int BM = NW * QB * 32;
-    using Tile = PagedTile16<D, BN, NT>;
+    using Tile = PagedTile16<D, BN, NT, false>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Tile::BYTES];
     __shared__ int wave_range[2][NW];
+    __shared__ int win[PAGE_WIN + 1];
 
     int u = blockIdx.x;
     const int hg = u % p.n_head_groups;
@@ -71,6 +72,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int kv_len = p.cu_kv[b + 1] - kv_start;
     const int h0 = hg << p.pack_log2;
     const int hk = h0 / p.group;
+    const bool neg = p.c < 0.f;
+    const float c = fabsf(p.c);
 
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         for (int t = 0; t < D / 16; ++t) {
             u32x4_t v = {0u, 0u, 0u, 0u};
             if (valid[qb]) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-            st.q[qb][t] = v;
+            st.q[qb][t] = neg ? neg16x8(v) : v;
         }
         int lo = 0, hi = kv_len;
         if (valid[qb]) {
@@ -132,34 +135,41 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         kv_end = max(kv_end, wave_range[1][i]);
     }
     kv_begin &= ~15;   // 16-key aligned: a V unit never straddles a page
-    const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BN - 1) / BN : 0;
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
     const int tok_stride = p.num_kv_heads * D;
     const int head_off = hk * D;
+    const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
     Tile ld;
-    if (n_tiles > 0) {
-        ld.load(p.k_cache, p.v_cache, table, kv_begin, kv_len, p.bs_log2, tok_stride, head_off,
-                tid);
-        ld.store(smem, tid);
-    }
-    __syncthreads();
 
-    for (int it = 0; it < n_tiles; ++it) {
-        const int j = kv_begin + it * BN;
-        const uint8_t* cur = smem + (it & 1) * Tile::BYTES;
-        const bool has_next = it + 1 < n_tiles;
-        if (has_next)
-            ld.load(p.k_cache, p.v_cache, table, j + BN, kv_len, p.bs_log2, tok_stride,
-                    head_off, tid);
-        if (w_any && j < w_hi && j + BN > w_lo) {
-            if (j >= w_lo_max && j + BN <= w_hi_min)
-                tile_step<D, BN, BN / 32, QB, BF16, false>(st, cur, j, 0, p.c);
-            else
-                tile_step<D, BN, BN / 32, QB, BF16, true>(st, cur, j, 0, p.c);
-        }
-        if (has_next) ld.store(smem + ((it + 1) & 1) * Tile::BYTES, tid);
+    // Key chunks of PAGE_WIN blocks: stage the chunk's block ids, then stream
+    // its tiles with the next tile's loads in flight during the current one.
+    for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
+        const int n_tiles = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
+        const int first = cs >> p.bs_log2;
+        fill_page_window(win, table, first, n_blocks, tid, NT);
         __syncthreads();
+        ld.load(p.k_cache, p.v_cache, win, first, cs, kv_len, p.bs_log2, tok_stride, head_off,
+                tid);
+        ld.store(smem, cs, kv_len, tid);
+        __syncthreads();
+        for (int it = 0; it < n_tiles; ++it) {
+            const int j = cs + it * BN;
+            const uint8_t* cur = smem + (it & 1) * Tile::BYTES;
+            const bool has_next = it + 1 < n_tiles;
+            if (has_next)
+                ld.load(p.k_cache, p.v_cache, win, first, j + BN, kv_len, p.bs_log2, tok_stride,
+                        head_off, tid);
+            if (w_any && j < w_hi && j + BN > w_lo) {
+                if (j >= w_lo_max && j + BN <= w_hi_min)
+                    tile_step<D, BN, BN / 32, QB, BF16, false>(st, cur, j, 0, c);
+                else
+                    tile_step<D, BN, BN / 32, QB, BF16, true>(st, cur, j, 0, c);
+            }
+            if (has_next) ld.store(smem + ((it + 1) & 1) * Tile::BYTES, j + BN, kv_len, tid);
+            __syncthreads();
+        }
     }
 
 #pragma unroll
@@ -193,15 +203,24 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
 
 }  // namespace
 
+// Tile configurations (BN keys per tile, QB query blocks of 32 rows per wave,
+// NW waves per workgroup).
+#ifndef ATTN_PREFILL_D128
+#define ATTN_PREFILL_D128 64, 1, 8
+#endif
+#ifndef ATTN_PREFILL_D64
+#define ATTN_PREFILL_D64 128, 1, 8
+#endif
+
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16,
                                 int max_seqlen_q, hipStream_t s) {
     if (head_size == 128) {
-        return bf16 ? launch_cfg<128, 64, 2, 4, true>(p, max_seqlen_q, s)
-                    : launch_cfg<128, 64, 2, 4, false>(p, max_seqlen_q, s);
+        return bf16 ? launch_cfg<128, ATTN_PREFILL_D128, true>(p, max_seqlen_q, s)
+                    : launch_cfg<128, ATTN_PREFILL_D128, false>(p, max_seqlen_q, s);
     }
     if (head_size == 64) {
-        return bf16 ? launch_cfg<64, 128, 2, 4, true>(p, max_seqlen_q, s)
-                    : launch_cfg<64, 128, 2, 4, false>(p, max_seqlen_q, s);
+        return bf16 ? launch_cfg<64, ATTN_PREFILL_D64, true>(p, max_seqlen_q, s)
+                    : launch_cfg<64, ATTN_PREFILL_D64, false>(p, max_seqlen_q, s);
     }
     return hipErrorInvalidValue;
 }

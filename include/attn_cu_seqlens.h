@@ -176,8 +176,9 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
  * with their logsumexp (the LSE output of the blt issue's kernel options).
  *   q            [batch, num_heads, head_size], ATTN_F16 or ATTN_BF16
  *   cu_seqlens_kv int32 [batch + 1]; max_seqlen_kv bounds every kv length
- *   split_tokens keys per split, a multiple of 256, or 0 to let the library
- *                choose from (batch, num_kv_heads, max_seqlen_kv)
+ *   split_tokens keys per split: a multiple of 256 no larger than 8192, or 0
+ *                to let the library choose from (batch, num_kv_heads,
+ *                max_seqlen_kv)
  *   out          [batch, num_heads, head_size], same dtype as q
  *   lse          float32 [batch, num_heads] or NULL
  *   workspace    device scratch of at least

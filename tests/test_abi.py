@@ -99,6 +99,7 @@ def test_decode_host_checks(lib):
     ws = lib.attn_paged_decode_workspace_bytes
     assert ws(64, 32, 8, 128, 32768, 0) > 0
     assert ws(64, 32, 8, 128, 32768, 100) == 0          # split not a multiple of 256
+    assert ws(64, 32, 8, 128, 32768, 8448) == 0         # split above 8192
     assert ws(0, 32, 8, 128, 1, 0) == 0
     need = ws(4, 8, 2, 128, 1000, 256)
     assert need == 4 * 8 * 4 * 128 * 4 + 4 * 8 * 4 * 2 * 4
@@ -116,6 +117,7 @@ def test_decode_host_checks(lib):
     assert call(ws=ctypes.c_void_p(128)) == 6             # not 256-byte aligned
     assert call(hq=66, hkv=1) == 3                      # group above 32
     assert call(split=300) == 2
+    assert call(split=8448) == 2                        # above 8192
     assert call(batch=0) == 0
 
 

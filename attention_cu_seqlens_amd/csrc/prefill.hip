@@ -12,9 +12,8 @@
 // diagonal of a tile spans BM / P tokens.
 //
 // Work decomposition needs no device->host sync: the host sizes the grid from
-// max_seqlen_q; workgroup ids map to (query tile, sequence, head group) with
-// the LAST query tiles first (the longest causal rows start earliest), and a
-// workgroup whose tile lies past its sequence's end exits.
+// max_seqlen_q; workgroup ids map to (sequence, head group, query tile) -- see
+// the kernel -- and a workgroup whose tile lies past its sequence's end exits.
 //
 // Masks reduce to one visible key interval [lo, hi) per query row: causal
 // (bottom-right) and patch bound hi, document ids (non-decreasing within a
@@ -24,6 +23,7 @@
 
 #include "device_common.h"
 #include "kernels.h"
+#include "ring.h"
 
 namespace attn {
 
@@ -49,20 +49,76 @@ __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int x) {
 
 }  // namespace
 
+// Ring depth: up to kStages - 1 tiles in flight while one is consumed.
+constexpr int kStages = 4;
+
+// Per-wave pipeline state of one 32-row block.
+template <int D, int BN>
+struct PrefillWave {
+    f32x16_t s[BN / 32];      // scores of the tile waiting for its softmax
+    u32x4_t pb[BN / 32][2];   // probabilities of the tile waiting for its P.V
+    f32x16_t o[D / 32];
+    float m, lpart, alpha;
+    bool need;
+};
+
+// Softmax phase (VALU): mask the scores of the tile at key j0 when partial,
+// then probabilities into pb.
+template <int D, int BN, bool BF16>
+__device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool partial, int j0, int lo,
+                                              int hi, float c) {
+    if (partial) {
+        const int g = lane_id() >> 5;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                if (!(key >= lo && key < hi)) st.s[kb][r] = kNegInf;
+            }
+        softmax_tile<BN, BF16, true>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need);
+    } else {
+        softmax_tile<BN, BF16, false>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need);
+    }
+}
+
+// MFMA phase: O^T += V^T P^T for the softmaxed tile (after the rare rescale),
+// then S^T = K Q^T for the next tile.
+template <int D, int BN, bool BF16>
+__device__ __forceinline__ void phase_mfma(PrefillWave<D, BN>& st, const u32x4_t (&q)[D / 16],
+                                           const uint8_t* v_stage, const uint8_t* k_stage) {
+    if (v_stage != nullptr) {
+        if (st.need) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) st.o[db] *= st.alpha;
+            st.need = false;
+        }
+        pv_tile<D, BN, BF16>(st.o, v_stage, st.pb);
+    }
+    if (k_stage != nullptr) qk_tile<D, BN, BF16>(st.s, k_stage, q);
+}
+
 template <int D, int BN, int QB, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
-    constexpr int NT = NW * 64;
-    constexpr int BM = NW * QB * 32;
-    using Tile = PagedTile16<D, BN, NT, false>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Tile::BYTES];
+    static_assert(QB == 1 && NW == 8, "two groups of four single-block waves");
+    constexpr int BM = NW * 32;
+    using R = Ring16<D, BN, NW>;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * R::STAGE];
     __shared__ int wave_range[2][NW];
     __shared__ int win[PAGE_WIN + 1];
 
-    int u = blockIdx.x;
-    const int hg = u % p.n_head_groups;
-    u /= p.n_head_groups;
-    const int b = u % p.batch;
-    const int qt = p.n_qtiles - 1 - u / p.batch;
+    // Workgroup i runs on XCD i % 8.  Units (sequence, head group) are dealt
+    // to XCDs round-robin; an XCD runs its units one after another, each unit's
+    // query tiles longest first, so the tiles that share one K/V stream run
+    // together on one XCD and share its L2.
+    const int xcd = blockIdx.x & 7;
+    const int k = blockIdx.x >> 3;
+    const int m = k / p.n_qtiles;
+    const int qt = p.n_qtiles - 1 - (k - m * p.n_qtiles);
+    const int unit = xcd + 8 * m;
+    if (unit >= p.batch * p.n_head_groups) return;
+    const int b = unit / p.n_head_groups;
+    const int hg = unit - b * p.n_head_groups;
 
     const int q_start = p.cu_q[b];
     const int q_len = p.cu_q[b + 1] - q_start;
@@ -78,50 +134,43 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
     const int col = lane & 31, g = lane >> 5;
+    // Waves 0-3 and 4-7 each hold one wave per SIMD; the second group runs
+    // half a tile behind the first, so on every SIMD one wave issues MFMAs
+    // while the other computes a softmax.
+    const bool lead = w < NW / 2;
 
-    RowsState<D, QB> st;
-    st.init();
-    int tok[QB], head[QB];
-    bool valid[QB];
-    int my_lo = 0x7fffffff, my_hi = -0x7fffffff, my_lo_max = -0x7fffffff, my_hi_min = 0x7fffffff;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int r = (w * QB + qb) * 32 + col;
-        tok[qb] = tok0 + (r >> p.pack_log2);
-        head[qb] = h0 + (r & ((1 << p.pack_log2) - 1));
-        valid[qb] = tok[qb] < q_len;
-        const uint16_t* qp =
-            p.q + ((int64_t)(q_start + tok[qb]) * p.num_heads + head[qb]) * D + 8 * g;
+    // this lane's query row
+    const int r = w * 32 + col;
+    const int tok = tok0 + (r >> p.pack_log2);
+    const int head = h0 + (r & ((1 << p.pack_log2) - 1));
+    const bool valid = tok < q_len;
+    u32x4_t q[D / 16];
+    {
+        const uint16_t* qp = p.q + ((int64_t)(q_start + tok) * p.num_heads + head) * D + 8 * g;
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
             u32x4_t v = {0u, 0u, 0u, 0u};
-            if (valid[qb]) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-            st.q[qb][t] = neg ? neg16x8(v) : v;
+            if (valid) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
+            q[t] = neg ? neg16x8(v) : v;
         }
-        int lo = 0, hi = kv_len;
-        if (valid[qb]) {
-            if (p.mask & kMaskCausal) hi = min(hi, tok[qb] + (kv_len - q_len) + 1);
-            if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok[qb]] + 1);
-            if (p.mask & kMaskDocument) {
-                const int doc = p.q_ids[q_start + tok[qb]];
-                lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
-                hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
-            }
-            if (hi < lo) hi = lo;
-            my_lo = min(my_lo, lo);
-            my_hi = max(my_hi, hi);
-            my_lo_max = max(my_lo_max, lo);
-            my_hi_min = min(my_hi_min, hi);
-        } else {
-            lo = 0;
-            hi = 0;
+    }
+    int lo = 0, hi = 0;
+    if (valid) {
+        hi = kv_len;
+        if (p.mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
+        if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
+        if (p.mask & kMaskDocument) {
+            const int doc = p.q_ids[q_start + tok];
+            lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
+            hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
         }
-        st.lo[qb] = lo;
-        st.hi[qb] = hi;
+        if (hi < lo) hi = lo;
     }
     // Wave extremes over valid rows; an all-invalid wave gets an empty range.
-    const int w_lo = wave_min(my_lo), w_hi = wave_max(my_hi);
-    const int w_lo_max = wave_max(my_lo_max), w_hi_min = wave_min(my_hi_min);
+    const int w_lo = wave_min(valid ? lo : 0x7fffffff);
+    const int w_hi = wave_max(valid ? hi : -0x7fffffff);
+    const int w_lo_max = wave_max(valid ? lo : -0x7fffffff);
+    const int w_hi_min = wave_min(valid ? hi : 0x7fffffff);
     const bool w_any = w_hi > w_lo;
     if (lane == 0) {
         wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
@@ -134,54 +183,86 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         kv_begin = min(kv_begin, wave_range[0][i]);
         kv_end = max(kv_end, wave_range[1][i]);
     }
-    kv_begin &= ~15;   // 16-key aligned: a V unit never straddles a page
+    kv_begin &= ~15;
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
     const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
     const int tok_stride = p.num_kv_heads * D;
     const int head_off = hk * D;
     const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
-    Tile ld;
+    R ld;
+    ld.init(lane, w);
+
+    PrefillWave<D, BN> st;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
+    st.m = kNegInf;
+    st.lpart = 0.f;
+    st.alpha = 1.f;
+    st.need = false;
 
     // Key chunks of PAGE_WIN blocks: stage the chunk's block ids, then stream
-    // its tiles with the next tile's loads in flight during the current one.
+    // its tiles through the ring.
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
-        const int n_tiles = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
+        const int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
-        fill_page_window(win, table, first, n_blocks, tid, NT);
+        fill_page_window(win, table, first, n_blocks, tid, NW * 64);
         __syncthreads();
-        ld.load(p.k_cache, p.v_cache, win, first, cs, kv_len, p.bs_log2, tok_stride, head_off,
-                tid);
-        ld.store(smem, cs, kv_len, tid);
-        __syncthreads();
-        for (int it = 0; it < n_tiles; ++it) {
-            const int j = cs + it * BN;
-            const uint8_t* cur = smem + (it & 1) * Tile::BYTES;
-            const bool has_next = it + 1 < n_tiles;
-            if (has_next)
-                ld.load(p.k_cache, p.v_cache, win, first, j + BN, kv_len, p.bs_log2, tok_stride,
-                        head_off, tid);
-            if (w_any && j < w_hi && j + BN > w_lo) {
-                if (j >= w_lo_max && j + BN <= w_hi_min)
-                    tile_step<D, BN, BN / 32, QB, BF16, false>(st, cur, j, 0, c);
-                else
-                    tile_step<D, BN, BN / 32, QB, BF16, true>(st, cur, j, 0, c);
-            }
-            if (has_next) ld.store(smem + ((it + 1) & 1) * Tile::BYTES, j + BN, kv_len, tid);
-            __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kStages - 1; ++k)
+            if (k < n)
+                ld.issue(ring + k * R::STAGE, p.k_cache, p.v_cache, win, first, cs + k * BN,
+                         kv_len, p.bs_log2, tok_stride, head_off, w);
+        {
+            const int later = min(n - 1, kStages - 2);   // tiles issued after tile 0
+            if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
+        block_barrier();
+        if (lead) phase_mfma<D, BN, BF16>(st, q, nullptr, ring);
+
+        for (int jt = 0; jt < n; ++jt) {
+            const int j0 = cs + jt * BN;
+            const bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
+            const uint8_t* st_cur = ring + (jt % kStages) * R::STAGE;
+            const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
+            const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
+            // phase 1: lead softmaxes tile jt; trail finishes tile jt-1 and scores tile jt
+            if (lead)
+                phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
+            else
+                phase_mfma<D, BN, BF16>(st, q, jt > 0 ? st_prev + R::TILE : nullptr, st_cur);
+            if (jt + 1 < n) {
+                // tile jt+1 must have landed; the one after it may stay in flight
+                if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+            block_barrier();
+            // the stage of tile jt-1 is free now: refill it with tile jt+3
+            if (jt + kStages - 1 < n)
+                ld.issue(ring + ((jt + kStages - 1) % kStages) * R::STAGE, p.k_cache, p.v_cache,
+                         win, first, cs + (jt + kStages - 1) * BN, kv_len, p.bs_log2, tok_stride,
+                         head_off, w);
+            // phase 2: lead finishes tile jt and scores tile jt+1; trail softmaxes tile jt
+            if (lead)
+                phase_mfma<D, BN, BF16>(st, q, st_cur + R::TILE, jt + 1 < n ? st_next : nullptr);
+            else
+                phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
+            block_barrier();
+        }
+        if (!lead && n > 0)
+            phase_mfma<D, BN, BF16>(st, q, ring + ((n - 1) % kStages) * R::STAGE + R::TILE,
+                                    nullptr);
+        block_barrier();   // the next chunk's window and ring refill start after all reads
     }
 
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        if (!valid[qb]) continue;
-        const int64_t row = (int64_t)(q_start + tok[qb]) * p.num_heads + head[qb];
-        f32x16_t o_db[D / 32];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o_db[db] = st.o[db][qb];
-        store_row<D, BF16>(o_db, st.l[qb], p.out + row * D);
+    const float l = st.lpart + xor32(st.lpart);
+    if (valid) {
+        const int64_t rowi = (int64_t)(q_start + tok) * p.num_heads + head;
+        store_row<D, BF16>(st.o, l, p.out + rowi * D);
         if (p.lse != nullptr && g == 0)
-            p.lse[row] = st.l[qb] > 0.f ? (st.m[qb] + __builtin_log2f(st.l[qb])) * kLn2 : kNegInf;
+            p.lse[rowi] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
     }
 }
 
@@ -193,7 +274,8 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
     PrefillParams p = p0;
     const int tokens_per_tile = BM >> p.pack_log2;
     p.n_qtiles = (max_seqlen_q + tokens_per_tile - 1) / tokens_per_tile;
-    const int64_t grid = (int64_t)p.n_qtiles * p.batch * p.n_head_groups;
+    const int64_t units = (int64_t)p.batch * p.n_head_groups;
+    const int64_t grid = 8 * ((units + 7) / 8) * p.n_qtiles;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16>), dim3((unsigned)grid),
@@ -209,7 +291,7 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
 #define ATTN_PREFILL_D128 64, 1, 8
 #endif
 #ifndef ATTN_PREFILL_D64
-#define ATTN_PREFILL_D64 128, 1, 8
+#define ATTN_PREFILL_D64 64, 1, 8
 #endif
 
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16,

@@ -1,0 +1,246 @@
+// Multi-stage LDS ring for paged K/V tiles of 16-bit dtypes, filled with
+// direct global->LDS loads (no register staging), plus the MFMA tile
+// products that read it.
+//
+// Tile layout in LDS (both K and V): row-major, one row per key, D/8
+// 16-byte chunks per row; logical chunk c of row r is stored at chunk
+// c ^ swz<D>(r).  gfx950's LDS serves 256 bytes per clock (64 banks = 16
+// groups of 16 bytes), so the swizzle makes
+//   * the 16 lanes that read one chunk of 16 consecutive K rows (the A
+//     operand of S^T = K.Q^T, 16 bytes per lane) hit 16 bank groups;
+//   * the 32 lanes of one transposed V read (4 rows x 4 chunks x 2 halves,
+//     8 bytes per lane) hit all 64 banks once.
+// A direct LDS load writes 64 lanes x 16 bytes = 1 KB of consecutive LDS per
+// instruction, so each lane simply fetches the global chunk that belongs at
+// its LDS position.
+//
+// V is consumed with the gfx950 transposed LDS read (16-bit elements, 8 bytes
+// per lane): within each group of 16 lanes, output lane i receives element
+// i%4 of the 8-byte rows read by lanes 4e + i/4, e = 0..3.  Pointing lane
+// 4e + q of the group at V[key0 + e][d0 + 4q .. +3] gives lane i the four keys
+// key0..key0+3 of dimension d0 + i -- the key-contiguous V^T operand, read
+// from a plain row-major V tile (the layout question of the FlexAttention fp8
+// commit, "[FlexAttention] Enforce Q,K,V memory layouts for fp8 flex
+// attention...", Context, answered in the LDS read instead of in HBM).
+#pragma once
+
+#include "device_common.h"
+
+namespace attn {
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (other counters untouched).
+__host__ __device__ constexpr unsigned vmcnt_imm(int n) {
+    return 0x0F70u | (unsigned)(n & 15) | ((unsigned)((n >> 4) & 3) << 14);
+}
+
+// Workgroup barrier without a memory fence: the direct-to-LDS loads of later
+// tiles stay in flight across it (each wave waits for its own loads with an
+// explicit vmcnt first).  The memory clobber keeps the compiler from moving
+// LDS accesses across it.
+// Every LDS read this wave issued has returned before it signals the barrier
+// (lgkmcnt(0)), so a stage may be refilled right after the barrier.
+__device__ __forceinline__ void block_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07Fu);   // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// D = 128: 256-byte rows, one row spans all banks; the low two row bits pick
+// the 4-chunk group of a V read and bits 2-3 separate the 16 K rows.
+// D = 64: 128-byte rows, row parity already selects the bank half.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// One direct global->LDS load of 16 bytes per lane: lane i's bytes land at
+// LDS address lds_base + 16*i (lds_base must be wave-uniform).  Written as
+// inline asm so the compiler does not drain it with vmcnt(0) before every
+// later LDS read (it cannot tell ring stages apart); the code that reads a
+// stage waits with an explicit vmcnt first.  The instruction has no
+// destination register.
+__device__ __forceinline__ void dma16(const void* gptr, const uint8_t* lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(lds_base));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(m0), "v"(gptr)
+                 : "memory", "m0");
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ u32x2_t ds_read_tr16(const uint8_t* p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+    return __builtin_bit_cast(u32x2_t, v);
+}
+
+template <int D, int BN, int NW>
+struct Ring16 {
+    static constexpr int CPR = D / 8;           // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;          // bytes per row
+    static constexpr int TILE = BN * ROWB;      // bytes of one K (or V) tile
+    static constexpr int STAGE = 2 * TILE;      // K tile then V tile
+    static constexpr int RPI = 64 / CPR;        // rows per 1 KB load instruction
+    static constexpr int IPW = TILE / 1024 / NW;  // load instructions per wave per tensor
+    static_assert(TILE % (1024 * NW) == 0, "tile does not divide over the waves");
+    static constexpr int LOADS_PER_TILE = 2 * IPW;  // per thread: K and V
+
+    int row[IPW];     // tile-relative key row each load instruction of this lane fetches
+    int chunk[IPW];   // logical chunk of that row (the swizzle applied)
+
+    __device__ __forceinline__ void init(int lane, int w) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int b = w * IPW + i;
+            row[i] = b * RPI + lane / CPR;
+            chunk[i] = (lane % CPR) ^ swz<D>(row[i]);
+        }
+    }
+
+    // Keys [j0, j0 + BN) of one sequence (kv_len >= 1) into `stage`.  Rows past
+    // kv_len read row kv_len - 1: they hold finite values and every key past
+    // kv_len is masked to probability 0 by the caller.
+    __device__ __forceinline__ void issue(uint8_t* stage, const uint16_t* cache_k,
+                                          const uint16_t* cache_v, const int* win, int first,
+                                          int j0, int kv_len, int bs_log2, int tok_stride,
+                                          int head_off, int w) const {
+        const int bs_mask = (1 << bs_log2) - 1;
+        const int64_t page_stride = (int64_t)tok_stride << bs_log2;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const int tok = min(j0 + row[i], kv_len - 1);
+            const int page = win[(tok >> bs_log2) - first];
+            const int64_t off = page * page_stride +
+                                ((tok & bs_mask) * tok_stride + head_off + chunk[i] * 8);
+            const uint8_t* dst = stage + (w * IPW + i) * 1024;
+            dma16(cache_k + off, dst);
+            dma16(cache_v + off, dst + TILE);
+        }
+    }
+};
+
+// Operand prefetch depths (in MFMA steps) of the two tile products: the LDS
+// reads of step t + PD issue before the MFMAs of step t, so LDS latency hides
+// under the MFMAs; sched_barrier pins that order against the scheduler.
+constexpr int kQkPrefetch = 2;
+constexpr int kPvPrefetch = 4;
+
+// S^T[kb] += K_tile(kb) . Q^T for the BN/32 key blocks of a tile.
+template <int D, int BN, bool BF16>
+__device__ __forceinline__ void qk_tile(f32x16_t (&s)[BN / 32], const uint8_t* kt,
+                                        const u32x4_t (&q)[D / 16]) {
+    constexpr int ROWB = D * 2;
+    constexpr int NKB = BN / 32;
+    constexpr int T = D / 16;
+    constexpr int PD = kQkPrefetch < T ? kQkPrefetch : T;
+    const int lane = lane_id();
+    const int col = lane & 31, g = lane >> 5;
+    const int sw = swz<D>(col);   // rows kb*32 + col share their low 5 bits
+    const uint8_t* base = kt + col * ROWB;
+    auto frag = [&](int t, int kb) {
+        return *reinterpret_cast<const u32x4_t*>(base + kb * 32 * ROWB +
+                                                 (((2 * t + g) ^ sw) << 4));
+    };
+    u32x4_t a[PD + 1][NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16_t{};
+#pragma unroll
+    for (int t = 0; t < PD; ++t)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) a[t][kb] = frag(t, kb);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t + PD < T) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) a[(t + PD) % (PD + 1)][kb] = frag(t + PD, kb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32<BF16>(a[t % (PD + 1)][kb], q[t], s[kb]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// O^T[db] += V_tile^T(db) . P^T with P^T packed per (key block, 16-key step).
+template <int D, int BN, bool BF16>
+__device__ __forceinline__ void pv_tile(f32x16_t (&o)[D / 32], const uint8_t* vt,
+                                        const u32x4_t (&pb)[BN / 32][2]) {
+    constexpr int ROWB = D * 2;
+    constexpr int NKB = BN / 32;
+    constexpr int STEPS = (D / 32) * NKB * 2;
+    constexpr int PD = kPvPrefetch < STEPS ? kPvPrefetch : STEPS;
+    const int lane = lane_id();
+    const int j = lane & 15, h = lane >> 4, g = h >> 1;
+    const int r0 = 4 * g + (j >> 2);                 // row (mod 16) of the first read
+    const int sw_lo = swz<D>(r0), sw_hi = swz<D>(r0 + 8);
+    const uint8_t* base = vt + r0 * ROWB + (j & 1) * 8;
+    auto frag = [&](int i) {
+        const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
+        const int c = (db * 32 + 16 * (h & 1) + 4 * (j & 3)) >> 3;
+        const uint8_t* p0 = base + (kb * 32 + 16 * tp) * ROWB;
+        const u32x2_t lo = ds_read_tr16(p0 + ((c ^ sw_lo) << 4));
+        const u32x2_t hi = ds_read_tr16(p0 + 8 * ROWB + ((c ^ sw_hi) << 4));
+        return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+    };
+    u32x4_t a[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) a[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+        if (i + PD < STEPS) a[(i + PD) % (PD + 1)] = frag(i + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
+        o[db] = mfma32<BF16>(a[i % (PD + 1)], pb[kb][tp], o[db]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Online softmax of one tile's scores for one 32-row block (QB = 1).
+// s: raw S^T accumulators (masked entries already -inf when MASKED);
+// on return pb holds the packed probabilities, m may have moved (then *need
+// is set and alpha holds exp2(m_old - m_new)), and lpart accumulated this
+// lane's partial row sum (relative to the final m after any rescale).
+template <int BN, bool BF16, bool MASKED>
+__device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], float c, float& m,
+                                             float& lpart, u32x4_t (&pb)[BN / 32][2],
+                                             float& alpha, bool& need) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, xor32(mx));
+    mx = (mx == kNegInf) ? kNegInf : mx * c;
+    const bool up = mx > m + kRescaleSlack;
+    need = __any(up);
+    const float mnew = need ? fmaxf(m, mx) : m;
+    alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
+    m = mnew;
+    const float nm = (mnew == kNegInf) ? 0.f : -mnew;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, nm));
+            if constexpr (MASKED) p[r] = (s[kb][r] == kNegInf) ? 0.f : p[r];
+            rs += p[r];
+        }
+#pragma unroll
+        for (int tp = 0; tp < 2; ++tp) {
+            u32x4_t wv;
+            wv.x = pack2<BF16>(p[8 * tp + 0], p[8 * tp + 1]);
+            wv.y = pack2<BF16>(p[8 * tp + 2], p[8 * tp + 3]);
+            wv.z = pack2<BF16>(p[8 * tp + 4], p[8 * tp + 5]);
+            wv.w = pack2<BF16>(p[8 * tp + 6], p[8 * tp + 7]);
+            pb[kb][tp] = wv;
+        }
+    }
+    lpart = lpart * alpha + rs;
+}
+
+}  // namespace attn

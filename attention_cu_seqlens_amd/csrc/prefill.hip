@@ -82,27 +82,32 @@ __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool parti
     }
 }
 
-// MFMA phase: O^T += V^T P^T for the softmaxed tile (after the rare rescale),
-// then S^T = K Q^T for the next tile.
-template <int D, int BN, bool BF16>
-__device__ __forceinline__ void phase_mfma(PrefillWave<D, BN>& st, const u32x4_t (&q)[D / 16],
-                                           const uint8_t* v_stage, const uint8_t* k_stage) {
-    if (v_stage != nullptr) {
-        if (st.need) {
+// O^T += V^T P^T for the softmaxed tile (after the rare rescale); `hook`
+// runs after every MFMA.
+template <int D, int BN, bool BF16, class Hook = NoHook>
+__device__ __forceinline__ void step_pv(PrefillWave<D, BN>& st, const uint8_t* v_tile,
+                                        const Hook& hook = Hook{}) {
+    if (st.need) {
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) st.o[db] *= st.alpha;
-            st.need = false;
-        }
-        pv_tile<D, BN, BF16>(st.o, v_stage, st.pb);
+        for (int db = 0; db < D / 32; ++db) st.o[db] *= st.alpha;
+        st.need = false;
     }
-    if (k_stage != nullptr) qk_tile<D, BN, BF16>(st.s, k_stage, q);
+    pv_tile<D, BN, BF16>(st.o, v_tile, st.pb, hook);
+}
+
+// S^T = K Q^T for a tile; `hook` runs after every MFMA, steps from step0.
+template <int D, int BN, bool BF16, class Hook = NoHook>
+__device__ __forceinline__ void step_qk(PrefillWave<D, BN>& st, const u32x4_t (&q)[D / 16],
+                                        const uint8_t* k_tile, const Hook& hook = Hook{},
+                                        int step0 = 0) {
+    qk_tile<D, BN, BF16>(st.s, k_tile, q, hook, step0);
 }
 
 template <int D, int BN, int QB, int NW, bool BF16>
 __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     static_assert(QB == 1 && NW == 8, "two groups of four single-block waves");
     constexpr int BM = NW * 32;
-    using R = Ring16<D, BN, NW>;
+    using R = Ring16<D, BN, NW / 2>;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * R::STAGE];
     __shared__ int wave_range[2][NW];
     __shared__ int win[PAGE_WIN + 1];
@@ -132,11 +137,13 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const float c = fabsf(p.c);
 
     const int tid = threadIdx.x;
-    const int lane = lane_id(), w = wave_id();
+    const int lane = lane_id();
+    const int w = wave_id();
     const int col = lane & 31, g = lane >> 5;
     // Waves 0-3 and 4-7 each hold one wave per SIMD; the second group runs
     // half a tile behind the first, so on every SIMD one wave issues MFMAs
-    // while the other computes a softmax.
+    // while the other computes a softmax.  The first group alone loads the
+    // K/V ring, between the MFMAs of its MFMA phase.
     const bool lead = w < NW / 2;
 
     // this lane's query row
@@ -183,7 +190,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         kv_begin = min(kv_begin, wave_range[0][i]);
         kv_end = max(kv_end, wave_range[1][i]);
     }
-    kv_begin &= ~15;
+    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin & ~15);
+    kv_end = __builtin_amdgcn_readfirstlane(kv_end);
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
     const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
@@ -191,7 +199,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int head_off = hk * D;
     const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
     R ld;
-    ld.init(lane, w);
+    ld.init(lane, w & (NW / 2 - 1), tok_stride);
+    const uint32_t ring_lds = lds_addr(ring);
 
     PrefillWave<D, BN> st;
 #pragma unroll
@@ -203,24 +212,43 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 
     // Key chunks of PAGE_WIN blocks: stage the chunk's block ids, then stream
     // its tiles through the ring.
+    //
+    // Per tile j each wave runs QK(j) -> softmax(j) -> PV(j).  The two waves
+    // of a SIMD are offset by half a tile, so that one issues MFMAs (and their
+    // LDS operand reads) while the other runs the softmax on the VALU:
+    //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
+    //   phase 2 of tile j: lead PV(j), QK(j+1), loads    trail softmax(j)
+    // The lead waves alone load the ring: tile j+3 goes into the stage of
+    // tile j-1 (free once phase 1 of tile j is over), one load after every
+    // other MFMA of the lead's P.V.
+    constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
+#ifndef ATTN_DMA_OVER_QK
+#define ATTN_DMA_OVER_QK 0
+#endif
+    // loads go out over P.V alone, or over P.V and the QK that follows it
+    constexpr int kDmaSteps = kPvSteps + (ATTN_DMA_OVER_QK ? (D / 16) * (BN / 32) : 0);
+    static_assert(kDmaSteps % R::LOADS_PER_TILE == 0, "loads spread evenly over the MFMAs");
+    using Hook = DmaHook<R, kDmaSteps / R::LOADS_PER_TILE>;
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
         const int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
         fill_page_window(win, table, first, n_blocks, tid, NW * 64);
         __syncthreads();
+        if (lead) {
 #pragma unroll
-        for (int k = 0; k < kStages - 1; ++k)
-            if (k < n)
-                ld.issue(ring + k * R::STAGE, p.k_cache, p.v_cache, win, first, cs + k * BN,
-                         kv_len, p.bs_log2, tok_stride, head_off, w);
-        {
-            const int later = min(n - 1, kStages - 2);   // tiles issued after tile 0
-            if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
-            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+            for (int k = 0; k < kStages - 1; ++k)
+                if (k < n)
+                    ld.issue(ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first, cs + k * BN,
+                             kv_len, p.bs_log2, tok_stride, head_off, w,
+                             win[R::slot(cs + k * BN, first, p.bs_log2, w)]);
+            // tile 0 must have landed; tiles 1 and 2 may stay in flight
+            static_assert(kStages == 4, "wait counts below");
+            if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
+            else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
         block_barrier();
-        if (lead) phase_mfma<D, BN, BF16>(st, q, nullptr, ring);
+        if (lead) step_qk<D, BN, BF16>(st, q, ring);
 
         for (int jt = 0; jt < n; ++jt) {
             const int j0 = cs + jt * BN;
@@ -228,32 +256,49 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             const uint8_t* st_cur = ring + (jt % kStages) * R::STAGE;
             const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
             const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
-            // phase 1: lead softmaxes tile jt; trail finishes tile jt-1 and scores tile jt
-            if (lead)
+            // phase 1
+            if (lead) {
                 phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
-            else
-                phase_mfma<D, BN, BF16>(st, q, jt > 0 ? st_prev + R::TILE : nullptr, st_cur);
-            if (jt + 1 < n) {
-                // tile jt+1 must have landed; the one after it may stay in flight
+            } else {
+                if (jt > 0) step_pv<D, BN, BF16>(st, st_prev + R::TILE);
+                step_qk<D, BN, BF16>(st, q, st_cur);
+            }
+            const int j3 = cs + (jt + kStages - 1) * BN;
+            const bool load3 = lead && jt + kStages - 1 < n;
+            int page = 0;
+            if (load3) page = win[R::slot(j3, first, p.bs_log2, w)];
+            // tile jt+1 must have landed; tile jt+2, issued after it, may stay in
+            // flight
+            if (lead && jt + 1 < n) {
                 if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             block_barrier();
-            // the stage of tile jt-1 is free now: refill it with tile jt+3
-            if (jt + kStages - 1 < n)
-                ld.issue(ring + ((jt + kStages - 1) % kStages) * R::STAGE, p.k_cache, p.v_cache,
-                         win, first, cs + (jt + kStages - 1) * BN, kv_len, p.bs_log2, tok_stride,
-                         head_off, w);
-            // phase 2: lead finishes tile jt and scores tile jt+1; trail softmaxes tile jt
-            if (lead)
-                phase_mfma<D, BN, BF16>(st, q, st_cur + R::TILE, jt + 1 < n ? st_next : nullptr);
-            else
+            // phase 2
+            if (lead) {
+                const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
+                const bool spread = load3 && R::whole(j3, kv_len, w);
+                if (load3 && !spread)
+                    ld.issue(st3, p.k_cache, p.v_cache, win, first, j3, kv_len, p.bs_log2,
+                             tok_stride, head_off, w, page);
+                typename R::Src sr{p.k_cache, p.v_cache};
+                if (spread)
+                    sr = R::src(p.k_cache, p.v_cache, page, j3, w, p.bs_log2, tok_stride, head_off);
+                const Hook hook{ld, sr, st3, w, spread};
+                step_pv<D, BN, BF16>(st, st_cur + R::TILE, hook);
+                // (with ATTN_DMA_OVER_QK the last loads ride on this QK; it runs
+                // whenever tile jt+3 exists)
+                if (jt + 1 < n) {
+                    if (ATTN_DMA_OVER_QK) step_qk<D, BN, BF16>(st, q, st_next, hook, kPvSteps);
+                    else step_qk<D, BN, BF16>(st, q, st_next);
+                }
+            } else {
                 phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
+            }
             block_barrier();
         }
         if (!lead && n > 0)
-            phase_mfma<D, BN, BF16>(st, q, ring + ((n - 1) % kStages) * R::STAGE + R::TILE,
-                                    nullptr);
+            step_pv<D, BN, BF16>(st, ring + ((n - 1) % kStages) * R::STAGE + R::TILE);
         block_barrier();   // the next chunk's window and ring refill start after all reads
     }
 

@@ -55,17 +55,39 @@ __device__ __forceinline__ int swz(int r) {
 }
 
 // One direct global->LDS load of 16 bytes per lane: lane i's bytes land at
-// LDS address lds_base + 16*i (lds_base must be wave-uniform).  Written as
+// LDS byte address lds + 16*i (lds must be wave-uniform; lds_addr() gives the
+// address of a __shared__ object).  Written as
 // inline asm so the compiler does not drain it with vmcnt(0) before every
 // later LDS read (it cannot tell ring stages apart); the code that reads a
 // stage waits with an explicit vmcnt first.  The instruction has no
 // destination register.
-__device__ __forceinline__ void dma16(const void* gptr, const uint8_t* lds_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(lds_base));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)(p);
+}
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
                  : "s"(m0), "v"(gptr)
+                 : "memory", "m0");
+}
+
+// The same load with a wave-uniform 64-bit base in SGPRs and a 32-bit
+// per-lane byte offset: no per-lane address arithmetic.
+// The base goes through readfirstlane so it is in SGPRs even where the
+// compiler cannot prove it uniform (a no-op where it can).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    const uint64_t a = (uint64_t)(uintptr_t)sbase;
+    // readfirstlane returns int: take each half back to uint32_t before
+    // widening so the low half is not sign-extended into the high one.
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint64_t u = ((uint64_t)hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(m0), "v"(voff), "s"(u)
                  : "memory", "m0");
 }
 
@@ -77,47 +99,126 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(const uint8_t* p) {
     return __builtin_bit_cast(u32x2_t, v);
 }
 
-template <int D, int BN, int NW>
+// Ring of K/V tiles filled by NL loading waves.  Loading wave wl fetches the
+// RW consecutive key rows [wl*RW, (wl+1)*RW) of a tile; tiles start on
+// multiples of 16 and pages hold at least 16 keys, so those rows lie in one
+// page: one page id per wave and tile, and a wave-uniform source address.
+template <int D, int BN, int NL>
 struct Ring16 {
     static constexpr int CPR = D / 8;           // 16-byte chunks per row
     static constexpr int ROWB = D * 2;          // bytes per row
     static constexpr int TILE = BN * ROWB;      // bytes of one K (or V) tile
     static constexpr int STAGE = 2 * TILE;      // K tile then V tile
     static constexpr int RPI = 64 / CPR;        // rows per 1 KB load instruction
-    static constexpr int IPW = TILE / 1024 / NW;  // load instructions per wave per tensor
-    static_assert(TILE % (1024 * NW) == 0, "tile does not divide over the waves");
-    static constexpr int LOADS_PER_TILE = 2 * IPW;  // per thread: K and V
+    static constexpr int IPW = TILE / 1024 / NL;  // load instructions per wave per tensor
+    static_assert(TILE % (1024 * NL) == 0, "tile does not divide over the waves");
+    static constexpr int LOADS_PER_TILE = 2 * IPW;  // per loading wave: K and V
+    static constexpr int RW = IPW * RPI;
+    static_assert(RW == 16, "a loading wave's rows must be one aligned 16-key group");
 
-    int row[IPW];     // tile-relative key row each load instruction of this lane fetches
-    int chunk[IPW];   // logical chunk of that row (the swizzle applied)
+    // Load instruction i of loading wave wl puts lane l's 16 bytes at tile
+    // row row(i) = (wl*IPW + i)*RPI + l/CPR, logical chunk chunk(i) (the
+    // swizzle applied); voff[i] is that chunk's byte offset from the wave's
+    // first row in the cache.
+    uint32_t voff[IPW];
 
-    __device__ __forceinline__ void init(int lane, int w) {
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int b = w * IPW + i;
-            row[i] = b * RPI + lane / CPR;
-            chunk[i] = (lane % CPR) ^ swz<D>(row[i]);
-        }
+    __device__ __forceinline__ static int row(int lane, int wl, int i) {
+        return (wl * IPW + i) * RPI + lane / CPR;
+    }
+    __device__ __forceinline__ static int chunk(int lane, int wl, int i) {
+        return (lane % CPR) ^ swz<D>(row(lane, wl, i));
     }
 
-    // Keys [j0, j0 + BN) of one sequence (kv_len >= 1) into `stage`.  Rows past
-    // kv_len read row kv_len - 1: they hold finite values and every key past
-    // kv_len is masked to probability 0 by the caller.
-    __device__ __forceinline__ void issue(uint8_t* stage, const uint16_t* cache_k,
+    __device__ __forceinline__ void init(int lane, int wl, int tok_stride) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            voff[i] = (uint32_t)(((row(lane, wl, i) - wl * RW) * tok_stride +
+                                  chunk(lane, wl, i) * 8) * 2);
+    }
+
+    // Window slot of the page holding this wave's rows of the tile at j0.
+    __device__ __forceinline__ static int slot(int j0, int first, int bs_log2, int wl) {
+        return ((j0 + wl * RW) >> bs_log2) - first;
+    }
+
+    // True when all of this wave's rows of the tile at j0 are below kv_len.
+    __device__ __forceinline__ static bool whole(int j0, int kv_len, int wl) {
+        return j0 + (wl + 1) * RW <= kv_len;
+    }
+
+    struct Src {
+        const uint16_t* k;
+        const uint16_t* v;
+    };
+
+    // Wave-uniform source rows of a whole() tile; page = win[slot()].
+    __device__ __forceinline__ static Src src(const uint16_t* cache_k, const uint16_t* cache_v,
+                                              int page, int j0, int wl, int bs_log2,
+                                              int tok_stride, int head_off) {
+        const int r0 = __builtin_amdgcn_readfirstlane(j0 + wl * RW);
+        const int pg = __builtin_amdgcn_readfirstlane(page);
+        const int64_t off = ((int64_t)pg * tok_stride << bs_log2) +
+                            (((r0 & ((1 << bs_log2) - 1)) * tok_stride) + head_off);
+        return Src{cache_k + off, cache_v + off};
+    }
+
+    // Load number k (< LOADS_PER_TILE: K rows first, then V) of a whole() tile.
+    // stage: LDS byte address of the ring stage.
+    __device__ __forceinline__ void dma(int k, const Src& sr, uint32_t stage, int wl) const {
+        const int i = k % IPW;
+        const bool isv = k >= IPW;
+        dma16_s(isv ? sr.v : sr.k, voff[i], stage + (isv ? TILE : 0) + (wl * IPW + i) * 1024);
+    }
+
+    // All of this wave's loads of the tile at j0 at once (kv_len >= 1).  Rows
+    // past kv_len read row kv_len - 1: they hold finite values and every key
+    // past kv_len is masked to probability 0 by the caller.  `page` is
+    // win[slot()], read by the caller ahead of time (any value when the tile
+    // is not whole()).
+    __device__ __forceinline__ void issue(uint32_t stage, const uint16_t* cache_k,
                                           const uint16_t* cache_v, const int* win, int first,
                                           int j0, int kv_len, int bs_log2, int tok_stride,
-                                          int head_off, int w) const {
+                                          int head_off, int wl, int page) const {
+        if (whole(j0, kv_len, wl)) {
+            const Src sr = src(cache_k, cache_v, page, j0, wl, bs_log2, tok_stride, head_off);
+#pragma unroll
+            for (int k = 0; k < LOADS_PER_TILE; ++k) dma(k, sr, stage, wl);
+            return;
+        }
         const int bs_mask = (1 << bs_log2) - 1;
         const int64_t page_stride = (int64_t)tok_stride << bs_log2;
+        const int lane = lane_id();
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
-            const int tok = min(j0 + row[i], kv_len - 1);
-            const int page = win[(tok >> bs_log2) - first];
-            const int64_t off = page * page_stride +
-                                ((tok & bs_mask) * tok_stride + head_off + chunk[i] * 8);
-            const uint8_t* dst = stage + (w * IPW + i) * 1024;
+            const int tok = min(j0 + row(lane, wl, i), kv_len - 1);
+            const int pg = win[(tok >> bs_log2) - first];
+            const int64_t off = pg * page_stride +
+                                ((tok & bs_mask) * tok_stride + head_off + chunk(lane, wl, i) * 8);
+            const uint32_t dst = stage + (wl * IPW + i) * 1024;
             dma16(cache_k + off, dst);
             dma16(cache_v + off, dst + TILE);
+        }
+    }
+};
+
+// Callbacks run after each MFMA of a tile product (step = MFMA index within
+// the product): NoHook does nothing; DmaHook issues one load of a ring tile
+// after every EVERY-th MFMA, so a tile's loads go out between the MFMAs
+// instead of arriving at the load unit as one burst.
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <class R, int EVERY>
+struct DmaHook {
+    const R& ld;
+    typename R::Src sr;
+    uint32_t stage;
+    int wl;
+    bool on;
+    __device__ __forceinline__ void operator()(int step) const {
+        if (step % EVERY == EVERY - 1 && step / EVERY < R::LOADS_PER_TILE) {
+            if (on) ld.dma(step / EVERY, sr, stage, wl);
         }
     }
 };
@@ -125,24 +226,37 @@ struct Ring16 {
 // Operand prefetch depths (in MFMA steps) of the two tile products: the LDS
 // reads of step t + PD issue before the MFMAs of step t, so LDS latency hides
 // under the MFMAs; sched_barrier pins that order against the scheduler.
-constexpr int kQkPrefetch = 2;
-constexpr int kPvPrefetch = 4;
+#ifndef ATTN_QK_PREFETCH
+#define ATTN_QK_PREFETCH 3
+#endif
+#ifndef ATTN_PV_PREFETCH
+#define ATTN_PV_PREFETCH 6
+#endif
+constexpr int kQkPrefetch = ATTN_QK_PREFETCH;
+constexpr int kPvPrefetch = ATTN_PV_PREFETCH;
 
-// S^T[kb] += K_tile(kb) . Q^T for the BN/32 key blocks of a tile.
-template <int D, int BN, bool BF16>
+// S^T[kb] += K_tile(kb) . Q^T for the BN/32 key blocks of a tile;
+// (D/16) * (BN/32) MFMAs, hook steps from step0 upwards.
+template <int D, int BN, bool BF16, class Hook>
 __device__ __forceinline__ void qk_tile(f32x16_t (&s)[BN / 32], const uint8_t* kt,
-                                        const u32x4_t (&q)[D / 16]) {
+                                        const u32x4_t (&q)[D / 16], const Hook& hook,
+                                        int step0) {
     constexpr int ROWB = D * 2;
     constexpr int NKB = BN / 32;
     constexpr int T = D / 16;
     constexpr int PD = kQkPrefetch < T ? kQkPrefetch : T;
     const int lane = lane_id();
     const int col = lane & 31, g = lane >> 5;
-    const int sw = swz<D>(col);   // rows kb*32 + col share their low 5 bits
-    const uint8_t* base = kt + col * ROWB;
+    // Lane offset of chunk g of row col (rows kb*32 + col share their low 5
+    // bits, so one swizzle serves every key block).  Step t reads chunk
+    // 2t + g, i.e. this offset XOR (2t << 4): row bits sit above bit 7, so
+    // the XOR only touches the chunk bits.  The empty asm keeps the compiler
+    // from hoisting the eight XORed offsets out of the tile loop into
+    // registers that would stay live across it.
+    uint32_t lo = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
+    asm volatile("" : "+v"(lo));
     auto frag = [&](int t, int kb) {
-        return *reinterpret_cast<const u32x4_t*>(base + kb * 32 * ROWB +
-                                                 (((2 * t + g) ^ sw) << 4));
+        return *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + (lo ^ (uint32_t)(t << 5)));
     };
     u32x4_t a[PD + 1][NKB];
 #pragma unroll
@@ -159,15 +273,19 @@ __device__ __forceinline__ void qk_tile(f32x16_t (&s)[BN / 32], const uint8_t* k
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma32<BF16>(a[t % (PD + 1)][kb], q[t], s[kb]);
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = mfma32<BF16>(a[t % (PD + 1)][kb], q[t], s[kb]);
+            hook(step0 + t * NKB + kb);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// O^T[db] += V_tile^T(db) . P^T with P^T packed per (key block, 16-key step).
-template <int D, int BN, bool BF16>
+// O^T[db] += V_tile^T(db) . P^T with P^T packed per (key block, 16-key step);
+// (D/32) * (BN/32) * 2 MFMAs, hook steps 0 upwards.
+template <int D, int BN, bool BF16, class Hook>
 __device__ __forceinline__ void pv_tile(f32x16_t (&o)[D / 32], const uint8_t* vt,
-                                        const u32x4_t (&pb)[BN / 32][2]) {
+                                        const u32x4_t (&pb)[BN / 32][2], const Hook& hook) {
     constexpr int ROWB = D * 2;
     constexpr int NKB = BN / 32;
     constexpr int STEPS = (D / 32) * NKB * 2;
@@ -175,14 +293,21 @@ __device__ __forceinline__ void pv_tile(f32x16_t (&o)[D / 32], const uint8_t* vt
     const int lane = lane_id();
     const int j = lane & 15, h = lane >> 4, g = h >> 1;
     const int r0 = 4 * g + (j >> 2);                 // row (mod 16) of the first read
-    const int sw_lo = swz<D>(r0), sw_hi = swz<D>(r0 + 8);
-    const uint8_t* base = vt + r0 * ROWB + (j & 1) * 8;
+    // Chunk of dimension block db is c0 + 4*db; rows r0 + 16*tp + 32*kb keep
+    // the swizzle of r0 (it depends on the row mod 16), row r0 + 8 has its
+    // own.  Offsets of db = 0 for both rows; db adds (4*db << 4) by XOR
+    // (those chunk bits of c0 are zero).  The empty asm stops the compiler
+    // from hoisting the XORed offsets of every db out of the tile loop.
+    const int c0 = (16 * (h & 1) + 4 * (j & 3)) >> 3;
+    uint32_t lo0 = (uint32_t)(r0 * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0)) << 4));
+    uint32_t hi0 = (uint32_t)((r0 + 8) * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0 + 8)) << 4));
+    asm volatile("" : "+v"(lo0), "+v"(hi0));
     auto frag = [&](int i) {
         const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
-        const int c = (db * 32 + 16 * (h & 1) + 4 * (j & 3)) >> 3;
-        const uint8_t* p0 = base + (kb * 32 + 16 * tp) * ROWB;
-        const u32x2_t lo = ds_read_tr16(p0 + ((c ^ sw_lo) << 4));
-        const u32x2_t hi = ds_read_tr16(p0 + 8 * ROWB + ((c ^ sw_hi) << 4));
+        const uint8_t* p0 = vt + (kb * 32 + 16 * tp) * ROWB;
+        const uint32_t x = (uint32_t)(db << 6);
+        const u32x2_t lo = ds_read_tr16(p0 + (lo0 ^ x));
+        const u32x2_t hi = ds_read_tr16(p0 + (hi0 ^ x));
         return u32x4_t{lo.x, lo.y, hi.x, hi.y};
     };
     u32x4_t a[PD + 1];
@@ -194,6 +319,7 @@ __device__ __forceinline__ void pv_tile(f32x16_t (&o)[D / 32], const uint8_t* vt
         __builtin_amdgcn_sched_barrier(0);
         const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
         o[db] = mfma32<BF16>(a[i % (PD + 1)], pb[kb][tp], o[db]);
+        hook(i);
         __builtin_amdgcn_sched_barrier(0);
     }
 }

@@ -167,3 +167,75 @@ def compare(out_gpu, lse_gpu, out_ref, lse_ref, atol, rel=None, rows=None, what=
 
 
 requires_gpu = pytest.mark.skipif(not gpu_available(), reason="needs a GPU")
+
+
+# ------------------------------------------------------- sampled full-size runs
+
+def sub_workload(w, seqs, decode=False):
+    """The sequences `seqs` of a paged workload, alone: the same tokens and
+    ids, their pages renumbered 0..n-1 in order.  Lets the oracle check
+    sampled outputs of a full-size GPU run without building the whole cache
+    in fp64 (placement does not change the result: the oracle's permutation
+    pin).  Returns (sub, q_index) where q_index[i] is the row of w holding
+    row i of sub."""
+    assert np.array_equal(w.new_lens, w.kv_lens)
+    seqs = [int(b) for b in seqs]
+    cq = np.concatenate([[0], np.cumsum(w.q_lens, dtype=np.int64)])
+    ck = np.concatenate([[0], np.cumsum(w.kv_lens, dtype=np.int64)])
+    bs = w.block_size
+    nblk = [(int(w.kv_lens[b]) + bs - 1) // bs for b in seqs]
+    table = np.zeros((len(seqs), max(1, max(nblk))), dtype=np.int32)
+    nxt = 0
+    for i, n in enumerate(nblk):
+        table[i, :n] = np.arange(nxt, nxt + n)
+        nxt += n
+    kv_idx = np.concatenate([np.arange(ck[b], ck[b + 1]) for b in seqs])
+    if decode:
+        q_idx = np.asarray(seqs, dtype=np.int64)
+    else:
+        q_idx = np.concatenate([np.arange(cq[b], cq[b + 1]) for b in seqs])
+    tq = torch.as_tensor(q_idx, device=w.q.device)
+    tk = torch.as_tensor(kv_idx, device=w.k_new.device)
+    import dataclasses
+    sub = dataclasses.replace(
+        w, q_lens=w.q_lens[seqs].copy(), kv_lens=w.kv_lens[seqs].copy(),
+        new_lens=w.new_lens[seqs].copy(), num_blocks=max(1, nxt), block_table=table,
+        q_ids=None if w.q_ids is None else np.asarray(w.q_ids)[q_idx],
+        kv_ids=None if w.kv_ids is None else np.asarray(w.kv_ids)[kv_idx],
+        q=w.q[tq].cpu(), k_new=w.k_new[tk].cpu(), v_new=w.v_new[tk].cpu(), extra={})
+    return sub, q_idx
+
+
+def sub_fp8(w, seqs):
+    """fp8 counterpart of sub_workload (dense, V column-major)."""
+    seqs = [int(b) for b in seqs]
+    cq = np.concatenate([[0], np.cumsum(w.q_lens, dtype=np.int64)])
+    ck = np.concatenate([[0], np.cumsum(w.kv_lens, dtype=np.int64)])
+    q_idx = np.concatenate([np.arange(cq[b], cq[b + 1]) for b in seqs])
+    kv_idx = np.concatenate([np.arange(ck[b], ck[b + 1]) for b in seqs])
+    tq = torch.as_tensor(q_idx, device=w.q.device)
+    tk = torch.as_tensor(kv_idx, device=w.k_new.device)
+    import dataclasses
+    sub = dataclasses.replace(
+        w, q_lens=w.q_lens[seqs].copy(), kv_lens=w.kv_lens[seqs].copy(),
+        new_lens=w.new_lens[seqs].copy(), block_table=w.block_table[seqs].copy(),
+        q_ids=None if w.q_ids is None else np.asarray(w.q_ids)[q_idx],
+        kv_ids=None if w.kv_ids is None else np.asarray(w.kv_ids)[kv_idx],
+        q=w.q[tq].cpu(), k_new=w.k_new[tk].cpu(),
+        v8_colmajor=w.v8_colmajor[:, :, tk].cpu(), extra={})
+    return sub, q_idx
+
+
+def sample_rows(q_lens, per_seq, seed):
+    """Row indices (within the concatenated sequences) to check: each
+    sequence's first two rows, its middle and last row, and `per_seq` more
+    drawn at random."""
+    rng = np.random.default_rng(seed)
+    rows, base = [], 0
+    for n in (int(x) for x in q_lens):
+        if n:
+            pick = {0, min(1, n - 1), n // 2, n - 1}
+            pick |= set(rng.choice(n, size=min(per_seq, n), replace=False).tolist())
+            rows += [base + i for i in sorted(pick)]
+        base += n
+    return np.asarray(rows, dtype=np.int64)

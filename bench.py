@@ -11,14 +11,22 @@ visible query-key pairs, each needing a D-long dot product and a D-long
 weighted sum) divided by the step time.
 
 The same JSON line carries the prefill kernel's roofline figure, the fp64 CPU
-oracle timed on a bounded sample of the same workload, and three more
-single-GPU measurements: paged decode (HBM GB/s), byte->patch cross attention
-and dense causal fp8 (TFLOP/s).
+oracle timed on a bounded sample of the same workload, and more single-GPU
+measurements: paged decode (HBM GB/s, with its own roofline figure), a plain
+device-to-device copy (the practical HBM ceiling, and the calibration kernel
+for the traffic counters), byte->patch cross attention and dense causal fp8
+(TFLOP/s).
+
+`roofline.traffic` is the HBM bytes one prefill launch moves, from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json;
+it is reported only while the hash of the kernel sources matches the one the
+counters were taken with, and is null otherwise.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-extra] [--no-cpu]
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -33,6 +41,14 @@ import numpy as np  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CSRC = os.path.join(ROOT, "attention_cu_seqlens_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# sources that define each measured kernel; a change to any of them voids its
+# recorded counter traffic
+KERNEL_SOURCES = {
+    "k_paged_prefill": ["prefill.hip", "ring.h", "device_common.h", "kernels.h"],
+    "k_paged_decode": ["decode.hip", "device_common.h", "kernels.h"],
+}
 
 
 def log(msg):
@@ -70,6 +86,27 @@ def timed(fn, iters, torch):
     return ev[0].elapsed_time(ev[1]) / iters
 
 
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from profiles/traffic.json, or None when absent or
+    taken with different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)[f"{kernel} {workload}"]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def i32(a, torch, dev):
     return torch.as_tensor(np.ascontiguousarray(a), dtype=torch.int32, device=dev)
 
@@ -84,8 +121,9 @@ def paged_inputs(w, A, torch, dev):
     return lens_q, lens_kv, kc, vc, bt
 
 
-def cpu_baseline(w, n_heads):
-    """The fp64 oracle on sequence 0 of the workload, n_heads query heads."""
+def cpu_baseline(w, n_seqs):
+    """The fp64 oracle on the first n_seqs sequences of the workload, all heads:
+    cache fill through reshape_and_cache, then paged causal attention."""
     import oracle as ORC
     try:
         from threadpoolctl import threadpool_info
@@ -93,26 +131,44 @@ def cpu_baseline(w, n_heads):
         cores = int(max(blas)) if blas else 1
     except Exception:
         cores = 1
-    L = int(w.q_lens[0])
-    hkv = w.num_kv_heads
-    g = w.num_heads // hkv
-    q = w.q[:L, :n_heads].double().cpu().numpy()
-    k = w.k_new[:L, :max(1, n_heads // g)].double().cpu().numpy()
-    v = w.v_new[:L, :max(1, n_heads // g)].double().cpu().numpy()
+    lens = [int(x) for x in w.q_lens[:n_seqs]]
+    tot = sum(lens)
+    q = w.q[:tot].double().cpu().numpy()
+    k = w.k_new[:tot].double().cpu().numpy()
+    v = w.v_new[:tot].double().cpu().numpy()
     bs = w.block_size
-    nblk = (L + bs - 1) // bs
-    kc = np.zeros((nblk, bs) + k.shape[1:])
+    nblk = [(n + bs - 1) // bs for n in lens]
+    table = np.zeros((len(lens), max(nblk)), dtype=np.int32)
+    base = 0
+    for i, n in enumerate(nblk):
+        table[i, :n] = np.arange(base, base + n)
+        base += n
+    kc = np.zeros((base, bs) + k.shape[1:])
     vc = np.zeros_like(kc)
-    table = np.arange(nblk, dtype=np.int32)[None]
-    cu = ORC.cu_seqlens([L])
+    cu = ORC.cu_seqlens(lens)
     t0 = time.perf_counter()
     kc, vc = ORC.reshape_and_cache(k, v, kc, vc, table, cu, cu, bs)
     ORC.paged_attention(q, kc, vc, table, cu, cu, bs, w.scale, w.mask_flags)
     dt = time.perf_counter() - t0
-    flops = 4.0 * w.head_size * n_heads * L * (L + 1) / 2
+    flops = 4.0 * w.head_size * w.num_heads * sum(n * (n + 1) / 2 for n in lens)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"sequence 0 (length {L}) x {n_heads} of {w.num_heads} query heads, "
-                      f"cache fill + paged causal attention in fp64 numpy, {dt:.1f} s"}
+            "sample": f"sequences 0-{len(lens) - 1} (lengths {lens}) x all {w.num_heads} query "
+                      f"heads of the same workload: cache fill + paged causal attention in fp64 "
+                      f"numpy, {dt:.1f} s; BLAS threads = cores"}
+
+
+def bench_copy(torch, dev, nbytes=2 << 30, iters=10):
+    """Device-to-device copy: the practical HBM ceiling (read + write bytes)."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(2):
+        y.copy_(x)
+    ms = timed(lambda: y.copy_(x), iters, torch)
+    del x, y
+    torch.cuda.empty_cache()
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_copied": nbytes, "ms": round(ms, 4), "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
 def bench_decode(A, W, torch, dev, iters=20):
@@ -140,7 +196,11 @@ def bench_decode(A, W, torch, dev, iters=20):
               + used_blocks * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
-           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
+           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+           "roofline": {"kernel": "k_paged_decode + k_decode_combine", "bound": "hbm",
+                        "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4),
+                        "traffic": recorded_traffic("k_paged_decode", w.name)}}
     del kc, vc
     torch.cuda.empty_cache()
     return res
@@ -193,7 +253,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-extra", action="store_true", help="skip decode / cross / fp8 lines")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-seqs", type=int, default=3,
+                    help="sequences of the workload in the CPU oracle sample")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this attention hot path has no multi-GPU "
@@ -273,13 +334,16 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "k_paged_prefill", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic("k_paged_prefill", w.name),
                      "kernel_ms": round(k_ms, 5), "flops_per_launch": flops},
     }
     del kc, vc, out
     torch.cuda.empty_cache()
 
     if not args.no_extra:
+        log("hbm copy")
+        line["hbm_copy"] = bench_copy(torch, dev)
         log("decode")
         line["decode"] = bench_decode(A, W, torch, dev)
         torch.cuda.empty_cache()
@@ -294,7 +358,7 @@ def main():
 
     if not args.no_cpu:
         log("cpu oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_heads)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
 
     print(json.dumps(line), flush=True)
 

@@ -36,11 +36,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int* win = reinterpret_cast<int*>(smem + L::WIN_OFF);
 
-    int u = blockIdx.x;
-    const int s = u % p.max_splits;
-    u /= p.max_splits;
-    const int hk = u % p.num_kv_heads;
-    const int b = u / p.num_kv_heads;
+    // Split index outermost: workgroup i runs on XCD i % 8, so consecutive
+    // workgroups are different (sequence, kv head) units of the same split
+    // and every XCD gets an equal share of each split index.  (Split-fastest
+    // order piles the low split indices, which every sequence has, onto the
+    // XCDs they map to whenever the split count is a multiple of 8.)
+    const int units = p.batch * p.num_kv_heads;
+    const int s = blockIdx.x / units;
+    const int unit = blockIdx.x - s * units;
+    const int hk = unit % p.num_kv_heads;
+    const int b = unit / p.num_kv_heads;
     const int kv_start = p.cu_kv[b];
     const int kv_len = p.cu_kv[b + 1] - kv_start;
     const int k0 = s * p.split_tokens;

@@ -151,14 +151,18 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int tok = tok0 + (r >> p.pack_log2);
     const int head = h0 + (r & ((1 << p.pack_log2) - 1));
     const bool valid = tok < q_len;
+    // Q operand; a row past the sequence end reads row tok0 instead (its keys
+    // are all masked and it is never stored), so the loads issue back to back
+    // with no branch and their latency overlaps the set-up below.
     u32x4_t q[D / 16];
     {
-        const uint16_t* qp = p.q + ((int64_t)(q_start + tok) * p.num_heads + head) * D + 8 * g;
+        const uint16_t* qp =
+            p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D + 8 * g;
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (valid) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-            q[t] = neg ? neg16x8(v) : v;
+        for (int t = 0; t < D / 16; ++t) q[t] = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
+        if (neg) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) q[t] = neg16x8(q[t]);
         }
     }
     int lo = 0, hi = 0;

@@ -165,6 +165,7 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
     p.group = num_heads / num_kv_heads;
     p.pack_log2 = pack_log2_for_group(p.group);
     p.n_head_groups = num_heads >> p.pack_log2;
+    p.total_q = total_q;
     p.bs_log2 = ilog2(block_size);
     p.mask = mask_flags;
     p.c = scale * 1.4426950408889634f;
@@ -279,6 +280,7 @@ attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor
     p.group = num_heads / num_kv_heads;
     p.pack_log2 = pack_log2_for_group(p.group);
     p.n_head_groups = num_heads >> p.pack_log2;
+    p.total_q = total_q;
     p.mask = mask_flags;
     p.scale = scale;
     return from_hip(attn::launch_fp8_prefill(p, head_size, max_seqlen_q,

@@ -79,6 +79,66 @@ __device__ __forceinline__ int wave_min(int x) {
     for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s, 64));
     return x;
 }
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+        const int t = __shfl_up(x, s, 64);
+        if (lane >= s) x += t;
+    }
+    return x;
+}
+
+// Work item k of XCD `xcd` (workgroup i runs on XCD i % 8, k = i / 8) ->
+// (sequence b, head group hg, query tile qt), for query tiles of `tt` tokens.
+// Units u = b * n_hg + hg are dealt to XCDs round-robin (XCD x owns units
+// x, x + 8, ...); an XCD walks its units in order and each unit's query
+// tiles longest first, so the tiles that share one K/V stream run together
+// on one XCD and its L2.  Only existing tiles get a work item, so short
+// sequences leave no idle workgroups behind; returns false past the XCD's
+// last tile.  Wave-uniform; every wave of a workgroup computes the same.
+__device__ __forceinline__ bool map_tile(const int32_t* cu_q, int batch, int n_hg, int tt, int xcd,
+                                         int k, int& b, int& hg, int& qt) {
+    const int units = batch * n_hg;
+    const int lane = lane_id();
+    int base = 0;   // tiles of the chunks before this one
+    for (int m0 = 0; xcd + 8 * m0 < units; m0 += 64) {
+        const int u = xcd + 8 * (m0 + lane);
+        int t = 0;
+        if (u < units) {
+            const int bb = u / n_hg;
+            t = (cu_q[bb + 1] - cu_q[bb] + tt - 1) / tt;
+        }
+        const int incl = wave_incl_scan(t);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        if (k < base + total) {
+            const bool mine = k >= base + incl - t && k < base + incl;
+            const uint64_t who = __ballot(mine);
+            const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(who));
+            const int uu = __builtin_amdgcn_readlane(u, src);
+            const int first = __builtin_amdgcn_readlane(incl - t, src);
+            const int tu = __builtin_amdgcn_readlane(t, src);
+            b = uu / n_hg;
+            hg = uu - b * n_hg;
+            qt = tu - 1 - (k - base - first);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// Workgroups per XCD that cover every query tile of tt tokens: each XCD owns
+// at most ceil(n_hg / 8) units of any one sequence, and a sequence of len
+// tokens has ceil(len / tt) <= (len + tt - 1) / tt tiles.
+inline int64_t tiles_per_xcd(int batch, int n_hg, int total_q, int max_seqlen_q, int tt) {
+    const int64_t units = (int64_t)batch * n_hg;
+    const int64_t by_len = ((units + 7) / 8) * ((max_seqlen_q + tt - 1) / tt);
+    const int64_t by_total = (int64_t)((n_hg + 7) / 8) * (((int64_t)total_q + (int64_t)batch * (tt - 1)) / tt);
+    return by_len < by_total ? by_len : by_total;
+}
+
 __device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) x = max(x, __shfl_xor(x, s, 64));

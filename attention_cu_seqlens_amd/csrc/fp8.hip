@@ -273,15 +273,13 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Tile::BYTES];
     __shared__ int wave_range[2][NW];
 
-    int u = blockIdx.x;
-    const int hg = u % p.n_head_groups;
-    u /= p.n_head_groups;
-    const int b = u % p.batch;
-    const int qt = p.n_qtiles - 1 - u / p.batch;
+    int b, hg, qt;
+    if (!map_tile(p.cu_q, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
+                  blockIdx.x >> 3, b, hg, qt))
+        return;
     const int q_start = p.cu_q[b];
     const int q_len = p.cu_q[b + 1] - q_start;
     const int tok0 = qt * (BM >> p.pack_log2);
-    if (tok0 >= q_len) return;
     const int kv_start = p.cu_kv[b];
     const int kv_len = p.cu_kv[b + 1] - kv_start;
     const int h0 = hg << p.pack_log2;
@@ -409,7 +407,8 @@ hipError_t launch_fp8_prefill(const Fp8Params& p0, int head_size, int max_seqlen
     Fp8Params p = p0;
     const int tokens_per_tile = BM >> p.pack_log2;
     p.n_qtiles = (max_seqlen_q + tokens_per_tile - 1) / tokens_per_tile;
-    const int64_t grid = (int64_t)p.n_qtiles * p.batch * p.n_head_groups;
+    const int64_t grid = 8 * tiles_per_xcd(p.batch, p.n_head_groups, p.total_q, max_seqlen_q,
+                                           tokens_per_tile);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_fp8_prefill<QB, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);

@@ -30,6 +30,7 @@ struct PrefillParams {
     int pack_log2;              // log2 of q heads packed per workgroup
     int n_head_groups;          // num_heads >> pack_log2
     int n_qtiles;               // tiles per sequence at max_seqlen_q
+    int total_q;
     int bs_log2;
     uint32_t mask;
     float c;                    // scale * log2(e)
@@ -77,6 +78,7 @@ struct Fp8Params {
     int pack_log2;
     int n_head_groups;
     int n_qtiles;
+    int total_q;
     uint32_t mask;
     float scale;
 };

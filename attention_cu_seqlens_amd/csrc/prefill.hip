@@ -11,9 +11,10 @@
 // Every K/V tile staged in LDS therefore serves P heads, and the causal
 // diagonal of a tile spans BM / P tokens.
 //
-// Work decomposition needs no device->host sync: the host sizes the grid from
-// max_seqlen_q; workgroup ids map to (sequence, head group, query tile) -- see
-// the kernel -- and a workgroup whose tile lies past its sequence's end exits.
+// Work decomposition needs no device->host sync: the host bounds the grid by
+// max_seqlen_q and total_q, and each workgroup finds its (sequence, head
+// group, query tile) from cu_seqlens_q (map_tile); the few workgroups past
+// the last tile exit at once.
 //
 // Masks reduce to one visible key interval [lo, hi) per query row: causal
 // (bottom-right) and patch bound hi, document ids (non-decreasing within a
@@ -112,23 +113,14 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     __shared__ int wave_range[2][NW];
     __shared__ int win[PAGE_WIN + 1];
 
-    // Workgroup i runs on XCD i % 8.  Units (sequence, head group) are dealt
-    // to XCDs round-robin; an XCD runs its units one after another, each unit's
-    // query tiles longest first, so the tiles that share one K/V stream run
-    // together on one XCD and share its L2.
-    const int xcd = blockIdx.x & 7;
-    const int k = blockIdx.x >> 3;
-    const int m = k / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (k - m * p.n_qtiles);
-    const int unit = xcd + 8 * m;
-    if (unit >= p.batch * p.n_head_groups) return;
-    const int b = unit / p.n_head_groups;
-    const int hg = unit - b * p.n_head_groups;
+    int b, hg, qt;
+    if (!map_tile(p.cu_q, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
+                  blockIdx.x >> 3, b, hg, qt))
+        return;
 
     const int q_start = p.cu_q[b];
     const int q_len = p.cu_q[b + 1] - q_start;
     const int tok0 = qt * (BM >> p.pack_log2);
-    if (tok0 >= q_len) return;
     const int kv_start = p.cu_kv[b];
     const int kv_len = p.cu_kv[b + 1] - kv_start;
     const int h0 = hg << p.pack_log2;
@@ -323,8 +315,8 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
     PrefillParams p = p0;
     const int tokens_per_tile = BM >> p.pack_log2;
     p.n_qtiles = (max_seqlen_q + tokens_per_tile - 1) / tokens_per_tile;
-    const int64_t units = (int64_t)p.batch * p.n_head_groups;
-    const int64_t grid = 8 * ((units + 7) / 8) * p.n_qtiles;
+    const int64_t grid = 8 * tiles_per_xcd(p.batch, p.n_head_groups, p.total_q, max_seqlen_q,
+                                           tokens_per_tile);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16>), dim3((unsigned)grid),

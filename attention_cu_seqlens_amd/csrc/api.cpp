@@ -33,6 +33,10 @@ attn_status check_device() {
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+// Tensor base addresses must be 16-byte aligned: the kernels move 16-byte
+// chunks.
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int ilog2(int x) {
@@ -111,6 +115,7 @@ attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, 
     if (k == nullptr || v == nullptr || k_cache == nullptr || v_cache == nullptr ||
         block_table == nullptr || cu_seqlens_new == nullptr || cu_seqlens_kv == nullptr)
         return ATTN_ERR_NULL_ARG;
+    if (!al16(k) || !al16(v) || !al16(k_cache) || !al16(v_cache)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0 || total_new == 0) return ATTN_OK;
     const attn_status d = check_device();
     if (d != ATTN_OK) return d;
@@ -143,6 +148,7 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
     if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
         cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || out == nullptr)
         return ATTN_ERR_NULL_ARG;
+    if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0 || total_q == 0) return ATTN_OK;
     const attn_status d = check_device();
     if (d != ATTN_OK) return d;
@@ -206,6 +212,7 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
         cu_seqlens_kv == nullptr || out == nullptr)
         return ATTN_ERR_NULL_ARG;
+    if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0) return ATTN_OK;
     const int st = attn::decode_split_tokens(batch, num_kv_heads, max_seqlen_kv, split_tokens);
     const size_t need = attn::decode_workspace_bytes(batch, num_heads, head_size, max_seqlen_kv, st);
@@ -258,6 +265,10 @@ attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor
     if (q8 == nullptr || k8 == nullptr || v8_colmajor == nullptr || descale_qkv == nullptr ||
         cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || out_bf16 == nullptr)
         return ATTN_ERR_NULL_ARG;
+    if (!al16(q8) || !al16(k8) || !al16(v8_colmajor) || !al16(out_bf16))
+        return ATTN_ERR_BAD_SHAPE;
+    // the kernel addresses 32 V rows of one head with 32-bit offsets
+    if (total_kv > (1 << 27)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0 || total_q == 0) return ATTN_OK;
     const attn_status d = check_device();
     if (d != ATTN_OK) return d;

@@ -4,8 +4,8 @@
 // layouts for fp8 flex attention to avoid perf degradation": Q and K are
 // row-major, V is column-major ([Hkv, D, total_kv], key-contiguous), which is
 // the layout the P.V product wants for its V operand (commit message,
-// Context; _enforce_mem_layouts).  Here that V tile is a plain 16-byte copy
-// into LDS.
+// Context; _enforce_mem_layouts).  Here a V tile is 128 rows (one per
+// dimension) of 128 consecutive key bytes, copied straight into LDS.
 //
 // Both products use the 32x32x64 fp8 MFMA (format E4M3 for both operands,
 // no block scale).  S^T = K.Q^T as in the 16-bit kernels; for P^T.V the
@@ -15,13 +15,21 @@
 // 32g .. 32g+31 of the 64-key group, which makes each lane's V^T operand 32
 // consecutive bytes of one V^T row.
 //
+// Pipeline: the same as the 16-bit prefill kernel -- a four-stage LDS ring
+// of K/V^T tiles filled by direct global->LDS loads from the first group of
+// four waves, and two groups of waves half a tile apart so that on every SIMD
+// one wave issues MFMAs while the other computes a softmax.
+//
 // Numerics: scores = (scale * dq * dk) * (q8 . k8) in fp32; online softmax in
 // fp32; P is rounded to e4m3 (nearest even) for the P.V product and the row
-// normaliser l is summed from those rounded values, so O = dv * (P8 . V8) / l
-// is a convex combination of V rows.
+// normaliser l is the sum of those rounded values, so O = dv * (P8 . V8) / l
+// is a convex combination of V rows.  The sum is one more MFMA per 64-key
+// group with an all-ones operand: every partial sum of at most 64 e4m3
+// values in [2^-9, 2^8] is exact in fp32, so this equals the plain sum.
 
 #include "device_common.h"
 #include "kernels.h"
+#include "ring.h"
 
 namespace attn {
 
@@ -49,228 +57,254 @@ __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int x) {
     return lo;
 }
 
-// K tile row read by A-operand lane row j of 32-key block kb = 2*gp + a.
-__device__ __forceinline__ int fp8_krow(int kb, int j) {
-    const int gp = kb >> 1, a = kb & 1;
-    return 64 * gp + 16 * a + 32 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
-}
-__device__ __forceinline__ int fp8_kswz(int row) { return (row & 3) | (((row >> 5) & 1) << 2); }
-
 constexpr int D8 = 128;     // head size (bytes per row)
 constexpr int BN8 = 128;    // keys per tile
+constexpr int kStages8 = 4;
 
-// LDS: K [BN8][128 B] (chunk c at c ^ fp8_kswz(row)), then Vt [128][BN8 B]
-// (key-contiguous rows, chunk c at c ^ (d & 7)).
-template <int NT>
-struct DenseTile8 {
-    static constexpr int K_BYTES = BN8 * D8;
-    static constexpr int V_BYTES = D8 * BN8;
-    static constexpr int BYTES = K_BYTES + V_BYTES;
-    static constexpr int KPT = (K_BYTES / 16) / NT;
-    static constexpr int VPT = (V_BYTES / 16) / NT;
-    static_assert(KPT >= 1 && VPT >= 1, "tile too small for the workgroup");
-    u32x4_t kreg[KPT];
-    u32x4_t vreg[VPT];
+// LDS tile layouts (128-byte rows, 8 chunks of 16 bytes).  gfx950's LDS
+// serves 16 lanes x 16 bytes per clock from 64 banks; a row covers half of
+// them, so a 16-lane read is conflict-free when its lanes' (row parity,
+// stored chunk) pairs are all distinct.
+//   K: chunk c of key row r is stored at c ^ kswz(r).  The 16 lanes of one
+//      A-operand read take rows that differ in bits 0, 1, 2 (or 3) and 5.
+//   V^T: chunk c of dimension row d is stored at c ^ vswz(d); one read takes
+//      16 consecutive rows.
+__device__ __forceinline__ int kswz(int r) {
+    return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r >> 5) & 1) << 2);
+}
+__device__ __forceinline__ int vswz(int d) { return (d >> 1) & 7; }
 
-    // keys [j0, j0 + BN8) of a sequence starting at global key kv_start
-    // (kv_len >= 1).  Loads past kv_len read a valid row / chunk of the same
-    // sequence and are zeroed by store(), so the loads issue back to back.
-    __device__ __forceinline__ void load(const uint8_t* __restrict__ k, const uint8_t* __restrict__ vt,
-                                         int64_t total_kv, int kv_start, int j0, int kv_len,
-                                         int k_tok_stride, int k_head_off, int64_t v_head_base,
-                                         bool v_aligned, int tid) {
-        const int last = kv_len - 1;
+// Key row (within the tile) read by A-operand row j of 32-key block kb.
+__device__ __forceinline__ int fp8_krow(int kb, int j) {
+    return 64 * (kb >> 1) + 16 * (kb & 1) + 32 * ((j >> 2) & 1) + 4 * (j >> 3) + (j & 3);
+}
+
+// Ring of K / V^T tiles of the fp8 kernel, loaded by four waves.  Loading
+// wave wl owns K rows and V^T rows [32 wl, 32 wl + 32) of every tile: four
+// direct loads of 1 KB (8 rows) each per tensor.
+struct Ring8 {
+    static constexpr int TILE = BN8 * D8;          // 16 KB per tensor
+    static constexpr int STAGE = 2 * TILE;         // K tile then V^T tile
+    static constexpr int IPW = 4;                  // loads per wave per tensor
+    static constexpr int LOADS_PER_TILE = 2 * IPW;
+
+    uint32_t koff[IPW];   // lane's byte offset from the wave's first K row
+    uint32_t voff[IPW];   // lane's byte offset from the wave's first V^T row
+
+    __device__ __forceinline__ static int row(int lane, int wl, int i) {
+        return 32 * wl + 8 * i + (lane >> 3);
+    }
+    __device__ __forceinline__ static int kchunk(int lane, int wl, int i) {
+        return (lane & 7) ^ kswz(row(lane, wl, i));
+    }
+    __device__ __forceinline__ static int vchunk(int lane, int wl, int i) {
+        return (lane & 7) ^ vswz(row(lane, wl, i));
+    }
+
+    __device__ __forceinline__ void init(int lane, int wl, int k_stride, int total_kv) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            const int row = idx >> 3, c = idx & 7;
-            const int key = min(j0 + row, last);
-            kreg[i] = *reinterpret_cast<const u32x4_t*>(
-                k + (int64_t)(kv_start + key) * k_tok_stride + k_head_off + c * 16);
-        }
-        if (v_aligned) {
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int idx = tid + i * NT;
-                const int d = idx >> 3, c = idx & 7;
-                const int key0 = min(j0 + c * 16, last & ~15);
-                vreg[i] = *reinterpret_cast<const u32x4_t*>(
-                    vt + v_head_base + (int64_t)d * total_kv + kv_start + key0);
-            }
-        } else {
-            // unaligned varlen layout: byte loads of the valid keys only
-#pragma unroll
-            for (int i = 0; i < VPT; ++i) {
-                const int idx = tid + i * NT;
-                const int d = idx >> 3, c = idx & 7;
-                const int key0 = j0 + c * 16;
-                const uint8_t* src = vt + v_head_base + (int64_t)d * total_kv + kv_start + key0;
-                uint32_t wds[4] = {0u, 0u, 0u, 0u};
-                const int n = kv_len - key0;
-                for (int bI = 0; bI < 16 && bI < n; ++bI)
-                    wds[bI >> 2] |= (uint32_t)src[bI] << (8 * (bI & 3));
-                vreg[i] = u32x4_t{wds[0], wds[1], wds[2], wds[3]};
-            }
+        for (int i = 0; i < IPW; ++i) {
+            const int rr = 8 * i + (lane >> 3);
+            koff[i] = (uint32_t)(rr * k_stride + kchunk(lane, wl, i) * 16);
+            voff[i] = (uint32_t)rr * (uint32_t)total_kv + (uint32_t)(vchunk(lane, wl, i) * 16);
         }
     }
 
-    __device__ __forceinline__ void store(uint8_t* lds, int j0, int kv_len, int tid) const {
-        const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int idx = tid + i * NT;
-            const int row = idx >> 3, c = idx & 7;
-            const u32x4_t v = (j0 + row < kv_len) ? kreg[i] : zero;
-            *reinterpret_cast<u32x4_t*>(lds + row * D8 + ((c ^ fp8_kswz(row)) << 4)) = v;
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int idx = tid + i * NT;
-            const int d = idx >> 3, c = idx & 7;
-            const int n = kv_len - (j0 + c * 16);   // valid keys in this 16-key chunk
-            u32x4_t v = vreg[i];
-            if (n < 16) {
-#pragma unroll
-                for (int wd = 0; wd < 4; ++wd) {
-                    const int keep = n - 4 * wd;
-                    const uint32_t msk = keep >= 4 ? 0xffffffffu
-                                       : keep <= 0 ? 0u
-                                                   : (0xffffffffu >> (32 - 8 * keep));
-                    v[wd] &= msk;
-                }
-            }
-            *reinterpret_cast<u32x4_t*>(lds + K_BYTES + d * BN8 + ((c ^ (d & 7)) << 4)) = v;
-        }
+    struct Src {
+        const uint8_t* k;   // K row 32 wl of the tile
+        const uint8_t* v;   // V^T row 32 wl, key j0 of the tile
+    };
+
+    // Load k (< LOADS_PER_TILE: K first, then V^T) of a tile fetched with
+    // wave-uniform bases.  stage: LDS byte address of the ring stage.
+    __device__ __forceinline__ void dma(int k, const Src& sr, uint32_t stage, int wl) const {
+        const int i = k % IPW;
+        if (k < IPW) dma16_s(sr.k, koff[i], stage + (wl * IPW + i) * 1024);
+        else dma16_s(sr.v, voff[i], stage + TILE + (wl * IPW + i) * 1024);
     }
 };
 
-template <int QB>
-struct Fp8Rows {
-    i32x8_t q[QB][2];          // Q^T operand: dims 64t + 32g .. +31 per lane-half
-    f32x16_t o[4][QB];         // O^T accumulators (P8 . V8, unscaled)
-    float m[QB], l[QB];
-    int lo[QB], hi[QB];
+// Per-wave pipeline state of one 32-row block.
+struct Fp8Wave {
+    f32x16_t s[4];       // scores of the tile waiting for its softmax
+    i32x8_t pb[2];       // e4m3 probabilities of the tile waiting for its P.V
+    f32x16_t o[4];       // O^T accumulators (P8 . V8, unscaled)
+    f32x16_t l;          // row sums of P8 (every row of a column holds it)
+    float m, alpha;
+    bool need;
 };
 
-template <int QB, bool MASKED>
-__device__ __forceinline__ void fp8_tile_step(Fp8Rows<QB>& st, const uint8_t* lds, int j0,
-                                              float c) {
-    const uint8_t* lk = lds;
-    const uint8_t* lv = lds + BN8 * D8;
-    const int lane = lane_id();
-    const int col = lane & 31, g = lane >> 5;
-
-    f32x16_t s[4][QB];
+// Online softmax of one tile (VALU): mask when partial, new running max
+// (lazy: moved only when some row's tile max exceeds it by more than
+// kRescaleSlack), probabilities rounded to e4m3 into pb.
+template <bool MASKED>
+__device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, int hi) {
+    const int g = lane_id() >> 5;
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16_t{};
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int row = fp8_krow(kb, col);
-            const uint8_t* rp = lk + row * D8;
-            const int c0 = 4 * t + 2 * g;
-            const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(rp + ((c0 ^ fp8_kswz(row)) << 4));
-            const u32x4_t hi4 =
-                *reinterpret_cast<const u32x4_t*>(rp + (((c0 + 1) ^ fp8_kswz(row)) << 4));
-            const i32x8_t a = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                               (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma_fp8(a, st.q[qb][t], s[kb][qb]);
-        }
-
-    float mx[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mx[qb] = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                if constexpr (MASKED) {
-                    // key held by register r of block kb for this lane
-                    const int key = j0 + 64 * (kb >> 1) + 32 * g + 16 * (kb & 1) + r;
-                    if (!(key >= st.lo[qb] && key < st.hi[qb])) s[kb][qb][r] = kNegInf;
-                }
-                mx[qb] = fmaxf(mx[qb], s[kb][qb][r]);
+                // key held by register r of block kb for this lane
+                const int key = j0 + 64 * (kb >> 1) + 32 * g + 16 * (kb & 1) + r;
+                if (!(key >= lo && key < hi)) st.s[kb][r] = kNegInf;
             }
-
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = fmaxf(mx[qb], xor32(mx[qb]));
-        mx[qb] = (mx[qb] == kNegInf) ? kNegInf : mx[qb] * c;
-        need |= mx[qb] > st.m[qb] + kRescaleSlack;
     }
-    if (__any(need)) {
+    float mx = kNegInf;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float mnew = fmaxf(st.m[qb], mx[qb]);
-            const float alpha = (mnew == kNegInf) ? 1.f : fast_exp2(st.m[qb] - mnew);
-            st.m[qb] = mnew;
-            st.l[qb] *= alpha;
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int db = 0; db < 4; ++db) st.o[db][qb] *= alpha;
-        }
-    }
-
-    float rs[QB];
-    i32x8_t pb[2][QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        rs[qb] = 0.f;
-        const float nm = (st.m[qb] == kNegInf) ? 0.f : -st.m[qb];
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-#pragma unroll
-            for (int wd = 0; wd < 8; ++wd) {
-                const int kb = 2 * gp + (wd >> 2);
-                const int r0 = 4 * (wd & 3);
-                float pv[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float sv = s[kb][qb][r0 + e];
-                    pv[e] = fast_exp2(__builtin_fmaf(sv, c, nm));
-                    if constexpr (MASKED) pv[e] = (sv == kNegInf) ? 0.f : pv[e];
-                }
-                int packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
-                packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], packed, true);
-                pb[gp][qb][wd] = packed;
-                const f32x2_t back_lo = __builtin_amdgcn_cvt_pk_f32_fp8(packed, false);
-                const f32x2_t back_hi = __builtin_amdgcn_cvt_pk_f32_fp8(packed, true);
-                rs[qb] += (back_lo.x + back_lo.y) + (back_hi.x + back_hi.y);
-            }
-        }
-        st.l[qb] += rs[qb] + xor32(rs[qb]);
-    }
-
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st.s[kb][r]);
+    mx = fmaxf(mx, xor32(mx));
+    mx = (mx == kNegInf) ? kNegInf : mx * c;
+    const bool up = mx > st.m + kRescaleSlack;
+    st.need = __any(up);
+    const float mnew = st.need ? fmaxf(st.m, mx) : st.m;
+    st.alpha = (mnew == kNegInf) ? 1.f : fast_exp2(st.m - mnew);
+    st.m = mnew;
+    const float nm = (mnew == kNegInf) ? 0.f : -mnew;
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int d = db * 32 + col;
-            const uint8_t* rp = lv + d * BN8;
-            const int c0 = 4 * gp + 2 * g;
-            const u32x4_t lo4 = *reinterpret_cast<const u32x4_t*>(rp + ((c0 ^ (d & 7)) << 4));
-            const u32x4_t hi4 = *reinterpret_cast<const u32x4_t*>(rp + (((c0 + 1) ^ (d & 7)) << 4));
-            const i32x8_t a = {(int)lo4.x, (int)lo4.y, (int)lo4.z, (int)lo4.w,
-                               (int)hi4.x, (int)hi4.y, (int)hi4.z, (int)hi4.w};
+        for (int wd = 0; wd < 8; ++wd) {
+            const int kb = 2 * gp + (wd >> 2);
+            const int r0 = 4 * (wd & 3);
+            float pv[4];
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) st.o[db][qb] = mfma_fp8(a, pb[gp][qb], st.o[db][qb]);
+            for (int e = 0; e < 4; ++e) {
+                const float sv = st.s[kb][r0 + e];
+                pv[e] = fast_exp2(__builtin_fmaf(sv, c, nm));
+                if constexpr (MASKED) pv[e] = (sv == kNegInf) ? 0.f : pv[e];
+            }
+            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
+            packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], packed, true);
+            st.pb[gp][wd] = packed;
         }
 }
 
+__device__ __forceinline__ i32x8_t frag8(const uint8_t* p, uint32_t off) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p + off);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(p + (off ^ 16u));
+    return i32x8_t{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+
+// The 16 bytes at p (any alignment) with bytes nv .. 15 zeroed (nv <= 0: all
+// zero), read as the dword-aligned words that hold bytes 0 .. nv-1 only: a
+// word holding one of
+// them lies inside the tensor (the tensor starts on a 16-byte boundary and
+// its size is a multiple of 128 bytes), so nothing past it is touched.
+__device__ __forceinline__ u32x4_t load16_any(const uint8_t* p, int nv) {
+    const uintptr_t a = (uintptr_t)p;
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
+    const uint32_t sh = (uint32_t)(a & 3);
+    uint32_t wd[5];
+#pragma unroll
+    for (int t = 0; t < 5; ++t) wd[t] = (nv > 0 && 4 * t < (int)sh + nv) ? wp[t] : 0u;
+    u32x4_t r;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        // bytes 4t .. 4t+3 of the result: window bytes sh + 4t ..
+        uint32_t x = __builtin_amdgcn_alignbyte(wd[t + 1], wd[t], sh);
+        const int keep = nv - 4 * t;
+        x &= keep >= 4 ? 0xffffffffu : keep <= 0 ? 0u : (0xffffffffu >> (32 - 8 * keep));
+        r[t] = x;
+    }
+    return r;
+}
+
+constexpr int kQk8Prefetch = 3;
+constexpr int kPv8Prefetch = 3;
+
+// S^T[kb] = K_tile(kb) . Q^T: 8 MFMAs, step t*4 + kb.  Called for every
+// tile, visible keys or not, so the scores are always overwritten here and
+// the previous tile's are never live across the P.V that precedes a call.
+__device__ __forceinline__ void qk8(f32x16_t (&s)[4], const uint8_t* kt, const i32x8_t (&q)[2]) {
+    const int lane = lane_id();
+    const int col = lane & 31, g = lane >> 5;
+    // Row fp8_krow(kb, col) = kb's block base + rb; its swizzle depends on
+    // bits 1, 2, 5 only, which kb does not touch.  Step t reads chunks
+    // 4t + 2g and 4t + 2g + 1: this offset XOR (t << 6), then XOR 16.
+    const int rb = fp8_krow(0, col);
+    uint32_t lo = (uint32_t)(rb * D8 + (((2 * g) ^ kswz(rb)) << 4));
+    asm volatile("" : "+v"(lo));
+    auto frag = [&](int i) {
+        const int t = i >> 2, kb = i & 3;
+        return frag8(kt + (64 * (kb >> 1) + 16 * (kb & 1)) * D8, lo ^ (uint32_t)(t << 6));
+    };
+    constexpr int PD = kQk8Prefetch;
+    i32x8_t a[PD + 1];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < PD; ++i) a[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i + PD < 8) a[(i + PD) % (PD + 1)] = frag(i + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        s[i & 3] = mfma_fp8(a[i % (PD + 1)], q[i >> 2], s[i & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// O^T[db] += V^T_tile(db, gp) . P^T(gp) (8 MFMAs, step db*2 + gp, `hook`
+// after each), then the two row-sum MFMAs.
+template <class Hook>
+__device__ __forceinline__ void pv8(Fp8Wave& st, const uint8_t* vt, const Hook& hook) {
+    if (st.need) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) st.o[db] *= st.alpha;
+        st.l *= st.alpha;
+        st.need = false;
+    }
+    const int lane = lane_id();
+    const int col = lane & 31, g = lane >> 5;
+    // V^T row db*32 + col: the swizzle depends on col only; group gp reads
+    // chunks 4gp + 2g and 4gp + 2g + 1.
+    uint32_t lo = (uint32_t)(col * D8 + (((2 * g) ^ vswz(col)) << 4));
+    asm volatile("" : "+v"(lo));
+    auto frag = [&](int i) {
+        const int db = i >> 1, gp = i & 1;
+        return frag8(vt + db * 32 * D8, lo ^ (uint32_t)(gp << 6));
+    };
+    constexpr int PD = kPv8Prefetch;
+    i32x8_t a[PD + 1];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) a[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (i + PD < 8) a[(i + PD) % (PD + 1)] = frag(i + PD);
+        __builtin_amdgcn_sched_barrier(0);
+        st.o[i >> 1] = mfma_fp8(a[i % (PD + 1)], st.pb[i & 1], st.o[i >> 1]);
+        hook(i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const int one4 = 0x38383838;   // four e4m3 1.0
+    const i32x8_t ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+    st.l = mfma_fp8(ones, st.pb[0], st.l);
+    st.l = mfma_fp8(ones, st.pb[1], st.l);
+}
+
+template <class R>
+struct Dma8Hook {
+    const R& ld;
+    typename R::Src sr;
+    uint32_t stage;
+    int wl;
+    bool on;
+    __device__ __forceinline__ void operator()(int step) const {
+        if (on) ld.dma(step, sr, stage, wl);
+    }
+};
+
 }  // namespace
 
-template <int QB, int NW>
+template <int NW>
 __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
-    constexpr int NT = NW * 64;
-    constexpr int BM = NW * QB * 32;
-    using Tile = DenseTile8<NT>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Tile::BYTES];
+    static_assert(NW == 8, "two groups of four single-block waves");
+    constexpr int BM = NW * 32;
+    using R = Ring8;
+    static_assert(R::LOADS_PER_TILE == 8, "one load per P.V MFMA");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages8 * R::STAGE];
     __shared__ int wave_range[2][NW];
 
     int b, hg, qt;
@@ -289,60 +323,49 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     const bool neg = c_signed < 0.f;
     const float c = fabsf(c_signed);
 
-    const int tid = threadIdx.x;
-    const int lane = lane_id(), w = wave_id();
+    const int lane = lane_id();
+    const int w = wave_id();
     const int col = lane & 31, g = lane >> 5;
+    // Waves 0-3 lead, waves 4-7 trail by half a tile; the lead waves alone
+    // load the ring, between the MFMAs of their P.V.
+    const bool lead = w < NW / 2;
+    const int wl = w & (NW / 2 - 1);
 
-    Fp8Rows<QB> st;
-    int tok[QB], head[QB];
-    bool valid[QB];
-    int my_lo = 0x7fffffff, my_hi = -0x7fffffff, my_lo_max = -0x7fffffff, my_hi_min = 0x7fffffff;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        st.m[qb] = kNegInf;
-        st.l[qb] = 0.f;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) st.o[db][qb] = f32x16_t{};
-        const int r = (w * QB + qb) * 32 + col;
-        tok[qb] = tok0 + (r >> p.pack_log2);
-        head[qb] = h0 + (r & ((1 << p.pack_log2) - 1));
-        valid[qb] = tok[qb] < q_len;
-        const uint8_t* qp = p.q + ((int64_t)(q_start + tok[qb]) * p.num_heads + head[qb]) * D8 + 32 * g;
+    const int r = w * 32 + col;
+    const int tok = tok0 + (r >> p.pack_log2);
+    const int head = h0 + (r & ((1 << p.pack_log2) - 1));
+    const bool valid = tok < q_len;
+    // Q^T operand (dims 64t + 32g .. +31); a row past the sequence end reads
+    // row tok0 (its keys are all masked and it is never stored).
+    i32x8_t q[2];
+    {
+        const uint8_t* qp =
+            p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D8 + 32 * g;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            i32x8_t v = {};
-            if (valid[qb]) {
-                const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t);
-                const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t + 16);
-                v = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                            (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-                if (neg) v ^= (int)0x80808080u;   // apply a negative scale to -q
-            }
-            st.q[qb][t] = v;
+            const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t);
+            const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t + 16);
+            q[t] = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+            if (neg) q[t] ^= (int)0x80808080u;   // a negative scale applied to -q
         }
-        int lo = 0, hi = kv_len;
-        if (valid[qb]) {
-            if (p.mask & kMaskCausal) hi = min(hi, tok[qb] + (kv_len - q_len) + 1);
-            if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok[qb]] + 1);
-            if (p.mask & kMaskDocument) {
-                const int doc = p.q_ids[q_start + tok[qb]];
-                lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
-                hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
-            }
-            if (hi < lo) hi = lo;
-            my_lo = min(my_lo, lo);
-            my_hi = max(my_hi, hi);
-            my_lo_max = max(my_lo_max, lo);
-            my_hi_min = min(my_hi_min, hi);
-        } else {
-            lo = 0;
-            hi = 0;
-        }
-        st.lo[qb] = lo;
-        st.hi[qb] = hi;
     }
-    const int w_lo = wave_min(my_lo), w_hi = wave_max(my_hi);
-    const int w_lo_max = wave_max(my_lo_max), w_hi_min = wave_min(my_hi_min);
+    int lo = 0, hi = 0;
+    if (valid) {
+        hi = kv_len;
+        if (p.mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
+        if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
+        if (p.mask & kMaskDocument) {
+            const int doc = p.q_ids[q_start + tok];
+            lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
+            hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
+        }
+        if (hi < lo) hi = lo;
+    }
+    const int w_lo = wave_min(valid ? lo : 0x7fffffff);
+    const int w_hi = wave_max(valid ? hi : -0x7fffffff);
+    const int w_lo_max = wave_max(valid ? lo : -0x7fffffff);
+    const int w_hi_min = wave_min(valid ? hi : 0x7fffffff);
     const bool w_any = w_hi > w_lo;
     if (lane == 0) {
         wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
@@ -355,55 +378,166 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
         kv_begin = min(kv_begin, wave_range[0][i]);
         kv_end = max(kv_end, wave_range[1][i]);
     }
-    kv_begin &= ~15;
-    const int n_tiles = kv_end > kv_begin ? (kv_end - kv_begin + BN8 - 1) / BN8 : 0;
+    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin & ~15);
+    kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+    const int n = kv_end > kv_begin ? (kv_end - kv_begin + BN8 - 1) / BN8 : 0;
 
-    const int k_tok_stride = p.num_kv_heads * D8;
-    const int k_head_off = hk * D8;
-    const int64_t v_head_base = (int64_t)hk * D8 * p.total_kv;
+    const int k_stride = p.num_kv_heads * D8;
+    const uint8_t* k_head = p.k + (int64_t)kv_start * k_stride + hk * D8;
+    const uint8_t* v_head = p.vt + (int64_t)hk * D8 * p.total_kv + kv_start;
+    // Direct loads need 16-byte aligned V^T chunks: every V^T row offset and
+    // the sequence start on a 16-key boundary.
     const bool v_aligned = ((p.total_kv & 15) == 0) && ((kv_start & 15) == 0);
-    Tile ld;
-    if (n_tiles > 0) {
-        ld.load(p.k, p.vt, p.total_kv, kv_start, kv_begin, kv_len, k_tok_stride, k_head_off,
-                v_head_base, v_aligned, tid);
-        ld.store(smem, kv_begin, kv_len, tid);
-    }
-    __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-        const int j = kv_begin + it * BN8;
-        const uint8_t* cur = smem + (it & 1) * Tile::BYTES;
-        const bool has_next = it + 1 < n_tiles;
-        if (has_next)
-            ld.load(p.k, p.vt, p.total_kv, kv_start, j + BN8, kv_len, k_tok_stride, k_head_off,
-                    v_head_base, v_aligned, tid);
-        if (w_any && j < w_hi && j + BN8 > w_lo) {
-            if (j >= w_lo_max && j + BN8 <= w_hi_min)
-                fp8_tile_step<QB, false>(st, cur, j, c);
-            else
-                fp8_tile_step<QB, true>(st, cur, j, c);
+    R ld;
+    ld.init(lane, wl, k_stride, p.total_kv);
+    const uint32_t ring_lds = lds_addr(ring);
+
+    // Loads of the tile at key j0 into the stage at LDS address `stage`:
+    // with wave-uniform bases when the tile lies inside the sequence and V^T
+    // is aligned (`spread`: the caller issues them one per MFMA), otherwise
+    // all at once here with per-lane clamped addresses; rows past kv_len
+    // repeat row kv_len - 1 (K) or the last aligned 16-key chunk (V^T), whose
+    // probabilities are 0.  An unaligned V^T is gathered from aligned words
+    // and written to LDS by the wave (those loads have all returned on exit).
+    auto fast = [&](int j0) { return v_aligned && j0 + BN8 <= kv_len; };
+    auto src = [&](int j0) {
+        return R::Src{k_head + (int64_t)(j0 + 32 * wl) * k_stride,
+                      v_head + (int64_t)(32 * wl) * p.total_kv + j0};
+    };
+    auto issue_all = [&](int j0, uint32_t stage) {
+        if (fast(j0)) {
+            const R::Src sr = src(j0);
+#pragma unroll
+            for (int k = 0; k < R::LOADS_PER_TILE; ++k) ld.dma(k, sr, stage, wl);
+            return;
         }
-        if (has_next) ld.store(smem + ((it + 1) & 1) * Tile::BYTES, j + BN8, kv_len, tid);
-        __syncthreads();
+        const int last = kv_len - 1;
+        // the empty asm keeps the row addresses below from being hoisted out
+        // of the tile loop into registers held across it
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        if (!v_aligned) {
+            const uint32_t stage_off = stage - ring_lds;
+#pragma unroll
+            for (int i = 0; i < R::IPW; ++i) {
+                const int d = R::row(ln, wl, i);
+                const int key0 = j0 + 16 * R::vchunk(ln, wl, i);
+                const int nv = min(max(kv_len - key0, 0), 16);
+                const u32x4_t v = load16_any(v_head + (int64_t)d * p.total_kv + key0, nv);
+                *reinterpret_cast<u32x4_t*>(ring + stage_off + R::TILE + (wl * R::IPW + i) * 1024 +
+                                            16 * ln) = v;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < R::IPW; ++i) {
+            const int rr = R::row(ln, wl, i);
+            const int key = min(j0 + rr, last);
+            dma16(k_head + (int64_t)key * k_stride + R::kchunk(ln, wl, i) * 16,
+                  stage + (wl * R::IPW + i) * 1024);
+            if (v_aligned) {
+                const int key0 = min(j0 + 16 * R::vchunk(ln, wl, i), last & ~15);
+                dma16(v_head + (int64_t)rr * p.total_kv + key0,
+                      stage + R::TILE + (wl * R::IPW + i) * 1024);
+            }
+        }
+    };
+    // this wave has no visible key in the tile at j0
+    auto empty = [&](int j0) { return !w_any || j0 >= w_hi || j0 + BN8 <= w_lo; };
+    auto full = [&](int j0) { return j0 >= w_lo_max && j0 + BN8 <= w_hi_min; };
+
+    Fp8Wave st;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) st.o[db] = f32x16_t{};
+    st.l = f32x16_t{};
+    st.m = kNegInf;
+    st.alpha = 1.f;
+    st.need = false;
+
+    auto softmax = [&](int j0) {
+        if (full(j0)) softmax8<false>(st, c, j0, lo, hi);
+        else softmax8<true>(st, c, j0, lo, hi);
+    };
+
+    if (n > 0) {
+        // Per tile j: QK(j) -> softmax(j) -> PV(j), the groups offset by half
+        // a tile:
+        //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
+        //   phase 2 of tile j: lead PV(j) + loads, QK(j+1)   trail softmax(j)
+        // Tile j+3 goes into the stage of tile j-1, free once phase 1 of
+        // tile j is over.
+        if (lead) {
+#pragma unroll
+            for (int k = 0; k < kStages8 - 1; ++k)
+                if (k < n) issue_all(kv_begin + k * BN8, ring_lds + k * R::STAGE);
+            static_assert(kStages8 == 4, "wait counts below");
+            if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
+            else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
+        block_barrier();
+        if (lead) qk8(st.s, ring, q);
+
+        for (int jt = 0; jt < n; ++jt) {
+            const int j0 = kv_begin + jt * BN8;
+            const uint8_t* st_cur = ring + (jt % kStages8) * R::STAGE;
+            const uint8_t* st_prev = ring + ((jt + kStages8 - 1) % kStages8) * R::STAGE;
+            const uint8_t* st_next = ring + ((jt + 1) % kStages8) * R::STAGE;
+            // phase 1
+            if (lead) {
+                if (!empty(j0)) softmax(j0);
+            } else {
+                if (jt > 0 && !empty(j0 - BN8)) pv8(st, st_prev + R::TILE, NoHook{});
+                qk8(st.s, st_cur, q);
+            }
+            // tile jt+1 must have landed; tile jt+2, issued after it, may stay
+            // in flight
+            if (lead && jt + 1 < n) {
+                if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            }
+            block_barrier();
+            // phase 2
+            if (lead) {
+                const int j3 = j0 + (kStages8 - 1) * BN8;
+                const bool load3 = jt + kStages8 - 1 < n;
+                const uint32_t st3 = ring_lds + ((jt + kStages8 - 1) % kStages8) * R::STAGE;
+                const bool compute = !empty(j0);
+                const bool spread = load3 && compute && fast(j3);
+                if (load3 && !spread) issue_all(j3, st3);
+                if (compute) {
+                    R::Src sr{p.k, p.vt};
+                    if (spread) sr = src(j3);
+                    pv8(st, st_cur + R::TILE, Dma8Hook<R>{ld, sr, st3, wl, spread});
+                }
+                if (jt + 1 < n) qk8(st.s, st_next, q);
+            } else {
+                if (!empty(j0)) softmax(j0);
+            }
+            block_barrier();
+        }
+        if (!lead && !empty(kv_begin + (n - 1) * BN8))
+            pv8(st, ring + ((n - 1) % kStages8) * R::STAGE + R::TILE, NoHook{});
     }
 
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        if (!valid[qb]) continue;
-        const int64_t row = (int64_t)(q_start + tok[qb]) * p.num_heads + head[qb];
+    if (valid) {
+        const float l = st.l[0];
+        const int64_t row = (int64_t)(q_start + tok) * p.num_heads + head;
         f32x16_t o_db[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o_db[db] = st.o[db][qb] * dv;
-        store_row<D8, true>(o_db, st.l[qb], p.out + row * D8);
+        for (int db = 0; db < 4; ++db) o_db[db] = st.o[db] * dv;
+        store_row<D8, true>(o_db, l, p.out + row * D8);
         if (p.lse != nullptr && g == 0)
-            p.lse[row] = st.l[qb] > 0.f ? (st.m[qb] + __builtin_log2f(st.l[qb])) * kLn2 : kNegInf;
+            p.lse[row] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
     }
 }
 
 hipError_t launch_fp8_prefill(const Fp8Params& p0, int head_size, int max_seqlen_q,
                               hipStream_t s) {
     if (head_size != D8) return hipErrorInvalidValue;
-    constexpr int QB = 1, NW = 8;
-    constexpr int BM = NW * QB * 32;
+    // V^T row offsets of one loading wave (32 rows) are 32-bit
+    if (p0.total_kv > (1 << 27)) return hipErrorInvalidValue;
+    constexpr int NW = 8;
+    constexpr int BM = NW * 32;
     Fp8Params p = p0;
     const int tokens_per_tile = BM >> p.pack_log2;
     p.n_qtiles = (max_seqlen_q + tokens_per_tile - 1) / tokens_per_tile;
@@ -411,7 +545,7 @@ hipError_t launch_fp8_prefill(const Fp8Params& p0, int head_size, int max_seqlen
                                            tokens_per_tile);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_fp8_prefill<QB, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((k_fp8_prefill<NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
 

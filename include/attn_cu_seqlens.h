@@ -50,6 +50,8 @@
  *     cu arrays must be non-decreasing with cu[batch] equal to the stated
  *     total, used table entries must lie in [0, num_blocks), and no sequence
  *     may be longer than the max_seqlen arguments.
+ *   - Tensor arguments (q, k, v, caches, out) must start on a 16-byte
+ *     boundary; otherwise ATTN_ERR_BAD_SHAPE.
  *   - The device must be gfx950; otherwise ATTN_ERR_UNSUPPORTED.  The check
  *     runs on the first call on each device and is cached.
  *   - Calls with nothing to compute (batch == 0, total == 0) return ATTN_OK
@@ -211,7 +213,10 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
  *   lse          float32 [total_q, num_heads] or NULL
  * Scores and the softmax run in fp32.  The probabilities are rounded to e4m3
  * (nearest even) for the P.V product, and each row's normaliser is summed
- * from those rounded values.  Supported: head_size 128.
+ * from those rounded values.  Supported: head_size 128, total_kv <= 2^27
+ * (ATTN_ERR_BAD_SHAPE beyond).  Sequences whose V columns do not start on a
+ * 16-key boundary (total_kv or a cu_seqlens_kv entry not a multiple of 16)
+ * are supported on a slower load path.
  */
 attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor,
                          const float* descale_qkv, const int32_t* cu_seqlens_q,

@@ -265,6 +265,41 @@ def test_fp8_causal(A, lens, hq, hkv):
     compare(out, lse, ref_o, ref_l, ATOL_FP8, what=f"fp8_causal_{lens}", lse_atol=LSE_ATOL_FP8)
 
 
+@pytest.mark.parametrize("q_lens,kv_lens,hq,hkv", [
+    ([1024, 640], [1024, 640], 16, 2),    # many tiles through the ring, V^T aligned
+    ([1000, 777], [1000, 777], 4, 4),     # many tiles, V^T unaligned (total 1777)
+    ([40, 600], [40, 600], 8, 8),         # total aligned, second sequence starts at key 40
+    ([100, 37], [700, 301], 8, 2),        # bottom-right causal, q shorter than kv
+])
+def test_fp8_causal_multi_tile(A, q_lens, kv_lens, hq, hkv):
+    w = W.make_fp8("fp8m", 43, q_lens, kv_lens, hq, hkv, 128, W.MASK_CAUSAL)
+    banner(f"fp8 causal q={q_lens} kv={kv_lens} H={hq}/{hkv}")
+    out, lse = gpu_fp8(w, A)
+    ref_o, ref_l = oracle_fp8(w)
+    compare(out, lse, ref_o, ref_l, ATOL_FP8, what=f"fp8_multi_{q_lens}_{kv_lens}",
+            lse_atol=LSE_ATOL_FP8)
+
+
+def test_fp8_document_mask_negative_scale(A):
+    """Document ids bound each row's keys on both sides; a negative scale
+    flips the sign of every score."""
+    rng = np.random.default_rng(7)
+    lens = [530, 333]
+    docs = []
+    for n in lens:
+        cuts = np.sort(rng.choice(np.arange(1, n), 5, replace=False))
+        docs.append(np.searchsorted(cuts, np.arange(n), side="right").astype(np.int32))
+    ids = np.concatenate(docs)
+    for flags, scale in ((W.MASK_DOCUMENT, -0.07), (W.MASK_DOCUMENT | W.MASK_CAUSAL, 0.09)):
+        w = W.make_fp8("fp8doc", 44, lens, lens, 8, 2, 128, flags, q_ids=ids, kv_ids=ids,
+                       scale=scale)
+        banner(f"fp8 document flags={flags} scale={scale}")
+        out, lse = gpu_fp8(w, A)
+        ref_o, ref_l = oracle_fp8(w)
+        compare(out, lse, ref_o, ref_l, ATOL_FP8, what=f"fp8_document_{flags}",
+                lse_atol=LSE_ATOL_FP8)
+
+
 def test_fp8_unaligned_varlen_no_mask(A):
     """Lengths that are not multiples of 16 exercise the unaligned V path."""
     w = W.make_fp8("fp8u", 42, [37, 100, 5], [50, 77, 130], 4, 2, 128, W.MASK_NONE)

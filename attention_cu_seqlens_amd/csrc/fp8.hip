@@ -212,45 +212,23 @@ __device__ __forceinline__ u32x4_t load16_any(const uint8_t* p, int nv) {
     return r;
 }
 
-constexpr int kQk8Prefetch = 3;
-constexpr int kPv8Prefetch = 3;
+constexpr int kStream8Prefetch = 3;
 
-// S^T[kb] = K_tile(kb) . Q^T: 8 MFMAs, step t*4 + kb.  Called for every
-// tile, visible keys or not, so the scores are always overwritten here and
-// the previous tile's are never live across the P.V that precedes a call.
-__device__ __forceinline__ void qk8(f32x16_t (&s)[4], const uint8_t* kt, const i32x8_t (&q)[2]) {
-    const int lane = lane_id();
-    const int col = lane & 31, g = lane >> 5;
-    // Row fp8_krow(kb, col) = kb's block base + rb; its swizzle depends on
-    // bits 1, 2, 5 only, which kb does not touch.  Step t reads chunks
-    // 4t + 2g and 4t + 2g + 1: this offset XOR (t << 6), then XOR 16.
-    const int rb = fp8_krow(0, col);
-    uint32_t lo = (uint32_t)(rb * D8 + (((2 * g) ^ kswz(rb)) << 4));
-    asm volatile("" : "+v"(lo));
-    auto frag = [&](int i) {
-        const int t = i >> 2, kb = i & 3;
-        return frag8(kt + (64 * (kb >> 1) + 16 * (kb & 1)) * D8, lo ^ (uint32_t)(t << 6));
-    };
-    constexpr int PD = kQk8Prefetch;
-    i32x8_t a[PD + 1];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x16_t{};
-#pragma unroll
-    for (int i = 0; i < PD; ++i) a[i] = frag(i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (i + PD < 8) a[(i + PD) % (PD + 1)] = frag(i + PD);
-        __builtin_amdgcn_sched_barrier(0);
-        s[i & 3] = mfma_fp8(a[i % (PD + 1)], q[i >> 2], s[i & 3]);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// O^T[db] += V^T_tile(db, gp) . P^T(gp) (8 MFMAs, step db*2 + gp, `hook`
-// after each), then the two row-sum MFMAs.
-template <class Hook>
-__device__ __forceinline__ void pv8(Fp8Wave& st, const uint8_t* vt, const Hook& hook) {
-    if (st.need) {
+// The MFMA work of one pipeline phase as a single stream, so the LDS operand
+// prefetch runs on across the boundary between the products instead of
+// refilling at the start of each:
+//   PV: the row sums of P8 (two MFMAs with an all-ones operand, no LDS
+//       operand: they cover the first operand reads), then
+//       O^T[db] += V^T_tile(db, gp) . P^T(gp), 8 MFMAs (step db*2 + gp,
+//       `hook` after each);
+//   QK: S^T[kb] = K_tile(kb) . Q^T, 8 MFMAs (step t*4 + kb).
+// QK runs for every tile, visible keys or not, so the scores are always
+// overwritten and the previous tile's are never live across the P.V.
+template <bool PV, bool QK, class Hook>
+__device__ __forceinline__ void mfma_stream8(Fp8Wave& st, const uint8_t* vt, const uint8_t* kt,
+                                             const i32x8_t (&q)[2], const Hook& hook) {
+    static_assert(PV || QK, "empty stream");
+    if (PV && st.need) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) st.o[db] *= st.alpha;
         st.l *= st.alpha;
@@ -258,30 +236,47 @@ __device__ __forceinline__ void pv8(Fp8Wave& st, const uint8_t* vt, const Hook& 
     }
     const int lane = lane_id();
     const int col = lane & 31, g = lane >> 5;
-    // V^T row db*32 + col: the swizzle depends on col only; group gp reads
-    // chunks 4gp + 2g and 4gp + 2g + 1.
-    uint32_t lo = (uint32_t)(col * D8 + (((2 * g) ^ vswz(col)) << 4));
-    asm volatile("" : "+v"(lo));
+    // V^T row db*32 + col: its swizzle depends on col only; group gp reads
+    // chunks 4gp + 2g and 4gp + 2g + 1 (offset XOR (gp << 6), then XOR 16).
+    // K row fp8_krow(kb, col) = kb's block base + rb: its swizzle depends on
+    // bits 1, 2, 5 only, which kb does not touch; step t reads chunks
+    // 4t + 2g and 4t + 2g + 1.  The empty asm keeps the compiler from
+    // hoisting the XORed offsets out of the tile loop.
+    const int rb = fp8_krow(0, col);
+    uint32_t lov = (uint32_t)(col * D8 + (((2 * g) ^ vswz(col)) << 4));
+    uint32_t lok = (uint32_t)(rb * D8 + (((2 * g) ^ kswz(rb)) << 4));
+    asm volatile("" : "+v"(lov), "+v"(lok));
+    constexpr int NPV = PV ? 8 : 0;
+    constexpr int N = NPV + (QK ? 8 : 0);
     auto frag = [&](int i) {
-        const int db = i >> 1, gp = i & 1;
-        return frag8(vt + db * 32 * D8, lo ^ (uint32_t)(gp << 6));
+        if (i < NPV) return frag8(vt + (i >> 1) * 32 * D8, lov ^ (uint32_t)((i & 1) << 6));
+        const int j = i - NPV, t = j >> 2, kb = j & 3;
+        return frag8(kt + (64 * (kb >> 1) + 16 * (kb & 1)) * D8, lok ^ (uint32_t)(t << 6));
     };
-    constexpr int PD = kPv8Prefetch;
+    constexpr int PD = kStream8Prefetch;
     i32x8_t a[PD + 1];
 #pragma unroll
     for (int i = 0; i < PD; ++i) a[i] = frag(i);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (PV) {
+        const int one4 = 0x38383838;   // four e4m3 1.0
+        const i32x8_t ones = {one4, one4, one4, one4, one4, one4, one4, one4};
+        st.l = mfma_fp8(ones, st.pb[0], st.l);
+        st.l = mfma_fp8(ones, st.pb[1], st.l);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (i + PD < 8) a[(i + PD) % (PD + 1)] = frag(i + PD);
+    for (int i = 0; i < N; ++i) {
+        if (i + PD < N) a[(i + PD) % (PD + 1)] = frag(i + PD);
         __builtin_amdgcn_sched_barrier(0);
-        st.o[i >> 1] = mfma_fp8(a[i % (PD + 1)], st.pb[i & 1], st.o[i >> 1]);
-        hook(i);
+        if (i < NPV) {
+            st.o[i >> 1] = mfma_fp8(a[i % (PD + 1)], st.pb[i & 1], st.o[i >> 1]);
+            hook(i);
+        } else {
+            const int j = i - NPV;
+            st.s[j & 3] = mfma_fp8(a[i % (PD + 1)], q[j >> 2], j < 4 ? f32x16_t{} : st.s[j & 3]);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
-    const int one4 = 0x38383838;   // four e4m3 1.0
-    const i32x8_t ones = {one4, one4, one4, one4, one4, one4, one4, one4};
-    st.l = mfma_fp8(ones, st.pb[0], st.l);
-    st.l = mfma_fp8(ones, st.pb[1], st.l);
 }
 
 template <class R>
@@ -371,6 +366,12 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
         wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
         wave_range[1][w] = w_any ? w_hi : -0x7fffffff;
     }
+    // The trailing waves' first P.V reads the V^T tile of the last stage
+    // before any tile has been loaded there; zeroed, it contributes exactly
+    // nothing (uninitialised LDS could hold NaN codes).
+    for (int i = threadIdx.x; i < R::TILE / 16; i += NW * 64)
+        *reinterpret_cast<u32x4_t*>(ring + (kStages8 - 1) * R::STAGE + R::TILE + 16 * i) =
+            u32x4_t{0u, 0u, 0u, 0u};
     __syncthreads();
     int kv_begin = 0x7fffffff, kv_end = -0x7fffffff;
 #pragma unroll
@@ -441,18 +442,20 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             }
         }
     };
-    // this wave has no visible key in the tile at j0
-    auto empty = [&](int j0) { return !w_any || j0 >= w_hi || j0 + BN8 <= w_lo; };
     auto full = [&](int j0) { return j0 >= w_lo_max && j0 + BN8 <= w_hi_min; };
 
     Fp8Wave st;
 #pragma unroll
     for (int db = 0; db < 4; ++db) st.o[db] = f32x16_t{};
     st.l = f32x16_t{};
+    st.pb[0] = i32x8_t{};
+    st.pb[1] = i32x8_t{};
     st.m = kNegInf;
     st.alpha = 1.f;
     st.need = false;
 
+    // Every wave runs every tile: a tile with no visible key for this wave
+    // (a causal diagonal) gives P = 0 and leaves m, l and O unchanged.
     auto softmax = [&](int j0) {
         if (full(j0)) softmax8<false>(st, c, j0, lo, hi);
         else softmax8<true>(st, c, j0, lo, hi);
@@ -475,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
         block_barrier();
-        if (lead) qk8(st.s, ring, q);
+        if (lead) mfma_stream8<false, true>(st, ring, ring, q, NoHook{});
 
         for (int jt = 0; jt < n; ++jt) {
             const int j0 = kv_begin + jt * BN8;
@@ -484,10 +487,11 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             const uint8_t* st_next = ring + ((jt + 1) % kStages8) * R::STAGE;
             // phase 1
             if (lead) {
-                if (!empty(j0)) softmax(j0);
+                softmax(j0);
             } else {
-                if (jt > 0 && !empty(j0 - BN8)) pv8(st, st_prev + R::TILE, NoHook{});
-                qk8(st.s, st_cur, q);
+                // (at jt == 0 this P.V multiplies P8 = 0 by the zeroed V^T of
+                // the last stage: it adds nothing)
+                mfma_stream8<true, true>(st, st_prev + R::TILE, st_cur, q, NoHook{});
             }
             // tile jt+1 must have landed; tile jt+2, issued after it, may stay
             // in flight
@@ -496,27 +500,26 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             block_barrier();
-            // phase 2
+            // phase 2 (after the last tile the lead's QK reads a stale stage;
+            // those scores are never used)
             if (lead) {
                 const int j3 = j0 + (kStages8 - 1) * BN8;
                 const bool load3 = jt + kStages8 - 1 < n;
                 const uint32_t st3 = ring_lds + ((jt + kStages8 - 1) % kStages8) * R::STAGE;
-                const bool compute = !empty(j0);
-                const bool spread = load3 && compute && fast(j3);
+                const bool spread = load3 && fast(j3);
                 if (load3 && !spread) issue_all(j3, st3);
-                if (compute) {
-                    R::Src sr{p.k, p.vt};
-                    if (spread) sr = src(j3);
-                    pv8(st, st_cur + R::TILE, Dma8Hook<R>{ld, sr, st3, wl, spread});
-                }
-                if (jt + 1 < n) qk8(st.s, st_next, q);
+                R::Src sr{p.k, p.vt};
+                if (spread) sr = src(j3);
+                mfma_stream8<true, true>(st, st_cur + R::TILE, st_next, q,
+                                         Dma8Hook<R>{ld, sr, st3, wl, spread});
             } else {
-                if (!empty(j0)) softmax(j0);
+                softmax(j0);
             }
             block_barrier();
         }
-        if (!lead && !empty(kv_begin + (n - 1) * BN8))
-            pv8(st, ring + ((n - 1) % kStages8) * R::STAGE + R::TILE, NoHook{});
+        if (!lead)
+            mfma_stream8<true, false>(st, ring + ((n - 1) % kStages8) * R::STAGE + R::TILE, ring, q,
+                                      NoHook{});
     }
 
     if (valid) {

@@ -83,25 +83,19 @@ __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool parti
     }
 }
 
-// O^T += V^T P^T for the softmaxed tile (after the rare rescale); `hook`
-// runs after every MFMA.
-template <int D, int BN, bool BF16, class Hook = NoHook>
-__device__ __forceinline__ void step_pv(PrefillWave<D, BN>& st, const uint8_t* v_tile,
-                                        const Hook& hook = Hook{}) {
-    if (st.need) {
+// The MFMA work of a phase: P.V of the softmaxed tile (after the rare
+// rescale; `hook` runs after each of its MFMAs) when PV, then QK of the next
+// tile when QK.
+template <int D, int BN, bool BF16, bool PV, bool QK, class Hook = NoHook>
+__device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t (&q)[D / 16],
+                                          const uint8_t* v_tile, const uint8_t* k_tile,
+                                          const Hook& hook = Hook{}) {
+    if (PV && st.need) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) st.o[db] *= st.alpha;
         st.need = false;
     }
-    pv_tile<D, BN, BF16>(st.o, v_tile, st.pb, hook);
-}
-
-// S^T = K Q^T for a tile; `hook` runs after every MFMA, steps from step0.
-template <int D, int BN, bool BF16, class Hook = NoHook>
-__device__ __forceinline__ void step_qk(PrefillWave<D, BN>& st, const u32x4_t (&q)[D / 16],
-                                        const uint8_t* k_tile, const Hook& hook = Hook{},
-                                        int step0 = 0) {
-    qk_tile<D, BN, BF16>(st.s, k_tile, q, hook, step0);
+    mfma_stream16<D, BN, BF16, PV, QK>(st.o, st.s, st.pb, q, v_tile, k_tile, hook);
 }
 
 template <int D, int BN, int QB, int NW, bool BF16>
@@ -217,14 +211,17 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     // The lead waves alone load the ring: tile j+3 goes into the stage of
     // tile j-1 (free once phase 1 of tile j is over), one load after every
     // other MFMA of the lead's P.V.
+    // The trailing waves' first P.V of a chunk multiplies P = 0 (pb zeroed
+    // here and after each chunk) by the V tile of the last stage: zeroed here
+    // (uninitialised LDS could hold NaN codes), later a finite cache tile.
     constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
-#ifndef ATTN_DMA_OVER_QK
-#define ATTN_DMA_OVER_QK 0
-#endif
-    // loads go out over P.V alone, or over P.V and the QK that follows it
-    constexpr int kDmaSteps = kPvSteps + (ATTN_DMA_OVER_QK ? (D / 16) * (BN / 32) : 0);
-    static_assert(kDmaSteps % R::LOADS_PER_TILE == 0, "loads spread evenly over the MFMAs");
-    using Hook = DmaHook<R, kDmaSteps / R::LOADS_PER_TILE>;
+    static_assert(kPvSteps % R::LOADS_PER_TILE == 0, "loads spread evenly over the MFMAs");
+    using Hook = DmaHook<R, kPvSteps / R::LOADS_PER_TILE>;
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = tid; i < R::TILE / 16; i += NW * 64)
+        *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
+            u32x4_t{0u, 0u, 0u, 0u};
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
         const int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
@@ -244,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
         block_barrier();
-        if (lead) step_qk<D, BN, BF16>(st, q, ring);
+        if (lead) step_mfma<D, BN, BF16, false, true>(st, q, ring, ring);
 
         for (int jt = 0; jt < n; ++jt) {
             const int j0 = cs + jt * BN;
@@ -253,12 +250,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
             const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
             // phase 1
-            if (lead) {
-                phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
-            } else {
-                if (jt > 0) step_pv<D, BN, BF16>(st, st_prev + R::TILE);
-                step_qk<D, BN, BF16>(st, q, st_cur);
-            }
+            if (lead) phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
+            else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
             const int j3 = cs + (jt + kStages - 1) * BN;
             const bool load3 = lead && jt + kStages - 1 < n;
             int page = 0;
@@ -270,7 +263,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             block_barrier();
-            // phase 2
+            // phase 2 (after the last tile the lead's QK reads a stale stage;
+            // those scores are never used)
             if (lead) {
                 const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
                 const bool spread = load3 && R::whole(j3, kv_len, w);
@@ -280,21 +274,19 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 typename R::Src sr{p.k_cache, p.v_cache};
                 if (spread)
                     sr = R::src(p.k_cache, p.v_cache, page, j3, w, p.bs_log2, tok_stride, head_off);
-                const Hook hook{ld, sr, st3, w, spread};
-                step_pv<D, BN, BF16>(st, st_cur + R::TILE, hook);
-                // (with ATTN_DMA_OVER_QK the last loads ride on this QK; it runs
-                // whenever tile jt+3 exists)
-                if (jt + 1 < n) {
-                    if (ATTN_DMA_OVER_QK) step_qk<D, BN, BF16>(st, q, st_next, hook, kPvSteps);
-                    else step_qk<D, BN, BF16>(st, q, st_next);
-                }
+                step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next,
+                                                   Hook{ld, sr, st3, w, spread});
             } else {
                 phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
             }
             block_barrier();
         }
-        if (!lead && n > 0)
-            step_pv<D, BN, BF16>(st, ring + ((n - 1) % kStages) * R::STAGE + R::TILE);
+        if (!lead && n > 0) {
+            step_mfma<D, BN, BF16, true, false>(st, q, ring + ((n - 1) % kStages) * R::STAGE + R::TILE,
+                                                ring);
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+        }
         block_barrier();   // the next chunk's window and ring refill start after all reads
     }
 

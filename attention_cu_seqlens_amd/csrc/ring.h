@@ -223,103 +223,79 @@ struct DmaHook {
     }
 };
 
-// Operand prefetch depths (in MFMA steps) of the two tile products: the LDS
-// reads of step t + PD issue before the MFMAs of step t, so LDS latency hides
-// under the MFMAs; sched_barrier pins that order against the scheduler.
-#ifndef ATTN_QK_PREFETCH
-#define ATTN_QK_PREFETCH 3
+// Operand prefetch depth of the MFMA stream, in MFMA steps: the LDS reads of
+// step t + PD issue before the MFMA of step t, so LDS latency hides under the
+// MFMAs; sched_barrier pins that order against the scheduler.
+#ifndef ATTN_STREAM_PREFETCH
+#define ATTN_STREAM_PREFETCH 6
 #endif
-#ifndef ATTN_PV_PREFETCH
-#define ATTN_PV_PREFETCH 6
-#endif
-constexpr int kQkPrefetch = ATTN_QK_PREFETCH;
-constexpr int kPvPrefetch = ATTN_PV_PREFETCH;
+constexpr int kStreamPrefetch = ATTN_STREAM_PREFETCH;
 
-// S^T[kb] += K_tile(kb) . Q^T for the BN/32 key blocks of a tile;
-// (D/16) * (BN/32) MFMAs, hook steps from step0 upwards.
-template <int D, int BN, bool BF16, class Hook>
-__device__ __forceinline__ void qk_tile(f32x16_t (&s)[BN / 32], const uint8_t* kt,
-                                        const u32x4_t (&q)[D / 16], const Hook& hook,
-                                        int step0) {
+// The MFMA work of one pipeline phase as a single stream, so the operand
+// prefetch runs on across the boundary between the two products instead of
+// refilling at the start of each:
+//   PV: O^T[db] += V_tile^T(db) . P^T, P^T packed per (key block, 16-key
+//       step): (D/32) * (BN/32) * 2 MFMAs (steps db, kb, tp; `hook` after
+//       each);
+//   QK: S^T[kb] = K_tile(kb) . Q^T for the BN/32 key blocks: (D/16) * (BN/32)
+//       MFMAs (steps t, kb).
+template <int D, int BN, bool BF16, bool PV, bool QK, class Hook>
+__device__ __forceinline__ void mfma_stream16(f32x16_t (&o)[D / 32], f32x16_t (&s)[BN / 32],
+                                              const u32x4_t (&pb)[BN / 32][2],
+                                              const u32x4_t (&q)[D / 16], const uint8_t* vt,
+                                              const uint8_t* kt, const Hook& hook) {
+    static_assert(PV || QK, "empty stream");
     constexpr int ROWB = D * 2;
     constexpr int NKB = BN / 32;
-    constexpr int T = D / 16;
-    constexpr int PD = kQkPrefetch < T ? kQkPrefetch : T;
+    constexpr int NPV = PV ? (D / 32) * NKB * 2 : 0;
+    constexpr int N = NPV + (QK ? (D / 16) * NKB : 0);
+    constexpr int PD = kStreamPrefetch < N ? kStreamPrefetch : N;
     const int lane = lane_id();
-    const int col = lane & 31, g = lane >> 5;
-    // Lane offset of chunk g of row col (rows kb*32 + col share their low 5
-    // bits, so one swizzle serves every key block).  Step t reads chunk
-    // 2t + g, i.e. this offset XOR (2t << 4): row bits sit above bit 7, so
-    // the XOR only touches the chunk bits.  The empty asm keeps the compiler
-    // from hoisting the eight XORed offsets out of the tile loop into
-    // registers that would stay live across it.
-    uint32_t lo = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
-    asm volatile("" : "+v"(lo));
-    auto frag = [&](int t, int kb) {
-        return *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + (lo ^ (uint32_t)(t << 5)));
-    };
-    u32x4_t a[PD + 1][NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16_t{};
-#pragma unroll
-    for (int t = 0; t < PD; ++t)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) a[t][kb] = frag(t, kb);
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        if (t + PD < T) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) a[(t + PD) % (PD + 1)][kb] = frag(t + PD, kb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = mfma32<BF16>(a[t % (PD + 1)][kb], q[t], s[kb]);
-            hook(step0 + t * NKB + kb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// O^T[db] += V_tile^T(db) . P^T with P^T packed per (key block, 16-key step);
-// (D/32) * (BN/32) * 2 MFMAs, hook steps 0 upwards.
-template <int D, int BN, bool BF16, class Hook>
-__device__ __forceinline__ void pv_tile(f32x16_t (&o)[D / 32], const uint8_t* vt,
-                                        const u32x4_t (&pb)[BN / 32][2], const Hook& hook) {
-    constexpr int ROWB = D * 2;
-    constexpr int NKB = BN / 32;
-    constexpr int STEPS = (D / 32) * NKB * 2;
-    constexpr int PD = kPvPrefetch < STEPS ? kPvPrefetch : STEPS;
-    const int lane = lane_id();
-    const int j = lane & 15, h = lane >> 4, g = h >> 1;
-    const int r0 = 4 * g + (j >> 2);                 // row (mod 16) of the first read
-    // Chunk of dimension block db is c0 + 4*db; rows r0 + 16*tp + 32*kb keep
-    // the swizzle of r0 (it depends on the row mod 16), row r0 + 8 has its
-    // own.  Offsets of db = 0 for both rows; db adds (4*db << 4) by XOR
-    // (those chunk bits of c0 are zero).  The empty asm stops the compiler
-    // from hoisting the XORed offsets of every db out of the tile loop.
+    // V (transposed reads): within each group of 16 lanes, lane j reads row
+    // r0 + 16*tp + 32*kb (and the row 8 below) at chunk c0 + 4*db.  Rows
+    // r0 + 16*tp + 32*kb keep the swizzle of r0 (it depends on the row mod
+    // 16), row r0 + 8 has its own.  Offsets of db = 0 for both rows; db adds
+    // (4*db << 4) by XOR (those chunk bits of c0 are zero).
+    const int j = lane & 15, h = lane >> 4, gv = h >> 1;
+    const int r0 = 4 * gv + (j >> 2);
     const int c0 = (16 * (h & 1) + 4 * (j & 3)) >> 3;
     uint32_t lo0 = (uint32_t)(r0 * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0)) << 4));
     uint32_t hi0 = (uint32_t)((r0 + 8) * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0 + 8)) << 4));
-    asm volatile("" : "+v"(lo0), "+v"(hi0));
+    // K: lane offset of chunk g of row col (rows kb*32 + col share their low
+    // 5 bits, so one swizzle serves every key block).  Step t reads chunk
+    // 2t + g: this offset XOR (2t << 4); row bits sit above bit 7.
+    const int col = lane & 31, g = lane >> 5;
+    uint32_t lok = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
+    // The empty asm keeps the compiler from hoisting the XORed offsets of
+    // every step out of the tile loop into registers held across it.
+    asm volatile("" : "+v"(lo0), "+v"(hi0), "+v"(lok));
     auto frag = [&](int i) {
-        const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
-        const uint8_t* p0 = vt + (kb * 32 + 16 * tp) * ROWB;
-        const uint32_t x = (uint32_t)(db << 6);
-        const u32x2_t lo = ds_read_tr16(p0 + (lo0 ^ x));
-        const u32x2_t hi = ds_read_tr16(p0 + (hi0 ^ x));
-        return u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        if (i < NPV) {
+            const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
+            const uint8_t* p0 = vt + (kb * 32 + 16 * tp) * ROWB;
+            const uint32_t x = (uint32_t)(db << 6);
+            const u32x2_t l2 = ds_read_tr16(p0 + (lo0 ^ x));
+            const u32x2_t h2 = ds_read_tr16(p0 + (hi0 ^ x));
+            return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+        }
+        const int k = i - NPV, t = k / NKB, kb = k % NKB;
+        return *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + (lok ^ (uint32_t)(t << 5)));
     };
     u32x4_t a[PD + 1];
 #pragma unroll
     for (int i = 0; i < PD; ++i) a[i] = frag(i);
 #pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-        if (i + PD < STEPS) a[(i + PD) % (PD + 1)] = frag(i + PD);
+    for (int i = 0; i < N; ++i) {
+        if (i + PD < N) a[(i + PD) % (PD + 1)] = frag(i + PD);
         __builtin_amdgcn_sched_barrier(0);
-        const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
-        o[db] = mfma32<BF16>(a[i % (PD + 1)], pb[kb][tp], o[db]);
-        hook(i);
+        if (i < NPV) {
+            const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
+            o[db] = mfma32<BF16>(a[i % (PD + 1)], pb[kb][tp], o[db]);
+            hook(i);
+        } else {
+            const int k = i - NPV, t = k / NKB, kb = k % NKB;
+            s[kb] = mfma32<BF16>(a[i % (PD + 1)], q[t], t == 0 ? f32x16_t{} : s[kb]);
+        }
         __builtin_amdgcn_sched_barrier(0);
     }
 }

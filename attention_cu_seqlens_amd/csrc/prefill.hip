@@ -56,18 +56,21 @@ constexpr int kStages = 4;
 // Per-wave pipeline state of one 32-row block.
 template <int D, int BN>
 struct PrefillWave {
+    static constexpr int NPRE = pv_preload<D, BN>();
     f32x16_t s[BN / 32];      // scores of the tile waiting for its softmax
     u32x4_t pb[BN / 32][2];   // probabilities of the tile waiting for its P.V
+    u32x4_t pre[NPRE > 0 ? NPRE : 1];   // first V^T operands of that P.V, read ahead
     f32x16_t o[D / 32];
     float m, lpart, alpha;
     bool need;
 };
 
 // Softmax phase (VALU): mask the scores of the tile at key j0 when partial,
-// then probabilities into pb.
+// then probabilities into pb; finally read the first operands of the tile's
+// P.V from its V tile v_tile.
 template <int D, int BN, bool BF16>
 __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool partial, int j0, int lo,
-                                              int hi, float c) {
+                                              int hi, float c, const uint8_t* v_tile) {
     if (partial) {
         const int g = lane_id() >> 5;
 #pragma unroll
@@ -81,6 +84,7 @@ __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool parti
     } else {
         softmax_tile<BN, BF16, false>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need);
     }
+    preload_pv<D, BN, PrefillWave<D, BN>::NPRE>(st.pre, v_tile);
 }
 
 // The MFMA work of a phase: P.V of the softmaxed tile (after the rare
@@ -95,7 +99,8 @@ __device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t 
         for (int db = 0; db < D / 32; ++db) st.o[db] *= st.alpha;
         st.need = false;
     }
-    mfma_stream16<D, BN, BF16, PV, QK>(st.o, st.s, st.pb, q, v_tile, k_tile, hook);
+    mfma_stream16<D, BN, BF16, PV, QK, PrefillWave<D, BN>::NPRE>(st.o, st.s, st.pb, q, st.pre,
+                                                                v_tile, k_tile, hook);
 }
 
 template <int D, int BN, int QB, int NW, bool BF16>
@@ -219,6 +224,9 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     using Hook = DmaHook<R, kPvSteps / R::LOADS_PER_TILE>;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < (PrefillWave<D, BN>::NPRE > 0 ? PrefillWave<D, BN>::NPRE : 1); ++i)
+        st.pre[i] = u32x4_t{0u, 0u, 0u, 0u};
     for (int i = tid; i < R::TILE / 16; i += NW * 64)
         *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
             u32x4_t{0u, 0u, 0u, 0u};
@@ -250,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
             const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
             // phase 1
-            if (lead) phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
+            if (lead) phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c, st_cur + R::TILE);
             else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
             const int j3 = cs + (jt + kStages - 1) * BN;
             const bool load3 = lead && jt + kStages - 1 < n;
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next,
                                                    Hook{ld, sr, st3, w, spread});
             } else {
-                phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c);
+                phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c, st_cur + R::TILE);
             }
             block_barrier();
         }

@@ -231,70 +231,115 @@ struct DmaHook {
 #endif
 constexpr int kStreamPrefetch = ATTN_STREAM_PREFETCH;
 
+// Lane offsets of the transposed V reads of the P.V product: within each
+// group of 16 lanes, lane j reads row r0 + 16*tp + 32*kb (and the row 8
+// below) at chunk c0 + 4*db.  Rows r0 + 16*tp + 32*kb keep the swizzle of r0
+// (it depends on the row mod 16), row r0 + 8 has its own.  These are the
+// offsets of db = 0 for both rows; db adds (4*db << 4) by XOR (those chunk
+// bits of c0 are zero).
+template <int D>
+__device__ __forceinline__ void pv_offsets(uint32_t& lo0, uint32_t& hi0) {
+    constexpr int ROWB = D * 2;
+    const int lane = lane_id();
+    const int j = lane & 15, h = lane >> 4, gv = h >> 1;
+    const int r0 = 4 * gv + (j >> 2);
+    const int c0 = (16 * (h & 1) + 4 * (j & 3)) >> 3;
+    lo0 = (uint32_t)(r0 * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0)) << 4));
+    hi0 = (uint32_t)((r0 + 8) * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0 + 8)) << 4));
+}
+
+// V^T operand of P.V step i (db, kb, tp) read from the V tile at vt.
+template <int D, int BN>
+__device__ __forceinline__ u32x4_t pv_frag(const uint8_t* vt, uint32_t lo0, uint32_t hi0, int i) {
+    constexpr int ROWB = D * 2;
+    constexpr int NKB = BN / 32;
+    const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
+    const uint8_t* p0 = vt + (kb * 32 + 16 * tp) * ROWB;
+    const uint32_t x = (uint32_t)(db << 6);
+    const u32x2_t l2 = ds_read_tr16(p0 + (lo0 ^ x));
+    const u32x2_t h2 = ds_read_tr16(p0 + (hi0 ^ x));
+    return u32x4_t{l2.x, l2.y, h2.x, h2.y};
+}
+
+// Number of P.V operands a wave reads ahead, at the end of its softmax phase
+// (the LDS issue slots of that phase are otherwise idle and the tile's scores
+// are dead by then, so their registers hold the operands).  D = 128 only: at
+// D = 64 the softmax phase is the longer one and the extra reads slow it.
+template <int D, int BN>
+constexpr int pv_preload() {
+    constexpr int steps = (D / 32) * (BN / 32) * 2;
+    constexpr int by_regs = (BN / 32) * 16 / 4;   // the scores' registers, 4 per operand
+    return D < 128 ? 0 : steps < by_regs ? steps : by_regs;
+}
+
+// pre holds max(NPRE, 1) operands; nothing is read when NPRE == 0.
+template <int D, int BN, int NPRE, int N>
+__device__ __forceinline__ void preload_pv(u32x4_t (&pre)[N], const uint8_t* vt) {
+    static_assert(N == (NPRE > 0 ? NPRE : 1), "preload array size");
+    if constexpr (NPRE > 0) {
+        uint32_t lo0, hi0;
+        pv_offsets<D>(lo0, hi0);
+#pragma unroll
+        for (int i = 0; i < NPRE; ++i) pre[i] = pv_frag<D, BN>(vt, lo0, hi0, i);
+    }
+}
+
 // The MFMA work of one pipeline phase as a single stream, so the operand
 // prefetch runs on across the boundary between the two products instead of
 // refilling at the start of each:
 //   PV: O^T[db] += V_tile^T(db) . P^T, P^T packed per (key block, 16-key
 //       step): (D/32) * (BN/32) * 2 MFMAs (steps db, kb, tp; `hook` after
-//       each);
+//       each); the first NPRE operands (NPRE may be 0) come read already in
+//       `pre`, which holds max(NPRE, 1);
 //   QK: S^T[kb] = K_tile(kb) . Q^T for the BN/32 key blocks: (D/16) * (BN/32)
 //       MFMAs (steps t, kb).
-template <int D, int BN, bool BF16, bool PV, bool QK, class Hook>
+template <int D, int BN, bool BF16, bool PV, bool QK, int NPRE, int NP, class Hook>
 __device__ __forceinline__ void mfma_stream16(f32x16_t (&o)[D / 32], f32x16_t (&s)[BN / 32],
                                               const u32x4_t (&pb)[BN / 32][2],
-                                              const u32x4_t (&q)[D / 16], const uint8_t* vt,
+                                              const u32x4_t (&q)[D / 16],
+                                              const u32x4_t (&pre)[NP], const uint8_t* vt,
                                               const uint8_t* kt, const Hook& hook) {
     static_assert(PV || QK, "empty stream");
+    static_assert(NPRE >= 0 && NPRE <= (D / 32) * (BN / 32) * 2, "preload count");
+    static_assert(NP == (NPRE > 0 ? NPRE : 1), "preload array size");
     constexpr int ROWB = D * 2;
     constexpr int NKB = BN / 32;
     constexpr int NPV = PV ? (D / 32) * NKB * 2 : 0;
     constexpr int N = NPV + (QK ? (D / 16) * NKB : 0);
-    constexpr int PD = kStreamPrefetch < N ? kStreamPrefetch : N;
-    const int lane = lane_id();
-    // V (transposed reads): within each group of 16 lanes, lane j reads row
-    // r0 + 16*tp + 32*kb (and the row 8 below) at chunk c0 + 4*db.  Rows
-    // r0 + 16*tp + 32*kb keep the swizzle of r0 (it depends on the row mod
-    // 16), row r0 + 8 has its own.  Offsets of db = 0 for both rows; db adds
-    // (4*db << 4) by XOR (those chunk bits of c0 are zero).
-    const int j = lane & 15, h = lane >> 4, gv = h >> 1;
-    const int r0 = 4 * gv + (j >> 2);
-    const int c0 = (16 * (h & 1) + 4 * (j & 3)) >> 3;
-    uint32_t lo0 = (uint32_t)(r0 * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0)) << 4));
-    uint32_t hi0 = (uint32_t)((r0 + 8) * ROWB + (j & 1) * 8 + ((c0 ^ swz<D>(r0 + 8)) << 4));
+    constexpr int P0 = PV ? NPRE : 0;             // steps whose operand is preloaded
+    constexpr int PD = kStreamPrefetch < N - P0 ? kStreamPrefetch : N - P0;
+    uint32_t lo0, hi0;
+    pv_offsets<D>(lo0, hi0);
     // K: lane offset of chunk g of row col (rows kb*32 + col share their low
     // 5 bits, so one swizzle serves every key block).  Step t reads chunk
     // 2t + g: this offset XOR (2t << 4); row bits sit above bit 7.
+    const int lane = lane_id();
     const int col = lane & 31, g = lane >> 5;
     uint32_t lok = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
     // The empty asm keeps the compiler from hoisting the XORed offsets of
     // every step out of the tile loop into registers held across it.
     asm volatile("" : "+v"(lo0), "+v"(hi0), "+v"(lok));
     auto frag = [&](int i) {
-        if (i < NPV) {
-            const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
-            const uint8_t* p0 = vt + (kb * 32 + 16 * tp) * ROWB;
-            const uint32_t x = (uint32_t)(db << 6);
-            const u32x2_t l2 = ds_read_tr16(p0 + (lo0 ^ x));
-            const u32x2_t h2 = ds_read_tr16(p0 + (hi0 ^ x));
-            return u32x4_t{l2.x, l2.y, h2.x, h2.y};
-        }
+        if (i < NPV) return pv_frag<D, BN>(vt, lo0, hi0, i);
         const int k = i - NPV, t = k / NKB, kb = k % NKB;
         return *reinterpret_cast<const u32x4_t*>(kt + kb * 32 * ROWB + (lok ^ (uint32_t)(t << 5)));
     };
     u32x4_t a[PD + 1];
 #pragma unroll
-    for (int i = 0; i < PD; ++i) a[i] = frag(i);
+    for (int i = 0; i < PD; ++i) a[i] = frag(P0 + i);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        if (i + PD < N) a[(i + PD) % (PD + 1)] = frag(i + PD);
+        // buffer slot of step k >= P0: (k - P0) % (PD + 1)
+        if (i >= P0 && i + PD < N) a[(i - P0 + PD) % (PD + 1)] = frag(i + PD);
         __builtin_amdgcn_sched_barrier(0);
+        const u32x4_t op = i < P0 ? pre[i < P0 ? i : 0] : a[(i - P0) % (PD + 1)];
         if (i < NPV) {
             const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
-            o[db] = mfma32<BF16>(a[i % (PD + 1)], pb[kb][tp], o[db]);
+            o[db] = mfma32<BF16>(op, pb[kb][tp], o[db]);
             hook(i);
         } else {
             const int k = i - NPV, t = k / NKB, kb = k % NKB;
-            s[kb] = mfma32<BF16>(a[i % (PD + 1)], q[t], t == 0 ? f32x16_t{} : s[kb]);
+            s[kb] = mfma32<BF16>(op, q[t], t == 0 ? f32x16_t{} : s[kb]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }

@@ -28,6 +28,14 @@ Readings where the pages are silent (each is also listed in the design doc):
     kernel options: OUTPUT_LOGSUMEXP True, PRESCALE_QK False).
   * fp8 is OCP e4m3fn ([FLEX] _enforce_mem_layouts names torch.float8_e4m3fn);
     a tensor's real value is descale * decoded code.
+  * local window and softcap: [ORT] Testing lists "local window on/off" and
+    "softcap 0/50" as axes of its parity matrix without defining them.  Read
+    here as (a) a left window of W keys ending at the query's own position:
+    query i sees key j only if j > i + (kv_len - q_len) - W (same bottom-right
+    alignment as CAUSAL; W = 0 means no window), and (b) a score cap c > 0
+    applied to the scaled score before masking and softmax,
+    s -> c * tanh(s / c) (c = 0 means no cap); LSE is taken over the capped
+    scores.
 """
 
 import math
@@ -43,10 +51,13 @@ PIN_STATUS = {
     "cu_seqlens": "pinned: numpy.cumsum special case, hand-written golden example",
     "reshape_and_cache": "pinned: hand-written golden placement example, gather round trip",
     "gather_paged": "pinned: identity table equals packed layout; permuted tables agree",
-    "visibility": "pinned: np.tril closed forms, page predicate q_idx >= kv_idx, brute-force counts",
-    "attention_varlen": "pinned: torch CPU fp64 SDPA (dense, GQA), closed forms, invariants",
+    "visibility": "pinned: np.tril closed forms, page predicate q_idx >= kv_idx, brute-force counts, "
+                  "window bands from np.tril/np.triu",
+    "attention_varlen": "pinned: torch CPU fp64 SDPA (dense, GQA, banded window mask), closed forms "
+                        "(incl. saturated softcap), invariants",
     "paged_attention": "pinned: equals attention_varlen on gathered K/V; block-table permutation invariance",
-    "paged_decode": "pinned: equals the last row of a causal prefill over the same cache",
+    "paged_decode": "pinned: equals the last row of a causal prefill over the same cache; a window "
+                    "equals decode over the cache cut to its last W keys",
     "e4m3_decode": "pinned: all 256 codes against torch.float8_e4m3fn; closed-form extremes",
     "fp8_attention": "pinned: equals attention_varlen on decoded values; hand-derived two-key example",
     "default_scale": "pinned: golden value 0.0625 at E=256 from [BLT]",
@@ -124,7 +135,7 @@ def gather_paged(cache, table_row, kv_len, block_size):
     return out
 
 
-def visibility(q_len, kv_len, flags, q_ids=None, kv_ids=None):
+def visibility(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
     """Boolean [q_len, kv_len]: may query i of a sequence attend to key j.
 
     Conjunction of
@@ -135,6 +146,8 @@ def visibility(q_len, kv_len, flags, q_ids=None, kv_ids=None):
       * PATCH:    j <= q_ids[i]              ([BLT] CrossAttention: byte
                   queries see their own and earlier patch keys; q_ids holds
                   each byte's patch index within its sequence)
+      * window W > 0: j > i + (kv_len - q_len) - W  (local window, see the
+                  module docstring)
     Every key index j < kv_len exists; there is no other bound.
     """
     if flags & MASK_DOCUMENT and flags & MASK_PATCH:
@@ -148,6 +161,8 @@ def visibility(q_len, kv_len, flags, q_ids=None, kv_ids=None):
         vis &= np.asarray(q_ids)[:q_len, None] == np.asarray(kv_ids)[None, :kv_len]
     if flags & MASK_PATCH:
         vis &= j <= np.asarray(q_ids)[:q_len, None]
+    if window > 0:
+        vis &= j > i + (kv_len - q_len) - window
     return vis
 
 
@@ -173,7 +188,8 @@ def _softmax_rows(s, vis, v):
     return out, lse
 
 
-def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, rows=None):
+def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, rows=None,
+                     window=0, softcap=0.0):
     """Varlen attention over packed (non-paged) K/V, fp64.
 
     q: [total_q, Hq, D]; k: [total_kv, Hkv, D]; v: [total_kv, Hkv, Dv];
@@ -186,6 +202,8 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
     q_ids / kv_ids are indexed by global token ([total_q] / [total_kv]).
     rows: optional global query indices to compute (others stay 0 / -inf);
     used to sample outputs of full-size workloads.
+    window, softcap: local window and score cap (module docstring); the cap
+    acts on the scaled scores before the mask.
     Returns (out [total_q, Hq, Dv], lse [total_q, Hq]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -210,10 +228,12 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
             continue
         qi = None if q_ids is None else np.asarray(q_ids)[q0:q1]
         ki = None if kv_ids is None else np.asarray(kv_ids)[k0:k1]
-        vis = visibility(q_len, kv_len, flags, qi, ki)[sel]
+        vis = visibility(q_len, kv_len, flags, qi, ki, window)[sel]
         for h in range(hq):
             kvh = h // group
             s = scale * (q[q0 + sel, h, :] @ k[k0:k1, kvh, :].T)
+            if softcap > 0:
+                s = softcap * np.tanh(s / softcap)
             o, l = _softmax_rows(s, vis, v[k0:k1, kvh, :])
             out[q0 + sel, h] = o
             lse[q0 + sel, h] = l
@@ -221,7 +241,7 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
 
 
 def paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, scale,
-                    flags=0, q_ids=None, kv_ids=None, rows=None):
+                    flags=0, q_ids=None, kv_ids=None, rows=None, window=0, softcap=0.0):
     """Attention whose K/V live in a paged cache ([ORT] Implementation, step 2
     then step 3): gather each sequence's K/V through block_table into a packed
     buffer, then run ``attention_varlen`` on it.  Returns (out, lse) in fp64.
@@ -234,22 +254,24 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, s
         vs.append(gather_paged(v_cache, block_table[b], kv_len, block_size))
     k = np.concatenate(ks, axis=0) if ks else np.zeros((0,) + tuple(k_cache.shape[2:]))
     v = np.concatenate(vs, axis=0) if vs else np.zeros((0,) + tuple(v_cache.shape[2:]))
-    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows)
+    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows, window, softcap)
 
 
-def paged_decode(q, k_cache, v_cache, block_table, cu_kv, block_size, scale, batches=None):
+def paged_decode(q, k_cache, v_cache, block_table, cu_kv, block_size, scale, batches=None,
+                 window=0, softcap=0.0):
     """One new query per sequence (q: [batch, Hq, D]) against its paged cache.
 
     This is paged_attention with q_len = 1; under bottom-right causal
     alignment the single query sits at the last position and sees every key,
-    so no mask applies.  ``batches`` optionally restricts the sequences
-    computed.  Returns (out [batch, Hq, Dv], lse [batch, Hq]).
+    so no causal mask bites; a window W leaves its last W keys.  ``batches``
+    optionally restricts the sequences computed.
+    Returns (out [batch, Hq, Dv], lse [batch, Hq]).
     """
     batch = len(cu_kv) - 1
     cu_q = np.arange(batch + 1, dtype=np.int64)
     rows = None if batches is None else np.asarray(batches)
     return paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, scale,
-                           MASK_CAUSAL, rows=rows)
+                           MASK_CAUSAL, rows=rows, window=window, softcap=softcap)
 
 
 def e4m3_decode(codes):
@@ -280,7 +302,7 @@ def e4m3_decode(codes):
 
 
 def fp8_attention(q8, k8, v8_colmajor, descale, cu_q, cu_kv, scale, flags=0,
-                  q_ids=None, kv_ids=None, rows=None):
+                  q_ids=None, kv_ids=None, rows=None, window=0, softcap=0.0):
     """fp8 e4m3 attention: decode, apply per-tensor descales, then attend.
 
     q8: uint8 codes [total_q, Hq, D]; k8: [total_kv, Hkv, D];
@@ -294,4 +316,4 @@ def fp8_attention(q8, k8, v8_colmajor, descale, cu_q, cu_kv, scale, flags=0,
     q = dq * e4m3_decode(q8)
     k = dk * e4m3_decode(k8)
     v = dv * np.transpose(e4m3_decode(v8_colmajor), (2, 0, 1))
-    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows)
+    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows, window, softcap)

@@ -397,6 +397,113 @@ def check_fp8_attention(A):
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+def check_window_bands(A):
+    """Causal + window W: a band of W keys ending on the (bottom-right) diagonal,
+    built here from np.tril / np.triu; without CAUSAL the window only bounds j
+    from below; a window wider than the sequence changes nothing."""
+    for q_len, kv_len, W in ((7, 7, 1), (7, 7, 3), (5, 9, 2), (9, 5, 4), (6, 6, 100)):
+        off = kv_len - q_len
+        ones = np.ones((q_len, kv_len), bool)
+        band = np.tril(ones, k=off) & np.triu(ones, k=off - W + 1)
+        assert np.array_equal(A.visibility(q_len, kv_len, ORC.MASK_CAUSAL, window=W), band)
+    assert np.array_equal(A.visibility(4, 6, 0, window=2), np.triu(np.ones((4, 6), bool), k=1))
+    assert np.array_equal(A.visibility(6, 6, ORC.MASK_CAUSAL, window=6),
+                          A.visibility(6, 6, ORC.MASK_CAUSAL))
+
+
+def check_window_vs_sdpa(A):
+    """Causal + window against torch SDPA given the same band as an explicit mask."""
+    rng = np.random.default_rng(8)
+    L, H, D, W = 19, 2, 8, 5
+    q, k, v = _rand(rng, L, H, D), _rand(rng, L, H, D), _rand(rng, L, H, D)
+    ones = np.ones((L, L), bool)
+    band = np.tril(ones) & np.triu(ones, k=-(W - 1))
+    out, _ = A.attention_varlen(q, k, v, [0, L], [0, L], 0.41, ORC.MASK_CAUSAL, window=W)
+    ref = _sdpa(q, k, v, 0.41, attn_mask=band)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_window_one_is_diagonal(A):
+    """Window 1 with causal leaves each row its own (bottom-right) key: O is that
+    V row exactly and LSE is its scaled score."""
+    rng = np.random.default_rng(9)
+    q_len, kv_len, D = 5, 8, 6
+    q, k, v = _rand(rng, q_len, 1, D), _rand(rng, kv_len, 1, D), _rand(rng, kv_len, 1, D)
+    out, lse = A.attention_varlen(q, k, v, [0, q_len], [0, kv_len], 0.3, ORC.MASK_CAUSAL, window=1)
+    for i in range(q_len):
+        j = i + kv_len - q_len
+        assert np.array_equal(out[i, 0], v[j, 0])
+        assert abs(lse[i, 0] - 0.3 * float(q[i, 0] @ k[j, 0])) < 1e-12
+
+
+def check_window_decode_is_truncated_cache(A):
+    """Decode with window W equals decode without one over the last W keys only
+    (through the paged path with an identity block table)."""
+    rng = np.random.default_rng(10)
+    lens, bs, W, Hq, Hkv, D = [13, 4, 9], 4, 6, 4, 2, 8
+    q = _rand(rng, len(lens), Hq, D)
+    out, lse = None, None
+    ks = [_rand(rng, n, Hkv, D) for n in lens]
+    vs = [_rand(rng, n, Hkv, D) for n in lens]
+    def paged(parts):
+        nbs = [(p.shape[0] + bs - 1) // bs for p in parts]
+        cache = np.zeros((sum(nbs), bs, Hkv, D))
+        table = np.zeros((len(parts), max(nbs)), dtype=np.int32)
+        blk = 0
+        for b, p in enumerate(parts):
+            for j in range(p.shape[0]):
+                cache[blk + j // bs, j % bs] = p[j]
+            table[b, :nbs[b]] = np.arange(blk, blk + nbs[b])
+            blk += nbs[b]
+        return cache, table
+    kc, table = paged(ks)
+    vc, _ = paged(vs)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    out, lse = A.paged_decode(q, kc, vc, table, cu, bs, 0.35, window=W)
+    cut = [min(W, n) for n in lens]
+    kc2, table2 = paged([p[-c:] for p, c in zip(ks, cut)])
+    vc2, _ = paged([p[-c:] for p, c in zip(vs, cut)])
+    out2, lse2 = A.paged_decode(q, kc2, vc2, table2, np.concatenate([[0], np.cumsum(cut)]), bs, 0.35)
+    assert np.allclose(out, out2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse, lse2, rtol=1e-12, atol=1e-12)
+
+
+def check_softcap_saturated(A):
+    """A huge scale drives every capped score to +-c (c = 50, the softcap value
+    in [ORT] Testing): keys with q.k > 0 weigh e^c, the others e^-c."""
+    rng = np.random.default_rng(11)
+    n, D, c = 9, 8, 50.0
+    q = _rand(rng, 1, 1, D)
+    k = _rand(rng, n, 1, D)
+    dots = k[:, 0] @ q[0, 0]
+    k[np.abs(dots) < 0.1] *= 0.0
+    k[np.abs(dots) < 0.1, 0, 0] = 1.0 / q[0, 0, 0]       # q.k = 1 for those rows
+    dots = k[:, 0] @ q[0, 0]
+    v = _rand(rng, n, 1, D)
+    out, lse = A.attention_varlen(q, k, v, [0, 1], [0, n], 1e6, softcap=c)
+    sign = np.where(dots > 0, 1.0, -1.0)
+    w = np.exp(sign * c - c)                               # shifted by the max, c
+    assert np.allclose(out[0, 0], (w @ v[:, 0]) / w.sum(), rtol=1e-12, atol=1e-12)
+    assert abs(lse[0, 0] - (c + math.log(w.sum()))) < 1e-12
+
+
+def check_softcap_large_cap_limit(A):
+    """c -> infinity recovers the uncapped scores; a finite cap keeps every
+    score in [-c, c] (tanh saturates to exactly +-1 in fp64 for large
+    arguments), so LSE lies within c of ln(visible keys)."""
+    rng = np.random.default_rng(12)
+    L, H, D = 11, 2, 8
+    q, k, v = _rand(rng, L, H, D), _rand(rng, L, H, D), _rand(rng, L, H, D)
+    o0, l0 = A.attention_varlen(q, k, v, [0, L], [0, L], 0.5, ORC.MASK_CAUSAL)
+    o1, l1 = A.attention_varlen(q, k, v, [0, L], [0, L], 0.5, ORC.MASK_CAUSAL, softcap=1e7)
+    assert np.allclose(o0, o1, rtol=1e-9, atol=1e-9) and np.allclose(l0, l1, rtol=1e-9, atol=1e-9)
+    c = 0.25
+    _, l2 = A.attention_varlen(q, k, v, [0, L], [0, L], 40.0, ORC.MASK_CAUSAL, softcap=c)
+    n = np.arange(1, L + 1)[:, None]
+    assert np.all(l2 <= np.log(n) + c + 1e-12) and np.all(l2 >= np.log(n) - c - 1e-12)
+    assert np.ptp(l2 - np.log(n)) > 0.1      # the cap is not a constant shift
+
+
 CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]
 
 
@@ -419,8 +526,8 @@ def test_pin_status_covers_exports():
 # ----------------------------------------------------------------------------
 
 def _mut_visibility_off_by_one(orig):
-    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None):
-        vis = orig(q_len, kv_len, flags & ~ORC.MASK_CAUSAL, q_ids, kv_ids)
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
+        vis = orig(q_len, kv_len, flags & ~ORC.MASK_CAUSAL, q_ids, kv_ids, window)
         if flags & ORC.MASK_CAUSAL:
             i = np.arange(q_len)[:, None]
             j = np.arange(kv_len)[None, :]
@@ -430,8 +537,8 @@ def _mut_visibility_off_by_one(orig):
 
 
 def _mut_visibility_top_left(orig):
-    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None):
-        vis = orig(q_len, kv_len, flags & ~ORC.MASK_CAUSAL, q_ids, kv_ids)
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
+        vis = orig(q_len, kv_len, flags & ~ORC.MASK_CAUSAL, q_ids, kv_ids, window)
         if flags & ORC.MASK_CAUSAL:
             vis &= np.arange(kv_len)[None, :] <= np.arange(q_len)[:, None]
         return vis
@@ -439,8 +546,8 @@ def _mut_visibility_top_left(orig):
 
 
 def _mut_visibility_patch_strict(orig):
-    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None):
-        vis = orig(q_len, kv_len, flags, q_ids, kv_ids)
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
+        vis = orig(q_len, kv_len, flags, q_ids, kv_ids, window)
         if flags & ORC.MASK_PATCH:
             vis &= np.arange(kv_len)[None, :] < np.asarray(q_ids)[:q_len, None]
         return vis
@@ -527,6 +634,30 @@ def _mut_default_scale_inverse(orig):
     return lambda e: math.sqrt(e)
 
 
+def _mut_window_one_extra_key(orig):
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
+        return orig(q_len, kv_len, flags, q_ids, kv_ids, window + 1 if window > 0 else 0)
+    return f
+
+
+def _mut_window_top_left(orig):
+    def f(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
+        vis = orig(q_len, kv_len, flags, q_ids, kv_ids, 0)
+        if window > 0:
+            vis &= np.arange(kv_len)[None, :] > np.arange(q_len)[:, None] - window
+        return vis
+    return f
+
+
+def _mut_softcap_no_division(orig):
+    # c * tanh(s) instead of c * tanh(s / c): scale the cap into the scores
+    def f(q, k, v, cu_q, cu_kv, scale, *a, softcap=0.0, **kw):
+        if softcap <= 0:
+            return orig(q, k, v, cu_q, cu_kv, scale, *a, **kw)
+        return orig(q, k, v, cu_q, cu_kv, scale * softcap, *a, softcap=softcap * softcap, **kw)
+    return f
+
+
 MUTATIONS = {
     "causal_off_by_one": ("visibility", _mut_visibility_off_by_one),
     "causal_top_left": ("visibility", _mut_visibility_top_left),
@@ -542,6 +673,9 @@ MUTATIONS = {
     "cu_seqlens_inclusive": ("cu_seqlens", _mut_cu_inclusive),
     "fp8_v_read_row_major": ("fp8_attention", _mut_fp8_v_rowmajor),
     "default_scale_inverted": ("default_scale", _mut_default_scale_inverse),
+    "window_one_extra_key": ("visibility", _mut_window_one_extra_key),
+    "window_top_left": ("visibility", _mut_window_top_left),
+    "softcap_no_division": ("attention_varlen", _mut_softcap_no_division),
 }
 
 

@@ -91,8 +91,9 @@ def attn_reshape_and_cache(k, v, k_cache, v_cache, block_table, cu_seqlens_new, 
 
 def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seqlens_kv,
                            max_seqlen_q, max_seqlen_kv, scale=None, mask_flags=0, q_ids=None,
-                           kv_ids=None, out=None, return_lse=False):
-    """Paged varlen attention; returns out (and lse [total_q, Hq] fp32 if asked)."""
+                           kv_ids=None, out=None, return_lse=False, window=0, softcap=0.0):
+    """Paged varlen attention; returns out (and lse [total_q, Hq] fp32 if asked).
+    window: local window in keys (0 = none); softcap: score cap (0 = none)."""
     dev = q.device
     _need(q, "q", (torch.float16, torch.bfloat16))
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -120,7 +121,8 @@ def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_se
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
             _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), batch, total_q, int(max_seqlen_q),
             int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale), int(mask_flags), _ptr(q_ids),
-            _ptr(kv_ids), _DT[q.dtype], _ptr(out), _ptr(lse), _stream(dev)))
+            _ptr(kv_ids), int(window), float(softcap), _DT[q.dtype], _ptr(out), _ptr(lse),
+            _stream(dev)))
     return (out, lse) if return_lse else out
 
 
@@ -131,8 +133,10 @@ def attn_paged_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_size,
 
 
 def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_seqlen_kv,
-                          scale=None, split_tokens=0, out=None, return_lse=False, workspace=None):
-    """One query per sequence (q [batch, Hq, D]) against the paged cache."""
+                          scale=None, split_tokens=0, out=None, return_lse=False, workspace=None,
+                          window=0, softcap=0.0):
+    """One query per sequence (q [batch, Hq, D]) against the paged cache.
+    window: keep each sequence's last `window` keys (0 = all); softcap: score cap."""
     dev = q.device
     _need(q, "q", (torch.float16, torch.bfloat16))
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
@@ -156,14 +160,14 @@ def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_s
         _lib.check("attn_paged_decode_fwd", lib.attn_paged_decode_fwd(
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
             _ptr(cu_seqlens_kv), batch, int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale),
-            int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse), _ptr(workspace),
-            workspace.numel(), _stream(dev)))
+            int(window), float(softcap), int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(dev)))
     return (out, lse) if return_lse else out
 
 
 def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                  max_seqlen_kv, scale=None, mask_flags=0, q_ids=None, kv_ids=None, out=None,
-                 return_lse=False):
+                 return_lse=False, window=0, softcap=0.0):
     """fp8 e4m3 attention: q8 [total_q, Hq, D], k8 [total_kv, Hkv, D],
     v8_colmajor [Hkv, D, total_kv] (uint8 codes or float8_e4m3fn), descale fp32 [3]."""
     dev = q8.device
@@ -192,6 +196,6 @@ def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_
         _lib.check("attn_fp8_fwd", lib.attn_fp8_fwd(
             _ptr(q8), _ptr(k8), _ptr(v8), _ptr(descale), _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv),
             batch, total_q, total_kv, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d,
-            float(scale), int(mask_flags), _ptr(q_ids), _ptr(kv_ids), _ptr(out), _ptr(lse),
-            _stream(dev)))
+            float(scale), int(mask_flags), _ptr(q_ids), _ptr(kv_ids), int(window),
+            float(softcap), _ptr(out), _ptr(lse), _stream(dev)))
     return (out, lse) if return_lse else out

@@ -53,6 +53,23 @@ int pack_log2_for_group(int g) {
     return r;
 }
 
+// Local window and score cap: W >= 0, c >= 0 and finite (0 = off).
+bool window_cap_ok(int32_t window_left, float softcap) {
+    return window_left >= 0 && std::isfinite(softcap) && softcap >= 0.f;
+}
+
+// Score-cap constants in the kernels' log2 domain (see SoftCap).
+void set_cap(float scale, float softcap, float& in2, float& out) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    if (softcap > 0.f) {
+        in2 = 2.f * std::fabs(scale) * kLog2e / softcap;
+        out = softcap * kLog2e;
+    } else {
+        in2 = 0.f;
+        out = 0.f;
+    }
+}
+
 attn_status check_mask(uint32_t mask, const int32_t* q_ids, const int32_t* kv_ids) {
     if (mask & ~(ATTN_MASK_CAUSAL | ATTN_MASK_DOCUMENT | ATTN_MASK_PATCH))
         return ATTN_ERR_UNSUPPORTED;
@@ -131,8 +148,8 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
                                    int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
                                    int32_t head_size, int32_t block_size, int32_t num_blocks,
                                    float scale, uint32_t mask_flags, const int32_t* q_ids,
-                                   const int32_t* kv_ids, attn_dtype dtype, void* out, float* lse,
-                                   void* stream) {
+                                   const int32_t* kv_ids, int32_t window_left, float softcap,
+                                   attn_dtype dtype, void* out, float* lse, void* stream) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
@@ -143,6 +160,7 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
     if (max_blocks_per_seq <= 0 || num_blocks <= 0) return ATTN_ERR_BAD_SHAPE;
     if ((int64_t)max_blocks_per_seq * block_size < max_seqlen_kv) return ATTN_ERR_BAD_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+    if (!window_cap_ok(window_left, softcap)) return ATTN_ERR_BAD_SHAPE;
     const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
     if (m != ATTN_OK) return m;
     if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
@@ -175,6 +193,8 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
     p.bs_log2 = ilog2(block_size);
     p.mask = mask_flags;
     p.c = scale * 1.4426950408889634f;
+    p.window = window_left;
+    set_cap(scale, softcap, p.cap_in2, p.cap_out);
     return from_hip(attn::launch_paged_prefill(p, head_size, dtype == ATTN_BF16, max_seqlen_q,
                                                static_cast<hipStream_t>(stream)));
 }
@@ -194,9 +214,9 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
                                   const int32_t* cu_seqlens_kv, int32_t batch,
                                   int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
-                                  float scale, int32_t split_tokens, attn_dtype dtype, void* out,
-                                  float* lse, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  float scale, int32_t window_left, float softcap,
+                                  int32_t split_tokens, attn_dtype dtype, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
@@ -209,6 +229,7 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     if (split_tokens < 0 || split_tokens % 256 != 0 || split_tokens > 8192)
         return ATTN_ERR_BAD_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+    if (!window_cap_ok(window_left, softcap)) return ATTN_ERR_BAD_SHAPE;
     if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
         cu_seqlens_kv == nullptr || out == nullptr)
         return ATTN_ERR_NULL_ARG;
@@ -243,6 +264,8 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     p.bs_log2 = ilog2(block_size);
     p.split_tokens = st;
     p.c = scale * 1.4426950408889634f;
+    p.window = window_left;
+    set_cap(scale, softcap, p.cap_in2, p.cap_out);
     return from_hip(attn::launch_paged_decode(p, head_size, dtype == ATTN_BF16,
                                               static_cast<hipStream_t>(stream)));
 }
@@ -253,13 +276,15 @@ attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor
                          int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
                          int32_t num_heads, int32_t num_kv_heads, int32_t head_size, float scale,
                          uint32_t mask_flags, const int32_t* q_ids, const int32_t* kv_ids,
-                         void* out_bf16, float* lse, void* stream) {
+                         int32_t window_left, float softcap, void* out_bf16, float* lse,
+                         void* stream) {
     if (head_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (batch < 0 || total_q < 0 || total_kv < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0)
         return ATTN_ERR_BAD_SHAPE;
     if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
         return ATTN_ERR_BAD_SHAPE;
     if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
+    if (!window_cap_ok(window_left, softcap)) return ATTN_ERR_BAD_SHAPE;
     const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
     if (m != ATTN_OK) return m;
     if (q8 == nullptr || k8 == nullptr || v8_colmajor == nullptr || descale_qkv == nullptr ||
@@ -294,6 +319,8 @@ attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor
     p.total_q = total_q;
     p.mask = mask_flags;
     p.scale = scale;
+    p.window = window_left;
+    p.softcap = softcap;
     return from_hip(attn::launch_fp8_prefill(p, head_size, max_seqlen_q,
                                              static_cast<hipStream_t>(stream)));
 }

@@ -29,7 +29,7 @@ struct DecodeLayout {
     static constexpr int LDS_BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
 };
 
-template <int D, int NW, bool BF16>
+template <int D, int NW, bool BF16, bool CAP>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_decode(DecodeParams p) {
     using L = DecodeLayout<D, NW, BF16>;
     using Tile = typename L::Tile;
@@ -72,7 +72,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             st.q[0][t] = neg ? neg16x8(v) : v;
         }
     }
-    st.lo[0] = 0;
+    // a local window keeps the last p.window keys of the sequence
+    const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
+    st.lo[0] = lo_w;
     st.hi[0] = k1;
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
@@ -86,22 +88,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int tok_stride = p.num_kv_heads * D;
     const int head_off = hk * D;
     const int n_t = (k1 - k0 + 31) >> 5;
+    // tiles wholly below the window hold no visible key: start past them
+    const int t_first = lo_w > k0 ? (lo_w - k0) >> 5 : 0;
     uint8_t* mine = smem + w * Tile::BYTES;
     Tile ld;
-    if (w < n_t)
-        ld.load(p.k_cache, p.v_cache, win, first, k0 + 32 * w, k1, p.bs_log2, tok_stride,
-                head_off, lane);
-    for (int t = w; t < n_t; t += NW) {
+    if (t_first + w < n_t)
+        ld.load(p.k_cache, p.v_cache, win, first, k0 + 32 * (t_first + w), k1, p.bs_log2,
+                tok_stride, head_off, lane);
+    for (int t = t_first + w; t < n_t; t += NW) {
         const int j = k0 + 32 * t;
         ld.store(mine, j, k1, lane);
         __builtin_amdgcn_wave_barrier();
         if (t + NW < n_t)
             ld.load(p.k_cache, p.v_cache, win, first, j + 32 * NW, k1, p.bs_log2, tok_stride,
                     head_off, lane);
-        if (j + 32 <= k1)
-            tile_step<D, 32, 1, 1, BF16, false>(st, mine, j, 0, c);
+        if (j >= lo_w && j + 32 <= k1)
+            tile_step<D, 32, 1, 1, BF16, false, CAP>(st, mine, j, 0, c, p.cap_in2, p.cap_out);
         else
-            tile_step<D, 32, 1, 1, BF16, true>(st, mine, j, 0, c);
+            tile_step<D, 32, 1, 1, BF16, true, CAP>(st, mine, j, 0, c, p.cap_in2, p.cap_out);
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
@@ -197,17 +201,17 @@ size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_s
 
 namespace {
 
-template <int D, int NW, bool BF16>
+template <int D, int NW, bool BF16, bool CAP>
 hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
     constexpr int lds = DecodeLayout<D, NW, BF16>::LDS_BYTES;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16>),
+        reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16, CAP>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     const int64_t grid = (int64_t)p.batch * p.num_kv_heads * p.max_splits;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16>), dim3((unsigned)grid), dim3(NW * 64), lds, s,
-                       p);
+    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16, CAP>), dim3((unsigned)grid), dim3(NW * 64),
+                       lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_decode_combine<D, BF16>), dim3((unsigned)(p.batch * p.num_heads)),
@@ -217,11 +221,17 @@ hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
+template <int D, bool BF16>
+hipError_t launch_decode_cap(const DecodeParams& p, hipStream_t s) {
+    return p.cap_out > 0.f ? launch_decode_cfg<D, 4, BF16, true>(p, s)
+                           : launch_decode_cfg<D, 4, BF16, false>(p, s);
+}
+
 hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s) {
     if (head_size == 128)
-        return bf16 ? launch_decode_cfg<128, 4, true>(p, s) : launch_decode_cfg<128, 4, false>(p, s);
+        return bf16 ? launch_decode_cap<128, true>(p, s) : launch_decode_cap<128, false>(p, s);
     if (head_size == 64)
-        return bf16 ? launch_decode_cfg<64, 4, true>(p, s) : launch_decode_cfg<64, 4, false>(p, s);
+        return bf16 ? launch_decode_cap<64, true>(p, s) : launch_decode_cap<64, false>(p, s);
     return hipErrorInvalidValue;
 }
 

@@ -71,6 +71,17 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Score cap (softcap c > 0) in the kernels' log2 domain: from the raw
+// product s, c * tanh(|scale| * s / c) * log2(e) = out * (1 - 2 / (1 + 2^(s * in2)))
+// with in2 = 2 * log2(e) * |scale| / c and out = c * log2(e).  2^(.)
+// overflows to +inf for large arguments (exactly +out) and underflows to 0
+// (exactly -out); a masked score (-inf) stays -inf.
+__device__ __forceinline__ float cap_score(float s, float in2, float out) {
+    const float e = fast_exp2(s * in2);
+    const float t = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
+    return s == kNegInf ? kNegInf : out * t;
+}
+
 // Exchange with lane ^ 32 (the other half of a 32-wide MFMA column).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -353,9 +364,10 @@ __device__ __forceinline__ u32x4_t neg16x8(u32x4_t v) {
 // 32-key blocks kb0 .. kb0+NKB-1 of it.  c = |scale| * log2(e) >= 0.  MASKED
 // evaluates each row's visible interval [lo, hi); otherwise every key of the
 // processed blocks is visible to every row.
-template <int D, int BN, int NKB, int QB, bool BF16, bool MASKED>
+template <int D, int BN, int NKB, int QB, bool BF16, bool MASKED, bool CAP = false>
 __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* lds, int j0,
-                                          int kb0, float c) {
+                                          int kb0, float c, float cap_in2 = 0.f,
+                                          float cap_out = 0.f) {
     constexpr int KP = k_pitch<D>();
     constexpr int VP = vt_pitch<BN>();
     const int lane = lane_id();
@@ -394,9 +406,12 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
                     const int key = j0 + (kb0 + kb) * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                     if (!(key >= st.lo[qb] && key < st.hi[qb])) s[kb][qb][r] = kNegInf;
                 }
+                // capped scores are already in log2 units (c = 1 below)
+                if constexpr (CAP) s[kb][qb][r] = cap_score(s[kb][qb][r], cap_in2, cap_out);
                 mx[qb] = fmaxf(mx[qb], s[kb][qb][r]);
             }
 
+    if constexpr (CAP) c = 1.f;
     bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {

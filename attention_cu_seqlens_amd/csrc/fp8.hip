@@ -134,11 +134,13 @@ struct Fp8Wave {
     bool need;
 };
 
-// Online softmax of one tile (VALU): mask when partial, new running max
-// (lazy: moved only when some row's tile max exceeds it by more than
+// Online softmax of one tile (VALU): mask when partial, cap the scores with
+// CAP (in log2 units, scale factor 1 after that), new running max (lazy:
+// moved only when some row's tile max exceeds it by more than
 // kRescaleSlack), probabilities rounded to e4m3 into pb.
-template <bool MASKED>
-__device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, int hi) {
+template <bool MASKED, bool CAP>
+__device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, int hi,
+                                         float cap_in2, float cap_out) {
     const int g = lane_id() >> 5;
     if constexpr (MASKED) {
 #pragma unroll
@@ -154,7 +156,11 @@ __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, i
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st.s[kb][r]);
+        for (int r = 0; r < 16; ++r) {
+            if constexpr (CAP) st.s[kb][r] = cap_score(st.s[kb][r], cap_in2, cap_out);
+            mx = fmaxf(mx, st.s[kb][r]);
+        }
+    if constexpr (CAP) c = 1.f;
     mx = fmaxf(mx, xor32(mx));
     mx = (mx == kNegInf) ? kNegInf : mx * c;
     const bool up = mx > st.m + kRescaleSlack;
@@ -293,7 +299,7 @@ struct Dma8Hook {
 
 }  // namespace
 
-template <int NW>
+template <int NW, bool CAP>
 __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     static_assert(NW == 8, "two groups of four single-block waves");
     constexpr int BM = NW * 32;
@@ -317,6 +323,9 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     const float c_signed = p.scale * dq * dk * kLog2e;
     const bool neg = c_signed < 0.f;
     const float c = fabsf(c_signed);
+    // score cap in log2 units (cap_score), on the descaled score
+    const float cap_in2 = CAP ? 2.f * c / p.softcap : 0.f;
+    const float cap_out = CAP ? p.softcap * kLog2e : 0.f;
 
     const int lane = lane_id();
     const int w = wave_id();
@@ -355,6 +364,8 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
             hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
         }
+        // local window: keys after the query's own position minus the window
+        if (p.window > 0) lo = max(lo, tok + (kv_len - q_len) - p.window + 1);
         if (hi < lo) hi = lo;
     }
     const int w_lo = wave_min(valid ? lo : 0x7fffffff);
@@ -457,8 +468,8 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     // Every wave runs every tile: a tile with no visible key for this wave
     // (a causal diagonal) gives P = 0 and leaves m, l and O unchanged.
     auto softmax = [&](int j0) {
-        if (full(j0)) softmax8<false>(st, c, j0, lo, hi);
-        else softmax8<true>(st, c, j0, lo, hi);
+        if (full(j0)) softmax8<false, CAP>(st, c, j0, lo, hi, cap_in2, cap_out);
+        else softmax8<true, CAP>(st, c, j0, lo, hi, cap_in2, cap_out);
     };
 
     if (n > 0) {
@@ -548,7 +559,10 @@ hipError_t launch_fp8_prefill(const Fp8Params& p0, int head_size, int max_seqlen
                                            tokens_per_tile);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_fp8_prefill<NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+    if (p.softcap > 0.f)
+        hipLaunchKernelGGL((k_fp8_prefill<NW, true>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
+    else
+        hipLaunchKernelGGL((k_fp8_prefill<NW, false>), dim3((unsigned)grid), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
 

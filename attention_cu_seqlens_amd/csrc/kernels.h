@@ -34,6 +34,8 @@ struct PrefillParams {
     int bs_log2;
     uint32_t mask;
     float c;                    // scale * log2(e)
+    int window;                 // local window (keys), 0 = none
+    float cap_in2, cap_out;     // score cap constants (SoftCap), cap_out == 0: none
 };
 
 // Paged decode (16-bit dtypes): split kernel + combine kernel.
@@ -56,6 +58,8 @@ struct DecodeParams {
     int split_tokens;
     int max_splits;
     float c;
+    int window;                 // local window (keys), 0 = none
+    float cap_in2, cap_out;     // score cap constants (SoftCap), cap_out == 0: none
 };
 
 // Dense varlen fp8 prefill.
@@ -81,6 +85,8 @@ struct Fp8Params {
     int total_q;
     uint32_t mask;
     float scale;
+    int window;                 // local window (keys), 0 = none
+    float softcap;              // score cap c, 0 = none
 };
 
 hipError_t launch_cu_seqlens(const int32_t* seqlens, int32_t* cu, int batch, hipStream_t s);

@@ -66,11 +66,12 @@ struct PrefillWave {
 };
 
 // Softmax phase (VALU): mask the scores of the tile at key j0 when partial,
-// then probabilities into pb; finally read the first operands of the tile's
-// P.V from its V tile v_tile.
-template <int D, int BN, bool BF16>
+// then probabilities into pb (scores capped first with CAP); finally read
+// the first operands of the tile's P.V from its V tile v_tile.
+template <int D, int BN, bool BF16, bool CAP>
 __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool partial, int j0, int lo,
-                                              int hi, float c, const uint8_t* v_tile) {
+                                              int hi, float c, const uint8_t* v_tile,
+                                              float cap_in2, float cap_out) {
     if (partial) {
         const int g = lane_id() >> 5;
 #pragma unroll
@@ -80,9 +81,11 @@ __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool parti
                 const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                 if (!(key >= lo && key < hi)) st.s[kb][r] = kNegInf;
             }
-        softmax_tile<BN, BF16, true>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need);
+        softmax_tile<BN, BF16, true, CAP>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need,
+                                          cap_in2, cap_out);
     } else {
-        softmax_tile<BN, BF16, false>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need);
+        softmax_tile<BN, BF16, false, CAP>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need,
+                                           cap_in2, cap_out);
     }
     preload_pv<D, BN, PrefillWave<D, BN>::NPRE>(st.pre, v_tile);
 }
@@ -103,7 +106,7 @@ __device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t 
                                                                 v_tile, k_tile, hook);
 }
 
-template <int D, int BN, int QB, int NW, bool BF16>
+template <int D, int BN, int QB, int NW, bool BF16, bool CAP>
 __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     static_assert(QB == 1 && NW == 8, "two groups of four single-block waves");
     constexpr int BM = NW * 32;
@@ -166,6 +169,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
             hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
         }
+        // local window: keys after the query's own position minus the window
+        if (p.window > 0) lo = max(lo, tok + (kv_len - q_len) - p.window + 1);
         if (hi < lo) hi = lo;
     }
     // Wave extremes over valid rows; an all-invalid wave gets an empty range.
@@ -258,7 +263,9 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
             const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
             // phase 1
-            if (lead) phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c, st_cur + R::TILE);
+            if (lead)
+                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo, hi, c, st_cur + R::TILE,
+                                                p.cap_in2, p.cap_out);
             else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
             const int j3 = cs + (jt + kStages - 1) * BN;
             const bool load3 = lead && jt + kStages - 1 < n;
@@ -285,7 +292,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next,
                                                    Hook{ld, sr, st3, w, spread});
             } else {
-                phase_softmax<D, BN, BF16>(st, partial, j0, lo, hi, c, st_cur + R::TILE);
+                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo, hi, c, st_cur + R::TILE,
+                                                p.cap_in2, p.cap_out);
             }
             block_barrier();
         }
@@ -309,7 +317,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 
 namespace {
 
-template <int D, int BN, int QB, int NW, bool BF16>
+template <int D, int BN, int QB, int NW, bool BF16, bool CAP>
 hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) {
     constexpr int BM = NW * QB * 32;
     PrefillParams p = p0;
@@ -319,7 +327,7 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
                                            tokens_per_tile);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
@@ -335,15 +343,25 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
 #define ATTN_PREFILL_D64 64, 1, 8
 #endif
 
+namespace {
+
+template <int D, int BN, int QB, int NW, bool BF16>
+hipError_t launch_cap(const PrefillParams& p, int max_seqlen_q, hipStream_t s) {
+    return p.cap_out > 0.f ? launch_cfg<D, BN, QB, NW, BF16, true>(p, max_seqlen_q, s)
+                           : launch_cfg<D, BN, QB, NW, BF16, false>(p, max_seqlen_q, s);
+}
+
+}  // namespace
+
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16,
                                 int max_seqlen_q, hipStream_t s) {
     if (head_size == 128) {
-        return bf16 ? launch_cfg<128, ATTN_PREFILL_D128, true>(p, max_seqlen_q, s)
-                    : launch_cfg<128, ATTN_PREFILL_D128, false>(p, max_seqlen_q, s);
+        return bf16 ? launch_cap<128, ATTN_PREFILL_D128, true>(p, max_seqlen_q, s)
+                    : launch_cap<128, ATTN_PREFILL_D128, false>(p, max_seqlen_q, s);
     }
     if (head_size == 64) {
-        return bf16 ? launch_cfg<64, ATTN_PREFILL_D64, true>(p, max_seqlen_q, s)
-                    : launch_cfg<64, ATTN_PREFILL_D64, false>(p, max_seqlen_q, s);
+        return bf16 ? launch_cap<64, ATTN_PREFILL_D64, true>(p, max_seqlen_q, s)
+                    : launch_cap<64, ATTN_PREFILL_D64, false>(p, max_seqlen_q, s);
     }
     return hipErrorInvalidValue;
 }

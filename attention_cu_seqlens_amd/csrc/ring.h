@@ -349,11 +349,21 @@ __device__ __forceinline__ void mfma_stream16(f32x16_t (&o)[D / 32], f32x16_t (&
 // s: raw S^T accumulators (masked entries already -inf when MASKED);
 // on return pb holds the packed probabilities, m may have moved (then *need
 // is set and alpha holds exp2(m_old - m_new)), and lpart accumulated this
-// lane's partial row sum (relative to the final m after any rescale).
-template <int BN, bool BF16, bool MASKED>
+// lane's partial row sum (relative to the final m after any rescale).  CAP
+// first replaces every score by its capped value in log2 units (cap_score),
+// after which the scale factor is 1.
+template <int BN, bool BF16, bool MASKED, bool CAP = false>
 __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], float c, float& m,
                                              float& lpart, u32x4_t (&pb)[BN / 32][2],
-                                             float& alpha, bool& need) {
+                                             float& alpha, bool& need, float cap_in2 = 0.f,
+                                             float cap_out = 0.f) {
+    if constexpr (CAP) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = cap_score(s[kb][r], cap_in2, cap_out);
+        c = 1.f;
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb)

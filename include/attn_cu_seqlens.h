@@ -39,6 +39,16 @@
  *     the byte->patch cross-attention of the blt issue.  CAUSAL combines with
  *     either; DOCUMENT and PATCH are exclusive.  q_ids / kv_ids are indexed by
  *     global token (q_ids[total_q], kv_ids[total_kv]).
+ *   - Local window and score cap (window_left, softcap): the onnxruntime PR's
+ *     parity matrix runs "local window on/off" and "softcap 0/50" (section
+ *     Testing) without defining them; read here as
+ *       window_left W > 0: key j is kept only if j > i + kv_len - q_len - W,
+ *       a window of W keys ending at the query's own (bottom-right) position,
+ *       combined with the mask flags; W = 0 means no window;
+ *       softcap c > 0: every scaled score s becomes c * tanh(s / c) before
+ *       the mask and the softmax (LSE is over the capped scores); c = 0
+ *       means no cap.
+ *     Negative, NaN or infinite values are ATTN_ERR_BAD_SHAPE.
  *   - A query row with no visible key outputs zeros and LSE = -inf (rows may
  *     be fully masked: "ROWS_GUARANTEED_SAFE: False" in the same kernel
  *     options).
@@ -67,7 +77,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -145,6 +155,7 @@ attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, 
  *                (host values; they size the launch, no device sync is made)
  *   mask_flags, q_ids, kv_ids    see Conventions (ids may be NULL unless the
  *                matching flag is set)
+ *   window_left, softcap         local window and score cap (Conventions)
  *   out          [total_q, num_heads, head_size], same dtype as q
  *   lse          float32 [total_q, num_heads] or NULL
  * Supported: head_size 64 or 128; block_size 16, 32 or 64;
@@ -158,8 +169,8 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
                                    int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
                                    int32_t head_size, int32_t block_size, int32_t num_blocks,
                                    float scale, uint32_t mask_flags, const int32_t* q_ids,
-                                   const int32_t* kv_ids, attn_dtype dtype, void* out, float* lse,
-                                   void* stream);
+                                   const int32_t* kv_ids, int32_t window_left, float softcap,
+                                   attn_dtype dtype, void* out, float* lse, void* stream);
 
 /*
  * attn_paged_decode_workspace_bytes -- workspace size attn_paged_decode_fwd
@@ -178,6 +189,8 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
  * with their logsumexp (the LSE output of the blt issue's kernel options).
  *   q            [batch, num_heads, head_size], ATTN_F16 or ATTN_BF16
  *   cu_seqlens_kv int32 [batch + 1]; max_seqlen_kv bounds every kv length
+ *   window_left, softcap  as prefill: the window keeps a sequence's last
+ *                window_left keys
  *   split_tokens keys per split: a multiple of 256 no larger than 8192, or 0
  *                to let the library choose from (batch, num_kv_heads,
  *                max_seqlen_kv)
@@ -194,9 +207,9 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
                                   const int32_t* cu_seqlens_kv, int32_t batch,
                                   int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
-                                  float scale, int32_t split_tokens, attn_dtype dtype, void* out,
-                                  float* lse, void* workspace, size_t workspace_bytes,
-                                  void* stream);
+                                  float scale, int32_t window_left, float softcap,
+                                  int32_t split_tokens, attn_dtype dtype, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * attn_fp8_fwd -- dense varlen fp8 e4m3 attention with a column-major V.
@@ -208,7 +221,8 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
  *   k8           uint8 e4m3 codes [total_kv, num_kv_heads, head_size]
  *   v8_colmajor  uint8 e4m3 codes [num_kv_heads, head_size, total_kv]
  *   descale_qkv  float32 [3] (device): real value = descale * decoded code
- *   cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, masks: as prefill
+ *   cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, masks,
+ *   window_left, softcap: as prefill (the cap applies to the descaled score)
  *   out_bf16     bf16 [total_q, num_heads, head_size]
  *   lse          float32 [total_q, num_heads] or NULL
  * Scores and the softmax run in fp32.  The probabilities are rounded to e4m3
@@ -224,7 +238,8 @@ attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor
                          int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
                          int32_t num_heads, int32_t num_kv_heads, int32_t head_size, float scale,
                          uint32_t mask_flags, const int32_t* q_ids, const int32_t* kv_ids,
-                         void* out_bf16, float* lse, void* stream);
+                         int32_t window_left, float softcap, void* out_bf16, float* lse,
+                         void* stream);
 
 #ifdef __cplusplus
 }

@@ -47,7 +47,7 @@ def banner(msg):
 
 # ---------------------------------------------------------------- oracle side
 
-def oracle_prefill(w, rows=None):
+def oracle_prefill(w, rows=None, window=0, softcap=0.0):
     cu_q = ORC.cu_seqlens(w.q_lens)
     cu_kv = ORC.cu_seqlens(w.kv_lens)
     cu_new = ORC.cu_seqlens(w.new_lens)
@@ -59,10 +59,10 @@ def oracle_prefill(w, rows=None):
     kc, vc = ORC.reshape_and_cache(k, v, kc, vc, w.block_table, cu_new, cu_kv, w.block_size)
     q = w.q.double().cpu().numpy()
     return ORC.paged_attention(q, kc, vc, w.block_table, cu_q, cu_kv, w.block_size, w.scale,
-                               w.mask_flags, w.q_ids, w.kv_ids, rows)
+                               w.mask_flags, w.q_ids, w.kv_ids, rows, window, softcap)
 
 
-def oracle_decode(w, batches=None):
+def oracle_decode(w, batches=None, window=0, softcap=0.0):
     cu_kv = ORC.cu_seqlens(w.kv_lens)
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
     kc = np.full(shape, np.nan)
@@ -71,15 +71,16 @@ def oracle_decode(w, batches=None):
     v = w.v_new.double().cpu().numpy()
     kc, vc = ORC.reshape_and_cache(k, v, kc, vc, w.block_table, cu_kv, cu_kv, w.block_size)
     q = w.q.double().cpu().numpy()
-    return ORC.paged_decode(q, kc, vc, w.block_table, cu_kv, w.block_size, w.scale, batches)
+    return ORC.paged_decode(q, kc, vc, w.block_table, cu_kv, w.block_size, w.scale, batches,
+                            window, softcap)
 
 
-def oracle_fp8(w, rows=None):
+def oracle_fp8(w, rows=None, window=0, softcap=0.0):
     cu_q = ORC.cu_seqlens(w.q_lens)
     cu_kv = ORC.cu_seqlens(w.kv_lens)
     return ORC.fp8_attention(w.q.cpu().numpy(), w.k_new.cpu().numpy(),
                              w.v8_colmajor.cpu().numpy(), w.descale, cu_q, cu_kv, w.scale,
-                             w.mask_flags, w.q_ids, w.kv_ids, rows)
+                             w.mask_flags, w.q_ids, w.kv_ids, rows, window, softcap)
 
 
 # ------------------------------------------------------------------- GPU side
@@ -102,7 +103,7 @@ def gpu_cache(w, A, poison=float("nan")):
     return kc, vc, bt, cu_kv
 
 
-def gpu_prefill(w, A, cache=None, scale=None, block_table=None):
+def gpu_prefill(w, A, cache=None, scale=None, block_table=None, window=0, softcap=0.0):
     kc, vc, bt, cu_kv = cache if cache is not None else gpu_cache(w, A)
     if block_table is not None:
         bt = _i32(block_table)
@@ -112,21 +113,23 @@ def gpu_prefill(w, A, cache=None, scale=None, block_table=None):
     out, lse = A.attn_paged_prefill_fwd(
         w.q.to(DEV).contiguous(), kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max(initial=0)),
         int(w.kv_lens.max(initial=0)), scale=w.scale if scale is None else scale,
-        mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, return_lse=True)
+        mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, return_lse=True, window=window,
+        softcap=softcap)
     torch.cuda.synchronize()
     return out, lse
 
 
-def gpu_decode(w, A, split_tokens=0, cache=None):
+def gpu_decode(w, A, split_tokens=0, cache=None, window=0, softcap=0.0):
     kc, vc, bt, cu_kv = cache if cache is not None else gpu_cache(w, A)
     out, lse = A.attn_paged_decode_fwd(w.q.to(DEV).contiguous(), kc, vc, bt, cu_kv,
                                        int(w.kv_lens.max(initial=0)), scale=w.scale,
-                                       split_tokens=split_tokens, return_lse=True)
+                                       split_tokens=split_tokens, return_lse=True, window=window,
+                                       softcap=softcap)
     torch.cuda.synchronize()
     return out, lse
 
 
-def gpu_fp8(w, A):
+def gpu_fp8(w, A, window=0, softcap=0.0):
     cu_q = A.attn_cu_seqlens(_i32(w.q_lens))
     cu_kv = A.attn_cu_seqlens(_i32(w.kv_lens))
     q_ids = None if w.q_ids is None else _i32(w.q_ids)
@@ -135,7 +138,7 @@ def gpu_fp8(w, A):
                               torch.as_tensor(w.descale, dtype=torch.float32).to(DEV), cu_q,
                               cu_kv, int(w.q_lens.max()), int(w.kv_lens.max()), scale=w.scale,
                               mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids,
-                              return_lse=True)
+                              return_lse=True, window=window, softcap=softcap)
     torch.cuda.synchronize()
     return out, lse
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 1
+    assert lib.attn_abi_version() == 2
     for code in range(7):
         assert lib.attn_status_string(code)
     assert lib.attn_status_string(99) == b"unknown status"
@@ -72,8 +72,8 @@ def test_reshape_and_cache_host_checks(lib):
 
 def _prefill_args(**kw):
     a = dict(q=P, kc=P, vc=P, bt=P, mbps=8, cuq=P, cukv=P, batch=2, total_q=100, msq=64, mskv=64,
-             hq=8, hkv=2, d=128, bs=16, nb=32, scale=0.1, mask=1, qids=None, kvids=None, dtype=1,
-             out=P, lse=None, stream=None)
+             hq=8, hkv=2, d=128, bs=16, nb=32, scale=0.1, mask=1, qids=None, kvids=None, window=0,
+             softcap=0.0, dtype=1, out=P, lse=None, stream=None)
     a.update(kw)
     return list(a.values())
 
@@ -91,6 +91,11 @@ def test_prefill_host_checks(lib):
     assert f(*_prefill_args(mask=8)) == 3
     assert f(*_prefill_args(mskv=129)) == 2             # table too narrow for the longest kv
     assert f(*_prefill_args(scale=float("nan"))) == 2
+    assert f(*_prefill_args(window=-1)) == 2
+    assert f(*_prefill_args(softcap=-1.0)) == 2
+    assert f(*_prefill_args(softcap=float("inf"))) == 2
+    assert f(*_prefill_args(softcap=float("nan"))) == 2
+    assert f(*_prefill_args(batch=0, window=64, softcap=50.0)) == 0
     assert f(*_prefill_args(batch=0)) == 0
     assert f(*_prefill_args(total_q=0)) == 0
 
@@ -106,7 +111,7 @@ def test_decode_host_checks(lib):
 
     def call(**kw):
         a = dict(q=P, kc=P, vc=P, bt=P, mbps=64, cukv=P, batch=4, mskv=1000, hq=8, hkv=2, d=128,
-                 bs=16, nb=300, scale=0.1, split=256, dtype=1, out=P, lse=None,
+                 bs=16, nb=300, scale=0.1, window=0, softcap=0.0, split=256, dtype=1, out=P, lse=None,
                  ws=ctypes.c_void_p(256), wsb=need, stream=None)
         a.update(kw)
         return lib.attn_paged_decode_fwd(*a.values())
@@ -118,6 +123,8 @@ def test_decode_host_checks(lib):
     assert call(hq=66, hkv=1) == 3                      # group above 32
     assert call(split=300) == 2
     assert call(split=8448) == 2                        # above 8192
+    assert call(window=-5) == 2
+    assert call(softcap=float("nan")) == 2
     assert call(batch=0) == 0
 
 
@@ -126,12 +133,15 @@ def test_fp8_host_checks(lib):
 
     def call(**kw):
         a = dict(q=P, k=P, v=P, ds=P, cuq=P, cukv=P, batch=2, tq=10, tkv=10, msq=5, mskv=5, hq=4,
-                 hkv=4, d=128, scale=0.1, mask=1, qids=None, kvids=None, out=P, lse=None,
-                 stream=None)
+                 hkv=4, d=128, scale=0.1, mask=1, qids=None, kvids=None, window=0, softcap=0.0,
+                 out=P, lse=None, stream=None)
         a.update(kw)
         return f(*a.values())
 
     assert call(d=64) == 3
     assert call(ds=None) == 1
     assert call(hq=6) == 2
+    assert call(window=-1) == 2
+    assert call(softcap=-0.5) == 2
+    assert call(tkv=(1 << 27) + 16) == 2                # V^T offsets of one wave must fit 32 bits
     assert call(tq=0) == 0

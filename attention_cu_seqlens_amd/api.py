@@ -127,9 +127,10 @@ def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_se
 
 
 def attn_paged_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_size, max_seqlen_kv,
-                                      split_tokens=0):
+                                      split_tokens=0, window=0):
     return int(_lib.load().attn_paged_decode_workspace_bytes(
-        batch, num_heads, num_kv_heads, head_size, int(max_seqlen_kv), int(split_tokens)))
+        batch, num_heads, num_kv_heads, head_size, int(max_seqlen_kv), int(window),
+        int(split_tokens)))
 
 
 def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_seqlen_kv,
@@ -147,7 +148,7 @@ def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_s
     nb, bs, hkv, _ = k_cache.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = attn_paged_decode_workspace_bytes(batch, hq, hkv, d, max_seqlen_kv, split_tokens)
+    need = attn_paged_decode_workspace_bytes(batch, hq, hkv, d, max_seqlen_kv, split_tokens, window)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev)

@@ -201,12 +201,14 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
 
 size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                          int32_t head_size, int32_t max_seqlen_kv,
-                                         int32_t split_tokens) {
+                                         int32_t window_left, int32_t split_tokens) {
     if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || max_seqlen_kv < 0)
         return 0;
     if (split_tokens < 0 || split_tokens % 256 != 0 || split_tokens > 8192) return 0;
-    const int st = attn::decode_split_tokens(batch, num_kv_heads, max_seqlen_kv, split_tokens);
-    return attn::decode_workspace_bytes(batch, num_heads, head_size, max_seqlen_kv, st);
+    if (window_left < 0) return 0;
+    const int span = attn::decode_span(max_seqlen_kv, window_left);
+    const int st = attn::decode_split_tokens(batch, num_kv_heads, span, split_tokens);
+    return attn::decode_workspace_bytes(batch, num_heads, head_size, span, st);
 }
 
 attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
@@ -235,8 +237,9 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
         return ATTN_ERR_NULL_ARG;
     if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0) return ATTN_OK;
-    const int st = attn::decode_split_tokens(batch, num_kv_heads, max_seqlen_kv, split_tokens);
-    const size_t need = attn::decode_workspace_bytes(batch, num_heads, head_size, max_seqlen_kv, st);
+    const int span = attn::decode_span(max_seqlen_kv, window_left);
+    const int st = attn::decode_split_tokens(batch, num_kv_heads, span, split_tokens);
+    const size_t need = attn::decode_workspace_bytes(batch, num_heads, head_size, span, st);
     if (workspace == nullptr || workspace_bytes < need ||
         (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
         return ATTN_ERR_WORKSPACE;
@@ -249,7 +252,7 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     p.v_cache = static_cast<const uint16_t*>(v_cache);
     p.block_table = block_table;
     p.cu_kv = cu_seqlens_kv;
-    p.max_splits = max_seqlen_kv > 0 ? (max_seqlen_kv + st - 1) / st : 1;
+    p.max_splits = span > 0 ? (span + st - 1) / st : 1;
     const int64_t rows = (int64_t)batch * num_heads * p.max_splits;
     const int64_t o_bytes = ((rows * head_size * 4 + 255) / 256) * 256;
     p.part_o = static_cast<float*>(workspace);

@@ -15,6 +15,8 @@
 // splits past a sequence's end exit at once and the merge kernel derives
 // each sequence's split count from its own length.
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,7 +50,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int b = unit / p.num_kv_heads;
     const int kv_start = p.cu_kv[b];
     const int kv_len = p.cu_kv[b + 1] - kv_start;
-    const int k0 = s * p.split_tokens;
+    // The splits tile the keys from window_base (0 without a local window):
+    // a window keeps the sequence's last p.window keys, lo_w on; the grid
+    // starts at lo_w rounded down to 32 keys (tiles stay 32-key aligned) and
+    // the keys before lo_w are masked.
+    const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
+    const int k0 = (lo_w & ~31) + s * p.split_tokens;
     if (k0 >= kv_len) return;
     const int k1 = min(kv_len, k0 + p.split_tokens);
     const bool neg = p.c < 0.f;
@@ -72,9 +79,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             st.q[0][t] = neg ? neg16x8(v) : v;
         }
     }
-    // a local window keeps the last p.window keys of the sequence
-    const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
-    st.lo[0] = lo_w;
+    st.lo[0] = lo_w;   // keys before the window are masked
     st.hi[0] = k1;
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
@@ -155,7 +160,8 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.num_heads;
     const int kv_len = p.cu_kv[b + 1] - p.cu_kv[b];
-    const int n_s = (kv_len + p.split_tokens - 1) / p.split_tokens;
+    const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
+    const int n_s = (kv_len - (lo_w & ~31) + p.split_tokens - 1) / p.split_tokens;
     const int d = threadIdx.x;
     const int64_t base = (int64_t)bh * p.max_splits;
     float mstar = kNegInf;
@@ -183,6 +189,13 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
 // start (block ids, first tile from HBM) less often; the paged GQA decode
 // workload (64 sequences, kv 1024-32768, 8 kv heads) measured 5.8-6.0 TB/s at
 // 4096 keys per split against 5.1 at 512 and 5.5 at 1024.
+// Keys a split grid must cover for kv lengths up to max_seqlen_kv: with a
+// local window W, at most W keys plus up to 31 before them (the grid starts
+// 32-key aligned).
+int decode_span(int max_seqlen_kv, int window) {
+    return window > 0 ? (int)std::min<int64_t>(max_seqlen_kv, (int64_t)window + 31) : max_seqlen_kv;
+}
+
 int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested) {
     if (requested > 0) return requested;
     const int64_t units = (int64_t)batch * num_kv_heads;

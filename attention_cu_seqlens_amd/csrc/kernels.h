@@ -100,6 +100,7 @@ hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, 
 hipError_t launch_fp8_prefill(const Fp8Params& p, int head_size, int max_seqlen_q, hipStream_t s);
 
 // Decode planning shared by the workspace query and the launch.
+int decode_span(int max_seqlen_kv, int window);
 int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested);
 size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_seqlen_kv,
                               int split_tokens);

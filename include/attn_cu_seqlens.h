@@ -174,12 +174,12 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
 
 /*
  * attn_paged_decode_workspace_bytes -- workspace size attn_paged_decode_fwd
- * needs for these sizes (same split_tokens argument).  Host only, no HIP call.
- * Returns 0 for invalid sizes.
+ * needs for these sizes (same window_left and split_tokens arguments).  Host
+ * only, no HIP call.  Returns 0 for invalid sizes.
  */
 size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                          int32_t head_size, int32_t max_seqlen_kv,
-                                         int32_t split_tokens);
+                                         int32_t window_left, int32_t split_tokens);
 
 /*
  * attn_paged_decode_fwd -- one query token per sequence against its paged
@@ -190,7 +190,7 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
  *   q            [batch, num_heads, head_size], ATTN_F16 or ATTN_BF16
  *   cu_seqlens_kv int32 [batch + 1]; max_seqlen_kv bounds every kv length
  *   window_left, softcap  as prefill: the window keeps a sequence's last
- *                window_left keys
+ *                window_left keys, and the splits then cover only those keys
  *   split_tokens keys per split: a multiple of 256 no larger than 8192, or 0
  *                to let the library choose from (batch, num_kv_heads,
  *                max_seqlen_kv)

@@ -102,12 +102,15 @@ def test_prefill_host_checks(lib):
 
 def test_decode_host_checks(lib):
     ws = lib.attn_paged_decode_workspace_bytes
-    assert ws(64, 32, 8, 128, 32768, 0) > 0
-    assert ws(64, 32, 8, 128, 32768, 100) == 0          # split not a multiple of 256
-    assert ws(64, 32, 8, 128, 32768, 8448) == 0         # split above 8192
-    assert ws(0, 32, 8, 128, 1, 0) == 0
-    need = ws(4, 8, 2, 128, 1000, 256)
+    assert ws(64, 32, 8, 128, 32768, 0, 0) > 0
+    assert ws(64, 32, 8, 128, 32768, 0, 100) == 0       # split not a multiple of 256
+    assert ws(64, 32, 8, 128, 32768, 0, 8448) == 0      # split above 8192
+    assert ws(64, 32, 8, 128, 32768, -1, 0) == 0        # negative window
+    assert ws(0, 32, 8, 128, 1, 0, 0) == 0
+    need = ws(4, 8, 2, 128, 1000, 0, 256)
     assert need == 4 * 8 * 4 * 128 * 4 + 4 * 8 * 4 * 2 * 4
+    # a window of 300 keys: the splits cover at most 300 + 31 keys -> 2 of 256
+    assert ws(4, 8, 2, 128, 1000, 300, 256) == 4 * 8 * 2 * 128 * 4 + 4 * 8 * 2 * 2 * 4
 
     def call(**kw):
         a = dict(q=P, kc=P, vc=P, bt=P, mbps=64, cukv=P, batch=4, mskv=1000, hq=8, hkv=2, d=128,

@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     attn_paged_prefill_fwd,
     attn_paged_decode_workspace_bytes,
     attn_paged_decode_fwd,
+    attn_paged_decode_fp8kv_fwd,
     attn_fp8_fwd,
     library_path,
 )

@@ -41,6 +41,9 @@ SIGNATURES = {
     "attn_paged_decode_fwd": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _f32, _i32, _f32, _i32, ctypes.c_int,
                                              _p, _p, _p, _size, _p]),
+    "attn_paged_decode_fp8kv_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _i32, _f32, _i32, _f32, _i32,
+                                                   ctypes.c_int, _p, _p, _p, _size, _p]),
     "attn_fp8_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _f32, _u32, _p, _p, _i32, _f32, _p, _p, _p]),
 }

@@ -166,6 +166,46 @@ def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_s
     return (out, lse) if return_lse else out
 
 
+def attn_paged_decode_fp8kv_fwd(q, k_cache8, v_cache8, kv_descale, block_table, cu_seqlens_kv,
+                                max_seqlen_kv, scale=None, split_tokens=0, out=None,
+                                return_lse=False, workspace=None, window=0, softcap=0.0):
+    """Decode against an fp8 e4m3 paged cache: k_cache8 / v_cache8 uint8 (or
+    float8_e4m3fn) [num_blocks, block_size, Hkv, D], kv_descale fp32 [2]
+    (dk, dv); q [batch, Hq, D] fp16 or bf16."""
+    dev = q.device
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    k8, v8 = _u8(k_cache8), _u8(v_cache8)
+    for name, t in (("k_cache8", k8), ("v_cache8", v8)):
+        _need(t, name, torch.uint8, dev)
+    if v8.shape != k8.shape:
+        raise ValueError("k_cache8 and v_cache8 shapes differ")
+    _need(kv_descale, "kv_descale", torch.float32, dev)
+    if kv_descale.numel() != 2:
+        raise ValueError("kv_descale must hold (dk, dv)")
+    for name, t in (("block_table", block_table), ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    batch, hq, d = q.shape
+    nb, bs, hkv, _ = k8.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = attn_paged_decode_workspace_bytes(batch, hq, hkv, d, max_seqlen_kv, split_tokens, window)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_paged_decode_fp8kv_fwd", lib.attn_paged_decode_fp8kv_fwd(
+            _ptr(q), _ptr(k8), _ptr(v8), _ptr(kv_descale), _ptr(block_table), block_table.shape[1],
+            _ptr(cu_seqlens_kv), batch, int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale),
+            int(window), float(softcap), int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse),
+            _ptr(workspace), workspace.numel(), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
 def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                  max_seqlen_kv, scale=None, mask_flags=0, q_ids=None, kv_ids=None, out=None,
                  return_lse=False, window=0, softcap=0.0):

@@ -211,14 +211,19 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
     return attn::decode_workspace_bytes(batch, num_heads, head_size, span, st);
 }
 
-attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_table, int32_t max_blocks_per_seq,
-                                  const int32_t* cu_seqlens_kv, int32_t batch,
-                                  int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
-                                  int32_t head_size, int32_t block_size, int32_t num_blocks,
-                                  float scale, int32_t window_left, float softcap,
-                                  int32_t split_tokens, attn_dtype dtype, void* out, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode over a 16-bit cache (kv_descale == nullptr) or an fp8 e4m3 cache.
+attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache, bool kv8,
+                        const float* kv_descale, const int32_t* block_table,
+                        int32_t max_blocks_per_seq, const int32_t* cu_seqlens_kv, int32_t batch,
+                        int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_size, int32_t block_size, int32_t num_blocks, float scale,
+                        int32_t window_left, float softcap, int32_t split_tokens, attn_dtype dtype,
+                        void* out, float* lse, void* workspace, size_t workspace_bytes,
+                        void* stream) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
@@ -233,7 +238,7 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     if (!std::isfinite(scale)) return ATTN_ERR_BAD_SHAPE;
     if (!window_cap_ok(window_left, softcap)) return ATTN_ERR_BAD_SHAPE;
     if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
-        cu_seqlens_kv == nullptr || out == nullptr)
+        cu_seqlens_kv == nullptr || out == nullptr || (kv8 && kv_descale == nullptr))
         return ATTN_ERR_NULL_ARG;
     if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0) return ATTN_OK;
@@ -248,8 +253,14 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
 
     attn::DecodeParams p{};
     p.q = static_cast<const uint16_t*>(q);
-    p.k_cache = static_cast<const uint16_t*>(k_cache);
-    p.v_cache = static_cast<const uint16_t*>(v_cache);
+    if (kv8) {
+        p.k8 = static_cast<const uint8_t*>(k_cache);
+        p.v8 = static_cast<const uint8_t*>(v_cache);
+        p.kv_descale = kv_descale;
+    } else {
+        p.k_cache = static_cast<const uint16_t*>(k_cache);
+        p.v_cache = static_cast<const uint16_t*>(v_cache);
+    }
     p.block_table = block_table;
     p.cu_kv = cu_seqlens_kv;
     p.max_splits = span > 0 ? (span + st - 1) / st : 1;
@@ -271,6 +282,39 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
     set_cap(scale, softcap, p.cap_in2, p.cap_out);
     return from_hip(attn::launch_paged_decode(p, head_size, dtype == ATTN_BF16,
                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_seqlens_kv, int32_t batch,
+                                  int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                  float scale, int32_t window_left, float softcap,
+                                  int32_t split_tokens, attn_dtype dtype, void* out, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(q, k_cache, v_cache, false, nullptr, block_table, max_blocks_per_seq,
+                       cu_seqlens_kv, batch, max_seqlen_kv, num_heads, num_kv_heads, head_size,
+                       block_size, num_blocks, scale, window_left, softcap, split_tokens, dtype,
+                       out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_paged_decode_fp8kv_fwd(const void* q, const void* k_cache8, const void* v_cache8,
+                                        const float* kv_descale, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, const int32_t* cu_seqlens_kv,
+                                        int32_t batch, int32_t max_seqlen_kv, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t block_size, int32_t num_blocks, float scale,
+                                        int32_t window_left, float softcap, int32_t split_tokens,
+                                        attn_dtype q_dtype, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    return decode_impl(q, k_cache8, v_cache8, true, kv_descale, block_table, max_blocks_per_seq,
+                       cu_seqlens_kv, batch, max_seqlen_kv, num_heads, num_kv_heads, head_size,
+                       block_size, num_blocks, scale, window_left, softcap, split_tokens, q_dtype,
+                       out, lse, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_fp8_fwd(const void* q8, const void* k8, const void* v8_colmajor,

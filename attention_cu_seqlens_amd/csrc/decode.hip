@@ -16,24 +16,26 @@
 // each sequence's split count from its own length.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
 
 namespace attn {
 
-template <int D, int NW, bool BF16>
+template <int D, int NW, bool BF16, bool KV8>
 struct DecodeLayout {
-    using Tile = PagedTile16<D, 32, 64, true>;            // one wave, 32 keys
+    // one wave, 32 keys; the fp8 cache loader fills the same 16-bit tile
+    using Tile = std::conditional_t<KV8, PagedTile8<D, BF16>, PagedTile16<D, 32, 64, true>>;
     static constexpr int WIN_OFF = NW * Tile::BYTES;
     static constexpr int TILE_BYTES = WIN_OFF + (PAGE_WIN + 1) * 4;
     static constexpr int RED_BYTES = NW * 32 * (D + 2) * 4;   // merge space, G <= 32
     static constexpr int LDS_BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
 };
 
-template <int D, int NW, bool BF16, bool CAP>
+template <int D, int NW, bool BF16, bool CAP, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_decode(DecodeParams p) {
-    using L = DecodeLayout<D, NW, BF16>;
+    using L = DecodeLayout<D, NW, BF16, KV8>;
     using Tile = typename L::Tile;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int* win = reinterpret_cast<int*>(smem + L::WIN_OFF);
@@ -59,7 +61,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     if (k0 >= kv_len) return;
     const int k1 = min(kv_len, k0 + p.split_tokens);
     const bool neg = p.c < 0.f;
-    const float c = fabsf(p.c);
+    // fp8 cache: the K descale joins the score scale (and the cap's input
+    // factor), the V descale multiplies the partial O
+    const float dk = KV8 ? p.kv_descale[0] : 1.f;
+    const float dv = KV8 ? p.kv_descale[1] : 1.f;
+    const float c = fabsf(p.c) * dk;
+    const float cap_in2 = p.cap_in2 * dk;
 
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
@@ -97,20 +104,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int t_first = lo_w > k0 ? (lo_w - k0) >> 5 : 0;
     uint8_t* mine = smem + w * Tile::BYTES;
     Tile ld;
-    if (t_first + w < n_t)
-        ld.load(p.k_cache, p.v_cache, win, first, k0 + 32 * (t_first + w), k1, p.bs_log2,
-                tok_stride, head_off, lane);
+    auto load = [&](int j) {
+        if constexpr (KV8)
+            ld.load(p.k8, p.v8, win, first, j, k1, p.bs_log2, tok_stride, head_off, lane);
+        else
+            ld.load(p.k_cache, p.v_cache, win, first, j, k1, p.bs_log2, tok_stride, head_off, lane);
+    };
+    if (t_first + w < n_t) load(k0 + 32 * (t_first + w));
     for (int t = t_first + w; t < n_t; t += NW) {
         const int j = k0 + 32 * t;
         ld.store(mine, j, k1, lane);
         __builtin_amdgcn_wave_barrier();
-        if (t + NW < n_t)
-            ld.load(p.k_cache, p.v_cache, win, first, j + 32 * NW, k1, p.bs_log2, tok_stride,
-                    head_off, lane);
+        if (t + NW < n_t) load(j + 32 * NW);
         if (j >= lo_w && j + 32 <= k1)
-            tile_step<D, 32, 1, 1, BF16, false, CAP>(st, mine, j, 0, c, p.cap_in2, p.cap_out);
+            tile_step<D, 32, 1, 1, BF16, false, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
         else
-            tile_step<D, 32, 1, 1, BF16, true, CAP>(st, mine, j, 0, c, p.cap_in2, p.cap_out);
+            tile_step<D, 32, 1, 1, BF16, true, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             osum += red_o[(i * G + cc) * D + d] * wgt;
         }
         const int64_t slot = ((int64_t)b * p.num_heads + hk * G + cc) * p.max_splits + s;
-        p.part_o[slot * D + d] = osum;
+        p.part_o[slot * D + d] = osum * dv;
         if (d == 0) {
             p.part_ml[slot * 2 + 0] = mstar;
             p.part_ml[slot * 2 + 1] = lsum;
@@ -214,16 +223,16 @@ size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_s
 
 namespace {
 
-template <int D, int NW, bool BF16, bool CAP>
+template <int D, int NW, bool BF16, bool CAP, bool KV8>
 hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
-    constexpr int lds = DecodeLayout<D, NW, BF16>::LDS_BYTES;
+    constexpr int lds = DecodeLayout<D, NW, BF16, KV8>::LDS_BYTES;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16, CAP>),
+        reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16, CAP, KV8>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     const int64_t grid = (int64_t)p.batch * p.num_kv_heads * p.max_splits;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16, CAP>), dim3((unsigned)grid), dim3(NW * 64),
+    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16, CAP, KV8>), dim3((unsigned)grid), dim3(NW * 64),
                        lds, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -234,18 +243,24 @@ hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool KV8>
 hipError_t launch_decode_cap(const DecodeParams& p, hipStream_t s) {
-    return p.cap_out > 0.f ? launch_decode_cfg<D, 4, BF16, true>(p, s)
-                           : launch_decode_cfg<D, 4, BF16, false>(p, s);
+    return p.cap_out > 0.f ? launch_decode_cfg<D, 4, BF16, true, KV8>(p, s)
+                           : launch_decode_cfg<D, 4, BF16, false, KV8>(p, s);
+}
+
+template <bool KV8>
+hipError_t launch_decode_kv(const DecodeParams& p, int head_size, bool bf16, hipStream_t s) {
+    if (head_size == 128)
+        return bf16 ? launch_decode_cap<128, true, KV8>(p, s) : launch_decode_cap<128, false, KV8>(p, s);
+    if (head_size == 64)
+        return bf16 ? launch_decode_cap<64, true, KV8>(p, s) : launch_decode_cap<64, false, KV8>(p, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s) {
-    if (head_size == 128)
-        return bf16 ? launch_decode_cap<128, true>(p, s) : launch_decode_cap<128, false>(p, s);
-    if (head_size == 64)
-        return bf16 ? launch_decode_cap<64, true>(p, s) : launch_decode_cap<64, false>(p, s);
-    return hipErrorInvalidValue;
+    return p.k8 != nullptr ? launch_decode_kv<true>(p, head_size, bf16, s)
+                           : launch_decode_kv<false>(p, head_size, bf16, s);
 }
 
 }  // namespace attn

@@ -321,6 +321,130 @@ struct PagedTile16 {
 };
 
 // ---------------------------------------------------------------------------
+// Paged K/V tile loader for an fp8 e4m3 cache (bytes, same page layout).
+//
+// Fills exactly the LDS tile PagedTile16 fills (16-bit K rows, V^T with key
+// slots swap23), converting each e4m3 code to the 16-bit type of the query
+// with v_cvt_scalef32_pk_{bf16,f16}_fp8 at scale 1: every e4m3 value is exact
+// in bf16 and in f16, so the products see the decoded codes unchanged; the
+// per-tensor descales are applied outside (K's to the score scale, V's to O).
+// Work per 32-key tile and 64 lanes: K in 16-byte chunks (16 codes), D/32
+// per lane; V in units of 4 keys x 16 dims (D/2 units: lanes below that take
+// one each), widened and transposed in registers like PagedTile16's 4 x 8
+// units.  Keys past kv_len read row kv_len - 1 and are zeroed when stored.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ u32x4_t widen_lo(u32x4_t c) {   // codes 0..7 of 16
+    u32x4_t r;
+    if constexpr (BF16) {
+        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.f, false));
+        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.f, true));
+        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.f, false));
+        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.f, true));
+    } else {
+        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.f, false));
+        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.f, true));
+        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.f, false));
+        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.f, true));
+    }
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ u32x4_t widen_hi(u32x4_t c) {   // codes 8..15 of 16
+    return widen_lo<BF16>(u32x4_t{c.z, c.w, 0u, 0u});
+}
+
+template <int D, bool BF16>
+struct PagedTile8 {
+    static constexpr int BN = 32;
+    static constexpr int CPR8 = D / 16;               // 16-byte fp8 chunks per key row
+    static constexpr int KPL = BN * CPR8 / 64;        // K chunks per lane
+    static constexpr int NVU = BN / 4 * CPR8;         // V units (4 keys x 16 dims)
+    static_assert(KPL >= 1 && BN * CPR8 % 64 == 0 && NVU <= 64, "tile does not fit one wave");
+    static constexpr int KP = k_pitch<D>();
+    static constexpr int VP = vt_pitch<BN>();
+    static constexpr int K_BYTES = BN * KP;
+    static constexpr int V_BYTES = D * VP;
+    static constexpr int BYTES = K_BYTES + V_BYTES;
+
+    u32x4_t kreg[KPL];
+    u32x4_t vreg[4];
+
+    __device__ __forceinline__ static u32x4_t ld(const uint8_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    }
+
+    // Issue the loads for keys [j0, j0 + 32) of one sequence (kv_len >= 1).
+    // win/first: block-table window; tok_stride = Hkv*D, head_off = hk*D
+    // (bytes = elements).
+    __device__ __forceinline__ void load(const uint8_t* __restrict__ cache_k,
+                                         const uint8_t* __restrict__ cache_v, const int* win,
+                                         int first, int j0, int kv_len, int bs_log2,
+                                         int tok_stride, int head_off, int lane) {
+        const int bs_mask = (1 << bs_log2) - 1;
+        const int last = kv_len - 1;
+        const int64_t page_stride = (int64_t)tok_stride << bs_log2;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / CPR8, c = idx % CPR8;
+            const int tok = min(j0 + row, last);
+            const int page = win[(tok >> bs_log2) - first];
+            kreg[i] = ld(cache_k + page * page_stride + ((tok & bs_mask) * tok_stride + head_off + c * 16));
+        }
+        if (NVU == 64 || lane < NVU) {
+            const int quad = lane % (BN / 4), dc = lane / (BN / 4);
+            const int tok0 = min(j0 + swap23(quad * 4), last);   // keys tok0 .. tok0+3, one page
+            const int page = win[(tok0 >> bs_log2) - first];
+            const uint8_t* src = cache_v + page * page_stride +
+                                 ((tok0 & bs_mask) * tok_stride + head_off + dc * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int step = (tok0 + e <= last) ? e : 0;
+                vreg[e] = ld(src + step * tok_stride);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(uint8_t* lds, int j0, int kv_len, int lane) const {
+        uint8_t* lk = lds;
+        uint8_t* lv = lds + K_BYTES;
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+            const int idx = lane + 64 * i;
+            const int row = idx / CPR8, c = idx % CPR8;
+            const bool in = j0 + row < kv_len;
+            *reinterpret_cast<u32x4_t*>(lk + row * KP + c * 32) = in ? widen_lo<BF16>(kreg[i]) : zero;
+            *reinterpret_cast<u32x4_t*>(lk + row * KP + c * 32 + 16) = in ? widen_hi<BF16>(kreg[i]) : zero;
+        }
+        if (NVU < 64 && lane >= NVU) return;
+        const int quad = lane % (BN / 4), dc = lane / (BN / 4);
+        const int tok0 = j0 + swap23(quad * 4);
+        uint8_t* dst = lv + (dc * 16) * VP + quad * 8;   // slots quad*4 .. quad*4+3
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            u32x4_t rows[4];   // 4 keys x 8 dims (16-bit) of dims half*8 .. half*8+7
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const u32x4_t w = half ? widen_hi<BF16>(vreg[e]) : widen_lo<BF16>(vreg[e]);
+                rows[e] = (tok0 + e < kv_len) ? w : zero;
+            }
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+                const int w = x >> 1;
+                u32x2_t out;
+                out.x = __builtin_amdgcn_perm(rows[1][w], rows[0][w], sel);
+                out.y = __builtin_amdgcn_perm(rows[3][w], rows[2][w], sel);
+                *reinterpret_cast<u32x2_t*>(dst + (half * 8 + x) * VP) = out;
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
 // Per-wave attention state for QB blocks of 32 query rows (one row per lane
 // column) and the tile step.
 //

@@ -41,8 +41,11 @@ struct PrefillParams {
 // Paged decode (16-bit dtypes): split kernel + combine kernel.
 struct DecodeParams {
     const uint16_t* q;          // [batch, Hq, D]
-    const uint16_t* k_cache;
+    const uint16_t* k_cache;    // 16-bit cache (null when k8 is set)
     const uint16_t* v_cache;
+    const uint8_t* k8;          // fp8 e4m3 cache (same layout, bytes) or null
+    const uint8_t* v8;
+    const float* kv_descale;    // [2] device (dk, dv) with k8
     const int32_t* block_table;
     const int32_t* cu_kv;
     float* part_o;              // [batch*Hq, max_splits, D]

@@ -12,7 +12,8 @@ weighted sum) divided by the step time.
 
 The same JSON line carries the prefill kernel's roofline figure, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and more single-GPU
-measurements: paged decode (HBM GB/s, with its own roofline figure), a plain
+measurements: paged decode (HBM GB/s, with its own roofline figure), the same
+decode over an fp8 e4m3 cache (one byte per element), a plain
 device-to-device copy (the practical HBM ceiling, and the calibration kernel
 for the traffic counters), byte->patch cross attention and dense causal fp8
 (TFLOP/s).
@@ -115,8 +116,9 @@ def paged_inputs(w, A, torch, dev):
     lens_q = i32(w.q_lens, torch, dev)
     lens_kv = i32(w.kv_lens, torch, dev)
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
-    kc = torch.full(shape, float("nan"), dtype=w.k_new.dtype, device=dev)
-    vc = torch.full(shape, float("nan"), dtype=w.k_new.dtype, device=dev)
+    poison = 0x7F if w.k_new.dtype == torch.uint8 else float("nan")   # NaN (e4m3 code 0x7F)
+    kc = torch.full(shape, poison, dtype=w.k_new.dtype, device=dev)
+    vc = torch.full(shape, poison, dtype=w.k_new.dtype, device=dev)
     bt = i32(w.block_table, torch, dev)
     return lens_q, lens_kv, kc, vc, bt
 
@@ -171,28 +173,37 @@ def bench_copy(torch, dev, nbytes=2 << 30, iters=10):
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
 
 
-def bench_decode(A, W, torch, dev, iters=20):
-    w = W.paged_gqa_decode_bf16(device=dev)
+def bench_decode(A, W, torch, dev, iters=20, fp8kv=False):
+    """Paged GQA decode; with fp8kv the cache holds e4m3 codes (one byte per
+    element, per-tensor descales) and the fp8-cache entry point runs."""
+    w = W.paged_gqa_decode_fp8kv(device=dev) if fp8kv else W.paged_gqa_decode_bf16(device=dev)
     lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
     cu_kv = A.attn_cu_seqlens(lens_kv)
     A.attn_reshape_and_cache(w.k_new, w.v_new, kc, vc, bt, cu_kv, cu_kv)
+    elem = w.k_new.element_size()
     del w.k_new, w.v_new
     maxkv = int(w.kv_lens.max())
     need = A.attn_paged_decode_workspace_bytes(w.batch, w.num_heads, w.num_kv_heads, w.head_size,
                                                maxkv)
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     out = torch.empty_like(w.q)
+    if fp8kv:
+        ds = torch.as_tensor(w.kv_descale, dtype=torch.float32).to(dev)
 
-    def run():
-        A.attn_paged_decode_fwd(w.q, kc, vc, bt, cu_kv, maxkv, scale=w.scale, out=out,
-                                workspace=ws)
+        def run():
+            A.attn_paged_decode_fp8kv_fwd(w.q, kc, vc, ds, bt, cu_kv, maxkv, scale=w.scale,
+                                          out=out, workspace=ws)
+    else:
+        def run():
+            A.attn_paged_decode_fwd(w.q, kc, vc, bt, cu_kv, maxkv, scale=w.scale, out=out,
+                                    workspace=ws)
 
     for _ in range(3):
         run()
     ms = timed(run, iters, torch)
     tokens = int(w.kv_lens.sum())
     used_blocks = int(sum(math.ceil(int(n) / w.block_size) for n in w.kv_lens))
-    nbytes = (2 * tokens * w.num_kv_heads * w.head_size * 2 + 2 * w.q.numel() * 2
+    nbytes = (2 * tokens * w.num_kv_heads * w.head_size * elem + 2 * w.q.numel() * 2
               + used_blocks * 4)
     gbs = nbytes / (ms * 1e-3) / 1e9
     res = {"workload": w.name, "ms": round(ms, 4), "GB/s": round(gbs, 1),
@@ -346,6 +357,9 @@ def main():
         line["hbm_copy"] = bench_copy(torch, dev)
         log("decode")
         line["decode"] = bench_decode(A, W, torch, dev)
+        torch.cuda.empty_cache()
+        log("decode, fp8 cache")
+        line["decode_fp8kv"] = bench_decode(A, W, torch, dev, fp8kv=True)
         torch.cuda.empty_cache()
         log("byte->patch cross attention")
         wc = W.byte_patch_cross_bf16(device=dev)

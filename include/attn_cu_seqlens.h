@@ -212,6 +212,32 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_paged_decode_fp8kv_fwd -- attn_paged_decode_fwd over an fp8 e4m3
+ * paged cache: the e4m3 format and per-tensor descales of the FlexAttention
+ * commit applied to the paged cache of the onnxruntime PR (the combination
+ * is this library's, not the pages').  Half the cache bytes per token.
+ *   k_cache8, v_cache8  uint8 e4m3 codes [num_blocks, block_size,
+ *                num_kv_heads, head_size] (attn_reshape_and_cache with
+ *                ATTN_FP8_E4M3 fills them)
+ *   kv_descale   float32 [2] (device): real K = kv_descale[0] * decoded code,
+ *                real V = kv_descale[1] * decoded code
+ *   q_dtype      ATTN_F16 or ATTN_BF16, the dtype of q and out
+ *   other arguments, the workspace (attn_paged_decode_workspace_bytes) and the
+ *   errors: as attn_paged_decode_fwd.
+ * Every e4m3 code is widened exactly to q's 16-bit type; scores, softmax and
+ * accumulation in fp32.
+ */
+attn_status attn_paged_decode_fp8kv_fwd(const void* q, const void* k_cache8, const void* v_cache8,
+                                        const float* kv_descale, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, const int32_t* cu_seqlens_kv,
+                                        int32_t batch, int32_t max_seqlen_kv, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_size,
+                                        int32_t block_size, int32_t num_blocks, float scale,
+                                        int32_t window_left, float softcap, int32_t split_tokens,
+                                        attn_dtype q_dtype, void* out, float* lse, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * attn_fp8_fwd -- dense varlen fp8 e4m3 attention with a column-major V.
  * The fp8 path of the FlexAttention commit: Q and K row-major, V column-major
  * so that the fp8 product softmax_scores @ V reads V contiguously along the

@@ -39,6 +39,7 @@ from .attention import (  # noqa: F401
     attention_varlen,
     paged_attention,
     paged_decode,
+    paged_decode_fp8kv,
     e4m3_decode,
     fp8_attention,
     default_scale,

@@ -58,6 +58,8 @@ PIN_STATUS = {
     "paged_attention": "pinned: equals attention_varlen on gathered K/V; block-table permutation invariance",
     "paged_decode": "pinned: equals the last row of a causal prefill over the same cache; a window "
                     "equals decode over the cache cut to its last W keys",
+    "paged_decode_fp8kv": "pinned: equals paged_decode on caches decoded by torch.float8_e4m3fn; "
+                          "hand-derived two-key example with distinct dk, dv; constant-V closed form",
     "e4m3_decode": "pinned: all 256 codes against torch.float8_e4m3fn; closed-form extremes",
     "fp8_attention": "pinned: equals attention_varlen on decoded values; hand-derived two-key example",
     "default_scale": "pinned: golden value 0.0625 at E=256 from [BLT]",
@@ -299,6 +301,25 @@ def e4m3_decode(codes):
             table[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
     flat_o[:] = table[flat_c]
     return out
+
+
+def paged_decode_fp8kv(q, k_cache8, v_cache8, kv_descale, block_table, cu_kv, block_size,
+                       scale, batches=None, window=0, softcap=0.0):
+    """Decode against a paged cache whose K and V hold fp8 e4m3 codes.
+
+    Combines two page features: the paged cache of [ORT] Implementation
+    (steps 1-2: tokens placed by reshape_and_cache, found through
+    block_table) and the e4m3 storage with per-tensor descales of [FLEX]
+    (the real tensor is descale times the decoded code).  The pages do not
+    combine them; the plain reading is that the cache holds codes, K is
+    dk * code and V is dv * code, and the query (fp16 / bf16) is unchanged.
+    k_cache8 / v_cache8: uint8 codes [num_blocks, block_size, Hkv, D];
+    kv_descale = (dk, dv).  Everything else as paged_decode.
+    """
+    dk, dv = (float(x) for x in kv_descale)
+    k = dk * e4m3_decode(k_cache8)
+    v = dv * e4m3_decode(v_cache8)
+    return paged_decode(q, k, v, block_table, cu_kv, block_size, scale, batches, window, softcap)
 
 
 def fp8_attention(q8, k8, v8_colmajor, descale, cu_q, cu_kv, scale, flags=0,

@@ -75,6 +75,20 @@ def oracle_decode(w, batches=None, window=0, softcap=0.0):
                             window, softcap)
 
 
+def oracle_decode_fp8kv(w, batches=None, window=0, softcap=0.0):
+    """Decode over the workload's fp8 cache: codes placed by the oracle's
+    reshape_and_cache into a cache of NaN codes (0x7F)."""
+    cu_kv = ORC.cu_seqlens(w.kv_lens)
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_size)
+    kc = np.full(shape, 0x7F, dtype=np.uint8)
+    vc = np.full(shape, 0x7F, dtype=np.uint8)
+    kc, vc = ORC.reshape_and_cache(w.k_new.cpu().numpy(), w.v_new.cpu().numpy(), kc, vc,
+                                   w.block_table, cu_kv, cu_kv, w.block_size)
+    q = w.q.double().cpu().numpy()
+    return ORC.paged_decode_fp8kv(q, kc, vc, w.kv_descale, w.block_table, cu_kv, w.block_size,
+                                  w.scale, batches, window, softcap)
+
+
 def oracle_fp8(w, rows=None, window=0, softcap=0.0):
     cu_q = ORC.cu_seqlens(w.q_lens)
     cu_kv = ORC.cu_seqlens(w.kv_lens)
@@ -125,6 +139,19 @@ def gpu_decode(w, A, split_tokens=0, cache=None, window=0, softcap=0.0):
                                        int(w.kv_lens.max(initial=0)), scale=w.scale,
                                        split_tokens=split_tokens, return_lse=True, window=window,
                                        softcap=softcap)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def gpu_decode_fp8kv(w, A, split_tokens=0, cache=None, window=0, softcap=0.0):
+    """Decode over the workload's fp8 cache, written by the library into a
+    cache poisoned with NaN codes."""
+    kc, vc, bt, cu_kv = cache if cache is not None else gpu_cache(w, A, poison=0x7F)
+    ds = torch.as_tensor(w.kv_descale, dtype=torch.float32).to(DEV)
+    out, lse = A.attn_paged_decode_fp8kv_fwd(w.q.to(DEV).contiguous(), kc, vc, ds, bt, cu_kv,
+                                             int(w.kv_lens.max(initial=0)), scale=w.scale,
+                                             split_tokens=split_tokens, return_lse=True,
+                                             window=window, softcap=softcap)
     torch.cuda.synchronize()
     return out, lse
 

@@ -131,6 +131,26 @@ def test_decode_host_checks(lib):
     assert call(batch=0) == 0
 
 
+def test_decode_fp8kv_host_checks(lib):
+    f = lib.attn_paged_decode_fp8kv_fwd
+    ws = lib.attn_paged_decode_workspace_bytes
+    need = ws(4, 8, 2, 128, 1000, 0, 256)
+
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, ds=P, bt=P, mbps=64, cukv=P, batch=4, mskv=1000, hq=8, hkv=2,
+                 d=128, bs=16, nb=300, scale=0.1, window=0, softcap=0.0, split=256, dtype=1,
+                 out=P, lse=None, ws=ctypes.c_void_p(256), wsb=need, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(ds=None) == 1                           # descales required
+    assert call(kc=None) == 1
+    assert call(dtype=2) == 3                           # q must be fp16 / bf16
+    assert call(wsb=need - 1) == 6
+    assert call(window=-1) == 2
+    assert call(batch=0) == 0
+
+
 def test_fp8_host_checks(lib):
     f = lib.attn_fp8_fwd
 

@@ -397,6 +397,48 @@ def check_fp8_attention(A):
     assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
 
 
+def check_decode_fp8kv(A):
+    """fp8 paged cache: a hand-derived two-key example whose dk and dv differ
+    (so a swap shows), a constant-V closed form, and a random paged case
+    against decode over caches that torch decodes from the same codes."""
+    one, two, nan_code = 0x38, 0x40, 0x7F
+    # page 1 holds the sequence, page 0 is NaN codes that must never be read
+    kc = np.full((2, 2, 1, 4), nan_code, dtype=np.uint8)
+    vc = np.full((2, 2, 1, 4), nan_code, dtype=np.uint8)
+    kc[1, 0, 0] = [one, 0, 0, 0]       # k0 = dk * (1, 0, 0, 0)
+    kc[1, 1, 0] = 0                    # k1 = 0
+    vc[1, 0, 0] = one                  # v0 = dv * 1
+    vc[1, 1, 0] = two                  # v1 = dv * 2
+    q = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    dk, dv, scale = 2.0 * math.log(3.0), 0.5, 0.5
+    # scores: scale * dk = ln 3 and 0, weights 3/4 and 1/4
+    out, lse = A.paged_decode_fp8kv(q, kc, vc, (dk, dv), np.array([[1]]), [0, 2], 2, scale)
+    assert np.allclose(out[0, 0], 0.75 * 0.5 + 0.25 * 1.0, rtol=0, atol=1e-14), out
+    assert abs(lse[0, 0] - math.log(4.0)) < 1e-14
+    # any keys, every V code 2.0: each output is exactly 2 dv
+    rng = np.random.default_rng(17)
+    bs, HQ, HKV, D = 4, 4, 2, 8
+    lens = np.array([7, 1, 10])
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    nb = 8
+    table = np.array([[5, 2, 0], [7, 0, 0], [1, 6, 3]], dtype=np.int32)
+    kc = rng.integers(0, 256, (nb, bs, HKV, D), dtype=np.uint8) & np.uint8(0xF7)
+    vc = np.full((nb, bs, HKV, D), two, dtype=np.uint8)
+    q = _rand(rng, 3, HQ, D)
+    out, _ = A.paged_decode_fp8kv(q, kc, vc, (0.3, 0.25), table, cu, bs, 0.2)
+    assert np.allclose(out, 0.5, rtol=0, atol=1e-14)
+    # random V, window and cap: decode over the torch-decoded, descaled caches
+    vc = rng.integers(0, 256, (nb, bs, HKV, D), dtype=np.uint8) & np.uint8(0xF7)
+    dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for window, cap in ((0, 0.0), (3, 0.0), (0, 2.0)):
+        out, lse = A.paged_decode_fp8kv(q, kc, vc, (0.3, 0.25), table, cu, bs, 0.2,
+                                        window=window, softcap=cap)
+        ref_o, ref_l = A.paged_decode(q, 0.3 * dec(kc), 0.25 * dec(vc), table, cu, bs, 0.2,
+                                      window=window, softcap=cap)
+        assert np.allclose(out, ref_o, rtol=1e-13, atol=1e-13)
+        assert np.allclose(lse, ref_l, rtol=1e-13, atol=1e-13)
+
+
 def check_window_bands(A):
     """Causal + window W: a band of W keys ending on the (bottom-right) diagonal,
     built here from np.tril / np.triu; without CAUSAL the window only bounds j
@@ -516,7 +558,7 @@ def test_pin_status_covers_exports():
     import oracle
     for name in ("cu_seqlens", "reshape_and_cache", "gather_paged", "visibility",
                  "attention_varlen", "paged_attention", "paged_decode", "e4m3_decode",
-                 "fp8_attention", "default_scale"):
+                 "fp8_attention", "default_scale", "paged_decode_fp8kv"):
         assert hasattr(oracle, name)
         assert "pinned" in ORC.PIN_STATUS[name]
 
@@ -658,6 +700,12 @@ def _mut_softcap_no_division(orig):
     return f
 
 
+def _mut_fp8kv_descales_swapped(orig):
+    def f(q, k8, v8, kv_descale, *a, **kw):
+        return orig(q, k8, v8, tuple(kv_descale)[::-1], *a, **kw)
+    return f
+
+
 MUTATIONS = {
     "causal_off_by_one": ("visibility", _mut_visibility_off_by_one),
     "causal_top_left": ("visibility", _mut_visibility_top_left),
@@ -676,6 +724,7 @@ MUTATIONS = {
     "window_one_extra_key": ("visibility", _mut_window_one_extra_key),
     "window_top_left": ("visibility", _mut_window_top_left),
     "softcap_no_division": ("attention_varlen", _mut_softcap_no_division),
+    "fp8kv_descales_swapped": ("paged_decode_fp8kv", _mut_fp8kv_descales_swapped),
 }
 
 

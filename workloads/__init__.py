@@ -58,6 +58,8 @@ class Workload:
     # fp8 workloads (dense, not paged)
     v8_colmajor: Optional[torch.Tensor] = None  # [Hkv, D, total_kv] uint8 codes
     descale: Optional[np.ndarray] = None        # float32 [3]: dq, dk, dv
+    # paged decode over an fp8 cache: k_new / v_new hold uint8 codes
+    kv_descale: Optional[np.ndarray] = None     # float32 [2]: dk, dv
     extra: dict = field(default_factory=dict)
 
     @property
@@ -213,6 +215,17 @@ def make_fp8(name, seed, q_lens, kv_lens, num_heads, num_kv_heads, head_size, ma
     return w
 
 
+def to_fp8_cache(w):
+    """Turn a paged workload's new K/V tokens into e4m3 codes with per-tensor
+    descales (quantize_e4m3); the query keeps its 16-bit type."""
+    k8, dk = quantize_e4m3(w.k_new.float())
+    v8, dv = quantize_e4m3(w.v_new.float())
+    w.k_new, w.v_new = k8, v8
+    w.kv_descale = np.asarray([dk, dv], dtype=np.float32)
+    w.name += "_fp8kv"
+    return w
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads and their scaled-down parity variants.
 # ---------------------------------------------------------------------------
@@ -242,6 +255,12 @@ def paged_gqa_decode_bf16(device="cpu", batch=64, lo=1024, hi=32768, seed=1003):
     lens = rng.integers(lo, hi, batch, endpoint=True).astype(np.int32)
     return make_decode(f"paged_gqa_decode_bf16_b{batch}_{lo}-{hi}", seed, "bf16", lens, 32, 8,
                        128, 16, device=device, rng=rng)
+
+
+def paged_gqa_decode_fp8kv(device="cpu", **kw):
+    """The paged GQA decode workload above with its K/V cache held as e4m3
+    codes (per-tensor descales); bf16 queries and output."""
+    return to_fp8_cache(paged_gqa_decode_bf16(device=device, **kw))
 
 
 def byte_patch_cross_bf16(device="cpu", batch=4, n_bytes=8192, n_keys=1024, seed=1004):

@@ -36,6 +36,8 @@ from .attention import (  # noqa: F401
     reshape_and_cache,
     gather_paged,
     visibility,
+    BlockMask,
+    block_visibility,
     attention_varlen,
     paged_attention,
     paged_decode,

@@ -36,7 +36,23 @@ Readings where the pages are silent (each is also listed in the design doc):
     applied to the scaled score before masking and softmax,
     s -> c * tanh(s / c) (c = 0 means no cap); LSE is taken over the capped
     scores.
+  * stored block-sparse masks: [BLT] (FlexAttention lowering arguments) and
+    [FLEX] (test graph inputs) show a BlockMask as kv_num_blocks /
+    kv_indices, full_kv_num_blocks / full_kv_indices, a Q and a KV block size
+    and a mask_mod.  Read for packed varlen sequences as: query block qb of a
+    sequence is its rows [qb*QB, (qb+1)*QB), key block kb its keys
+    [kb*KB, (kb+1)*KB); for each (sequence, mask head, qb) the first
+    kv_num entries of kv_indices are partial blocks, where the element mask
+    (the analytic masks above: causal, document, patch, window) decides, and
+    the first full_num entries of full_kv_indices are full blocks, visible
+    as a whole (the element mask is not evaluated, as FlexAttention skips
+    mask_mod there); every other block is invisible.  A block listed in both
+    lists counts as full.  Entries outside [0, ceil(kv_len / KB)) and counts
+    beyond the list capacity are ignored / clamped.  The mask's head count
+    is 1 (shared by all heads), Hkv (one list per kv head) or Hq.
 """
+
+import collections
 
 import math
 
@@ -56,6 +72,10 @@ PIN_STATUS = {
     "attention_varlen": "pinned: torch CPU fp64 SDPA (dense, GQA, banded window mask), closed forms "
                         "(incl. saturated softcap), invariants",
     "paged_attention": "pinned: equals attention_varlen on gathered K/V; block-table permutation invariance",
+    "block_visibility": "pinned: np.kron block expansion, every block partial equals the element mask, "
+                        "causal block lists give np.tril, full blocks override the element mask",
+    "attention_varlen(block_mask)": "pinned: torch CPU fp64 SDPA with the np.kron-built mask, per-head "
+                                    "lists (Hm = 1, Hkv, Hq) against per-head SDPA",
     "paged_decode": "pinned: equals the last row of a causal prefill over the same cache; a window "
                     "equals decode over the cache cut to its last W keys",
     "paged_decode_fp8kv": "pinned: equals paged_decode on caches decoded by torch.float8_e4m3fn; "
@@ -168,6 +188,57 @@ def visibility(q_len, kv_len, flags, q_ids=None, kv_ids=None, window=0):
     return vis
 
 
+BlockMask = collections.namedtuple(
+    "BlockMask", "q_block kv_block kv_num kv_idx full_num full_idx")
+BlockMask.__doc__ = """Stored block-sparse mask (module docstring, last reading).
+
+q_block, kv_block: block sizes in tokens; kv_num: int [batch, Hm, n_qb];
+kv_idx: int [batch, Hm, n_qb, cap]; full_num / full_idx the same shapes (or
+None: no full blocks)."""
+
+
+def block_visibility(elem_vis, q_block, kv_block, kv_num, kv_idx, full_num=None, full_idx=None):
+    """Boolean [q_len, kv_len] visibility of one sequence under one mask head.
+
+    elem_vis: the element mask ([q_len, kv_len], from ``visibility``), used
+    inside partial blocks.  kv_num [n_qb], kv_idx [n_qb, cap] (and the full
+    pair) are this sequence's and head's lists.  A full block is visible
+    wherever the key exists; a partial block where elem_vis says so.
+    """
+    q_len, kv_len = elem_vis.shape
+    n_kb = -(-kv_len // kv_block)
+    out = np.zeros((q_len, kv_len), dtype=bool)
+    for qb in range(-(-q_len // q_block)):
+        r0, r1 = qb * q_block, min(q_len, (qb + 1) * q_block)
+        if qb >= len(kv_num):
+            break
+        cap = kv_idx.shape[-1]
+        for kb in kv_idx[qb][:max(0, min(int(kv_num[qb]), cap))]:
+            kb = int(kb)
+            if 0 <= kb < n_kb:
+                c0, c1 = kb * kv_block, min(kv_len, (kb + 1) * kv_block)
+                out[r0:r1, c0:c1] |= elem_vis[r0:r1, c0:c1]
+        if full_num is None:
+            continue
+        for kb in full_idx[qb][:max(0, min(int(full_num[qb]), cap))]:
+            kb = int(kb)
+            if 0 <= kb < n_kb:
+                c0, c1 = kb * kv_block, min(kv_len, (kb + 1) * kv_block)
+                out[r0:r1, c0:c1] = True
+    return out
+
+
+def _mask_head(h, hq, hkv, hm):
+    """Which of the mask's Hm heads query head h uses (1, Hkv or Hq)."""
+    if hm == 1:
+        return 0
+    if hm == hq:
+        return h
+    if hm == hkv:
+        return h // (hq // hkv)
+    raise ValueError("block mask head count must be 1, num_kv_heads or num_heads")
+
+
 def _softmax_rows(s, vis, v):
     """O = softmax(s restricted to vis) @ v and LSE, row by row (fp64).
 
@@ -191,7 +262,7 @@ def _softmax_rows(s, vis, v):
 
 
 def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, rows=None,
-                     window=0, softcap=0.0):
+                     window=0, softcap=0.0, block_mask=None):
     """Varlen attention over packed (non-paged) K/V, fp64.
 
     q: [total_q, Hq, D]; k: [total_kv, Hkv, D]; v: [total_kv, Hkv, Dv];
@@ -206,6 +277,8 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
     used to sample outputs of full-size workloads.
     window, softcap: local window and score cap (module docstring); the cap
     acts on the scaled scores before the mask.
+    block_mask: optional BlockMask; the element mask then applies inside its
+    partial blocks only (``block_visibility``).
     Returns (out [total_q, Hq, Dv], lse [total_q, Hq]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -230,9 +303,18 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
             continue
         qi = None if q_ids is None else np.asarray(q_ids)[q0:q1]
         ki = None if kv_ids is None else np.asarray(kv_ids)[k0:k1]
-        vis = visibility(q_len, kv_len, flags, qi, ki, window)[sel]
+        elem = visibility(q_len, kv_len, flags, qi, ki, window)
+        vis = elem[sel]
         for h in range(hq):
             kvh = h // group
+            if block_mask is not None:
+                bm = block_mask
+                mh = _mask_head(h, hq, hkv, np.shape(bm.kv_num)[1])
+                vis = block_visibility(
+                    elem, bm.q_block, bm.kv_block, np.asarray(bm.kv_num)[b, mh],
+                    np.asarray(bm.kv_idx)[b, mh],
+                    None if bm.full_num is None else np.asarray(bm.full_num)[b, mh],
+                    None if bm.full_idx is None else np.asarray(bm.full_idx)[b, mh])[sel]
             s = scale * (q[q0 + sel, h, :] @ k[k0:k1, kvh, :].T)
             if softcap > 0:
                 s = softcap * np.tanh(s / softcap)
@@ -243,7 +325,8 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
 
 
 def paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, scale,
-                    flags=0, q_ids=None, kv_ids=None, rows=None, window=0, softcap=0.0):
+                    flags=0, q_ids=None, kv_ids=None, rows=None, window=0, softcap=0.0,
+                    block_mask=None):
     """Attention whose K/V live in a paged cache ([ORT] Implementation, step 2
     then step 3): gather each sequence's K/V through block_table into a packed
     buffer, then run ``attention_varlen`` on it.  Returns (out, lse) in fp64.
@@ -256,7 +339,8 @@ def paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, s
         vs.append(gather_paged(v_cache, block_table[b], kv_len, block_size))
     k = np.concatenate(ks, axis=0) if ks else np.zeros((0,) + tuple(k_cache.shape[2:]))
     v = np.concatenate(vs, axis=0) if vs else np.zeros((0,) + tuple(v_cache.shape[2:]))
-    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows, window, softcap)
+    return attention_varlen(q, k, v, cu_q, cu_kv, scale, flags, q_ids, kv_ids, rows, window, softcap,
+                            block_mask)
 
 
 def paged_decode(q, k_cache, v_cache, block_table, cu_kv, block_size, scale, batches=None,

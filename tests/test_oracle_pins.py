@@ -439,6 +439,129 @@ def check_decode_fp8kv(A):
         assert np.allclose(lse, ref_l, rtol=1e-13, atol=1e-13)
 
 
+def _block_lists(rng, blocks, cap, junk=True):
+    """Lists (counts [n_qb], indices [n_qb, cap]) holding the True entries of
+    the boolean block matrix ``blocks`` [n_qb, n_kb] in shuffled order, with
+    junk (out-of-range ids) after each count."""
+    n_qb = blocks.shape[0]
+    num = np.zeros(n_qb, dtype=np.int32)
+    idx = np.full((n_qb, cap), -7 if junk else 0, dtype=np.int32)
+    for qb in range(n_qb):
+        ids = rng.permutation(np.nonzero(blocks[qb])[0])
+        num[qb] = len(ids)
+        idx[qb, :len(ids)] = ids
+        if junk and len(ids) < cap:
+            idx[qb, len(ids):] = rng.choice([-1, blocks.shape[1], 10 ** 6], cap - len(ids))
+    return num, idx
+
+
+def _kron_mask(blocks, q_block, kv_block, q_len, kv_len):
+    return np.kron(blocks, np.ones((q_block, kv_block), dtype=bool))[:q_len, :kv_len].astype(bool)
+
+
+def check_block_visibility_kron(A):
+    """No element mask: visibility is the block matrix expanded by np.kron
+    (unequal block sizes, ragged edges, shuffled lists, junk past the count)."""
+    rng = np.random.default_rng(31)
+    q_len, kv_len, qbs, kbs = 23, 37, 3, 5
+    n_qb, n_kb = -(-q_len // qbs), -(-kv_len // kbs)
+    P = rng.random((n_qb, n_kb)) < 0.4
+    F = (rng.random((n_qb, n_kb)) < 0.3) & ~P
+    pn, pi = _block_lists(rng, P, n_kb + 2)
+    fn, fi = _block_lists(rng, F, n_kb + 2)
+    elem = np.ones((q_len, kv_len), dtype=bool)
+    got = A.block_visibility(elem, qbs, kbs, pn, pi, fn, fi)
+    assert np.array_equal(got, _kron_mask(P | F, qbs, kbs, q_len, kv_len))
+    # a count above the capacity reads the whole list and nothing beyond it
+    pn2 = pn.copy()
+    pn2[0] = 10 ** 6
+    got = A.block_visibility(elem, qbs, kbs, pn2, pi, None, None)
+    row0 = np.zeros((n_qb, n_kb), dtype=bool)
+    row0[0, [k for k in pi[0] if 0 <= k < n_kb]] = True
+    exp = _kron_mask(P & (np.arange(n_qb) > 0)[:, None] | row0, qbs, kbs, q_len, kv_len)
+    assert np.array_equal(got, exp)
+
+
+def check_block_all_partial_is_element_mask(A):
+    """Every block partial: the element mask alone (causal + window, q shorter
+    than kv; document ids)."""
+    rng = np.random.default_rng(32)
+    q_len, kv_len = 19, 45
+    for flags, window, qi, ki in ((ORC.MASK_CAUSAL, 9, None, None),
+                                  (ORC.MASK_DOCUMENT, 0, np.sort(rng.integers(0, 3, q_len)),
+                                   np.sort(rng.integers(0, 3, kv_len)))):
+        elem = A.visibility(q_len, kv_len, flags, qi, ki, window)
+        n_qb, n_kb = -(-q_len // 4), -(-kv_len // 8)
+        num, idx = _block_lists(rng, np.ones((n_qb, n_kb), dtype=bool), n_kb)
+        got = A.block_visibility(elem, 4, 8, num, idx)
+        assert np.array_equal(got, elem)
+
+
+def check_block_causal_lists(A):
+    """Causal block lists (diagonal partial, below it full) with a causal
+    element mask give np.tril; listing blocks above the diagonal as full
+    makes them wholly visible, as partial leaves them hidden."""
+    rng = np.random.default_rng(33)
+    L, bs = 30, 8
+    n = -(-L // bs)
+    P = np.eye(n, dtype=bool)
+    F = np.tril(np.ones((n, n), dtype=bool), -1)
+    pn, pi = _block_lists(rng, P, n)
+    fn, fi = _block_lists(rng, F, n)
+    elem = A.visibility(L, L, ORC.MASK_CAUSAL)
+    assert np.array_equal(A.block_visibility(elem, bs, bs, pn, pi, fn, fi),
+                          np.tril(np.ones((L, L), dtype=bool)))
+    up = np.triu(np.ones((n, n), dtype=bool), 2)
+    fn2, fi2 = _block_lists(rng, F | up, n)
+    exp = np.tril(np.ones((L, L), dtype=bool)) | _kron_mask(up, bs, bs, L, L)
+    assert np.array_equal(A.block_visibility(elem, bs, bs, pn, pi, fn2, fi2), exp)
+    pn3, pi3 = _block_lists(rng, P | up, n)
+    assert np.array_equal(A.block_visibility(elem, bs, bs, pn3, pi3, fn, fi),
+                          np.tril(np.ones((L, L), dtype=bool)))
+
+
+def check_block_sparse_attention_vs_sdpa(A):
+    """Two sequences, GQA 4/2, causal element mask, a BlockMask with one list
+    per mask head (Hm = 1, Hkv, Hq): each head against torch SDPA with the
+    explicit mask kron(F) | (kron(P) & tril)."""
+    rng = np.random.default_rng(34)
+    HQ, HKV, D, qbs, kbs = 4, 2, 8, 4, 8
+    lens = [21, 40]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = _rand(rng, cu[-1], HQ, D), _rand(rng, cu[-1], HKV, D), _rand(rng, cu[-1], HKV, D)
+    n_qb, n_kb = -(-max(lens) // qbs), -(-max(lens) // kbs)
+    for hm in (1, HKV, HQ):
+        Ps, Fs = {}, {}
+        kv_num = np.zeros((2, hm, n_qb), dtype=np.int32)
+        kv_idx = np.zeros((2, hm, n_qb, n_kb), dtype=np.int32)
+        full_num, full_idx = np.zeros_like(kv_num), np.zeros_like(kv_idx)
+        for b, L in enumerate(lens):
+            nq, nk = -(-L // qbs), -(-L // kbs)
+            for m in range(hm):
+                P = np.zeros((n_qb, n_kb), dtype=bool)
+                F = np.zeros((n_qb, n_kb), dtype=bool)
+                P[:nq, :nk] = rng.random((nq, nk)) < 0.5
+                F[:nq, :nk] = (rng.random((nq, nk)) < 0.3) & ~P[:nq, :nk]
+                for qb in range(nq):          # each row keeps its own key
+                    kb = (qb * qbs) // kbs
+                    if not F[qb, kb]:
+                        P[qb, kb] = True
+                Ps[b, m], Fs[b, m] = P, F
+                kv_num[b, m], kv_idx[b, m] = _block_lists(rng, P, n_kb, junk=False)
+                full_num[b, m], full_idx[b, m] = _block_lists(rng, F, n_kb, junk=False)
+        bm = A.BlockMask(qbs, kbs, kv_num, kv_idx, full_num, full_idx)
+        out, lse = A.attention_varlen(q, k, v, cu, cu, 0.3, ORC.MASK_CAUSAL, block_mask=bm)
+        for b, L in enumerate(lens):
+            for h in range(HQ):
+                m = 0 if hm == 1 else (h if hm == HQ else h // (HQ // HKV))
+                mask = (_kron_mask(Fs[b, m], qbs, kbs, L, L)
+                        | (_kron_mask(Ps[b, m], qbs, kbs, L, L) & np.tril(np.ones((L, L), dtype=bool))))
+                kvh = h // (HQ // HKV)
+                ref = _sdpa(q[cu[b]:cu[b + 1], h:h + 1], k[cu[b]:cu[b + 1], kvh:kvh + 1],
+                            v[cu[b]:cu[b + 1], kvh:kvh + 1], 0.3, attn_mask=mask)
+                assert np.allclose(out[cu[b]:cu[b + 1], h], ref[:, 0], rtol=1e-12, atol=1e-12), (hm, b, h)
+
+
 def check_window_bands(A):
     """Causal + window W: a band of W keys ending on the (bottom-right) diagonal,
     built here from np.tril / np.triu; without CAUSAL the window only bounds j
@@ -558,7 +681,7 @@ def test_pin_status_covers_exports():
     import oracle
     for name in ("cu_seqlens", "reshape_and_cache", "gather_paged", "visibility",
                  "attention_varlen", "paged_attention", "paged_decode", "e4m3_decode",
-                 "fp8_attention", "default_scale", "paged_decode_fp8kv"):
+                 "fp8_attention", "default_scale", "paged_decode_fp8kv", "block_visibility"):
         assert hasattr(oracle, name)
         assert "pinned" in ORC.PIN_STATUS[name]
 
@@ -706,6 +829,35 @@ def _mut_fp8kv_descales_swapped(orig):
     return f
 
 
+def _mut_block_full_masked(orig):
+    # full blocks treated like partial ones (element mask evaluated there too)
+    def f(elem_vis, q_block, kv_block, kv_num, kv_idx, full_num=None, full_idx=None):
+        out = orig(elem_vis, q_block, kv_block, kv_num, kv_idx, full_num, full_idx)
+        return out & elem_vis
+    return f
+
+
+def _mut_block_index_shift(orig):
+    def f(elem_vis, q_block, kv_block, kv_num, kv_idx, full_num=None, full_idx=None):
+        sh = lambda x: None if x is None else np.asarray(x) + 1
+        return orig(elem_vis, q_block, kv_block, kv_num, sh(kv_idx), full_num, sh(full_idx))
+    return f
+
+
+def _mut_block_sizes_swapped(orig):
+    def f(elem_vis, q_block, kv_block, *a, **kw):
+        return orig(elem_vis, kv_block, q_block, *a, **kw)
+    return f
+
+
+def _mut_mask_head_modulo(orig):
+    def f(h, hq, hkv, hm):
+        if hm == hkv and hm != hq and hm != 1:
+            return h % hkv
+        return orig(h, hq, hkv, hm)
+    return f
+
+
 MUTATIONS = {
     "causal_off_by_one": ("visibility", _mut_visibility_off_by_one),
     "causal_top_left": ("visibility", _mut_visibility_top_left),
@@ -725,6 +877,10 @@ MUTATIONS = {
     "window_top_left": ("visibility", _mut_window_top_left),
     "softcap_no_division": ("attention_varlen", _mut_softcap_no_division),
     "fp8kv_descales_swapped": ("paged_decode_fp8kv", _mut_fp8kv_descales_swapped),
+    "block_full_masked": ("block_visibility", _mut_block_full_masked),
+    "block_index_shift": ("block_visibility", _mut_block_index_shift),
+    "block_sizes_swapped": ("block_visibility", _mut_block_sizes_swapped),
+    "block_mask_head_modulo": ("_mask_head", _mut_mask_head_modulo),
 }
 
 

@@ -20,6 +20,7 @@ from .api import (  # noqa: F401
     attn_cu_seqlens,
     attn_reshape_and_cache,
     attn_paged_prefill_fwd,
+    attn_paged_prefill_block_sparse_fwd,
     attn_paged_decode_workspace_bytes,
     attn_paged_decode_fwd,
     attn_paged_decode_fp8kv_fwd,

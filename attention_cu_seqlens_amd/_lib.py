@@ -37,6 +37,10 @@ SIGNATURES = {
     "attn_paged_prefill_fwd": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _f32, _u32,
                                               _p, _p, _i32, _f32, ctypes.c_int, _p, _p, _p]),
+    "attn_paged_prefill_block_sparse_fwd": (
+        ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                       _i32, _i32, _f32, _u32, _p, _p, _i32, _f32, _i32, _i32, _i32, _i32, _i32,
+                       _p, _p, _p, _p, ctypes.c_int, _p, _p, _p]),
     "attn_paged_decode_workspace_bytes": (_size, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "attn_paged_decode_fwd": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _f32, _i32, _f32, _i32, ctypes.c_int,

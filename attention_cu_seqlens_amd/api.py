@@ -126,6 +126,61 @@ def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_se
     return (out, lse) if return_lse else out
 
 
+def attn_paged_prefill_block_sparse_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q,
+                                        cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, q_block,
+                                        kv_block, kv_num_blocks, kv_indices,
+                                        full_kv_num_blocks=None, full_kv_indices=None,
+                                        scale=None, mask_flags=0, q_ids=None, kv_ids=None,
+                                        out=None, return_lse=False, window=0, softcap=0.0):
+    """Paged varlen attention under a stored block-sparse mask: kv_num_blocks
+    int32 [batch, Hm, n_qb], kv_indices int32 [batch, Hm, n_qb, capacity]
+    (Hm = 1, num_kv_heads or num_heads); the full pair is optional."""
+    dev = q.device
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype, dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_kv", cu_seqlens_kv), ("kv_num_blocks", kv_num_blocks),
+                    ("kv_indices", kv_indices)):
+        _need(t, name, torch.int32, dev)
+    for name, t in (("q_ids", q_ids), ("kv_ids", kv_ids), ("full_kv_num_blocks", full_kv_num_blocks),
+                    ("full_kv_indices", full_kv_indices)):
+        if t is not None:
+            _need(t, name, torch.int32, dev)
+    if (full_kv_num_blocks is None) != (full_kv_indices is None):
+        raise ValueError("full_kv_num_blocks and full_kv_indices go together")
+    batch = cu_seqlens_q.numel() - 1
+    if kv_num_blocks.dim() != 3 or kv_num_blocks.shape[0] != batch:
+        raise ValueError("kv_num_blocks must be [batch, mask_heads, num_q_blocks]")
+    hm, n_qb = kv_num_blocks.shape[1], kv_num_blocks.shape[2]
+    if kv_indices.dim() != 4 or tuple(kv_indices.shape[:3]) != (batch, hm, n_qb):
+        raise ValueError("kv_indices must be [batch, mask_heads, num_q_blocks, capacity]")
+    cap = kv_indices.shape[3]
+    if full_kv_num_blocks is not None and (tuple(full_kv_num_blocks.shape) != (batch, hm, n_qb)
+                                           or tuple(full_kv_indices.shape) != tuple(kv_indices.shape)):
+        raise ValueError("the full lists must have the partial lists' shapes")
+    total_q, hq, d = q.shape
+    nb, bs, hkv, dk = k_cache.shape
+    if dk != d or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes disagree with q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_paged_prefill_block_sparse_fwd", lib.attn_paged_prefill_block_sparse_fwd(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+            _ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), batch, total_q, int(max_seqlen_q),
+            int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale), int(mask_flags), _ptr(q_ids),
+            _ptr(kv_ids), int(window), float(softcap), int(q_block), int(kv_block), hm, n_qb, cap,
+            _ptr(kv_num_blocks), _ptr(kv_indices), _ptr(full_kv_num_blocks),
+            _ptr(full_kv_indices), _DT[q.dtype], _ptr(out), _ptr(lse), _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
 def attn_paged_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_size, max_seqlen_kv,
                                       split_tokens=0, window=0):
     return int(_lib.load().attn_paged_decode_workspace_bytes(

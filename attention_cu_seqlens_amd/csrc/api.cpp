@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -141,15 +142,26 @@ attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, 
         batch, total_new, (int)row_bytes, ilog2(block_size), static_cast<hipStream_t>(stream)));
 }
 
-attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const void* v_cache,
-                                   const int32_t* block_table, int32_t max_blocks_per_seq,
-                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                                   int32_t batch, int32_t total_q, int32_t max_seqlen_q,
-                                   int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
-                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
-                                   float scale, uint32_t mask_flags, const int32_t* q_ids,
-                                   const int32_t* kv_ids, int32_t window_left, float softcap,
-                                   attn_dtype dtype, void* out, float* lse, void* stream) {
+namespace {
+
+// Stored block-sparse mask arguments (null kv_num: none).
+struct BlockSparseArgs {
+    int32_t q_block, kv_block, mask_heads, num_q_blocks, capacity;
+    const int32_t* kv_num;
+    const int32_t* kv_idx;
+    const int32_t* full_num;
+    const int32_t* full_idx;
+};
+
+attn_status prefill_impl(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
+                         int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                         int32_t block_size, int32_t num_blocks, float scale, uint32_t mask_flags,
+                         const int32_t* q_ids, const int32_t* kv_ids, int32_t window_left,
+                         float softcap, const BlockSparseArgs* bm, attn_dtype dtype, void* out,
+                         float* lse, void* stream) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
@@ -167,6 +179,26 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
         cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || out == nullptr)
         return ATTN_ERR_NULL_ARG;
     if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out)) return ATTN_ERR_BAD_SHAPE;
+    const int group = num_heads / num_kv_heads;
+    // a mask with one list per query head needs one head per workgroup
+    int pack_log2 = pack_log2_for_group(group);
+    int n_kb = 0;
+    if (bm != nullptr) {
+        if (bm->kv_num == nullptr || bm->kv_idx == nullptr) return ATTN_ERR_NULL_ARG;
+        if ((bm->full_num == nullptr) != (bm->full_idx == nullptr)) return ATTN_ERR_NULL_ARG;
+        if (!is_pow2(bm->q_block) || bm->q_block < 32 || bm->q_block > (1 << 30) ||
+            !is_pow2(bm->kv_block) || bm->kv_block < 64 || bm->kv_block > (1 << 30))
+            return ATTN_ERR_UNSUPPORTED;
+        if (bm->mask_heads != 1 && bm->mask_heads != num_kv_heads && bm->mask_heads != num_heads)
+            return ATTN_ERR_BAD_SHAPE;
+        if (bm->capacity <= 0 || bm->num_q_blocks <= 0 ||
+            (int64_t)bm->num_q_blocks * bm->q_block < max_seqlen_q)
+            return ATTN_ERR_BAD_SHAPE;
+        if (bm->mask_heads == num_heads && num_heads != num_kv_heads) pack_log2 = 0;
+        n_kb = (int)std::max<int64_t>(1, ((int64_t)max_seqlen_kv + bm->kv_block - 1) / bm->kv_block);
+        const int n_lq = std::max(1, (attn::kPrefillRows >> pack_log2) / bm->q_block);
+        if ((int64_t)n_lq * n_kb > attn::kBlockStateBytes) return ATTN_ERR_UNSUPPORTED;
+    }
     if (batch == 0 || total_q == 0) return ATTN_OK;
     const attn_status d = check_device();
     if (d != ATTN_OK) return d;
@@ -186,8 +218,8 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
     p.batch = batch;
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
-    p.group = num_heads / num_kv_heads;
-    p.pack_log2 = pack_log2_for_group(p.group);
+    p.group = group;
+    p.pack_log2 = pack_log2;
     p.n_head_groups = num_heads >> p.pack_log2;
     p.total_q = total_q;
     p.bs_log2 = ilog2(block_size);
@@ -195,8 +227,55 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
     p.c = scale * 1.4426950408889634f;
     p.window = window_left;
     set_cap(scale, softcap, p.cap_in2, p.cap_out);
+    if (bm != nullptr) {
+        p.bm_kv_num = bm->kv_num;
+        p.bm_kv_idx = bm->kv_idx;
+        p.bm_full_num = bm->full_num;
+        p.bm_full_idx = bm->full_idx;
+        p.bm_heads = bm->mask_heads;
+        p.bm_nqb = bm->num_q_blocks;
+        p.bm_cap = bm->capacity;
+        p.bm_n_kb = n_kb;
+        p.bm_qbs_log2 = ilog2(bm->q_block);
+        p.bm_kvbs_log2 = ilog2(bm->kv_block);
+    }
     return from_hip(attn::launch_paged_prefill(p, head_size, dtype == ATTN_BF16, max_seqlen_q,
                                                static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                   int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                   int32_t max_seqlen_kv, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t num_blocks,
+                                   float scale, uint32_t mask_flags, const int32_t* q_ids,
+                                   const int32_t* kv_ids, int32_t window_left, float softcap,
+                                   attn_dtype dtype, void* out, float* lse, void* stream) {
+    return prefill_impl(q, k_cache, v_cache, block_table, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_kv, batch, total_q, max_seqlen_q, max_seqlen_kv, num_heads,
+                        num_kv_heads, head_size, block_size, num_blocks, scale, mask_flags, q_ids,
+                        kv_ids, window_left, softcap, nullptr, dtype, out, lse, stream);
+}
+
+attn_status attn_paged_prefill_block_sparse_fwd(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, uint32_t mask_flags, const int32_t* q_ids,
+    const int32_t* kv_ids, int32_t window_left, float softcap, int32_t q_block, int32_t kv_block,
+    int32_t mask_heads, int32_t num_q_blocks, int32_t list_capacity,
+    const int32_t* kv_num_blocks, const int32_t* kv_indices, const int32_t* full_kv_num_blocks,
+    const int32_t* full_kv_indices, attn_dtype dtype, void* out, float* lse, void* stream) {
+    const BlockSparseArgs bm{q_block, kv_block, mask_heads, num_q_blocks, list_capacity,
+                             kv_num_blocks, kv_indices, full_kv_num_blocks, full_kv_indices};
+    return prefill_impl(q, k_cache, v_cache, block_table, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_kv, batch, total_q, max_seqlen_q, max_seqlen_kv, num_heads,
+                        num_kv_heads, head_size, block_size, num_blocks, scale, mask_flags, q_ids,
+                        kv_ids, window_left, softcap, &bm, dtype, out, lse, stream);
 }
 
 size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads,

@@ -36,7 +36,24 @@ struct PrefillParams {
     float c;                    // scale * log2(e)
     int window;                 // local window (keys), 0 = none
     float cap_in2, cap_out;     // score cap constants (SoftCap), cap_out == 0: none
+    // stored block-sparse mask (bm_kv_num null: none).  Lists per (sequence,
+    // mask head, query block): [batch, bm_heads, bm_nqb] counts and
+    // [batch, bm_heads, bm_nqb, bm_cap] kv-block ids; the full pair may be null.
+    const int32_t* bm_kv_num;
+    const int32_t* bm_kv_idx;
+    const int32_t* bm_full_num;
+    const int32_t* bm_full_idx;
+    int bm_heads;               // 1, num_kv_heads or num_heads
+    int bm_nqb;                 // query blocks per sequence in the arrays
+    int bm_cap;                 // list capacity
+    int bm_n_kb;                // ceil(max_seqlen_kv / kv block): state row length
+    int bm_qbs_log2, bm_kvbs_log2;
 };
+
+// Query rows (token x packed head) per prefill workgroup, and the bytes of
+// its block-sparse state: one byte per (local query block, key block).
+constexpr int kPrefillRows = 256;
+constexpr int kBlockStateBytes = 16384;
 
 // Paged decode (16-bit dtypes): split kernel + combine kernel.
 struct DecodeParams {

@@ -106,14 +106,22 @@ __device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t 
                                                                 v_tile, k_tile, hook);
 }
 
-template <int D, int BN, int QB, int NW, bool BF16, bool CAP>
+template <int D, int BN, int QB, int NW, bool BF16, bool CAP, bool BSP>
 __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     static_assert(QB == 1 && NW == 8, "two groups of four single-block waves");
     constexpr int BM = NW * 32;
+    static_assert(BM == kPrefillRows, "rows per workgroup as the host assumes");
+    static_assert(PAGE_WIN * 64 / BN <= NW * 64, "a chunk's tiles fit one per thread");
     using R = Ring16<D, BN, NW / 2>;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * R::STAGE];
     __shared__ int wave_range[2][NW];
     __shared__ int win[PAGE_WIN + 1];
+    // Stored block-sparse mask: the state of every key block for each query
+    // block the workgroup's rows touch (0 hidden, 1 partial, 2 full), and per
+    // key chunk the list of its tiles that some query block lists.
+    __shared__ uint8_t bstate[BSP ? kBlockStateBytes : 1];
+    __shared__ uint16_t tlist[BSP ? NW * 64 : 1];
+    __shared__ int bsum[NW + 2];
 
     int b, hg, qt;
     if (!map_tile(p.cu_q, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
@@ -190,7 +198,60 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         kv_begin = min(kv_begin, wave_range[0][i]);
         kv_end = max(kv_end, wave_range[1][i]);
     }
-    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin & ~15);
+    kv_begin &= ~15;
+
+    // Block-sparse: this wave's rows lie in one query block (its 32 >> pack
+    // tokens are aligned and a query block holds at least 32 tokens).  The
+    // key range becomes that of the listed blocks.
+    int lq_w = 0;
+    if constexpr (BSP) {
+        const int n_kb = p.bm_n_kb;
+        const int qb0 = tok0 >> p.bm_qbs_log2;
+        const int n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);
+        lq_w = ((tok0 + ((w * 32) >> p.pack_log2)) >> p.bm_qbs_log2) - qb0;
+        // key blocks of this sequence that have a state byte (a kv_len above
+        // max_seqlen_kv would otherwise run past the row)
+        const int n_kb_seq = min(n_kb, kv_len > 0 ? ((kv_len - 1) >> p.bm_kvbs_log2) + 1 : 0);
+        const int qb_last = q_len > 0 ? (q_len - 1) >> p.bm_qbs_log2 : -1;
+        const int mh = p.bm_heads == 1 ? 0 : (p.bm_heads == p.num_heads ? h0 : hk);
+        for (int i = tid; i < n_lq * n_kb; i += NW * 64) bstate[i] = 0;
+        if (tid == 0) {
+            bsum[NW] = 0x7fffffff;
+            bsum[NW + 1] = -1;
+        }
+        __syncthreads();
+        // partial lists first, then full ones: a block in both is full
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int32_t* num = pass ? p.bm_full_num : p.bm_kv_num;
+            const int32_t* idx = pass ? p.bm_full_idx : p.bm_kv_idx;
+            if (num != nullptr) {
+                for (int lq = 0; lq < n_lq; ++lq) {
+                    const int qb = qb0 + lq;
+                    if (qb > qb_last || qb >= p.bm_nqb) break;
+                    const int64_t row = ((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb;
+                    const int cnt = min(max(num[row], 0), p.bm_cap);
+                    for (int i = tid; i < cnt; i += NW * 64) {
+                        const int kb = idx[row * p.bm_cap + i];
+                        if (kb >= 0 && kb < n_kb_seq) {
+                            bstate[lq * n_kb + kb] = (uint8_t)(pass + 1);
+                            atomicMin(&bsum[NW], kb);
+                            atomicMax(&bsum[NW + 1], kb);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+        const int kb_lo = bsum[NW], kb_hi = bsum[NW + 1];
+        if (kb_hi < kb_lo) {
+            kv_begin = kv_end = 0;
+        } else {
+            kv_begin = kb_lo << p.bm_kvbs_log2;
+            kv_end = (int)min((int64_t)kv_len, (int64_t)(kb_hi + 1) << p.bm_kvbs_log2);
+        }
+    }
+    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin);
     kv_end = __builtin_amdgcn_readfirstlane(kv_end);
 
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
@@ -236,17 +297,44 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
             u32x4_t{0u, 0u, 0u, 0u};
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
-        const int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
+        int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
         fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+        if constexpr (BSP) {
+            // compact the chunk's listed tiles (thread t looks at tile t)
+            bool on = false;
+            if (tid < n) {
+                const int kb = (cs + tid * BN) >> p.bm_kvbs_log2;
+                const int n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);
+                for (int lq = 0; lq < n_lq; ++lq) on |= bstate[lq * p.bm_n_kb + kb] != 0;
+            }
+            const uint64_t bal = __ballot(on);
+            if (lane == 0) bsum[w] = __popcll(bal);
+            __syncthreads();
+            int off = 0, tot = 0;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                off += i < w ? bsum[i] : 0;
+                tot += bsum[i];
+            }
+            if (on) tlist[off + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)tid;
+            n = tot;
+        }
         __syncthreads();
+        // key offset of the chunk's k-th tile (listed tiles only when sparse)
+        auto tile_key = [&](int k) {
+            if constexpr (BSP) return cs + (int)tlist[max(0, min(k, n - 1))] * BN;
+            else return cs + k * BN;
+        };
         if (lead) {
 #pragma unroll
             for (int k = 0; k < kStages - 1; ++k)
-                if (k < n)
-                    ld.issue(ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first, cs + k * BN,
+                if (k < n) {
+                    const int jk = tile_key(k);
+                    ld.issue(ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first, jk,
                              kv_len, p.bs_log2, tok_stride, head_off, w,
-                             win[R::slot(cs + k * BN, first, p.bs_log2, w)]);
+                             win[R::slot(jk, first, p.bs_log2, w)]);
+                }
             // tile 0 must have landed; tiles 1 and 2 may stay in flight
             static_assert(kStages == 4, "wait counts below");
             if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
@@ -257,17 +345,30 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         if (lead) step_mfma<D, BN, BF16, false, true>(st, q, ring, ring);
 
         for (int jt = 0; jt < n; ++jt) {
-            const int j0 = cs + jt * BN;
-            const bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
+            const int j0 = tile_key(jt);
+            bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
+            int lo_t = lo, hi_t = hi;   // this tile's visible interval per row
+            if constexpr (BSP) {
+                const int stt = __builtin_amdgcn_readfirstlane(
+                    bstate[lq_w * p.bm_n_kb + (j0 >> p.bm_kvbs_log2)]);
+                if (stt == 2) {          // full block: every existing key
+                    lo_t = 0;
+                    hi_t = valid ? kv_len : 0;
+                    partial = j0 + BN > kv_len;
+                } else if (stt == 0) {   // not listed for this wave's rows
+                    lo_t = hi_t = 0;
+                    partial = true;
+                }
+            }
             const uint8_t* st_cur = ring + (jt % kStages) * R::STAGE;
             const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
             const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
             // phase 1
             if (lead)
-                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo, hi, c, st_cur + R::TILE,
+                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
                                                 p.cap_in2, p.cap_out);
             else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
-            const int j3 = cs + (jt + kStages - 1) * BN;
+            const int j3 = tile_key(jt + kStages - 1);
             const bool load3 = lead && jt + kStages - 1 < n;
             int page = 0;
             if (load3) page = win[R::slot(j3, first, p.bs_log2, w)];
@@ -292,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next,
                                                    Hook{ld, sr, st3, w, spread});
             } else {
-                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo, hi, c, st_cur + R::TILE,
+                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
                                                 p.cap_in2, p.cap_out);
             }
             block_barrier();
@@ -317,7 +418,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 
 namespace {
 
-template <int D, int BN, int QB, int NW, bool BF16, bool CAP>
+template <int D, int BN, int QB, int NW, bool BF16, bool CAP, bool BSP>
 hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) {
     constexpr int BM = NW * QB * 32;
     PrefillParams p = p0;
@@ -327,7 +428,7 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
                                            tokens_per_tile);
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP>), dim3((unsigned)grid),
+    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP, BSP>), dim3((unsigned)grid),
                        dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
@@ -345,10 +446,19 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
 
 namespace {
 
+template <int D, int BN, int QB, int NW, bool BF16, bool BSP>
+hipError_t launch_sparse(const PrefillParams& p, int max_seqlen_q, hipStream_t s) {
+    return p.cap_out > 0.f ? launch_cfg<D, BN, QB, NW, BF16, true, BSP>(p, max_seqlen_q, s)
+                           : launch_cfg<D, BN, QB, NW, BF16, false, BSP>(p, max_seqlen_q, s);
+}
+
 template <int D, int BN, int QB, int NW, bool BF16>
 hipError_t launch_cap(const PrefillParams& p, int max_seqlen_q, hipStream_t s) {
-    return p.cap_out > 0.f ? launch_cfg<D, BN, QB, NW, BF16, true>(p, max_seqlen_q, s)
-                           : launch_cfg<D, BN, QB, NW, BF16, false>(p, max_seqlen_q, s);
+    if (p.bm_kv_num != nullptr) {
+        static_assert(BN == 64, "block-sparse key blocks are multiples of 64 keys");
+        return launch_sparse<D, BN, QB, NW, BF16, true>(p, max_seqlen_q, s);
+    }
+    return launch_sparse<D, BN, QB, NW, BF16, false>(p, max_seqlen_q, s);
 }
 
 }  // namespace

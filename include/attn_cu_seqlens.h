@@ -173,6 +173,52 @@ attn_status attn_paged_prefill_fwd(const void* q, const void* k_cache, const voi
                                    attn_dtype dtype, void* out, float* lse, void* stream);
 
 /*
+ * attn_paged_prefill_block_sparse_fwd -- attn_paged_prefill_fwd under a
+ * stored block-sparse mask: the BlockMask of FlexAttention as the blt issue's
+ * lowering arguments and the FlexAttention commit's test graph show it
+ * (partial and full kv-block lists per query block, block sizes, mask_mod),
+ * applied per packed varlen sequence.  Query block qb of a sequence is its
+ * rows [qb*q_block, (qb+1)*q_block), key block kb its keys
+ * [kb*kv_block, (kb+1)*kv_block).  For a (sequence, mask head, query block)
+ * the first kv_num_blocks entries of kv_indices are partial blocks, where
+ * mask_flags / window_left decide per element, and the first
+ * full_kv_num_blocks entries of full_kv_indices are full blocks, visible
+ * wherever the key exists (the element mask is not evaluated there, as
+ * FlexAttention skips mask_mod on full blocks); every other block is hidden.
+ * A block in both lists counts as full.  Ids outside
+ * [0, ceil(kv_len / kv_block)) are ignored; counts are clamped to
+ * [0, list_capacity].
+ *   q_block      power of two, 32 .. 2^30;  kv_block  power of two, 64 .. 2^30
+ *   mask_heads   1 (one mask for all heads), num_kv_heads (one per kv head)
+ *                or num_heads (one per query head)
+ *   num_q_blocks query blocks per sequence in the arrays, at least
+ *                ceil(max_seqlen_q / q_block);  list_capacity  entries per list
+ *   kv_num_blocks, full_kv_num_blocks  int32 [batch, mask_heads, num_q_blocks]
+ *   kv_indices, full_kv_indices  int32 [batch, mask_heads, num_q_blocks,
+ *                list_capacity]; the full pair may both be NULL (no full
+ *                blocks).  Device memory, read only, owned by the caller.
+ * Other arguments as attn_paged_prefill_fwd.  Limit: a workgroup keeps one
+ * byte per (query block it touches, key block) in LDS, so
+ * max(1, rows / q_block) * ceil(max_seqlen_kv / kv_block) <= 16384 with rows
+ * = 256 / (query heads packed per kv head: the largest power of two up to 8
+ * dividing num_heads / num_kv_heads, 1 when mask_heads == num_heads);
+ * beyond it ATTN_ERR_UNSUPPORTED.  Errors: as attn_paged_prefill_fwd, plus
+ * ATTN_ERR_NULL_ARG for a missing list (or half of the full pair),
+ * ATTN_ERR_UNSUPPORTED for block sizes, ATTN_ERR_BAD_SHAPE for mask_heads,
+ * num_q_blocks or list_capacity.
+ */
+attn_status attn_paged_prefill_block_sparse_fwd(
+    const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+    int32_t num_heads, int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+    int32_t num_blocks, float scale, uint32_t mask_flags, const int32_t* q_ids,
+    const int32_t* kv_ids, int32_t window_left, float softcap, int32_t q_block, int32_t kv_block,
+    int32_t mask_heads, int32_t num_q_blocks, int32_t list_capacity,
+    const int32_t* kv_num_blocks, const int32_t* kv_indices, const int32_t* full_kv_num_blocks,
+    const int32_t* full_kv_indices, attn_dtype dtype, void* out, float* lse, void* stream);
+
+/*
  * attn_paged_decode_workspace_bytes -- workspace size attn_paged_decode_fwd
  * needs for these sizes (same window_left and split_tokens arguments).  Host
  * only, no HIP call.  Returns 0 for invalid sizes.

@@ -47,7 +47,7 @@ def banner(msg):
 
 # ---------------------------------------------------------------- oracle side
 
-def oracle_prefill(w, rows=None, window=0, softcap=0.0):
+def oracle_prefill(w, rows=None, window=0, softcap=0.0, block_mask=None):
     cu_q = ORC.cu_seqlens(w.q_lens)
     cu_kv = ORC.cu_seqlens(w.kv_lens)
     cu_new = ORC.cu_seqlens(w.new_lens)
@@ -59,7 +59,8 @@ def oracle_prefill(w, rows=None, window=0, softcap=0.0):
     kc, vc = ORC.reshape_and_cache(k, v, kc, vc, w.block_table, cu_new, cu_kv, w.block_size)
     q = w.q.double().cpu().numpy()
     return ORC.paged_attention(q, kc, vc, w.block_table, cu_q, cu_kv, w.block_size, w.scale,
-                               w.mask_flags, w.q_ids, w.kv_ids, rows, window, softcap)
+                               w.mask_flags, w.q_ids, w.kv_ids, rows, window, softcap,
+                               None if block_mask is None else ORC.BlockMask(*block_mask))
 
 
 def oracle_decode(w, batches=None, window=0, softcap=0.0):
@@ -127,6 +128,24 @@ def gpu_prefill(w, A, cache=None, scale=None, block_table=None, window=0, softca
     out, lse = A.attn_paged_prefill_fwd(
         w.q.to(DEV).contiguous(), kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max(initial=0)),
         int(w.kv_lens.max(initial=0)), scale=w.scale if scale is None else scale,
+        mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, return_lse=True, window=window,
+        softcap=softcap)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def gpu_prefill_sparse(w, A, block_mask, cache=None, window=0, softcap=0.0):
+    """block_mask: (q_block, kv_block, kv_num, kv_idx, full_num, full_idx),
+    numpy arrays (the full pair may be None)."""
+    kc, vc, bt, cu_kv = cache if cache is not None else gpu_cache(w, A)
+    qbs, kbs, kn, ki, fn, fi = block_mask
+    cu_q = A.attn_cu_seqlens(_i32(w.q_lens))
+    q_ids = None if w.q_ids is None else _i32(w.q_ids)
+    kv_ids = None if w.kv_ids is None else _i32(w.kv_ids)
+    out, lse = A.attn_paged_prefill_block_sparse_fwd(
+        w.q.to(DEV).contiguous(), kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max(initial=0)),
+        int(w.kv_lens.max(initial=0)), qbs, kbs, _i32(kn), _i32(ki),
+        None if fn is None else _i32(fn), None if fi is None else _i32(fi), scale=w.scale,
         mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, return_lse=True, window=window,
         softcap=softcap)
     torch.cuda.synchronize()

@@ -100,6 +100,43 @@ def test_prefill_host_checks(lib):
     assert f(*_prefill_args(total_q=0)) == 0
 
 
+def _sparse_args(**kw):
+    a = dict(q=P, kc=P, vc=P, bt=P, mbps=8, cuq=P, cukv=P, batch=2, total_q=100, msq=64, mskv=64,
+             hq=8, hkv=2, d=128, bs=16, nb=32, scale=0.1, mask=1, qids=None, kvids=None, window=0,
+             softcap=0.0, qblk=128, kvblk=128, mheads=2, nqb=1, cap=1, knum=P, kidx=P, fnum=None,
+             fidx=None, dtype=1, out=P, lse=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def test_block_sparse_prefill_host_checks(lib):
+    f = lib.attn_paged_prefill_block_sparse_fwd
+    assert f(*_sparse_args(batch=0)) == 0
+    assert f(*_sparse_args(batch=0, mheads=1, fnum=P, fidx=P)) == 0
+    assert f(*_sparse_args(batch=0, mheads=8)) == 0      # one list per query head
+    assert f(*_sparse_args(knum=None)) == 1
+    assert f(*_sparse_args(kidx=None)) == 1
+    assert f(*_sparse_args(fnum=P)) == 1                 # half of the full pair
+    assert f(*_sparse_args(qblk=96)) == 3                # not a power of two
+    assert f(*_sparse_args(qblk=16)) == 3                # below 32 rows
+    assert f(*_sparse_args(kvblk=32)) == 3               # below 64 keys
+    assert f(*_sparse_args(kvblk=(1 << 31) - 1)) == 3   # not a power of two
+    assert f(*_sparse_args(batch=0, qblk=1 << 30, kvblk=1 << 30)) == 0
+    assert f(*_sparse_args(mheads=4)) == 2               # neither 1, Hkv nor Hq
+    assert f(*_sparse_args(nqb=0)) == 2
+    assert f(*_sparse_args(msq=129, nqb=1)) == 2         # too few query blocks for 129 rows
+    assert f(*_sparse_args(cap=0)) == 2
+    # LDS state: 256 rows / 4 heads packed = 64 tokens -> 2 blocks of 32 rows;
+    # 2 x 8192 key blocks of 64 keys fit, 2 x 8193 do not
+    assert f(*_sparse_args(batch=0, qblk=32, kvblk=64, nqb=2, mskv=8192 * 64,
+                              mbps=8192 * 4)) == 0
+    assert f(*_sparse_args(qblk=32, kvblk=64, nqb=2, mskv=8193 * 64,
+                              mbps=8193 * 4)) == 3
+    # the element-mask checks of the plain prefill still apply
+    assert f(*_sparse_args(mask=2)) == 1
+    assert f(*_sparse_args(window=-1)) == 2
+
+
 def test_decode_host_checks(lib):
     ws = lib.attn_paged_decode_workspace_bytes
     assert ws(64, 32, 8, 128, 32768, 0, 0) > 0

@@ -226,6 +226,67 @@ def to_fp8_cache(w):
     return w
 
 
+def causal_block_mask(q_lens, kv_lens, q_block, kv_block, heads=1):
+    """Block lists of a bottom-right causal mask (query i sees key j iff
+    j <= i + kv_len - q_len): a key block is full for a query block when the
+    block's first row sees its last key, partial when its last row sees its
+    first key, hidden otherwise.  Returns int32 arrays kv_num [B, heads, n_qb],
+    kv_idx [B, heads, n_qb, n_kb], full_num, full_idx (ids in increasing
+    order, zeros past each count)."""
+    q_lens, kv_lens = np.asarray(q_lens), np.asarray(kv_lens)
+    B = len(q_lens)
+    n_qb = max(1, -(-int(q_lens.max(initial=0)) // q_block))
+    n_kb = max(1, -(-int(kv_lens.max(initial=0)) // kv_block))
+    kv_num = np.zeros((B, heads, n_qb), np.int32)
+    kv_idx = np.zeros((B, heads, n_qb, n_kb), np.int32)
+    full_num, full_idx = np.zeros_like(kv_num), np.zeros_like(kv_idx)
+    for b in range(B):
+        ql, kl = int(q_lens[b]), int(kv_lens[b])
+        off = kl - ql
+        for qb in range(-(-ql // q_block)):
+            r0, r1 = qb * q_block, min(ql, (qb + 1) * q_block)
+            part, full = [], []
+            for kb in range(-(-kl // kv_block)):
+                c0, c1 = kb * kv_block, min(kl, (kb + 1) * kv_block)
+                if c1 - 1 <= r0 + off:
+                    full.append(kb)
+                elif c0 <= r1 - 1 + off:
+                    part.append(kb)
+            kv_num[b, :, qb], full_num[b, :, qb] = len(part), len(full)
+            kv_idx[b, :, qb, :len(part)] = part
+            full_idx[b, :, qb, :len(full)] = full
+    return kv_num, kv_idx, full_num, full_idx
+
+
+def random_block_mask(rng, q_lens, kv_lens, q_block, kv_block, heads, p_partial=0.4, p_full=0.3,
+                      capacity=None, junk=True):
+    """Random block lists: each (sequence, head, query block, key block) is
+    partial with probability p_partial, else full with p_full, else hidden;
+    lists in shuffled order, padded with out-of-range ids (-1, a block past
+    the sequence, 10**6) when junk is set."""
+    q_lens, kv_lens = np.asarray(q_lens), np.asarray(kv_lens)
+    B = len(q_lens)
+    n_qb = max(1, -(-int(q_lens.max(initial=0)) // q_block))
+    n_kb = max(1, -(-int(kv_lens.max(initial=0)) // kv_block))
+    cap = n_kb + 2 if capacity is None else capacity
+    kv_num = np.zeros((B, heads, n_qb), np.int32)
+    kv_idx = np.zeros((B, heads, n_qb, cap), np.int32)
+    full_num, full_idx = np.zeros_like(kv_num), np.zeros_like(kv_idx)
+    for b in range(B):
+        nk = -(-int(kv_lens[b]) // kv_block)
+        for h in range(heads):
+            for qb in range(n_qb):
+                u = rng.random(nk)
+                part = rng.permutation(np.nonzero(u < p_partial)[0])[:cap]
+                full = rng.permutation(np.nonzero((u >= p_partial) & (u < p_partial + p_full))[0])[:cap]
+                for num, idx, ids in ((kv_num, kv_idx, part), (full_num, full_idx, full)):
+                    num[b, h, qb] = len(ids)
+                    idx[b, h, qb, :len(ids)] = ids
+                    if junk and len(ids) < cap:
+                        idx[b, h, qb, len(ids):] = rng.choice([-1, nk, 10 ** 6], cap - len(ids))
+    return kv_num, kv_idx, full_num, full_idx
+
+
 # ---------------------------------------------------------------------------
 # The five named workloads and their scaled-down parity variants.
 # ---------------------------------------------------------------------------

@@ -119,9 +119,11 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     // Stored block-sparse mask: the state of every key block for each query
     // block the workgroup's rows touch (0 hidden, 1 partial, 2 full), and per
     // key chunk the list of its tiles that some query block lists.
-    __shared__ uint8_t bstate[BSP ? kBlockStateBytes : 1];
+    __shared__ uint32_t bstate[BSP ? kBlockStateBytes / 4 : 1];
     __shared__ uint16_t tlist[BSP ? NW * 64 : 1];
     __shared__ int bsum[NW + 2];
+    __shared__ int bcnt[BSP ? 16 : 1];
+    const uint8_t* bstate8 = reinterpret_cast<const uint8_t*>(bstate);
 
     int b, hg, qt;
     if (!map_tile(p.cu_q, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
@@ -139,6 +141,28 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const float c = fabsf(p.c);
 
     const int tid = threadIdx.x;
+    // Block-sparse set-up, first half: the list counts of the query blocks
+    // this workgroup touches are loaded here, so their latency overlaps the
+    // Q loads and interval searches below; the state words are cleared.
+    int bm_cnt = 0;
+    int n_lq = 1, qb0 = 0, mh = 0;
+    if constexpr (BSP) {
+        n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);   // at most 8
+        qb0 = tok0 >> p.bm_qbs_log2;
+        mh = p.bm_heads == 1 ? 0 : (p.bm_heads == p.num_heads ? h0 : hk);
+        const int qb_last = q_len > 0 ? (q_len - 1) >> p.bm_qbs_log2 : -1;
+        if (tid < 2 * n_lq) {
+            const int pass = tid >= n_lq, qb = qb0 + tid - pass * n_lq;
+            const int32_t* num = pass ? p.bm_full_num : p.bm_kv_num;
+            if (num != nullptr && qb <= qb_last && qb < p.bm_nqb)
+                bm_cnt = min(max(num[((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb], 0), p.bm_cap);
+        }
+        for (int i = tid; i < (n_lq * p.bm_n_kb + 3) / 4; i += NW * 64) bstate[i] = 0u;
+        if (tid == 0) {
+            bsum[NW] = 0x7fffffff;
+            bsum[NW + 1] = -1;
+        }
+    }
     const int lane = lane_id();
     const int w = wave_id();
     const int col = lane & 31, g = lane >> 5;
@@ -191,6 +215,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
         wave_range[1][w] = w_any ? w_hi : -0x7fffffff;
     }
+    if (BSP && tid < 2 * n_lq) bcnt[tid] = bm_cnt;
     __syncthreads();
     int kv_begin = 0x7fffffff, kv_end = -0x7fffffff;
 #pragma unroll
@@ -200,49 +225,40 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     }
     kv_begin &= ~15;
 
-    // Block-sparse: this wave's rows lie in one query block (its 32 >> pack
-    // tokens are aligned and a query block holds at least 32 tokens).  The
-    // key range becomes that of the listed blocks.
+    // The element mask's key range, [el_lo, el_hi): a partial block's tiles
+    // outside it hold no visible key for any row of the workgroup.
+    const int el_lo = kv_begin, el_hi = kv_end;
+
+    // Block-sparse set-up, second half: read the listed block ids (flattened
+    // over the 2 * n_lq lists) and set their state bits, bit 0 partial and
+    // bit 1 full, one byte per (local query block, key block); a block in
+    // both lists reads as full.  This wave's rows lie in one query block
+    // (its 32 >> pack tokens are aligned and a query block holds at least
+    // 32 tokens).  The key range becomes that of the listed blocks.
     int lq_w = 0;
     if constexpr (BSP) {
         const int n_kb = p.bm_n_kb;
-        const int qb0 = tok0 >> p.bm_qbs_log2;
-        const int n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);
         lq_w = ((tok0 + ((w * 32) >> p.pack_log2)) >> p.bm_qbs_log2) - qb0;
         // key blocks of this sequence that have a state byte (a kv_len above
         // max_seqlen_kv would otherwise run past the row)
         const int n_kb_seq = min(n_kb, kv_len > 0 ? ((kv_len - 1) >> p.bm_kvbs_log2) + 1 : 0);
-        const int qb_last = q_len > 0 ? (q_len - 1) >> p.bm_qbs_log2 : -1;
-        const int mh = p.bm_heads == 1 ? 0 : (p.bm_heads == p.num_heads ? h0 : hk);
-        for (int i = tid; i < n_lq * n_kb; i += NW * 64) bstate[i] = 0;
-        if (tid == 0) {
-            bsum[NW] = 0x7fffffff;
-            bsum[NW + 1] = -1;
+        int total = 0;
+        for (int k = 0; k < 2 * n_lq; ++k) total += bcnt[k];
+        for (int e = tid; e < total; e += NW * 64) {
+            int k = 0, base = 0;
+            while (e >= base + bcnt[k]) base += bcnt[k++];
+            const int pass = k >= n_lq, lq = k - pass * n_lq;
+            const int32_t* idx = pass ? p.bm_full_idx : p.bm_kv_idx;
+            const int64_t row = ((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb0 + lq;
+            const int kb = idx[row * p.bm_cap + (e - base)];
+            if (kb >= 0 && kb < n_kb_seq) {
+                const int at = lq * n_kb + kb;
+                atomicOr(&bstate[at >> 2], (pass ? 2u : 1u) << (8 * (at & 3)));
+                atomicMin(&bsum[NW], kb);
+                atomicMax(&bsum[NW + 1], kb);
+            }
         }
         __syncthreads();
-        // partial lists first, then full ones: a block in both is full
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            const int32_t* num = pass ? p.bm_full_num : p.bm_kv_num;
-            const int32_t* idx = pass ? p.bm_full_idx : p.bm_kv_idx;
-            if (num != nullptr) {
-                for (int lq = 0; lq < n_lq; ++lq) {
-                    const int qb = qb0 + lq;
-                    if (qb > qb_last || qb >= p.bm_nqb) break;
-                    const int64_t row = ((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb;
-                    const int cnt = min(max(num[row], 0), p.bm_cap);
-                    for (int i = tid; i < cnt; i += NW * 64) {
-                        const int kb = idx[row * p.bm_cap + i];
-                        if (kb >= 0 && kb < n_kb_seq) {
-                            bstate[lq * n_kb + kb] = (uint8_t)(pass + 1);
-                            atomicMin(&bsum[NW], kb);
-                            atomicMax(&bsum[NW + 1], kb);
-                        }
-                    }
-                }
-            }
-            __syncthreads();
-        }
         const int kb_lo = bsum[NW], kb_hi = bsum[NW + 1];
         if (kb_hi < kb_lo) {
             kv_begin = kv_end = 0;
@@ -304,9 +320,11 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             // compact the chunk's listed tiles (thread t looks at tile t)
             bool on = false;
             if (tid < n) {
-                const int kb = (cs + tid * BN) >> p.bm_kvbs_log2;
-                const int n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);
-                for (int lq = 0; lq < n_lq; ++lq) on |= bstate[lq * p.bm_n_kb + kb] != 0;
+                const int jt = cs + tid * BN;
+                const int kb = jt >> p.bm_kvbs_log2;
+                int v = 0;
+                for (int lq = 0; lq < n_lq; ++lq) v |= bstate8[lq * p.bm_n_kb + kb];
+                on = (v & 2) || ((v & 1) && jt < el_hi && jt + BN > el_lo);
             }
             const uint64_t bal = __ballot(on);
             if (lane == 0) bsum[w] = __popcll(bal);
@@ -349,8 +367,9 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
             int lo_t = lo, hi_t = hi;   // this tile's visible interval per row
             if constexpr (BSP) {
-                const int stt = __builtin_amdgcn_readfirstlane(
-                    bstate[lq_w * p.bm_n_kb + (j0 >> p.bm_kvbs_log2)]);
+                const int v = __builtin_amdgcn_readfirstlane(
+                    bstate8[lq_w * p.bm_n_kb + (j0 >> p.bm_kvbs_log2)]);
+                const int stt = v >= 2 ? 2 : v;
                 if (stt == 2) {          // full block: every existing key
                     lo_t = 0;
                     hi_t = valid ? kv_len : 0;

@@ -13,7 +13,8 @@ weighted sum) divided by the step time.
 The same JSON line carries the prefill kernel's roofline figure, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and more single-GPU
 measurements: paged decode (HBM GB/s, with its own roofline figure), the same
-decode over an fp8 e4m3 cache (one byte per element), a plain
+decode over an fp8 e4m3 cache (one byte per element), the varlen prefill
+under 128x128 causal block lists through the block-sparse entry point, a plain
 device-to-device copy (the practical HBM ceiling, and the calibration kernel
 for the traffic counters), byte->patch cross attention and dense causal fp8
 (TFLOP/s).
@@ -217,18 +218,28 @@ def bench_decode(A, W, torch, dev, iters=20, fp8kv=False):
     return res
 
 
-def bench_prefill_generic(A, W, torch, dev, w, flops, iters=20):
+def bench_prefill_generic(A, W, torch, dev, w, flops, iters=20, block_mask=None):
+    """Paged prefill of w; block_mask = (q_block, kv_block, kv_num, kv_idx,
+    full_num, full_idx) numpy arrays runs the block-sparse entry point."""
     lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
     cu_q = A.attn_cu_seqlens(lens_q)
     cu_kv = A.attn_cu_seqlens(lens_kv)
     A.attn_reshape_and_cache(w.k_new, w.v_new, kc, vc, bt, cu_kv, cu_kv)
     q_ids = None if w.q_ids is None else i32(w.q_ids, torch, dev)
     out = torch.empty_like(w.q)
+    if block_mask is not None:
+        qbs, kbs, *lists = block_mask
+        kn, ki, fn, fi = (i32(a, torch, dev) for a in lists)
 
-    def run():
-        A.attn_paged_prefill_fwd(w.q, kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max()),
-                                 int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags,
-                                 q_ids=q_ids, out=out)
+        def run():
+            A.attn_paged_prefill_block_sparse_fwd(
+                w.q, kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max()), int(w.kv_lens.max()), qbs, kbs,
+                kn, ki, fn, fi, scale=w.scale, mask_flags=w.mask_flags, q_ids=q_ids, out=out)
+    else:
+        def run():
+            A.attn_paged_prefill_fwd(w.q, kc, vc, bt, cu_q, cu_kv, int(w.q_lens.max()),
+                                     int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags,
+                                     q_ids=q_ids, out=out)
 
     for _ in range(3):
         run()
@@ -366,6 +377,15 @@ def main():
         line["cross_attention"] = bench_prefill_generic(
             A, W, torch, dev, wc, 4.0 * wc.head_size * wc.num_heads * patch_pairs(wc))
         del wc
+        torch.cuda.empty_cache()
+        log("block-sparse prefill, causal block lists")
+        wb = W.varlen_gqa_causal_bf16(device=dev)
+        bm = (128, 128) + W.causal_block_mask(wb.q_lens, wb.kv_lens, 128, 128)
+        line["block_sparse"] = bench_prefill_generic(
+            A, W, torch, dev, wb, 4.0 * wb.head_size * wb.num_heads
+            * causal_pairs(wb.q_lens, wb.kv_lens), block_mask=bm)
+        line["block_sparse"]["blocks"] = "128x128 FlexAttention-style causal lists"
+        del wb
         torch.cuda.empty_cache()
         log("fp8")
         line["fp8"] = bench_fp8(A, W, torch, dev)

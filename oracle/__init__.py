@@ -34,6 +34,10 @@ from .attention import (  # noqa: F401
     MASK_PATCH,
     cu_seqlens,
     reshape_and_cache,
+    unpack_qkv,
+    new_token_positions,
+    rotary,
+    rotary_reshape_and_cache,
     gather_paged,
     visibility,
     BlockMask,

@@ -50,6 +50,18 @@ Readings where the pages are silent (each is also listed in the design doc):
     lists counts as full.  Entries outside [0, ceil(kv_len / KB)) and counts
     beyond the list capacity are ignored / clamped.  The mask's head count
     is 1 (shared by all heads), Hkv (one list per kv head) or Hq.
+  * rotary and packed QKV: [ORT] Implementation step 1 runs "rotary" and a
+    "packed-QKV unpack" before ReshapeAndCache, and [ORT] Testing has
+    "rotary on/off", "rotary_interleaved on/off" and "packed-QKV on/off" as
+    parity axes; none is defined there.  Read with their usual meanings:
+    a packed token row holds the Hq query heads, then the Hkv key heads, then
+    the Hkv value heads; rotary rotates the first rotary_dim features of
+    every Q and K head by angle tables indexed by the token's position in its
+    sequence (the new token i of a sequence sits at kv_len - n_new + i, where
+    reshape_and_cache puts it): non-interleaved pairs feature j with
+    j + rotary_dim/2, interleaved pairs 2j with 2j+1; each pair (a, b) goes
+    to (a cos - b sin, b cos + a sin) with the table entry j; features past
+    rotary_dim and V are unchanged.
 """
 
 import collections
@@ -80,6 +92,12 @@ PIN_STATUS = {
                     "equals decode over the cache cut to its last W keys",
     "paged_decode_fp8kv": "pinned: equals paged_decode on caches decoded by torch.float8_e4m3fn; "
                           "hand-derived two-key example with distinct dk, dv; constant-V closed form",
+    "unpack_qkv": "pinned: numpy.split of the packed row, hand-written golden row",
+    "new_token_positions": "pinned: hand-written golden positions (prefill, decode, chunked prefill)",
+    "rotary": "pinned: hand-derived 90-degree example for both pairings, complex multiplication "
+              "(interleaved) and the half-split permutation (non-interleaved), norm preservation, "
+              "relative-position invariance of q.k",
+    "rotary_reshape_and_cache": "pinned: composition of the pinned steps; decode position = kv_len - 1",
     "e4m3_decode": "pinned: all 256 codes against torch.float8_e4m3fn; closed-form extremes",
     "fp8_attention": "pinned: equals attention_varlen on decoded values; hand-derived two-key example",
     "default_scale": "pinned: golden value 0.0625 at E=256 from [BLT]",
@@ -111,6 +129,63 @@ def cu_seqlens(seqlens):
     if out[-1] >= 2**31:
         raise OverflowError("total length does not fit int32")
     return np.asarray(out, dtype=np.int32)
+
+
+def unpack_qkv(qkv, num_heads, num_kv_heads, head_size):
+    """Split packed rows [tokens, (Hq + 2 Hkv) * D] into q [tokens, Hq, D],
+    k and v [tokens, Hkv, D] (module docstring: rotary and packed QKV)."""
+    x = np.asarray(qkv)
+    x = x.reshape(x.shape[0], num_heads + 2 * num_kv_heads, head_size)
+    return (x[:, :num_heads], x[:, num_heads:num_heads + num_kv_heads],
+            x[:, num_heads + num_kv_heads:])
+
+
+def new_token_positions(cu_new, cu_kv):
+    """Position in its sequence of every new token: kv_len - n_new + i, the
+    slot reshape_and_cache writes it to ([ORT] Implementation, step 1)."""
+    pos = []
+    for b in range(len(cu_new) - 1):
+        n_new = int(cu_new[b + 1]) - int(cu_new[b])
+        kv_len = int(cu_kv[b + 1]) - int(cu_kv[b])
+        pos.extend(range(kv_len - n_new, kv_len))
+    return np.asarray(pos, dtype=np.int64)
+
+
+def rotary(x, positions, cos_table, sin_table, rotary_dim, interleaved):
+    """Rotary embedding of x [tokens, H, D] (module docstring), fp64.
+
+    cos_table, sin_table: [max_position, rotary_dim / 2]; token t uses row
+    positions[t].  Features at or past rotary_dim are copied.
+    """
+    out = np.array(x, dtype=np.float64, copy=True)
+    if rotary_dim == 0:
+        return out
+    half = rotary_dim // 2
+    c = np.asarray(cos_table, dtype=np.float64)[positions][:, None, :half]
+    s = np.asarray(sin_table, dtype=np.float64)[positions][:, None, :half]
+    xd = np.asarray(x, dtype=np.float64)
+    if interleaved:
+        a, b = xd[..., 0:rotary_dim:2], xd[..., 1:rotary_dim:2]
+        out[..., 0:rotary_dim:2] = a * c - b * s
+        out[..., 1:rotary_dim:2] = b * c + a * s
+    else:
+        a, b = xd[..., :half], xd[..., half:rotary_dim]
+        out[..., :half] = a * c - b * s
+        out[..., half:rotary_dim] = b * c + a * s
+    return out
+
+
+def rotary_reshape_and_cache(q, k, v, cos_table, sin_table, rotary_dim, interleaved, k_cache,
+                             v_cache, block_table, cu_new, cu_kv, block_size):
+    """The preprocessing of [ORT] Implementation step 1 in order: rotary on
+    the new tokens' Q and K at their positions, then reshape_and_cache of K
+    and V.  Returns (q_rotated, k_cache, v_cache) in fp64."""
+    pos = new_token_positions(cu_new, cu_kv)
+    qr = rotary(q, pos, cos_table, sin_table, rotary_dim, interleaved)
+    kr = rotary(k, pos, cos_table, sin_table, rotary_dim, interleaved)
+    kc, vc = reshape_and_cache(kr, np.asarray(v, dtype=np.float64), k_cache, v_cache, block_table,
+                               cu_new, cu_kv, block_size)
+    return qr, kc, vc
 
 
 def reshape_and_cache(k_new, v_new, k_cache, v_cache, block_table, cu_new, cu_kv, block_size):

@@ -562,6 +562,103 @@ def check_block_sparse_attention_vs_sdpa(A):
                 assert np.allclose(out[cu[b]:cu[b + 1], h], ref[:, 0], rtol=1e-12, atol=1e-12), (hm, b, h)
 
 
+def check_unpack_qkv(A):
+    row = np.arange(8.0)[None]                       # Hq 2, Hkv 1, D 2
+    q, k, v = A.unpack_qkv(row, 2, 1, 2)
+    assert np.array_equal(q, [[[0, 1], [2, 3]]])
+    assert np.array_equal(k, [[[4, 5]]]) and np.array_equal(v, [[[6, 7]]])
+    rng = np.random.default_rng(41)
+    x = _rand(rng, 5, (8 + 2 * 2) * 4)
+    q, k, v = A.unpack_qkv(x, 8, 2, 4)
+    sq, sk, sv = np.split(x, [8 * 4, 10 * 4], axis=1)
+    assert np.array_equal(q.reshape(5, -1), sq) and np.array_equal(k.reshape(5, -1), sk)
+    assert np.array_equal(v.reshape(5, -1), sv)
+
+
+def check_new_token_positions(A):
+    # a 3-token prefill, a decode step at kv_len 7, a 2-token chunk ending at 5
+    got = A.new_token_positions([0, 3, 4, 6], [0, 3, 10, 15])
+    assert np.array_equal(got, [0, 1, 2, 6, 3, 4])
+
+
+def check_rotary_golden(A):
+    """A quarter turn (cos 0, sin 1) by hand: non-interleaved pairs (x0, x2),
+    (x1, x3); interleaved pairs (x0, x1), (x2, x3); a rotary_dim of 2 leaves
+    the last two features alone."""
+    x = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    cos, sin = np.zeros((1, 2)), np.ones((1, 2))
+    assert np.array_equal(A.rotary(x, [0], cos, sin, 4, False)[0, 0], [-3, -4, 1, 2])
+    assert np.array_equal(A.rotary(x, [0], cos, sin, 4, True)[0, 0], [-2, 1, -4, 3])
+    assert np.array_equal(A.rotary(x, [0], cos[:, :1], sin[:, :1], 2, False)[0, 0], [-2, 1, 3, 4])
+    assert np.array_equal(A.rotary(x, [0], cos, sin, 0, False), x)
+
+
+def _rope_tables(max_pos, rd, base=10000.0):
+    theta = base ** (-np.arange(rd // 2) * 2.0 / rd)
+    ang = np.arange(max_pos)[:, None] * theta[None, :]
+    return np.cos(ang), np.sin(ang), ang
+
+
+def check_rotary_complex_and_permutation(A):
+    """Interleaved rotary is the complex product (x_2j + i x_2j+1) e^{i a};
+    the non-interleaved one is the interleaved one on features reordered
+    (j, j + R/2) -> (2j, 2j + 1)."""
+    rng = np.random.default_rng(42)
+    T, H, D, R = 6, 3, 12, 8
+    cos, sin, ang = _rope_tables(40, R)
+    pos = rng.integers(0, 40, T)
+    x = _rand(rng, T, H, D)
+    got = A.rotary(x, pos, cos, sin, R, True)
+    z = (x[..., 0:R:2] + 1j * x[..., 1:R:2]) * np.exp(1j * ang[pos])[:, None, :]
+    assert np.allclose(got[..., 0:R:2], z.real, atol=1e-13)
+    assert np.allclose(got[..., 1:R:2], z.imag, atol=1e-13)
+    assert np.array_equal(got[..., R:], x[..., R:])
+    perm = np.empty(R, dtype=int)
+    perm[0::2], perm[1::2] = np.arange(R // 2), np.arange(R // 2, R)
+    xi = x.copy()
+    xi[..., :R] = x[..., perm]
+    yi = A.rotary(xi, pos, cos, sin, R, True)
+    back = yi.copy()
+    back[..., perm] = yi[..., :R]
+    assert np.allclose(A.rotary(x, pos, cos, sin, R, False), back, atol=1e-13)
+
+
+def check_rotary_norm_and_relative_position(A):
+    """A rotation keeps each head's norm, and with angle tables p * theta_j
+    the product of a rotated q at m and k at n depends on m - n only."""
+    rng = np.random.default_rng(43)
+    D, R = 16, 16
+    cos, sin, _ = _rope_tables(64, R)
+    q, k = _rand(rng, 1, 1, D), _rand(rng, 1, 1, D)
+    for inter in (False, True):
+        y = A.rotary(q, [37], cos, sin, R, inter)
+        assert abs(np.linalg.norm(y) - np.linalg.norm(q)) < 1e-12
+        dots = [float(np.sum(A.rotary(q, [m], cos, sin, R, inter)
+                             * A.rotary(k, [m - 7], cos, sin, R, inter))) for m in (7, 20, 63)]
+        assert np.allclose(dots, dots[0], rtol=0, atol=1e-12)
+        plain = float(np.sum(q * k))
+        assert abs(dots[0] - plain) > 1e-6          # the angle difference 7 does act
+
+
+def check_rotary_reshape_and_cache(A):
+    """A decode step: the one new token sits at kv_len - 1, its rotated K
+    lands in that slot and the rotated Q is returned; V is copied."""
+    rng = np.random.default_rng(44)
+    H, HKV, D, R, bs = 2, 1, 8, 4, 4
+    cos, sin, _ = _rope_tables(16, R)
+    q, k, v = _rand(rng, 1, H, D), _rand(rng, 1, HKV, D), _rand(rng, 1, HKV, D)
+    kc = np.zeros((4, bs, HKV, D))
+    vc = np.zeros((4, bs, HKV, D))
+    table = np.array([[2, 0, 3]])
+    qr, kc2, vc2 = A.rotary_reshape_and_cache(q, k, v, cos, sin, R, False, kc, vc, table, [0, 1],
+                                              [0, 10], bs)
+    # position 9: page table[0][2] = 3, slot 1
+    assert np.allclose(qr, A.rotary(q, [9], cos, sin, R, False), atol=0)
+    assert np.allclose(kc2[3, 1], A.rotary(k, [9], cos, sin, R, False)[0], atol=0)
+    assert np.array_equal(vc2[3, 1], v[0])
+    assert np.count_nonzero(kc2) == np.count_nonzero(kc2[3, 1])
+
+
 def check_window_bands(A):
     """Causal + window W: a band of W keys ending on the (bottom-right) diagonal,
     built here from np.tril / np.triu; without CAUSAL the window only bounds j
@@ -681,7 +778,8 @@ def test_pin_status_covers_exports():
     import oracle
     for name in ("cu_seqlens", "reshape_and_cache", "gather_paged", "visibility",
                  "attention_varlen", "paged_attention", "paged_decode", "e4m3_decode",
-                 "fp8_attention", "default_scale", "paged_decode_fp8kv", "block_visibility"):
+                 "fp8_attention", "default_scale", "paged_decode_fp8kv", "block_visibility", "unpack_qkv",
+                 "new_token_positions", "rotary", "rotary_reshape_and_cache"):
         assert hasattr(oracle, name)
         assert "pinned" in ORC.PIN_STATUS[name]
 
@@ -858,6 +956,31 @@ def _mut_mask_head_modulo(orig):
     return f
 
 
+def _mut_rotary_sin_sign(orig):
+    def f(x, positions, cos_table, sin_table, rotary_dim, interleaved):
+        return orig(x, positions, cos_table, -np.asarray(sin_table), rotary_dim, interleaved)
+    return f
+
+
+def _mut_rotary_pairing(orig):
+    def f(x, positions, cos_table, sin_table, rotary_dim, interleaved):
+        return orig(x, positions, cos_table, sin_table, rotary_dim, not interleaved)
+    return f
+
+
+def _mut_positions_from_zero(orig):
+    def f(cu_new, cu_kv):
+        return orig(cu_new, cu_new)
+    return f
+
+
+def _mut_unpack_kv_swapped(orig):
+    def f(qkv, hq, hkv, d):
+        q, k, v = orig(qkv, hq, hkv, d)
+        return q, v, k
+    return f
+
+
 MUTATIONS = {
     "causal_off_by_one": ("visibility", _mut_visibility_off_by_one),
     "causal_top_left": ("visibility", _mut_visibility_top_left),
@@ -881,6 +1004,10 @@ MUTATIONS = {
     "block_index_shift": ("block_visibility", _mut_block_index_shift),
     "block_sizes_swapped": ("block_visibility", _mut_block_sizes_swapped),
     "block_mask_head_modulo": ("_mask_head", _mut_mask_head_modulo),
+    "rotary_sin_sign": ("rotary", _mut_rotary_sin_sign),
+    "rotary_pairing_swapped": ("rotary", _mut_rotary_pairing),
+    "positions_from_zero": ("new_token_positions", _mut_positions_from_zero),
+    "unpack_kv_swapped": ("unpack_qkv", _mut_unpack_kv_swapped),
 }
 
 

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
 from .api import (  # noqa: F401
     attn_cu_seqlens,
     attn_reshape_and_cache,
+    attn_rotary_reshape_and_cache,
     attn_paged_prefill_fwd,
     attn_paged_prefill_block_sparse_fwd,
     attn_paged_decode_workspace_bytes,

@@ -37,6 +37,9 @@ SIGNATURES = {
     "attn_paged_prefill_fwd": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32,
                                               _i32, _i32, _i32, _i32, _i32, _i32, _f32, _u32,
                                               _p, _p, _i32, _f32, ctypes.c_int, _p, _p, _p]),
+    "attn_rotary_reshape_and_cache": (
+        ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _i32, _p, _p,
+                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),
     "attn_paged_prefill_block_sparse_fwd": (
         ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                        _i32, _i32, _f32, _u32, _p, _p, _i32, _f32, _i32, _i32, _i32, _i32, _i32,

@@ -89,6 +89,76 @@ def attn_reshape_and_cache(k, v, k_cache, v_cache, block_table, cu_seqlens_new, 
             hkv, d, bs, nb, dtype, _stream(dev)))
 
 
+def attn_rotary_reshape_and_cache(k_cache, v_cache, block_table, cu_seqlens_new, cu_seqlens_kv,
+                                  max_seqlen_kv, qkv=None, num_heads=None, q=None, k=None, v=None,
+                                  cos_table=None, sin_table=None, rotary_dim=None,
+                                  interleaved=False, q_out=None, write_q=True):
+    """Rotary + packed-QKV unpack + cache write of the new tokens.
+
+    Either qkv [total_new, (num_heads + 2 Hkv) * D] (num_heads required) or
+    k, v [total_new, Hkv, D] and optionally q [total_new, Hq, D].  cos_table /
+    sin_table float32 [max_position, rotary_dim / 2]; rotary_dim defaults to
+    their full width (0 without tables).  Returns the rotated q
+    [total_new, Hq, D] (q_out, allocated when not given), or None when no
+    query is written."""
+    dev = k_cache.device
+    nb, bs, hkv, d = k_cache.shape
+    _need(k_cache, "k_cache", (torch.float16, torch.bfloat16))
+    _need(v_cache, "v_cache", k_cache.dtype, dev)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("cache shapes differ")
+    for name, t in (("block_table", block_table), ("cu_seqlens_new", cu_seqlens_new),
+                    ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    if qkv is not None:
+        _need(qkv, "qkv", k_cache.dtype, dev)
+        if num_heads is None:
+            raise ValueError("num_heads is required with packed qkv")
+        total = qkv.shape[0]
+        if qkv.dim() != 2 or qkv.shape[1] != (num_heads + 2 * hkv) * d:
+            raise ValueError("qkv must be [total_new, (num_heads + 2 * num_kv_heads) * head_size]")
+        hq = num_heads
+    else:
+        for name, t in (("k", k), ("v", v)):
+            _need(t, name, k_cache.dtype, dev)
+        total = k.shape[0]
+        if tuple(k.shape) != (total, hkv, d) or v.shape != k.shape:
+            raise ValueError("k / v shapes disagree with the cache")
+        if q is not None:
+            _need(q, "q", k_cache.dtype, dev)
+            if q.shape[0] != total or q.shape[2] != d:
+                raise ValueError("q shape disagrees")
+            hq = q.shape[1]
+        else:
+            hq = num_heads if num_heads is not None else hkv
+    has_q = qkv is not None or q is not None
+    if write_q and has_q and q_out is None:
+        q_out = torch.empty((total, hq, d), dtype=k_cache.dtype, device=dev)
+    if not (write_q and has_q):
+        q_out = None
+    if q_out is not None:
+        _need(q_out, "q_out", k_cache.dtype, dev)
+    if rotary_dim is None:
+        rotary_dim = 0 if cos_table is None else 2 * cos_table.shape[1]
+    max_pos = 0
+    if cos_table is not None:
+        for name, t in (("cos_table", cos_table), ("sin_table", sin_table)):
+            _need(t, name, torch.float32, dev)
+        if sin_table.shape != cos_table.shape:
+            raise ValueError("cos / sin tables differ in shape")
+        max_pos = cos_table.shape[0]
+    batch = cu_seqlens_new.numel() - 1
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_rotary_reshape_and_cache", lib.attn_rotary_reshape_and_cache(
+            _ptr(qkv), _ptr(q), _ptr(k), _ptr(v), _ptr(cos_table), _ptr(sin_table), max_pos,
+            int(rotary_dim), int(bool(interleaved)), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+            _ptr(block_table), block_table.shape[1], _ptr(cu_seqlens_new), _ptr(cu_seqlens_kv),
+            batch, total, int(max_seqlen_kv), hq, hkv, d, bs, nb, _DT[k_cache.dtype],
+            _stream(dev)))
+    return q_out
+
+
 def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seqlens_kv,
                            max_seqlen_q, max_seqlen_kv, scale=None, mask_flags=0, q_ids=None,
                            kv_ids=None, out=None, return_lse=False, window=0, softcap=0.0):

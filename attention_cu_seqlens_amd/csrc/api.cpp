@@ -142,6 +142,66 @@ attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, 
         batch, total_new, (int)row_bytes, ilog2(block_size), static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_rotary_reshape_and_cache(
+    const void* qkv, const void* q, const void* k, const void* v, const float* cos_table,
+    const float* sin_table, int32_t max_position, int32_t rotary_dim, int32_t interleaved,
+    void* q_out, void* k_cache, void* v_cache, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_new, const int32_t* cu_seqlens_kv,
+    int32_t batch, int32_t total_new, int32_t max_seqlen_kv, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t num_blocks,
+    attn_dtype dtype, void* stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (batch < 0 || total_new < 0 || max_seqlen_kv < 0) return ATTN_ERR_BAD_SHAPE;
+    if (num_heads <= 0 || num_kv_heads <= 0 || head_size <= 0 || head_size % 8 != 0 ||
+        head_size > 4096 || num_heads > 4096 || num_kv_heads > 4096)
+        return ATTN_ERR_BAD_SHAPE;
+    if (max_blocks_per_seq <= 0 || num_blocks <= 0 || !is_pow2(block_size))
+        return ATTN_ERR_BAD_SHAPE;
+    if ((int64_t)max_blocks_per_seq * block_size < max_seqlen_kv) return ATTN_ERR_BAD_SHAPE;
+    if (rotary_dim < 0 || rotary_dim % 16 != 0 || rotary_dim > head_size) return ATTN_ERR_BAD_SHAPE;
+    if (interleaved != 0 && interleaved != 1) return ATTN_ERR_BAD_SHAPE;
+    if (rotary_dim > 0) {
+        if (cos_table == nullptr || sin_table == nullptr) return ATTN_ERR_NULL_ARG;
+        if (max_position < max_seqlen_kv || max_position <= 0) return ATTN_ERR_BAD_SHAPE;
+        if (!al16(cos_table) || !al16(sin_table)) return ATTN_ERR_BAD_SHAPE;
+    }
+    if (qkv == nullptr && (k == nullptr || v == nullptr || (q_out != nullptr && q == nullptr)))
+        return ATTN_ERR_NULL_ARG;
+    if (k_cache == nullptr || v_cache == nullptr || block_table == nullptr ||
+        cu_seqlens_new == nullptr || cu_seqlens_kv == nullptr)
+        return ATTN_ERR_NULL_ARG;
+    for (const void* ptr : {qkv, q, k, v, static_cast<const void*>(q_out),
+                            static_cast<const void*>(k_cache), static_cast<const void*>(v_cache)})
+        if (ptr != nullptr && !al16(ptr)) return ATTN_ERR_BAD_SHAPE;
+    if (batch == 0 || total_new == 0) return ATTN_OK;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+    attn::RotaryParams p{};
+    p.qkv = static_cast<const uint16_t*>(qkv);
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.cos = cos_table;
+    p.sin = sin_table;
+    p.q_out = static_cast<uint16_t*>(q_out);
+    p.k_cache = static_cast<uint16_t*>(k_cache);
+    p.v_cache = static_cast<uint16_t*>(v_cache);
+    p.block_table = block_table;
+    p.cu_new = cu_seqlens_new;
+    p.cu_kv = cu_seqlens_kv;
+    p.mbps = max_blocks_per_seq;
+    p.batch = batch;
+    p.total_new = total_new;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.head_size = head_size;
+    p.bs_log2 = ilog2(block_size);
+    p.rotary_dim = rotary_dim;
+    p.max_position = max_position;
+    p.interleaved = interleaved;
+    return from_hip(attn::launch_rotary_cache(p, dtype == ATTN_BF16, static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Stored block-sparse mask arguments (null kv_num: none).

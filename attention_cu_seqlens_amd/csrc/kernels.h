@@ -50,6 +50,27 @@ struct PrefillParams {
     int bm_qbs_log2, bm_kvbs_log2;
 };
 
+// Rotary + packed-QKV unpack + reshape_and_cache, one pass over the new
+// tokens (16-bit dtypes).
+struct RotaryParams {
+    const uint16_t* qkv;        // packed [total_new, (Hq + 2 Hkv) * D] or null
+    const uint16_t* q;          // separate inputs (qkv null): [total_new, Hq, D]
+    const uint16_t* k;          // [total_new, Hkv, D]
+    const uint16_t* v;
+    const float* cos;           // [max_position, rotary_dim / 2]
+    const float* sin;
+    uint16_t* q_out;            // [total_new, Hq, D] or null (Q not written)
+    uint16_t* k_cache;          // [num_blocks, bs, Hkv, D]
+    uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* cu_new;
+    const int32_t* cu_kv;
+    int mbps, batch, total_new, num_heads, num_kv_heads, head_size, bs_log2;
+    int rotary_dim;             // 0: no rotation
+    int max_position;
+    int interleaved;
+};
+
 // Query rows (token x packed head) per prefill workgroup, and the bytes of
 // its block-sparse state: one byte per (local query block, key block).
 constexpr int kPrefillRows = 256;
@@ -114,6 +135,7 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     const int32_t* block_table, int mbps, const int32_t* cu_new,
                                     const int32_t* cu_kv, int batch, int total_new,
                                     int row_bytes, int bs_log2, hipStream_t s);
+hipError_t launch_rotary_cache(const RotaryParams& p, bool bf16, hipStream_t s);
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16,
                                 int max_seqlen_q, hipStream_t s);
 hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s);

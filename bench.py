@@ -14,7 +14,8 @@ The same JSON line carries the prefill kernel's roofline figure, the fp64 CPU
 oracle timed on a bounded sample of the same workload, and more single-GPU
 measurements: paged decode (HBM GB/s, with its own roofline figure), the same
 decode over an fp8 e4m3 cache (one byte per element), the varlen prefill
-under 128x128 causal block lists through the block-sparse entry point, a plain
+under 128x128 causal block lists through the block-sparse entry point, the
+fused rotary + packed-QKV unpack + cache write of its tokens (HBM GB/s), a plain
 device-to-device copy (the practical HBM ceiling, and the calibration kernel
 for the traffic counters), byte->patch cross attention and dense causal fp8
 (TFLOP/s).
@@ -218,6 +219,37 @@ def bench_decode(A, W, torch, dev, iters=20, fp8kv=False):
     return res
 
 
+def bench_rotary_cache(A, W, torch, dev, iters=20):
+    """Rotary + packed-QKV unpack + cache write of the varlen workload's
+    34,805 tokens (bf16, 32 + 2 x 8 heads, D 128, full-width rotary): HBM
+    bytes = the packed rows read + q_out, K and V written + the angle-table
+    rows read."""
+    w = W.varlen_gqa_causal_bf16(device=dev)
+    lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
+    cu = A.attn_cu_seqlens(lens_kv)
+    total, hq, hkv, d = w.total_q, w.num_heads, w.num_kv_heads, w.head_size
+    del w.k_new, w.v_new, w.q
+    qkv = W.make_packed_qkv(1006, "bf16", total, hq, hkv, d, device=dev)
+    cos, sin = (torch.from_numpy(t).to(dev) for t in W.rope_tables(int(w.kv_lens.max()), d))
+    q_out = torch.empty((total, hq, d), dtype=torch.bfloat16, device=dev)
+    maxkv = int(w.kv_lens.max())
+
+    def run():
+        A.attn_rotary_reshape_and_cache(kc, vc, bt, cu, cu, maxkv, qkv=qkv, num_heads=hq,
+                                        cos_table=cos, sin_table=sin, q_out=q_out)
+
+    for _ in range(3):
+        run()
+    ms = timed(run, iters, torch)
+    nbytes = 2 * qkv.numel() * 2 + total * d * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": w.name + "_packed_qkv_rotary", "ms": round(ms, 4), "GB/s": round(gbs, 1),
+           "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes}
+    del kc, vc, qkv, q_out
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill_generic(A, W, torch, dev, w, flops, iters=20, block_mask=None):
     """Paged prefill of w; block_mask = (q_block, kv_block, kv_num, kv_idx,
     full_num, full_idx) numpy arrays runs the block-sparse entry point."""
@@ -378,6 +410,8 @@ def main():
             A, W, torch, dev, wc, 4.0 * wc.head_size * wc.num_heads * patch_pairs(wc))
         del wc
         torch.cuda.empty_cache()
+        log("rotary + packed-QKV unpack + cache write")
+        line["rotary_cache"] = bench_rotary_cache(A, W, torch, dev)
         log("block-sparse prefill, causal block lists")
         wb = W.varlen_gqa_causal_bf16(device=dev)
         bm = (128, 128) + W.causal_block_mask(wb.q_lens, wb.kv_lens, 128, 128)

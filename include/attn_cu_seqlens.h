@@ -142,6 +142,45 @@ attn_status attn_reshape_and_cache(const void* k, const void* v, void* k_cache, 
                                    attn_dtype dtype, void* stream);
 
 /*
+ * attn_rotary_reshape_and_cache -- the rest of the onnxruntime PR's
+ * preprocessing (section Implementation, step 1: rotary, packed-QKV unpack,
+ * ReshapeAndCache) in one pass over the new tokens: unpack, rotate Q and K,
+ * write Q to q_out and K, V into the cache like attn_reshape_and_cache.
+ * Rotary: the first rotary_dim features of every Q and K head are rotated in
+ * pairs by the angle-table row of the token's position pos = kv_len - n + i
+ * (where attn_reshape_and_cache puts it): with c = cos_table[pos][j],
+ * s = sin_table[pos][j], a pair (a, b) becomes (a c - b s, b c + a s).
+ * interleaved = 0 pairs feature j with j + rotary_dim/2, interleaved = 1
+ * pairs 2j with 2j+1 (j < rotary_dim/2).  Features past rotary_dim and V are
+ * copied.  Arithmetic in fp32, results rounded to nearest even.
+ *   qkv          packed [total_new, (num_heads + 2 * num_kv_heads) * head_size]:
+ *                per token the query heads, then the key heads, then the
+ *                value heads; or NULL, then q, k, v are read:
+ *   q            [total_new, num_heads, head_size] (may be NULL when q_out is)
+ *   k, v         [total_new, num_kv_heads, head_size]
+ *   cos_table, sin_table  float32 [max_position, rotary_dim / 2] (device),
+ *                NULL allowed when rotary_dim == 0; max_position must be at
+ *                least max_seqlen_kv (every position is below kv_len)
+ *   rotary_dim   0 (no rotation) or a multiple of 16 up to head_size
+ *   q_out        [total_new, num_heads, head_size], or NULL to skip Q; may
+ *                be q itself (each element is read before it is written)
+ *   k_cache, v_cache, block_table, cu_seqlens_new, cu_seqlens_kv  as
+ *                attn_reshape_and_cache
+ *   dtype        ATTN_F16 or ATTN_BF16 (inputs, q_out and caches)
+ * All buffers 16-byte aligned device memory.  Errors: NULL pointer, bad
+ * shape (sizes, rotary_dim, max_position, head_size not a multiple of 8,
+ * alignment), unsupported dtype.
+ */
+attn_status attn_rotary_reshape_and_cache(
+    const void* qkv, const void* q, const void* k, const void* v, const float* cos_table,
+    const float* sin_table, int32_t max_position, int32_t rotary_dim, int32_t interleaved,
+    void* q_out, void* k_cache, void* v_cache, const int32_t* block_table,
+    int32_t max_blocks_per_seq, const int32_t* cu_seqlens_new, const int32_t* cu_seqlens_kv,
+    int32_t batch, int32_t total_new, int32_t max_seqlen_kv, int32_t num_heads,
+    int32_t num_kv_heads, int32_t head_size, int32_t block_size, int32_t num_blocks,
+    attn_dtype dtype, void* stream);
+
+/*
  * attn_paged_prefill_fwd -- varlen attention of packed queries against the
  * paged cache: out = softmax(scale * q k^T + mask) v per sequence and head.
  * The fused form of the onnxruntime PR's gather-then-varlen-attention path

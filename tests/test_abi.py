@@ -70,6 +70,34 @@ def test_reshape_and_cache_host_checks(lib):
     assert f(*bad) == 0
 
 
+def test_rotary_cache_host_checks(lib):
+    f = lib.attn_rotary_reshape_and_cache
+
+    def call(**kw):
+        a = dict(qkv=P, q=None, k=None, v=None, cos=P, sin=P, maxpos=64, rd=64, inter=0, qout=P,
+                 kc=P, vc=P, bt=P, mbps=4, cun=P, cukv=P, batch=2, total=10, mskv=64, hq=8, hkv=2,
+                 d=128, bs=16, nb=8, dtype=1, stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(batch=0) == 0
+    assert call(total=0, rd=0, cos=None, sin=None) == 0
+    assert call(batch=0, qkv=None, k=P, v=P, qout=None) == 0   # K/V only, no query
+    assert call(dtype=2) == 3                                  # fp8: no rotary arithmetic
+    assert call(rd=24) == 2                                    # not a multiple of 16
+    assert call(rd=144) == 2                                   # above head_size
+    assert call(inter=2) == 2
+    assert call(cos=None) == 1
+    assert call(maxpos=63) == 2                                # table shorter than the longest kv
+    assert call(qkv=None, k=P, v=P) == 1                       # q_out without q
+    assert call(qkv=None, q=P, k=None, v=P) == 1
+    assert call(kc=None) == 1
+    assert call(d=100) == 2
+    assert call(bs=24) == 2
+    assert call(mskv=65) == 2                                  # table too narrow
+    assert call(qout=ctypes.c_void_p(24)) == 2                 # misaligned
+
+
 def _prefill_args(**kw):
     a = dict(q=P, kc=P, vc=P, bt=P, mbps=8, cuq=P, cukv=P, batch=2, total_q=100, msq=64, mskv=64,
              hq=8, hkv=2, d=128, bs=16, nb=32, scale=0.1, mask=1, qids=None, kvids=None, window=0,

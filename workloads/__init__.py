@@ -226,6 +226,21 @@ def to_fp8_cache(w):
     return w
 
 
+def rope_tables(max_position, rotary_dim, base=10000.0):
+    """Angle tables of the usual rotary embedding, float32 [max_position,
+    rotary_dim / 2]: entry (p, j) is cos / sin of p * base^(-2j / rotary_dim)
+    (computed in float64, rounded once)."""
+    theta = base ** (-np.arange(rotary_dim // 2, dtype=np.float64) * 2.0 / rotary_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def make_packed_qkv(seed, dtype, total, num_heads, num_kv_heads, head_size, device="cpu"):
+    """Packed rows [total, (Hq + 2 Hkv) * D] ~ N(0, 1), cast to dtype."""
+    gen = _generator(seed, device)
+    return _cast(_randn(gen, (total, (num_heads + 2 * num_kv_heads) * head_size), device), dtype)
+
+
 def causal_block_mask(q_lens, kv_lens, q_block, kv_block, heads=1):
     """Block lists of a bottom-right causal mask (query i sees key j iff
     j <= i + kv_len - q_len): a key block is full for a query block when the

@@ -43,6 +43,7 @@ from .attention import (  # noqa: F401
     BlockMask,
     block_visibility,
     attention_varlen,
+    attention_varlen_bwd,
     paged_attention,
     paged_decode,
     paged_decode_fp8kv,

@@ -62,6 +62,13 @@ Readings where the pages are silent (each is also listed in the design doc):
     j + rotary_dim/2, interleaved pairs 2j with 2j+1; each pair (a, b) goes
     to (a cos - b sin, b cos + a sin) with the table entry j; features past
     rotary_dim and V are unchanged.
+  * backward: [BLT] sets OUTPUT_LOGSUMEXP (the forward saves LSE) and the
+    [VLLM] review shows the varlen function's backward returning dq, dk, dv;
+    the gradients themselves are not printed.  They are those of the
+    forward's definition above: with P the masked softmax, O = P V and an
+    upstream dO, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)),
+    dQ = scale dS K, dK = scale dS^T Q; GQA sums dK and dV over the query
+    heads of a kv head; a row with no visible key contributes nothing.
 """
 
 import collections
@@ -98,6 +105,9 @@ PIN_STATUS = {
               "(interleaved) and the half-split permutation (non-interleaved), norm preservation, "
               "relative-position invariance of q.k",
     "rotary_reshape_and_cache": "pinned: composition of the pinned steps; decode position = kv_len - 1",
+    "attention_varlen_bwd": "pinned: torch.autograd through CPU fp64 SDPA with explicit masks (GQA, causal, "
+                            "window, document, q shorter than kv), central finite differences on a tiny case, "
+                            "fully masked rows give zero gradients",
     "e4m3_decode": "pinned: all 256 codes against torch.float8_e4m3fn; closed-form extremes",
     "fp8_attention": "pinned: equals attention_varlen on decoded values; hand-derived two-key example",
     "default_scale": "pinned: golden value 0.0625 at E=256 from [BLT]",
@@ -397,6 +407,44 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
             out[q0 + sel, h] = o
             lse[q0 + sel, h] = l
     return out, lse
+
+
+def attention_varlen_bwd(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None,
+                         window=0):
+    """Gradients of attention_varlen (softcap 0) with respect to q, k, v for
+    the upstream gradient dout [total_q, Hq, Dv], fp64 (module docstring:
+    backward).  Per sequence and head the forward is recomputed from its
+    definition (no LSE input), then dV = P^T dO, dP = dO V^T,
+    dS = P * (dP - rowsum(dP * P)), dQ = scale dS K, dK = scale dS^T Q.
+    Returns (dq [total_q, Hq, D], dk [total_kv, Hkv, D], dv [total_kv, Hkv, Dv]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    hq, hkv = q.shape[1], k.shape[1]
+    group = hq // hkv
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_kv[b]), int(cu_kv[b + 1])
+        qi = None if q_ids is None else np.asarray(q_ids)[q0:q1]
+        ki = None if kv_ids is None else np.asarray(kv_ids)[k0:k1]
+        vis = visibility(q1 - q0, k1 - k0, flags, qi, ki, window)
+        for h in range(hq):
+            kvh = h // group
+            Q, K, V, dO = q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh], dout[q0:q1, h]
+            s = np.where(vis, scale * (Q @ K.T), -np.inf)
+            m = s.max(axis=1, initial=-np.inf, keepdims=True)
+            e = np.where(vis, np.exp(s - np.where(np.isfinite(m), m, 0.0)), 0.0)
+            tot = e.sum(axis=1, keepdims=True)
+            P = np.divide(e, tot, out=np.zeros_like(e), where=tot > 0)
+            dv[k0:k1, kvh] += P.T @ dO
+            dP = dO @ V.T
+            dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+            dq[q0:q1, h] = scale * (dS @ K)
+            dk[k0:k1, kvh] += scale * (dS.T @ Q)
+    return dq, dk, dv
 
 
 def paged_attention(q, k_cache, v_cache, block_table, cu_q, cu_kv, block_size, scale,

@@ -659,6 +659,88 @@ def check_rotary_reshape_and_cache(A):
     assert np.count_nonzero(kc2) == np.count_nonzero(kc2[3, 1])
 
 
+def _autograd_grads(q, k, v, dout, scale, mask):
+    """torch.autograd through CPU fp64 SDPA with an explicit boolean mask;
+    q [L, Hq, D], k/v [S, Hkv, D] (GQA by enable_gqa)."""
+    Q = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))[None].requires_grad_()
+    K = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None].requires_grad_()
+    V = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None].requires_grad_()
+    o = F.scaled_dot_product_attention(Q, K, V, attn_mask=torch.from_numpy(mask), scale=scale,
+                                       enable_gqa=True)
+    o.backward(torch.from_numpy(np.ascontiguousarray(dout.transpose(1, 0, 2)))[None])
+    return tuple(t.grad[0].permute(1, 0, 2).numpy() for t in (Q, K, V))
+
+
+def check_bwd_vs_autograd(A):
+    """GQA 4/2, two sequences (one with q shorter than kv), causal and a
+    window of 5: the oracle's gradients against autograd through SDPA with
+    the mask built from np.tril / np.triu."""
+    rng = np.random.default_rng(51)
+    HQ, HKV, D = 4, 2, 6
+    ql, kl = [9, 5], [9, 12]
+    cq, ck = np.concatenate([[0], np.cumsum(ql)]), np.concatenate([[0], np.cumsum(kl)])
+    q, k, v = _rand(rng, cq[-1], HQ, D), _rand(rng, ck[-1], HKV, D), _rand(rng, ck[-1], HKV, D)
+    do = _rand(rng, cq[-1], HQ, D)
+    for window in (0, 5):
+        dq, dk, dv = A.attention_varlen_bwd(q, k, v, do, cq, ck, 0.4, ORC.MASK_CAUSAL,
+                                            window=window)
+        for b in range(2):
+            off = kl[b] - ql[b]
+            mask = np.tril(np.ones((ql[b], kl[b]), dtype=bool), off)
+            if window:
+                mask &= np.triu(np.ones((ql[b], kl[b]), dtype=bool), off - window + 1)
+            gq, gk, gv = _autograd_grads(q[cq[b]:cq[b + 1]], k[ck[b]:ck[b + 1]],
+                                         v[ck[b]:ck[b + 1]], do[cq[b]:cq[b + 1]], 0.4, mask)
+            assert np.allclose(dq[cq[b]:cq[b + 1]], gq, rtol=1e-10, atol=1e-12), (window, b)
+            assert np.allclose(dk[ck[b]:ck[b + 1]], gk, rtol=1e-10, atol=1e-12), (window, b)
+            assert np.allclose(dv[ck[b]:ck[b + 1]], gv, rtol=1e-10, atol=1e-12), (window, b)
+
+
+def check_bwd_document_and_empty_rows(A):
+    """Document ids (non-causal): autograd with the id-equality mask; a
+    query whose document has no keys gets dq = 0 and adds nothing to dk, dv."""
+    rng = np.random.default_rng(52)
+    HQ, HKV, D = 2, 1, 4
+    qi = np.array([0, 0, 1, 1, 1, 2, 3], dtype=np.int32)
+    ki = np.array([0, 1, 1, 2, 2, 2], dtype=np.int32)
+    q, k, v = _rand(rng, 7, HQ, D), _rand(rng, 6, HKV, D), _rand(rng, 6, HKV, D)
+    do = _rand(rng, 7, HQ, D)
+    dq, dk, dv = A.attention_varlen_bwd(q, k, v, do, [0, 7], [0, 6], 0.7, ORC.MASK_DOCUMENT,
+                                        qi, ki)
+    assert np.all(dq[6] == 0)                          # document 3 has no keys
+    keep = qi != 3
+    mask = qi[keep][:, None] == ki[None, :]
+    gq, gk, gv = _autograd_grads(q[keep], k, v, do[keep], 0.7, mask)
+    assert np.allclose(dq[keep], gq, rtol=1e-10, atol=1e-12)
+    assert np.allclose(dk, gk, rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv, gv, rtol=1e-10, atol=1e-12)
+
+
+def check_bwd_finite_differences(A):
+    """Central differences of sum(out * dout) on a tiny causal GQA case."""
+    rng = np.random.default_rng(53)
+    q, k, v = _rand(rng, 3, 2, 2), _rand(rng, 4, 1, 2), _rand(rng, 4, 1, 2)
+    do = _rand(rng, 3, 2, 2)
+    cq, ck = [0, 3], [0, 4]
+    grads = A.attention_varlen_bwd(q, k, v, do, cq, ck, 0.9, ORC.MASK_CAUSAL)
+
+    def loss(q_, k_, v_):
+        return float(np.sum(A.attention_varlen(q_, k_, v_, cq, ck, 0.9, ORC.MASK_CAUSAL)[0] * do))
+
+    eps = 1e-6
+    for which, x in enumerate((q, k, v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert np.allclose(grads[which], num, rtol=1e-6, atol=1e-8), which
+
+
 def check_window_bands(A):
     """Causal + window W: a band of W keys ending on the (bottom-right) diagonal,
     built here from np.tril / np.triu; without CAUSAL the window only bounds j
@@ -779,7 +861,8 @@ def test_pin_status_covers_exports():
     for name in ("cu_seqlens", "reshape_and_cache", "gather_paged", "visibility",
                  "attention_varlen", "paged_attention", "paged_decode", "e4m3_decode",
                  "fp8_attention", "default_scale", "paged_decode_fp8kv", "block_visibility", "unpack_qkv",
-                 "new_token_positions", "rotary", "rotary_reshape_and_cache"):
+                 "new_token_positions", "rotary", "rotary_reshape_and_cache",
+                 "attention_varlen_bwd"):
         assert hasattr(oracle, name)
         assert "pinned" in ORC.PIN_STATUS[name]
 
@@ -981,6 +1064,54 @@ def _mut_unpack_kv_swapped(orig):
     return f
 
 
+def _bwd_variant(drop_delta=False, no_gqa_sum=False):
+    """The oracle's backward with one planted mistake (same steps otherwise)."""
+    def f(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, window=0):
+        q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+        hq, hkv = q.shape[1], k.shape[1]
+        g = hq // hkv
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(len(cu_q) - 1):
+            q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_kv[b]), int(cu_kv[b + 1])
+            qi = None if q_ids is None else np.asarray(q_ids)[q0:q1]
+            ki = None if kv_ids is None else np.asarray(kv_ids)[k0:k1]
+            vis = ORC.visibility(q1 - q0, k1 - k0, flags, qi, ki, window)
+            for h in range(hq):
+                kvh = h // g
+                Q, K, V, dO = q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh], dout[q0:q1, h]
+                s_ = np.where(vis, scale * (Q @ K.T), -np.inf)
+                m = s_.max(axis=1, initial=-np.inf, keepdims=True)
+                e = np.where(vis, np.exp(s_ - np.where(np.isfinite(m), m, 0.0)), 0.0)
+                tot = e.sum(axis=1, keepdims=True)
+                P = np.divide(e, tot, out=np.zeros_like(e), where=tot > 0)
+                dP = dO @ V.T
+                dS = P * dP if drop_delta else P * (dP - (dP * P).sum(axis=1, keepdims=True))
+                if no_gqa_sum:
+                    dv[k0:k1, kvh] = P.T @ dO
+                    dk[k0:k1, kvh] = scale * (dS.T @ Q)
+                else:
+                    dv[k0:k1, kvh] += P.T @ dO
+                    dk[k0:k1, kvh] += scale * (dS.T @ Q)
+                dq[q0:q1, h] = scale * (dS @ K)
+        return dq, dk, dv
+    return f
+
+
+def _mut_bwd_drop_delta(orig):
+    return _bwd_variant(drop_delta=True)
+
+
+def _mut_bwd_no_gqa_sum(orig):
+    return _bwd_variant(no_gqa_sum=True)
+
+
+def _mut_bwd_dq_unscaled(orig):
+    def f(q, k, v, dout, cu_q, cu_kv, scale, *a, **kw):
+        dq, dk, dv = orig(q, k, v, dout, cu_q, cu_kv, scale, *a, **kw)
+        return dq / scale, dk, dv
+    return f
+
+
 MUTATIONS = {
     "causal_off_by_one": ("visibility", _mut_visibility_off_by_one),
     "causal_top_left": ("visibility", _mut_visibility_top_left),
@@ -1008,6 +1139,9 @@ MUTATIONS = {
     "rotary_pairing_swapped": ("rotary", _mut_rotary_pairing),
     "positions_from_zero": ("new_token_positions", _mut_positions_from_zero),
     "unpack_kv_swapped": ("unpack_qkv", _mut_unpack_kv_swapped),
+    "bwd_drop_delta": ("attention_varlen_bwd", _mut_bwd_drop_delta),
+    "bwd_no_gqa_sum": ("attention_varlen_bwd", _mut_bwd_no_gqa_sum),
+    "bwd_dq_unscaled": ("attention_varlen_bwd", _mut_bwd_dq_unscaled),
 }
 
 

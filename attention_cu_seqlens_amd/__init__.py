@@ -26,5 +26,7 @@ from .api import (  # noqa: F401
     attn_paged_decode_fwd,
     attn_paged_decode_fp8kv_fwd,
     attn_fp8_fwd,
+    attn_varlen_bwd,
+    attn_varlen_bwd_workspace_bytes,
     library_path,
 )

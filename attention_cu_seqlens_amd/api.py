@@ -89,6 +89,57 @@ def attn_reshape_and_cache(k, v, k_cache, v_cache, block_table, cu_seqlens_new, 
             hkv, d, bs, nb, dtype, _stream(dev)))
 
 
+def attn_varlen_bwd_workspace_bytes(total_q, num_heads):
+    return int(_lib.load().attn_varlen_bwd_workspace_bytes(int(total_q), int(num_heads)))
+
+
+def attn_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
+                    max_seqlen_kv, scale=None, mask_flags=0, q_ids=None, kv_ids=None, window=0,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of varlen attention: q, out, dout [total_q, Hq, D],
+    k, v [total_kv, Hkv, D] (packed, 16-bit), lse float32 [total_q, Hq] from
+    the forward."""
+    dev = q.device
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _need(t, name, q.dtype, dev)
+    _need(lse, "lse", torch.float32, dev)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    for name, t in (("q_ids", q_ids), ("kv_ids", kv_ids)):
+        if t is not None:
+            _need(t, name, torch.int32, dev)
+    total_q, hq, d = q.shape
+    total_kv, hkv, _ = k.shape
+    if v.shape != k.shape or out.shape != q.shape or dout.shape != q.shape or k.shape[2] != d:
+        raise ValueError("q / k / v / out / dout shapes disagree")
+    if tuple(lse.shape) != (total_q, hq):
+        raise ValueError("lse must be [total_q, num_heads]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _need(t, name, q.dtype, dev)
+        if t.shape != ref.shape:
+            raise ValueError(f"{name} shape")
+    lib = _lib.load()
+    need = attn_varlen_bwd_workspace_bytes(total_q, hq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    batch = cu_seqlens_q.numel() - 1
+    with torch.cuda.device(dev):
+        _lib.check("attn_varlen_bwd", lib.attn_varlen_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens_q),
+            _ptr(cu_seqlens_kv), batch, total_q, total_kv, int(max_seqlen_q), int(max_seqlen_kv),
+            hq, hkv, d, float(scale), int(mask_flags), _ptr(q_ids), _ptr(kv_ids), int(window),
+            _DT[q.dtype], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+            _stream(dev)))
+    return dq, dk, dv
+
+
 def attn_rotary_reshape_and_cache(k_cache, v_cache, block_table, cu_seqlens_new, cu_seqlens_kv,
                                   max_seqlen_kv, qkv=None, num_heads=None, q=None, k=None, v=None,
                                   cos_table=None, sin_table=None, rotary_dim=None,

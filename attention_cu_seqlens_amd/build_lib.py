@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn_cu_seqlens.so")
-SOURCES = ["api.cpp", "small.hip", "prefill.hip", "decode.hip", "fp8.hip"]
+SOURCES = ["api.cpp", "small.hip", "prefill.hip", "decode.hip", "fp8.hip", "backward.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -202,6 +202,72 @@ attn_status attn_rotary_reshape_and_cache(
     return from_hip(attn::launch_rotary_cache(p, dtype == ATTN_BF16, static_cast<hipStream_t>(stream)));
 }
 
+size_t attn_varlen_bwd_workspace_bytes(int32_t total_q, int32_t num_heads) {
+    if (total_q < 0 || num_heads <= 0) return 0;
+    const size_t b = (size_t)total_q * (size_t)num_heads * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_kv, int32_t batch, int32_t total_q,
+                            int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            float scale, uint32_t mask_flags, const int32_t* q_ids,
+                            const int32_t* kv_ids, int32_t window_left, attn_dtype dtype,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+    if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
+    if (batch < 0 || total_q < 0 || total_kv < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
+        return ATTN_ERR_BAD_SHAPE;
+    if (!std::isfinite(scale) || window_left < 0) return ATTN_ERR_BAD_SHAPE;
+    const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
+    if (m != ATTN_OK) return m;
+    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
+        lse == nullptr || cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || dq == nullptr ||
+        dk == nullptr || dv == nullptr)
+        return ATTN_ERR_NULL_ARG;
+    for (const void* ptr : {q, k, v, out, dout, static_cast<const void*>(dq),
+                            static_cast<const void*>(dk), static_cast<const void*>(dv)})
+        if (!al16(ptr)) return ATTN_ERR_BAD_SHAPE;
+    if (batch == 0 || (total_q == 0 && total_kv == 0)) return ATTN_OK;
+    const size_t need = attn_varlen_bwd_workspace_bytes(total_q, num_heads);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need ||
+                     ((uintptr_t)workspace & 255) != 0))
+        return ATTN_ERR_WORKSPACE;
+    const attn_status d = check_device();
+    if (d != ATTN_OK) return d;
+    attn::BwdParams p{};
+    p.q = static_cast<const uint16_t*>(q);
+    p.k = static_cast<const uint16_t*>(k);
+    p.v = static_cast<const uint16_t*>(v);
+    p.out = static_cast<const uint16_t*>(out);
+    p.dout = static_cast<const uint16_t*>(dout);
+    p.lse = lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_kv = cu_seqlens_kv;
+    p.q_ids = q_ids;
+    p.kv_ids = kv_ids;
+    p.dq = static_cast<uint16_t*>(dq);
+    p.dk = static_cast<uint16_t*>(dk);
+    p.dv = static_cast<uint16_t*>(dv);
+    p.delta = static_cast<float*>(workspace);
+    p.batch = batch;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.group = num_heads / num_kv_heads;
+    p.total_q = total_q;
+    p.mask = mask_flags;
+    p.window = window_left;
+    p.scale = scale;
+    p.c = scale * 1.4426950408889634f;
+    return from_hip(attn::launch_varlen_bwd(p, head_size, dtype == ATTN_BF16, max_seqlen_q,
+                                            max_seqlen_kv, static_cast<hipStream_t>(stream)));
+}
+
 namespace {
 
 // Stored block-sparse mask arguments (null kv_num: none).

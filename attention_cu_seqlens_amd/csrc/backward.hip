@@ -1,0 +1,427 @@
+// Varlen attention backward on gfx950: dQ, dK, dV from Q, K, V, the forward
+// output O, the upstream gradient dO and the forward's saved logsumexp (the
+// LSE output the blt issue's FlexAttention kernel options turn on; the
+// vllm-project/flash-attention "Rope dim" review shows the varlen function's
+// backward returning dq, dk, dv).
+//
+// With P = exp(scale * Q K^T - LSE) (masked entries 0) and
+// delta = rowsum(dO * O) = rowsum(dP * P):
+//     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),
+//     dQ = scale dS K,  dK = scale dS^T Q.
+// Three kernels, no atomics:
+//   k_bwd_delta  delta per (query row, head);
+//   k_bwd_dq     a workgroup owns 128 query rows of one head (32 per wave,
+//                one per lane column, Q and dO in registers as the B
+//                operands) and streams 64-key K / V tiles:
+//                S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
+//   k_bwd_dkdv   a workgroup owns 128 keys of one kv head (K and V rows in
+//                registers) and streams 64-row Q / dO tiles of every query
+//                head of the group: S = Q K^T, dP = dO V^T, then
+//                dV^T += dO^T P and dK^T += Q^T dS -- the group's heads sum
+//                in registers.
+// Both stream kernels use the two MFMA patterns of the forward: rows of an
+// LDS tile against a register operand (the S^T = K Q^T product), and the
+// transposed LDS read against packed 16-bit accumulators (the P.V product),
+// on tiles in the same swizzled row-major LDS layout.  Tiles are staged
+// through registers and double-buffered: the next tile's global loads are in
+// flight while the current one is used.
+
+#include "device_common.h"
+#include "kernels.h"
+#include "ring.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kBwdTile = 64;    // rows of a streamed tile
+constexpr int kBwdRows = 128;   // rows a workgroup owns (4 waves x 32)
+
+// 64 rows x D of a [tokens, heads, D] tensor staged through registers into
+// the swizzled LDS tile layout (row r, chunk c at chunk c ^ swz<D>(r)).
+template <int D>
+struct StageRows {
+    static constexpr int CPR = D / 8;
+    static constexpr int ROWB = 2 * D;
+    static constexpr int PER = kBwdTile * CPR / 256;   // chunks per thread
+    u32x4_t r[PER];
+
+    // Rows r0 .. r0 + 63 of `base` (row stride in elements); rows at or past
+    // n read row n - 1 (n >= 1), which callers give probability 0.
+    __device__ __forceinline__ void load(const uint16_t* base, int64_t stride, int r0, int n,
+                                         int tid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ci = tid + 256 * i, row = ci / CPR, c = ci % CPR;
+            const int rr = min(r0 + row, n - 1);
+            r[i] = *reinterpret_cast<const u32x4_t*>(base + rr * stride + c * 8);
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t* tile, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ci = tid + 256 * i, row = ci / CPR, c = ci % CPR;
+            *reinterpret_cast<u32x4_t*>(tile + row * ROWB + ((c ^ swz<D>(row)) << 4)) = r[i];
+        }
+    }
+};
+
+// x[kb] (rows kb*32.. of the tile, column = lane's column) = tile rows . b
+// over D: the S^T = K Q^T pattern, b holding this lane column's row as the
+// B operand (dims 16t + 8g .. +7 in b[t]).
+template <int D, bool BF16>
+__device__ __forceinline__ void rows_dot(f32x16_t (&x)[2], const uint8_t* tile,
+                                         const u32x4_t (&b)[D / 16]) {
+    constexpr int ROWB = 2 * D;
+    const int lane = lane_id(), col = lane & 31, g = lane >> 5;
+    const uint32_t lok = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const u32x4_t a =
+                *reinterpret_cast<const u32x4_t*>(tile + kb * 32 * ROWB + (lok ^ (uint32_t)(t << 5)));
+            x[kb] = mfma32<BF16>(a, b[t], t == 0 ? f32x16_t{} : x[kb]);
+        }
+}
+
+// y[db] (rows = dims, column = lane's column) += tile^T . X with X the
+// packed 16-bit accumulators of a rows_dot product (rows = tile rows): the
+// P.V pattern with the transposed LDS read.
+template <int D, bool BF16>
+__device__ __forceinline__ void cols_acc(f32x16_t (&y)[D / 32], const uint8_t* tile,
+                                         const u32x4_t (&xb)[2][2]) {
+    uint32_t lo0, hi0;
+    pv_offsets<D>(lo0, hi0);
+#pragma unroll
+    for (int i = 0; i < (D / 32) * 4; ++i) {
+        const int db = i / 4, kb = (i / 2) % 2, tp = i % 2;
+        y[db] = mfma32<BF16>(pv_frag<D, kBwdTile>(tile, lo0, hi0, i), xb[kb][tp], y[db]);
+    }
+}
+
+// Accumulator values 8tp .. 8tp+7 of block kb packed as the B operand.
+template <bool BF16>
+__device__ __forceinline__ void pack_block(const float (&v)[16], u32x4_t (&xb)[2]) {
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp) {
+        u32x4_t w;
+        w.x = pack2<BF16>(v[8 * tp + 0], v[8 * tp + 1]);
+        w.y = pack2<BF16>(v[8 * tp + 2], v[8 * tp + 3]);
+        w.z = pack2<BF16>(v[8 * tp + 4], v[8 * tp + 5]);
+        w.w = pack2<BF16>(v[8 * tp + 6], v[8 * tp + 7]);
+        xb[tp] = w;
+    }
+}
+
+// Write acc^T (rows = dims, column = lane's column) times f to one D-long row.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_cols(const f32x16_t (&acc)[D / 32], float f, uint16_t* row) {
+    const int g = lane_id() >> 5;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+            u32x2_t w;
+            w.x = pack2<BF16>(acc[db][4 * rq + 0] * f, acc[db][4 * rq + 1] * f);
+            w.y = pack2<BF16>(acc[db][4 * rq + 2] * f, acc[db][4 * rq + 3] * f);
+            *reinterpret_cast<u32x2_t*>(row + db * 32 + 8 * rq + 4 * g) = w;
+        }
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x2_t unpack16(uint32_t w) {
+    if constexpr (BF16) {
+        return f32x2_t{__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)};
+    } else {
+        return __builtin_convertvector(__builtin_bit_cast(f16x2_t, w), f32x2_t);
+    }
+}
+
+// delta[row, h] = sum_d dO * O in fp32, one thread per (row, head).
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_delta(BwdParams p) {
+    const int64_t n = (int64_t)p.total_q * p.num_heads;
+    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const u32x4_t* o = reinterpret_cast<const u32x4_t*>(p.out + i * D);
+        const u32x4_t* d = reinterpret_cast<const u32x4_t*>(p.dout + i * D);
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const u32x4_t a = o[c], b = d[c];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x2_t fa = unpack16<BF16>(a[w]), fb = unpack16<BF16>(b[w]);
+                acc = __builtin_fmaf(fa.x, fb.x, acc);
+                acc = __builtin_fmaf(fa.y, fb.y, acc);
+            }
+        }
+        p.delta[i] = acc;
+    }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
+    constexpr int TILE = kBwdTile * 2 * D;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][K, V]
+    __shared__ int wave_range[2][4];
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int q_start = p.cu_q[b], q_len = p.cu_q[b + 1] - q_start;
+    const int row0 = blockIdx.x * kBwdRows;
+    if (row0 >= q_len) return;
+    const int kv_start = p.cu_kv[b], kv_len = p.cu_kv[b + 1] - kv_start;
+    const int hk = h / p.group;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int col = lane & 31, g = lane >> 5;
+    const int r = row0 + w * 32 + col;
+    const bool valid = r < q_len;
+    const int rr = valid ? r : q_len - 1;
+    const int64_t qrow = (int64_t)(q_start + rr) * p.num_heads + h;
+
+    u32x4_t qv[D / 16], dov[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+        qv[t] = *reinterpret_cast<const u32x4_t*>(p.q + qrow * D + 16 * t + 8 * g);
+        dov[t] = *reinterpret_cast<const u32x4_t*>(p.dout + qrow * D + 16 * t + 8 * g);
+    }
+    const float lse2 = p.lse[qrow] * kLog2e;
+    const float dlt = p.delta[qrow];
+    // this row's visible keys [lo, hi), as in the forward
+    int lo = 0, hi = 0;
+    if (valid) {
+        hi = kv_len;
+        if (p.mask & kMaskCausal) hi = min(hi, r + (kv_len - q_len) + 1);
+        if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + r] + 1);
+        if (p.mask & kMaskDocument) {
+            const int doc = p.q_ids[q_start + r];
+            lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
+            hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
+        }
+        if (p.window > 0) lo = max(lo, r + (kv_len - q_len) - p.window + 1);
+        if (hi < lo) hi = lo;
+    }
+    const bool any = valid && hi > lo;
+    const int w_lo = wave_min(any ? lo : 0x7fffffff);
+    const int w_hi = wave_max(any ? hi : -1);
+    if (lane == 0) {
+        wave_range[0][w] = w_lo;
+        wave_range[1][w] = w_hi;
+    }
+    __syncthreads();
+    int kv_begin = 0x7fffffff, kv_end = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        kv_begin = min(kv_begin, wave_range[0][i]);
+        kv_end = max(kv_end, wave_range[1][i]);
+    }
+    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin);
+    kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+    const int n_t = kv_end > kv_begin ? (kv_end - kv_begin + kBwdTile - 1) / kBwdTile : 0;
+
+    f32x16_t acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16_t{};
+    if (n_t > 0) {
+        const int64_t stride = (int64_t)p.num_kv_heads * D;
+        const uint16_t* kbase = p.k + ((int64_t)kv_start * p.num_kv_heads + hk) * D;
+        const uint16_t* vbase = p.v + ((int64_t)kv_start * p.num_kv_heads + hk) * D;
+        StageRows<D> sk, sv;
+        sk.load(kbase, stride, kv_begin, kv_len, tid);
+        sv.load(vbase, stride, kv_begin, kv_len, tid);
+        sk.store(lds[0], tid);
+        sv.store(lds[0] + TILE, tid);
+        __syncthreads();
+        for (int it = 0; it < n_t; ++it) {
+            const int j0 = kv_begin + it * kBwdTile;
+            const uint8_t* kt = lds[it & 1];
+            const uint8_t* vt = kt + TILE;
+            const bool more = it + 1 < n_t;
+            if (more) {
+                sk.load(kbase, stride, j0 + kBwdTile, kv_len, tid);
+                sv.load(vbase, stride, j0 + kBwdTile, kv_len, tid);
+            }
+            f32x16_t s[2], dp[2];
+            rows_dot<D, BF16>(s, kt, qv);
+            rows_dot<D, BF16>(dp, vt, dov);
+            u32x4_t xb[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float ds[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const float pr = (key >= lo && key < hi)
+                                         ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -lse2)) : 0.f;
+                    ds[e] = pr * (dp[kb][e] - dlt);
+                }
+                pack_block<BF16>(ds, xb[kb]);
+            }
+            cols_acc<D, BF16>(acc, kt, xb);
+            if (more) {
+                sk.store(lds[(it + 1) & 1], tid);
+                sv.store(lds[(it + 1) & 1] + TILE, tid);
+            }
+            __syncthreads();
+        }
+    }
+    if (valid) store_cols<D, BF16>(acc, p.scale, p.dq + qrow * D);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
+    constexpr int TILE = kBwdTile * 2 * D;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][Q, dO]
+    __shared__ __attribute__((aligned(16))) float rows_lse2[2][kBwdTile];
+    __shared__ __attribute__((aligned(16))) float rows_delta[2][kBwdTile];
+    __shared__ __attribute__((aligned(16))) int rows_id[2][kBwdTile];
+    const int b = blockIdx.z, hk = blockIdx.y;
+    const int kv_start = p.cu_kv[b], kv_len = p.cu_kv[b + 1] - kv_start;
+    const int k0 = blockIdx.x * kBwdRows;
+    if (k0 >= kv_len) return;
+    const int q_start = p.cu_q[b], q_len = p.cu_q[b + 1] - q_start;
+    const int off = kv_len - q_len;
+    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int col = lane & 31, g = lane >> 5;
+    const int key = k0 + w * 32 + col;
+    const bool kvalid = key < kv_len;
+    const int kk = kvalid ? key : kv_len - 1;
+    const int64_t krow = (int64_t)(kv_start + kk) * p.num_kv_heads + hk;
+
+    u32x4_t kr[D / 16], vr[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+        kr[t] = *reinterpret_cast<const u32x4_t*>(p.k + krow * D + 16 * t + 8 * g);
+        vr[t] = *reinterpret_cast<const u32x4_t*>(p.v + krow * D + 16 * t + 8 * g);
+    }
+    const bool causal = p.mask & kMaskCausal, patch = p.mask & kMaskPatch;
+    const bool doc = p.mask & kMaskDocument;
+    const int kid = doc ? p.kv_ids[kv_start + kk] : 0;
+
+    // queries that can see any of keys k0 .. k0 + 127
+    int qlo = 0, qhi = q_len;
+    if (causal) qlo = max(qlo, k0 - off);
+    if (p.window > 0) qhi = min(qhi, k0 + kBwdRows - 1 - off + p.window);
+    const int n_qt = qhi > qlo ? (qhi - qlo + kBwdTile - 1) / kBwdTile : 0;
+    const int n_t = n_qt * p.group;
+
+    f32x16_t dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16_t{};
+    if (n_t > 0 && q_len > 0) {
+        const int64_t stride = (int64_t)p.num_heads * D;
+        StageRows<D> sq, sd;
+        // rows of tile it: head hk * G + it / n_qt, queries qlo + (it % n_qt) * 64 ..
+        auto head_of = [&](int it) { return hk * p.group + it / n_qt; };
+        auto row0_of = [&](int it) { return qlo + (it % n_qt) * kBwdTile; };
+        auto load = [&](int it) {
+            const int h = head_of(it), j0 = row0_of(it);
+            const int64_t base = (int64_t)q_start * p.num_heads + h;
+            sq.load(p.q + base * D, stride, j0, q_len, tid);
+            sd.load(p.dout + base * D, stride, j0, q_len, tid);
+        };
+        // per-row values of tile it into buffer bf (threads 0..63)
+        auto rows = [&](int it, int bf) {
+            if (tid < kBwdTile) {
+                const int h = head_of(it), q = row0_of(it) + tid;
+                const bool in = q < q_len;
+                const int64_t i = (int64_t)(q_start + (in ? q : q_len - 1)) * p.num_heads + h;
+                // a row past the sequence gets probability 0 through lse2 = +inf
+                rows_lse2[bf][tid] = in ? p.lse[i] * kLog2e : __builtin_huge_valf();
+                rows_delta[bf][tid] = in ? p.delta[i] : 0.f;
+                rows_id[bf][tid] = (patch || doc) ? p.q_ids[q_start + (in ? q : q_len - 1)] : 0;
+            }
+        };
+        load(0);
+        rows(0, 0);
+        sq.store(lds[0], tid);
+        sd.store(lds[0] + TILE, tid);
+        __syncthreads();
+        for (int it = 0; it < n_t; ++it) {
+            const int bf = it & 1;
+            const int j0 = row0_of(it);
+            const uint8_t* qt = lds[bf];
+            const uint8_t* dt = qt + TILE;
+            const bool more = it + 1 < n_t;
+            if (more) load(it + 1);
+            f32x16_t s[2], dp[2];
+            rows_dot<D, BF16>(s, qt, kr);
+            rows_dot<D, BF16>(dp, dt, vr);
+            u32x4_t pbp[2][2], pbs[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                float pv[16], dsv[16];
+#pragma unroll
+                for (int rq = 0; rq < 4; ++rq) {
+                    const int tr = kb * 32 + 8 * rq + 4 * g;   // tile rows tr .. tr+3
+                    const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&rows_lse2[bf][tr]);
+                    const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&rows_delta[bf][tr]);
+                    const i32x4_t id4 = *reinterpret_cast<const i32x4_t*>(&rows_id[bf][tr]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * rq + i, q = j0 + tr + i;
+                        bool vis = kvalid;
+                        if (causal) vis = vis && key <= q + off;
+                        if (p.window > 0) vis = vis && key > q + off - p.window;
+                        if (patch) vis = vis && key <= id4[i];
+                        if (doc) vis = vis && kid == id4[i];
+                        const float pr =
+                            vis ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -l4[i])) : 0.f;
+                        pv[e] = pr;
+                        dsv[e] = pr * (dp[kb][e] - d4[i]);
+                    }
+                }
+                pack_block<BF16>(pv, pbp[kb]);
+                pack_block<BF16>(dsv, pbs[kb]);
+            }
+            cols_acc<D, BF16>(dv, dt, pbp);
+            cols_acc<D, BF16>(dk, qt, pbs);
+            if (more) {
+                rows(it + 1, bf ^ 1);
+                sq.store(lds[bf ^ 1], tid);
+                sd.store(lds[bf ^ 1] + TILE, tid);
+            }
+            __syncthreads();
+        }
+    }
+    if (kvalid) {
+        store_cols<D, BF16>(dk, p.scale, p.dk + krow * D);
+        store_cols<D, BF16>(dv, 1.f, p.dv + krow * D);
+    }
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_kv, hipStream_t s) {
+    const int64_t n = (int64_t)p.total_q * p.num_heads;
+    const int dblocks = (int)std::min<int64_t>((n + 255) / 256, 16384);
+    hipLaunchKernelGGL((k_bwd_delta<D, BF16>), dim3(dblocks), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned qt = (unsigned)((max_seqlen_q + kBwdRows - 1) / kBwdRows);
+    const unsigned kt = (unsigned)((max_seqlen_kv + kBwdRows - 1) / kBwdRows);
+    if (qt > 0) {
+        hipLaunchKernelGGL((k_bwd_dq<D, BF16>), dim3(qt, p.num_heads, p.batch), dim3(256), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (kt > 0) {
+        hipLaunchKernelGGL((k_bwd_dkdv<D, BF16>), dim3(kt, p.num_kv_heads, p.batch), dim3(256), 0,
+                           s, p);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_varlen_bwd(const BwdParams& p, int head_size, bool bf16, int max_seqlen_q,
+                             int max_seqlen_kv, hipStream_t s) {
+    if (head_size == 128)
+        return bf16 ? launch_bwd_cfg<128, true>(p, max_seqlen_q, max_seqlen_kv, s)
+                    : launch_bwd_cfg<128, false>(p, max_seqlen_q, max_seqlen_kv, s);
+    if (head_size == 64)
+        return bf16 ? launch_bwd_cfg<64, true>(p, max_seqlen_q, max_seqlen_kv, s)
+                    : launch_bwd_cfg<64, false>(p, max_seqlen_q, max_seqlen_kv, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -150,6 +150,25 @@ inline int64_t tiles_per_xcd(int batch, int n_hg, int total_q, int max_seqlen_q,
     return by_len < by_total ? by_len : by_total;
 }
 
+// Binary searches over a non-decreasing int32 array a[0..n).
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int x) {
+    int lo = 0, hi = n;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] <= x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ int wave_max(int x) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) x = max(x, __shfl_xor(x, s, 64));

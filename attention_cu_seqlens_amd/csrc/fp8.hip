@@ -39,24 +39,6 @@ __device__ __forceinline__ f32x16_t mfma_fp8(const i32x8_t& a, const i32x8_t& b,
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] <= x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
 constexpr int D8 = 128;     // head size (bytes per row)
 constexpr int BN8 = 128;    // keys per tile
 constexpr int kStages8 = 4;

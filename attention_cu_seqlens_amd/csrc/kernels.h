@@ -71,6 +71,29 @@ struct RotaryParams {
     int interleaved;
 };
 
+// Varlen backward (16-bit dtypes, packed K/V): delta, dQ and dK/dV kernels.
+struct BwdParams {
+    const uint16_t* q;          // [total_q, Hq, D]
+    const uint16_t* k;          // [total_kv, Hkv, D]
+    const uint16_t* v;
+    const uint16_t* out;        // forward output [total_q, Hq, D]
+    const uint16_t* dout;       // upstream gradient [total_q, Hq, D]
+    const float* lse;           // [total_q, Hq], natural log
+    const int32_t* cu_q;
+    const int32_t* cu_kv;
+    const int32_t* q_ids;
+    const int32_t* kv_ids;
+    uint16_t* dq;               // [total_q, Hq, D]
+    uint16_t* dk;               // [total_kv, Hkv, D]
+    uint16_t* dv;
+    float* delta;               // workspace [total_q, Hq]: rowsum(dO * O)
+    int batch, num_heads, num_kv_heads, group, total_q;
+    uint32_t mask;
+    int window;
+    float scale;
+    float c;                    // scale * log2(e)
+};
+
 // Query rows (token x packed head) per prefill workgroup, and the bytes of
 // its block-sparse state: one byte per (local query block, key block).
 constexpr int kPrefillRows = 256;
@@ -136,6 +159,8 @@ hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache,
                                     const int32_t* cu_kv, int batch, int total_new,
                                     int row_bytes, int bs_log2, hipStream_t s);
 hipError_t launch_rotary_cache(const RotaryParams& p, bool bf16, hipStream_t s);
+hipError_t launch_varlen_bwd(const BwdParams& p, int head_size, bool bf16, int max_seqlen_q,
+                             int max_seqlen_kv, hipStream_t s);
 hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16,
                                 int max_seqlen_q, hipStream_t s);
 hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s);

@@ -28,28 +28,6 @@
 
 namespace attn {
 
-namespace {
-
-__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-__device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int x) {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] <= x) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
-}  // namespace
-
 // Ring depth: up to kStages - 1 tiles in flight while one is consumed.
 constexpr int kStages = 4;
 

@@ -17,8 +17,8 @@ decode over an fp8 e4m3 cache (one byte per element), the varlen prefill
 under 128x128 causal block lists through the block-sparse entry point, the
 fused rotary + packed-QKV unpack + cache write of its tokens (HBM GB/s), a plain
 device-to-device copy (the practical HBM ceiling, and the calibration kernel
-for the traffic counters), byte->patch cross attention and dense causal fp8
-(TFLOP/s).
+for the traffic counters), byte->patch cross attention, dense causal fp8 and
+the varlen backward on the same workload (TFLOP/s).
 
 `roofline.traffic` is the HBM bytes one prefill launch moves, from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json;
@@ -281,6 +281,44 @@ def bench_prefill_generic(A, W, torch, dev, w, flops, iters=20, block_mask=None)
             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": flops}
 
 
+def bench_backward(A, W, torch, dev, iters=10):
+    """Varlen backward (delta + dQ + dK/dV kernels) on the varlen causal
+    workload, packed K / V; O and the LSE from the paged forward.  Work is
+    counted the usual way, 2.5x the forward's causal flops (five products
+    per visible pair: S, dP, dV, dK, dQ); the kernels recompute S and dP in
+    both the dQ and the dK/dV pass, seven products in all."""
+    w = W.varlen_gqa_causal_bf16(device=dev)
+    lens_q, lens_kv, kc, vc, bt = paged_inputs(w, A, torch, dev)
+    cu_q = A.attn_cu_seqlens(lens_q)
+    cu_kv = A.attn_cu_seqlens(lens_kv)
+    A.attn_reshape_and_cache(w.k_new, w.v_new, kc, vc, bt, cu_kv, cu_kv)
+    mq, mk = int(w.q_lens.max()), int(w.kv_lens.max())
+    out, lse = A.attn_paged_prefill_fwd(w.q, kc, vc, bt, cu_q, cu_kv, mq, mk, scale=w.scale,
+                                        mask_flags=w.mask_flags, return_lse=True)
+    del kc, vc
+    dout = W.make_dout(1007, w)
+    dq, dk, dv = torch.empty_like(w.q), torch.empty_like(w.k_new), torch.empty_like(w.v_new)
+    ws = torch.empty(A.attn_varlen_bwd_workspace_bytes(w.total_q, w.num_heads), dtype=torch.uint8,
+                     device=dev)
+
+    def run():
+        A.attn_varlen_bwd(w.q, w.k_new, w.v_new, out, dout, lse, cu_q, cu_kv, mq, mk,
+                          scale=w.scale, mask_flags=w.mask_flags, dq=dq, dk=dk, dv=dv,
+                          workspace=ws)
+
+    for _ in range(2):
+        run()
+    ms = timed(run, iters, torch)
+    flops = 2.5 * 4.0 * w.head_size * w.num_heads * causal_pairs(w.q_lens, w.kv_lens)
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+           "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": flops,
+           "flops_convention": "2.5 x forward causal flops"}
+    del out, lse, dout, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_fp8(A, W, torch, dev, iters=20):
     w = W.dense_causal_fp8(device=dev)
     cu_q = A.attn_cu_seqlens(i32(w.q_lens, torch, dev))
@@ -423,6 +461,8 @@ def main():
         torch.cuda.empty_cache()
         log("fp8")
         line["fp8"] = bench_fp8(A, W, torch, dev)
+        log("varlen backward")
+        line["backward"] = bench_backward(A, W, torch, dev)
 
     if not args.no_cpu:
         log("cpu oracle baseline")

@@ -258,6 +258,46 @@ attn_status attn_paged_prefill_block_sparse_fwd(
     const int32_t* full_kv_indices, attn_dtype dtype, void* out, float* lse, void* stream);
 
 /*
+ * attn_varlen_bwd_workspace_bytes -- workspace attn_varlen_bwd needs: one
+ * float per (query row, head), rounded up to 256 bytes.  Host only.
+ */
+size_t attn_varlen_bwd_workspace_bytes(int32_t total_q, int32_t num_heads);
+
+/*
+ * attn_varlen_bwd -- gradients of the varlen attention forward (the backward
+ * that the FlexAttention LSE output of the blt issue's kernel options and
+ * the varlen function of the vllm-project/flash-attention "Rope dim" review
+ * serve).  With P the masked softmax of scale * q k^T, the forward output
+ * O = P v, the upstream gradient dO and delta = rowsum(dO * O):
+ * dv = P^T dO, dS = P * (dO v^T - delta), dq = scale dS k, dk = scale dS^T q;
+ * dk and dv sum over the query heads of each kv head.  P is rebuilt from
+ * the forward's lse (natural log, as attn_paged_prefill_fwd returns it).
+ * K and V are packed varlen tensors here (training holds them unpaged).
+ *   q, out, dout [total_q, num_heads, head_size];  k, v [total_kv,
+ *                num_kv_heads, head_size];  lse float32 [total_q, num_heads]
+ *   cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
+ *   mask_flags, q_ids, kv_ids, window_left  as attn_paged_prefill_fwd (the
+ *                same mask; no softcap)
+ *   dq [total_q, num_heads, head_size], dk, dv [total_kv, num_kv_heads,
+ *                head_size]: written whole (rows no key or query reaches get 0)
+ *   workspace    device scratch of attn_varlen_bwd_workspace_bytes bytes,
+ *                256-byte aligned, owned by the caller, no initialisation;
+ *                calls sharing it must not overlap in time
+ * dtype ATTN_F16 or ATTN_BF16 for every 16-bit tensor; head_size 64 or 128.
+ * All tensors 16-byte aligned device memory.  Errors: as
+ * attn_paged_prefill_fwd, plus ATTN_ERR_WORKSPACE.
+ */
+attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
+                            const void* dout, const float* lse, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_kv, int32_t batch, int32_t total_q,
+                            int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            float scale, uint32_t mask_flags, const int32_t* q_ids,
+                            const int32_t* kv_ids, int32_t window_left, attn_dtype dtype,
+                            void* dq, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * attn_paged_decode_workspace_bytes -- workspace size attn_paged_decode_fwd
  * needs for these sizes (same window_left and split_tokens arguments).  Host
  * only, no HIP call.  Returns 0 for invalid sizes.

@@ -98,6 +98,35 @@ def test_rotary_cache_host_checks(lib):
     assert call(qout=ctypes.c_void_p(24)) == 2                 # misaligned
 
 
+def test_varlen_bwd_host_checks(lib):
+    ws = lib.attn_varlen_bwd_workspace_bytes
+    assert ws(100, 8) == 3328            # 3200 rounded up to 256
+    assert ws(-1, 8) == 0 and ws(10, 0) == 0
+    f = lib.attn_varlen_bwd
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, cuq=P, cukv=P, batch=2, tq=100, tkv=100,
+                 msq=64, mskv=64, hq=8, hkv=2, d=128, scale=0.1, mask=1, qids=None, kvids=None,
+                 window=0, dtype=1, dq=P, dk=P, dv=P, ws=ctypes.c_void_p(256), wsb=3328,
+                 stream=None)
+        a.update(kw)
+        return f(*a.values())
+
+    assert call(batch=0) == 0
+    assert call(lse=None) == 1
+    assert call(dk=None) == 1
+    assert call(d=96) == 3
+    assert call(dtype=2) == 3
+    assert call(hq=6, hkv=4) == 2
+    assert call(window=-1) == 2
+    assert call(scale=float("inf")) == 2
+    assert call(mask=2) == 1                      # DOCUMENT needs both id arrays
+    assert call(wsb=3327) == 6
+    assert call(ws=None) == 6
+    assert call(ws=ctypes.c_void_p(128)) == 6     # not 256-byte aligned
+    assert call(dq=ctypes.c_void_p(24)) == 2      # misaligned
+
+
 def _prefill_args(**kw):
     a = dict(q=P, kc=P, vc=P, bt=P, mbps=8, cuq=P, cukv=P, batch=2, total_q=100, msq=64, mskv=64,
              hq=8, hkv=2, d=128, bs=16, nb=32, scale=0.1, mask=1, qids=None, kvids=None, window=0,

@@ -226,6 +226,14 @@ def to_fp8_cache(w):
     return w
 
 
+def make_dout(seed, w, device=None):
+    """Upstream gradient for a workload's output: [total_q, Hq, D] ~ N(0, 1)
+    in the workload's 16-bit type."""
+    device = w.q.device if device is None else device
+    gen = _generator(seed, device)
+    return _cast(_randn(gen, (w.total_q, w.num_heads, w.head_size), device), w.dtype)
+
+
 def rope_tables(max_position, rotary_dim, base=10000.0):
     """Angle tables of the usual rotary embedding, float32 [max_position,
     rotary_dim / 2]: entry (p, j) is cos / sin of p * base^(-2j / rotary_dim)

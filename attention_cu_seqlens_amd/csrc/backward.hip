@@ -66,38 +66,72 @@ struct StageRows {
     }
 };
 
-// x[kb] (rows kb*32.. of the tile, column = lane's column) = tile rows . b
-// over D: the S^T = K Q^T pattern, b holding this lane column's row as the
-// B operand (dims 16t + 8g .. +7 in b[t]).
-template <int D, bool BF16>
-__device__ __forceinline__ void rows_dot(f32x16_t (&x)[2], const uint8_t* tile,
-                                         const u32x4_t (&b)[D / 16]) {
-    constexpr int ROWB = 2 * D;
-    const int lane = lane_id(), col = lane & 31, g = lane >> 5;
-    const uint32_t lok = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
+// MFMA steps 0 .. N-1 with their A operands read PD steps ahead through a
+// small register ring (the forward's prefetch queue): without it the
+// compiler reuses one operand register and every MFMA waits out a full LDS
+// read.  sched_barrier pins the order.
+template <int N, int PD, class Frag, class Op>
+__device__ __forceinline__ void mfma_queue(const Frag& frag, const Op& op) {
+    constexpr int P = PD < N ? PD : N;
+    u32x4_t a[P + 1];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t)
+    for (int i = 0; i < P; ++i) a[i] = frag(i);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const u32x4_t a =
-                *reinterpret_cast<const u32x4_t*>(tile + kb * 32 * ROWB + (lok ^ (uint32_t)(t << 5)));
-            x[kb] = mfma32<BF16>(a, b[t], t == 0 ? f32x16_t{} : x[kb]);
-        }
+    for (int i = 0; i < N; ++i) {
+        if (i + P < N) a[(i + P) % (P + 1)] = frag(i + P);
+        __builtin_amdgcn_sched_barrier(0);
+        op(i, a[i % (P + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
-// y[db] (rows = dims, column = lane's column) += tile^T . X with X the
-// packed 16-bit accumulators of a rows_dot product (rows = tile rows): the
-// P.V pattern with the transposed LDS read.
+constexpr int kBwdPrefetch = 4;
+
+// Two row products of one tile pair in one queue:
+//   x[kb] = tile_x rows . bx,  y[kb] = tile_y rows . by   (kb = 0, 1)
+// -- the S^T = K Q^T pattern: rows kb*32.. of the LDS tile against this lane
+// column's register row (dims 16t + 8g .. +7 in b[t]).
 template <int D, bool BF16>
-__device__ __forceinline__ void cols_acc(f32x16_t (&y)[D / 32], const uint8_t* tile,
-                                         const u32x4_t (&xb)[2][2]) {
+__device__ __forceinline__ void rows_dot2(f32x16_t (&x)[2], f32x16_t (&y)[2], const uint8_t* tx,
+                                          const uint8_t* ty, const u32x4_t (&bx)[D / 16],
+                                          const u32x4_t (&by)[D / 16]) {
+    constexpr int ROWB = 2 * D;
+    constexpr int H = (D / 16) * 2;   // steps per product
+    const int lane = lane_id(), col = lane & 31, g = lane >> 5;
+    uint32_t lok = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
+    asm volatile("" : "+v"(lok));
+    auto frag = [&](int i) {
+        const int j = i % H, t = j / 2, kb = j % 2;
+        const uint8_t* tile = i < H ? tx : ty;
+        return *reinterpret_cast<const u32x4_t*>(tile + kb * 32 * ROWB + (lok ^ (uint32_t)(t << 5)));
+    };
+    auto op = [&](int i, const u32x4_t& a) {
+        const int j = i % H, t = j / 2, kb = j % 2;
+        if (i < H) x[kb] = mfma32<BF16>(a, bx[t], t == 0 ? f32x16_t{} : x[kb]);
+        else y[kb] = mfma32<BF16>(a, by[t], t == 0 ? f32x16_t{} : y[kb]);
+    };
+    mfma_queue<2 * H, kBwdPrefetch>(frag, op);
+}
+
+// Column accumulations of one or two tiles in one queue:
+//   y1[db] += tile1^T . X1  (and y2[db] += tile2^T . X2 when TWO)
+// with X the packed 16-bit accumulators of a row product (rows = tile rows):
+// the P.V pattern with the transposed LDS read.
+template <int D, bool BF16, bool TWO>
+__device__ __forceinline__ void cols_acc(f32x16_t (&y1)[D / 32], const uint8_t* t1,
+                                         const u32x4_t (&x1)[2][2], f32x16_t (&y2)[D / 32],
+                                         const uint8_t* t2, const u32x4_t (&x2)[2][2]) {
+    constexpr int H = (D / 32) * 4;
     uint32_t lo0, hi0;
     pv_offsets<D>(lo0, hi0);
-#pragma unroll
-    for (int i = 0; i < (D / 32) * 4; ++i) {
-        const int db = i / 4, kb = (i / 2) % 2, tp = i % 2;
-        y[db] = mfma32<BF16>(pv_frag<D, kBwdTile>(tile, lo0, hi0, i), xb[kb][tp], y[db]);
-    }
+    asm volatile("" : "+v"(lo0), "+v"(hi0));
+    auto frag = [&](int i) { return pv_frag<D, kBwdTile>(i < H ? t1 : t2, lo0, hi0, i % H); };
+    auto op = [&](int i, const u32x4_t& a) {
+        const int j = i % H, db = j / 4, kb = (j / 2) % 2, tp = j % 2;
+        if (i < H) y1[db] = mfma32<BF16>(a, x1[kb][tp], y1[db]);
+        else y2[db] = mfma32<BF16>(a, x2[kb][tp], y2[db]);
+    };
+    mfma_queue<(TWO ? 2 : 1) * H, kBwdPrefetch>(frag, op);
 }
 
 // Accumulator values 8tp .. 8tp+7 of block kb packed as the B operand.
@@ -203,6 +237,10 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     const bool any = valid && hi > lo;
     const int w_lo = wave_min(any ? lo : 0x7fffffff);
     const int w_hi = wave_max(any ? hi : -1);
+    // a tile inside every row's interval needs no mask (rows past the
+    // sequence count as empty, so a wave holding any is never "full")
+    const int w_lo_max = wave_max(valid ? lo : 0x7fffffff);
+    const int w_hi_min = wave_min(valid ? hi : -1);
     if (lane == 0) {
         wave_range[0][w] = w_lo;
         wave_range[1][w] = w_hi;
@@ -240,23 +278,35 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
                 sk.load(kbase, stride, j0 + kBwdTile, kv_len, tid);
                 sv.load(vbase, stride, j0 + kBwdTile, kv_len, tid);
             }
-            f32x16_t s[2], dp[2];
-            rows_dot<D, BF16>(s, kt, qv);
-            rows_dot<D, BF16>(dp, vt, dov);
-            u32x4_t xb[2][2];
+            // this wave's rows against keys j0 .. j0 + 63: none visible (skip),
+            // all visible (no mask), or some
+            const bool skip = j0 >= w_hi || j0 + kBwdTile <= w_lo;
+            if (!skip) {
+                const bool full = j0 >= w_lo_max && j0 + kBwdTile <= w_hi_min;
+                f32x16_t s[2], dp[2];
+                rows_dot2<D, BF16>(s, dp, kt, vt, qv, dov);
+                u32x4_t xb[2][2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float ds[16];
+                for (int kb = 0; kb < 2; ++kb) {
+                    float ds[16];
+                    if (full) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                    const float pr = (key >= lo && key < hi)
-                                         ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -lse2)) : 0.f;
-                    ds[e] = pr * (dp[kb][e] - dlt);
+                        for (int e = 0; e < 16; ++e)
+                            ds[e] = fast_exp2(__builtin_fmaf(s[kb][e], p.c, -lse2)) * (dp[kb][e] - dlt);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+                            const float pr = (key >= lo && key < hi)
+                                                 ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -lse2))
+                                                 : 0.f;
+                            ds[e] = pr * (dp[kb][e] - dlt);
+                        }
+                    }
+                    pack_block<BF16>(ds, xb[kb]);
                 }
-                pack_block<BF16>(ds, xb[kb]);
+                cols_acc<D, BF16, false>(acc, kt, xb, acc, kt, xb);
             }
-            cols_acc<D, BF16>(acc, kt, xb);
             if (more) {
                 sk.store(lds[(it + 1) & 1], tid);
                 sv.store(lds[(it + 1) & 1] + TILE, tid);
@@ -273,7 +323,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][Q, dO]
     __shared__ __attribute__((aligned(16))) float rows_lse2[2][kBwdTile];
     __shared__ __attribute__((aligned(16))) float rows_delta[2][kBwdTile];
-    __shared__ __attribute__((aligned(16))) int rows_id[2][kBwdTile];
+    __shared__ __attribute__((aligned(16))) int rows_lo[2][kBwdTile];
+    __shared__ __attribute__((aligned(16))) int rows_hi[2][kBwdTile];
+    __shared__ int tile_ext[2][4];   // per tile: max lo, min hi, min lo, max hi
     const int b = blockIdx.z, hk = blockIdx.y;
     const int kv_start = p.cu_kv[b], kv_len = p.cu_kv[b + 1] - kv_start;
     const int k0 = blockIdx.x * kBwdRows;
@@ -293,9 +345,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
         kr[t] = *reinterpret_cast<const u32x4_t*>(p.k + krow * D + 16 * t + 8 * g);
         vr[t] = *reinterpret_cast<const u32x4_t*>(p.v + krow * D + 16 * t + 8 * g);
     }
-    const bool causal = p.mask & kMaskCausal, patch = p.mask & kMaskPatch;
-    const bool doc = p.mask & kMaskDocument;
-    const int kid = doc ? p.kv_ids[kv_start + kk] : 0;
+    const bool causal = p.mask & kMaskCausal;
+    // this wave's keys
+    const int wk_lo = k0 + w * 32;
+    const int wk_hi = min(wk_lo + 32, kv_len);   // exclusive
 
     // queries that can see any of keys k0 .. k0 + 127
     int qlo = 0, qhi = q_len;
@@ -319,16 +372,41 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
             sq.load(p.q + base * D, stride, j0, q_len, tid);
             sd.load(p.dout + base * D, stride, j0, q_len, tid);
         };
-        // per-row values of tile it into buffer bf (threads 0..63)
+        // per-row values of tile it into buffer bf (wave 0): LSE, delta and
+        // the row's visible keys [lo, hi) as in the forward (empty for rows
+        // past the sequence), plus the tile's extreme bounds
         auto rows = [&](int it, int bf) {
             if (tid < kBwdTile) {
                 const int h = head_of(it), q = row0_of(it) + tid;
                 const bool in = q < q_len;
                 const int64_t i = (int64_t)(q_start + (in ? q : q_len - 1)) * p.num_heads + h;
-                // a row past the sequence gets probability 0 through lse2 = +inf
-                rows_lse2[bf][tid] = in ? p.lse[i] * kLog2e : __builtin_huge_valf();
+                rows_lse2[bf][tid] = in ? p.lse[i] * kLog2e : 0.f;
                 rows_delta[bf][tid] = in ? p.delta[i] : 0.f;
-                rows_id[bf][tid] = (patch || doc) ? p.q_ids[q_start + (in ? q : q_len - 1)] : 0;
+                int lo = 0, hi = 0;
+                if (in) {
+                    hi = kv_len;
+                    if (causal) hi = min(hi, q + off + 1);
+                    if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + q] + 1);
+                    if (p.mask & kMaskDocument) {
+                        const int d = p.q_ids[q_start + q];
+                        lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, d);
+                        hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, d));
+                    }
+                    if (p.window > 0) lo = max(lo, q + off - p.window + 1);
+                    if (hi < lo) hi = lo;
+                }
+                rows_lo[bf][tid] = lo;
+                rows_hi[bf][tid] = hi;
+                const int lo_max = wave_max(lo), hi_min = wave_min(hi);
+                const bool ne = hi > lo;
+                const int lo_min = wave_min(ne ? lo : 0x7fffffff);
+                const int hi_max = wave_max(ne ? hi : -1);
+                if (tid == 0) {
+                    tile_ext[bf][0] = lo_max;
+                    tile_ext[bf][1] = hi_min;
+                    tile_ext[bf][2] = lo_min;
+                    tile_ext[bf][3] = hi_max;
+                }
             }
         };
         load(0);
@@ -343,38 +421,50 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
             const uint8_t* dt = qt + TILE;
             const bool more = it + 1 < n_t;
             if (more) load(it + 1);
-            f32x16_t s[2], dp[2];
-            rows_dot<D, BF16>(s, qt, kr);
-            rows_dot<D, BF16>(dp, dt, vr);
-            u32x4_t pbp[2][2], pbs[2][2];
+            // this wave's keys against the tile's rows: none visible (skip),
+            // all visible (no mask), or some
+            const int lo_max = tile_ext[bf][0], hi_min = tile_ext[bf][1];
+            const int lo_min = tile_ext[bf][2], hi_max = tile_ext[bf][3];
+            const bool skip = wk_hi <= wk_lo || wk_hi <= lo_min || wk_lo >= hi_max;
+            if (!skip) {
+                const bool full = lo_max <= wk_lo && hi_min >= wk_hi && wk_hi - wk_lo == 32;
+                f32x16_t s[2], dp[2];
+                rows_dot2<D, BF16>(s, dp, qt, dt, kr, vr);
+                u32x4_t pbp[2][2], pbs[2][2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float pv[16], dsv[16];
+                for (int kb = 0; kb < 2; ++kb) {
+                    float pv[16], dsv[16];
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int tr = kb * 32 + 8 * rq + 4 * g;   // tile rows tr .. tr+3
-                    const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&rows_lse2[bf][tr]);
-                    const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&rows_delta[bf][tr]);
-                    const i32x4_t id4 = *reinterpret_cast<const i32x4_t*>(&rows_id[bf][tr]);
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const int tr = kb * 32 + 8 * rq + 4 * g;   // tile rows tr .. tr+3
+                        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&rows_lse2[bf][tr]);
+                        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&rows_delta[bf][tr]);
+                        if (full) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int e = 4 * rq + i, q = j0 + tr + i;
-                        bool vis = kvalid;
-                        if (causal) vis = vis && key <= q + off;
-                        if (p.window > 0) vis = vis && key > q + off - p.window;
-                        if (patch) vis = vis && key <= id4[i];
-                        if (doc) vis = vis && kid == id4[i];
-                        const float pr =
-                            vis ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -l4[i])) : 0.f;
-                        pv[e] = pr;
-                        dsv[e] = pr * (dp[kb][e] - d4[i]);
+                            for (int i = 0; i < 4; ++i) {
+                                const int e = 4 * rq + i;
+                                pv[e] = fast_exp2(__builtin_fmaf(s[kb][e], p.c, -l4[i]));
+                                dsv[e] = pv[e] * (dp[kb][e] - d4[i]);
+                            }
+                        } else {
+                            const i32x4_t lo4 = *reinterpret_cast<const i32x4_t*>(&rows_lo[bf][tr]);
+                            const i32x4_t hi4 = *reinterpret_cast<const i32x4_t*>(&rows_hi[bf][tr]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int e = 4 * rq + i;
+                                const bool vis = kvalid && key >= lo4[i] && key < hi4[i];
+                                const float pr =
+                                    vis ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -l4[i])) : 0.f;
+                                pv[e] = pr;
+                                dsv[e] = pr * (dp[kb][e] - d4[i]);
+                            }
+                        }
                     }
+                    pack_block<BF16>(pv, pbp[kb]);
+                    pack_block<BF16>(dsv, pbs[kb]);
                 }
-                pack_block<BF16>(pv, pbp[kb]);
-                pack_block<BF16>(dsv, pbs[kb]);
+                cols_acc<D, BF16, true>(dv, dt, pbp, dk, qt, pbs);
             }
-            cols_acc<D, BF16>(dv, dt, pbp);
-            cols_acc<D, BF16>(dk, qt, pbs);
             if (more) {
                 rows(it + 1, bf ^ 1);
                 sq.store(lds[bf ^ 1], tid);

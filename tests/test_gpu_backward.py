@@ -146,3 +146,11 @@ def test_full_varlen_causal_sampled(A):
     _cmp(dq[gi], rq, f"{w.name} seqs {seqs} dq")
     _cmp(dk[ki], rk, f"{w.name} seqs {seqs} dk")
     _cmp(dv[ki], rv, f"{w.name} seqs {seqs} dv")
+
+
+def test_empty_sequences(A):
+    """A sequence with queries but no keys (O = 0, LSE = -inf: dq = 0) and
+    one with keys but no queries (dk = dv = 0), next to a normal one."""
+    w = W.make_prefill("bw5", 134, "bf16", [0, 50, 30], [20, 0, 30], 8, 2, 128, 16, 0,
+                       device=DEV)
+    _case(A, w, 135, "empty_sequences")

@@ -129,3 +129,22 @@ def test_full_varlen_causal_block_lists(A):
     g = torch.as_tensor(q_idx[rows], device=out.device)
     compare(out[g], lse[g], ref_o[rows], ref_l[rows], ATOL_16, REL_16,
             what=f"{w.name} block-sparse seqs {seqs}")
+
+
+@pytest.mark.parametrize("random_lists", [False, True])
+def test_keys_beyond_one_page_window(A, random_lists):
+    """kv_len 20000 at block size 16: the key range spans three chunks of
+    512 pages, each compacted to its own listed tiles."""
+    w = W.make_prefill("bslong", 136, "bf16", [200, 37], [20000, 9000], 8, 2, 128, 16,
+                       W.MASK_CAUSAL)
+    cache = gpu_cache(w, A)
+    if random_lists:
+        rng = np.random.default_rng(137)
+        bm = (64, 64) + W.random_block_mask(rng, w.q_lens, w.kv_lens, 64, 64, 2, p_partial=0.2,
+                                            p_full=0.2)
+        _case(A, w, bm, "long_kv_random", cache=cache)
+    else:
+        bm = (128, 128) + W.causal_block_mask(w.q_lens, w.kv_lens, 128, 128)
+        out, lse = _case(A, w, bm, "long_kv_causal_lists", cache=cache)
+        out_c, lse_c = gpu_prefill(w, A, cache=cache)
+        assert torch.equal(out, out_c) and torch.equal(lse, lse_c)

@@ -68,7 +68,9 @@ Readings where the pages are silent (each is also listed in the design doc):
     forward's definition above: with P the masked softmax, O = P V and an
     upstream dO, dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)),
     dQ = scale dS K, dK = scale dS^T Q; GQA sums dK and dV over the query
-    heads of a kv head; a row with no visible key contributes nothing.
+    heads of a kv head; a row with no visible key contributes nothing.  With
+    a score cap c the score is c tanh(scale q.k / c), so dS is multiplied by
+    its derivative 1 - tanh^2 before the dQ and dK products.
 """
 
 import collections
@@ -106,8 +108,9 @@ PIN_STATUS = {
               "relative-position invariance of q.k",
     "rotary_reshape_and_cache": "pinned: composition of the pinned steps; decode position = kv_len - 1",
     "attention_varlen_bwd": "pinned: torch.autograd through CPU fp64 SDPA with explicit masks (GQA, causal, "
-                            "window, document, q shorter than kv), central finite differences on a tiny case, "
-                            "fully masked rows give zero gradients",
+                            "window, document, q shorter than kv) and through composed capped attention, "
+                            "central finite differences (with and without a cap), fully masked rows give "
+                            "zero gradients",
     "e4m3_decode": "pinned: all 256 codes against torch.float8_e4m3fn; closed-form extremes",
     "fp8_attention": "pinned: equals attention_varlen on decoded values; hand-derived two-key example",
     "default_scale": "pinned: golden value 0.0625 at E=256 from [BLT]",
@@ -410,12 +413,13 @@ def attention_varlen(q, k, v, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=No
 
 
 def attention_varlen_bwd(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None,
-                         window=0):
-    """Gradients of attention_varlen (softcap 0) with respect to q, k, v for
-    the upstream gradient dout [total_q, Hq, Dv], fp64 (module docstring:
-    backward).  Per sequence and head the forward is recomputed from its
-    definition (no LSE input), then dV = P^T dO, dP = dO V^T,
-    dS = P * (dP - rowsum(dP * P)), dQ = scale dS K, dK = scale dS^T Q.
+                         window=0, softcap=0.0):
+    """Gradients of attention_varlen with respect to q, k, v for the upstream
+    gradient dout [total_q, Hq, Dv], fp64 (module docstring: backward).  Per
+    sequence and head the forward is recomputed from its definition (no LSE
+    input), then dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dP * P)),
+    times 1 - tanh^2 of the capped score when softcap > 0,
+    dQ = scale dS K, dK = scale dS^T Q.
     Returns (dq [total_q, Hq, D], dk [total_kv, Hkv, D], dv [total_kv, Hkv, Dv]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -434,7 +438,11 @@ def attention_varlen_bwd(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None,
         for h in range(hq):
             kvh = h // group
             Q, K, V, dO = q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh], dout[q0:q1, h]
-            s = np.where(vis, scale * (Q @ K.T), -np.inf)
+            raw = scale * (Q @ K.T)
+            if softcap > 0:
+                th = np.tanh(raw / softcap)
+                raw = softcap * th
+            s = np.where(vis, raw, -np.inf)
             m = s.max(axis=1, initial=-np.inf, keepdims=True)
             e = np.where(vis, np.exp(s - np.where(np.isfinite(m), m, 0.0)), 0.0)
             tot = e.sum(axis=1, keepdims=True)
@@ -442,6 +450,8 @@ def attention_varlen_bwd(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None,
             dv[k0:k1, kvh] += P.T @ dO
             dP = dO @ V.T
             dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+            if softcap > 0:
+                dS = dS * (1.0 - th * th)
             dq[q0:q1, h] = scale * (dS @ K)
             dk[k0:k1, kvh] += scale * (dS.T @ Q)
     return dq, dk, dv

@@ -741,6 +741,50 @@ def check_bwd_finite_differences(A):
         assert np.allclose(grads[which], num, rtol=1e-6, atol=1e-8), which
 
 
+def check_bwd_softcap(A):
+    """With a score cap: torch.autograd through the composed forward
+    (cap * tanh(scale q k^T / cap), masked softmax, P V) in fp64, and central
+    differences on a tiny case."""
+    rng = np.random.default_rng(54)
+    L, S, HQ, HKV, D, cap, scale = 7, 9, 2, 1, 4, 1.5, 0.8
+    q, k, v, do = _rand(rng, L, HQ, D), _rand(rng, S, HKV, D), _rand(rng, S, HKV, D), _rand(rng, L, HQ, D)
+    q = 2.0 * q                                     # scores large enough for the cap to bend
+    dq, dk, dv = A.attention_varlen_bwd(q, k, v, do, [0, L], [0, S], scale, ORC.MASK_CAUSAL,
+                                        softcap=cap)
+    mask = torch.from_numpy(np.tril(np.ones((L, S), dtype=bool), S - L))
+    Q = torch.from_numpy(q).requires_grad_()
+    K = torch.from_numpy(k).requires_grad_()
+    V = torch.from_numpy(v).requires_grad_()
+    outs = []
+    for h in range(HQ):
+        sc = cap * torch.tanh(scale * (Q[:, h] @ K[:, 0].T) / cap)
+        pr = torch.softmax(sc.masked_fill(~mask, float("-inf")), dim=1)
+        outs.append(pr @ V[:, 0])
+    torch.stack(outs, dim=1).backward(torch.from_numpy(do))
+    assert np.allclose(dq, Q.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dk, K.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv, V.grad.numpy(), rtol=1e-10, atol=1e-12)
+    # central differences on a smaller case
+    q2, k2, v2, do2 = q[:3, :1, :2], k[:4, :, :2], v[:4, :, :2], do[:3, :1, :2]
+    g = A.attention_varlen_bwd(q2, k2, v2, do2, [0, 3], [0, 4], 0.9, ORC.MASK_CAUSAL, softcap=0.7)
+
+    def loss(a, b, c):
+        o = A.attention_varlen(a, b, c, [0, 3], [0, 4], 0.9, ORC.MASK_CAUSAL, softcap=0.7)[0]
+        return float(np.sum(o * do2))
+
+    eps = 1e-6
+    for which, x in enumerate((q2, k2, v2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            ap, am = [q2, k2, v2], [q2, k2, v2]
+            ap[which], am[which] = xp, xm
+            num[idx] = (loss(*ap) - loss(*am)) / (2 * eps)
+        assert np.allclose(g[which], num, rtol=1e-6, atol=1e-8), which
+
+
 def check_window_bands(A):
     """Causal + window W: a band of W keys ending on the (bottom-right) diagonal,
     built here from np.tril / np.triu; without CAUSAL the window only bounds j
@@ -1066,7 +1110,8 @@ def _mut_unpack_kv_swapped(orig):
 
 def _bwd_variant(drop_delta=False, no_gqa_sum=False):
     """The oracle's backward with one planted mistake (same steps otherwise)."""
-    def f(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, window=0):
+    def f(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, window=0,
+          softcap=0.0):
         q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
         hq, hkv = q.shape[1], k.shape[1]
         g = hq // hkv
@@ -1079,13 +1124,19 @@ def _bwd_variant(drop_delta=False, no_gqa_sum=False):
             for h in range(hq):
                 kvh = h // g
                 Q, K, V, dO = q[q0:q1, h], k[k0:k1, kvh], v[k0:k1, kvh], dout[q0:q1, h]
-                s_ = np.where(vis, scale * (Q @ K.T), -np.inf)
+                raw = scale * (Q @ K.T)
+                if softcap > 0:
+                    th = np.tanh(raw / softcap)
+                    raw = softcap * th
+                s_ = np.where(vis, raw, -np.inf)
                 m = s_.max(axis=1, initial=-np.inf, keepdims=True)
                 e = np.where(vis, np.exp(s_ - np.where(np.isfinite(m), m, 0.0)), 0.0)
                 tot = e.sum(axis=1, keepdims=True)
                 P = np.divide(e, tot, out=np.zeros_like(e), where=tot > 0)
                 dP = dO @ V.T
                 dS = P * dP if drop_delta else P * (dP - (dP * P).sum(axis=1, keepdims=True))
+                if softcap > 0:
+                    dS = dS * (1.0 - th * th)
                 if no_gqa_sum:
                     dv[k0:k1, kvh] = P.T @ dO
                     dk[k0:k1, kvh] = scale * (dS.T @ Q)
@@ -1109,6 +1160,16 @@ def _mut_bwd_dq_unscaled(orig):
     def f(q, k, v, dout, cu_q, cu_kv, scale, *a, **kw):
         dq, dk, dv = orig(q, k, v, dout, cu_q, cu_kv, scale, *a, **kw)
         return dq / scale, dk, dv
+    return f
+
+
+def _mut_bwd_cap_derivative_dropped(orig):
+    # gradient of the uncapped scores reported for a capped forward
+    def f(q, k, v, dout, cu_q, cu_kv, scale, flags=0, q_ids=None, kv_ids=None, window=0,
+          softcap=0.0):
+        if softcap <= 0:
+            return orig(q, k, v, dout, cu_q, cu_kv, scale, flags, q_ids, kv_ids, window)
+        return orig(q, k, v, dout, cu_q, cu_kv, scale, flags, q_ids, kv_ids, window, 1e12)
     return f
 
 
@@ -1142,6 +1203,7 @@ MUTATIONS = {
     "bwd_drop_delta": ("attention_varlen_bwd", _mut_bwd_drop_delta),
     "bwd_no_gqa_sum": ("attention_varlen_bwd", _mut_bwd_no_gqa_sum),
     "bwd_dq_unscaled": ("attention_varlen_bwd", _mut_bwd_dq_unscaled),
+    "bwd_cap_derivative_dropped": ("attention_varlen_bwd", _mut_bwd_cap_derivative_dropped),
 }
 
 

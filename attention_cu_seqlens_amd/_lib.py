@@ -39,8 +39,8 @@ SIGNATURES = {
                                               _p, _p, _i32, _f32, ctypes.c_int, _p, _p, _p]),
     "attn_varlen_bwd_workspace_bytes": (_size, [_i32, _i32]),
     "attn_varlen_bwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32,
-                                       _i32, _i32, _i32, _f32, _u32, _p, _p, _i32, ctypes.c_int,
-                                       _p, _p, _p, _p, _size, _p]),
+                                       _i32, _i32, _i32, _f32, _u32, _p, _p, _i32, _f32,
+                                       ctypes.c_int, _p, _p, _p, _p, _size, _p]),
     "attn_rotary_reshape_and_cache": (
         ctypes.c_int, [_p, _p, _p, _p, _p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _i32, _p, _p,
                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _p]),

@@ -95,7 +95,7 @@ def attn_varlen_bwd_workspace_bytes(total_q, num_heads):
 
 def attn_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                     max_seqlen_kv, scale=None, mask_flags=0, q_ids=None, kv_ids=None, window=0,
-                    dq=None, dk=None, dv=None, workspace=None):
+                    softcap=0.0, dq=None, dk=None, dv=None, workspace=None):
     """Gradients (dq, dk, dv) of varlen attention: q, out, dout [total_q, Hq, D],
     k, v [total_kv, Hkv, D] (packed, 16-bit), lse float32 [total_q, Hq] from
     the forward."""
@@ -135,7 +135,8 @@ def attn_varlen_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, max_se
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(cu_seqlens_q),
             _ptr(cu_seqlens_kv), batch, total_q, total_kv, int(max_seqlen_q), int(max_seqlen_kv),
             hq, hkv, d, float(scale), int(mask_flags), _ptr(q_ids), _ptr(kv_ids), int(window),
-            _DT[q.dtype], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+            float(softcap), _DT[q.dtype], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            workspace.numel(),
             _stream(dev)))
     return dq, dk, dv
 

@@ -214,8 +214,8 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
                             int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
                             int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                             float scale, uint32_t mask_flags, const int32_t* q_ids,
-                            const int32_t* kv_ids, int32_t window_left, attn_dtype dtype,
-                            void* dq, void* dk, void* dv, void* workspace,
+                            const int32_t* kv_ids, int32_t window_left, float softcap,
+                            attn_dtype dtype, void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, void* stream) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
@@ -223,7 +223,7 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
         return ATTN_ERR_BAD_SHAPE;
     if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0)
         return ATTN_ERR_BAD_SHAPE;
-    if (!std::isfinite(scale) || window_left < 0) return ATTN_ERR_BAD_SHAPE;
+    if (!std::isfinite(scale) || !window_cap_ok(window_left, softcap)) return ATTN_ERR_BAD_SHAPE;
     const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
     if (m != ATTN_OK) return m;
     if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
@@ -264,6 +264,10 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
     p.window = window_left;
     p.scale = scale;
     p.c = scale * 1.4426950408889634f;
+    if (softcap > 0.f) {
+        p.cap_in2 = 2.f * 1.4426950408889634f * scale / softcap;
+        p.cap_out = softcap * 1.4426950408889634f;
+    }
     return from_hip(attn::launch_varlen_bwd(p, head_size, dtype == ATTN_BF16, max_seqlen_q,
                                             max_seqlen_kv, static_cast<hipStream_t>(stream)));
 }

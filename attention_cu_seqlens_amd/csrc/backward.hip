@@ -172,6 +172,26 @@ __device__ __forceinline__ f32x2_t unpack16(uint32_t w) {
     }
 }
 
+// P and dS of one score.  s: raw q.k; lse2: the row's LSE in log2 units.
+// Without a cap the log2 score is s * c.  With a cap (CAP) the score is
+// cap tanh(scale s / cap): t = 1 - 2 / (1 + 2^(s * in2)) with the signed
+// in2 = 2 log2(e) scale / cap (2^(.) overflowing to +inf gives t = 1, to 0
+// gives t = -1), the log2 score is out * t with out = cap log2(e), and dS
+// takes the derivative 1 - t^2.
+template <bool CAP>
+__device__ __forceinline__ float prob_ds(float s, float dp, float lse2, float delta,
+                                         const BwdParams& p, float& pr) {
+    if constexpr (CAP) {
+        const float e = fast_exp2(s * p.cap_in2);
+        const float t = __builtin_fmaf(-2.f, __builtin_amdgcn_rcpf(1.f + e), 1.f);
+        pr = fast_exp2(__builtin_fmaf(t, p.cap_out, -lse2));
+        return pr * (dp - delta) * __builtin_fmaf(-t, t, 1.f);
+    } else {
+        pr = fast_exp2(__builtin_fmaf(s, p.c, -lse2));
+        return pr * (dp - delta);
+    }
+}
+
 // delta[row, h] = sum_d dO * O in fp32, one thread per (row, head).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_bwd_delta(BwdParams p) {
@@ -194,7 +214,7 @@ __global__ __launch_bounds__(256) void k_bwd_delta(BwdParams p) {
     }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     constexpr int TILE = kBwdTile * 2 * D;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][K, V]
@@ -289,18 +309,17 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     float ds[16];
+                    float pr;
                     if (full) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e)
-                            ds[e] = fast_exp2(__builtin_fmaf(s[kb][e], p.c, -lse2)) * (dp[kb][e] - dlt);
+                            ds[e] = prob_ds<CAP>(s[kb][e], dp[kb][e], lse2, dlt, p, pr);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                            const float pr = (key >= lo && key < hi)
-                                                 ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -lse2))
-                                                 : 0.f;
-                            ds[e] = pr * (dp[kb][e] - dlt);
+                            const float d = prob_ds<CAP>(s[kb][e], dp[kb][e], lse2, dlt, p, pr);
+                            ds[e] = (key >= lo && key < hi) ? d : 0.f;
                         }
                     }
                     pack_block<BF16>(ds, xb[kb]);
@@ -317,7 +336,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     if (valid) store_cols<D, BF16>(acc, p.scale, p.dq + qrow * D);
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     constexpr int TILE = kBwdTile * 2 * D;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][Q, dO]
@@ -443,8 +462,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int e = 4 * rq + i;
-                                pv[e] = fast_exp2(__builtin_fmaf(s[kb][e], p.c, -l4[i]));
-                                dsv[e] = pv[e] * (dp[kb][e] - d4[i]);
+                                dsv[e] = prob_ds<CAP>(s[kb][e], dp[kb][e], l4[i], d4[i], p, pv[e]);
                             }
                         } else {
                             const i32x4_t lo4 = *reinterpret_cast<const i32x4_t*>(&rows_lo[bf][tr]);
@@ -453,10 +471,10 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
                             for (int i = 0; i < 4; ++i) {
                                 const int e = 4 * rq + i;
                                 const bool vis = kvalid && key >= lo4[i] && key < hi4[i];
-                                const float pr =
-                                    vis ? fast_exp2(__builtin_fmaf(s[kb][e], p.c, -l4[i])) : 0.f;
-                                pv[e] = pr;
-                                dsv[e] = pr * (dp[kb][e] - d4[i]);
+                                float pr;
+                                const float d = prob_ds<CAP>(s[kb][e], dp[kb][e], l4[i], d4[i], p, pr);
+                                pv[e] = vis ? pr : 0.f;
+                                dsv[e] = vis ? d : 0.f;
                             }
                         }
                     }
@@ -479,7 +497,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool CAP>
 hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_kv, hipStream_t s) {
     const int64_t n = (int64_t)p.total_q * p.num_heads;
     const int dblocks = (int)std::min<int64_t>((n + 255) / 256, 16384);
@@ -489,16 +507,23 @@ hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_k
     const unsigned qt = (unsigned)((max_seqlen_q + kBwdRows - 1) / kBwdRows);
     const unsigned kt = (unsigned)((max_seqlen_kv + kBwdRows - 1) / kBwdRows);
     if (qt > 0) {
-        hipLaunchKernelGGL((k_bwd_dq<D, BF16>), dim3(qt, p.num_heads, p.batch), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((k_bwd_dq<D, BF16, CAP>), dim3(qt, p.num_heads, p.batch), dim3(256), 0,
+                           s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (kt > 0) {
-        hipLaunchKernelGGL((k_bwd_dkdv<D, BF16>), dim3(kt, p.num_kv_heads, p.batch), dim3(256), 0,
+        hipLaunchKernelGGL((k_bwd_dkdv<D, BF16, CAP>), dim3(kt, p.num_kv_heads, p.batch), dim3(256), 0,
                            s, p);
         e = hipGetLastError();
     }
     return e;
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_cap(const BwdParams& p, int max_seqlen_q, int max_seqlen_kv, hipStream_t s) {
+    return p.cap_out > 0.f ? launch_bwd_cfg<D, BF16, true>(p, max_seqlen_q, max_seqlen_kv, s)
+                           : launch_bwd_cfg<D, BF16, false>(p, max_seqlen_q, max_seqlen_kv, s);
 }
 
 }  // namespace
@@ -506,11 +531,11 @@ hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_k
 hipError_t launch_varlen_bwd(const BwdParams& p, int head_size, bool bf16, int max_seqlen_q,
                              int max_seqlen_kv, hipStream_t s) {
     if (head_size == 128)
-        return bf16 ? launch_bwd_cfg<128, true>(p, max_seqlen_q, max_seqlen_kv, s)
-                    : launch_bwd_cfg<128, false>(p, max_seqlen_q, max_seqlen_kv, s);
+        return bf16 ? launch_bwd_cap<128, true>(p, max_seqlen_q, max_seqlen_kv, s)
+                    : launch_bwd_cap<128, false>(p, max_seqlen_q, max_seqlen_kv, s);
     if (head_size == 64)
-        return bf16 ? launch_bwd_cfg<64, true>(p, max_seqlen_q, max_seqlen_kv, s)
-                    : launch_bwd_cfg<64, false>(p, max_seqlen_q, max_seqlen_kv, s);
+        return bf16 ? launch_bwd_cap<64, true>(p, max_seqlen_q, max_seqlen_kv, s)
+                    : launch_bwd_cap<64, false>(p, max_seqlen_q, max_seqlen_kv, s);
     return hipErrorInvalidValue;
 }
 

@@ -92,6 +92,8 @@ struct BwdParams {
     int window;
     float scale;
     float c;                    // scale * log2(e)
+    float cap_in2;              // score cap: 2 log2(e) scale / cap (signed)
+    float cap_out;              // cap * log2(e); 0: no cap
 };
 
 // Query rows (token x packed head) per prefill workgroup, and the bytes of

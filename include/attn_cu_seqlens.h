@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -276,8 +276,10 @@ size_t attn_varlen_bwd_workspace_bytes(int32_t total_q, int32_t num_heads);
  *   q, out, dout [total_q, num_heads, head_size];  k, v [total_kv,
  *                num_kv_heads, head_size];  lse float32 [total_q, num_heads]
  *   cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, scale,
- *   mask_flags, q_ids, kv_ids, window_left  as attn_paged_prefill_fwd (the
- *                same mask; no softcap)
+ *   mask_flags, q_ids, kv_ids, window_left, softcap  as attn_paged_prefill_fwd
+ *                (the forward's mask and cap; under a cap c the score is
+ *                c tanh(scale q.k / c), so dS also takes its derivative
+ *                1 - tanh^2)
  *   dq [total_q, num_heads, head_size], dk, dv [total_kv, num_kv_heads,
  *                head_size]: written whole (rows no key or query reaches get 0)
  *   workspace    device scratch of attn_varlen_bwd_workspace_bytes bytes,
@@ -293,8 +295,8 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
                             int32_t total_kv, int32_t max_seqlen_q, int32_t max_seqlen_kv,
                             int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
                             float scale, uint32_t mask_flags, const int32_t* q_ids,
-                            const int32_t* kv_ids, int32_t window_left, attn_dtype dtype,
-                            void* dq, void* dk, void* dv, void* workspace,
+                            const int32_t* kv_ids, int32_t window_left, float softcap,
+                            attn_dtype dtype, void* dq, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, void* stream);
 
 /*

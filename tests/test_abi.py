@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 2
+    assert lib.attn_abi_version() == 3
     for code in range(7):
         assert lib.attn_status_string(code)
     assert lib.attn_status_string(99) == b"unknown status"
@@ -107,7 +107,7 @@ def test_varlen_bwd_host_checks(lib):
     def call(**kw):
         a = dict(q=P, k=P, v=P, out=P, dout=P, lse=P, cuq=P, cukv=P, batch=2, tq=100, tkv=100,
                  msq=64, mskv=64, hq=8, hkv=2, d=128, scale=0.1, mask=1, qids=None, kvids=None,
-                 window=0, dtype=1, dq=P, dk=P, dv=P, ws=ctypes.c_void_p(256), wsb=3328,
+                 window=0, softcap=0.0, dtype=1, dq=P, dk=P, dv=P, ws=ctypes.c_void_p(256), wsb=3328,
                  stream=None)
         a.update(kw)
         return f(*a.values())
@@ -119,6 +119,9 @@ def test_varlen_bwd_host_checks(lib):
     assert call(dtype=2) == 3
     assert call(hq=6, hkv=4) == 2
     assert call(window=-1) == 2
+    assert call(softcap=-1.0) == 2
+    assert call(softcap=float("nan")) == 2
+    assert call(batch=0, softcap=30.0) == 0
     assert call(scale=float("inf")) == 2
     assert call(mask=2) == 1                      # DOCUMENT needs both id arrays
     assert call(wsb=3327) == 6

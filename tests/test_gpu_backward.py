@@ -49,8 +49,8 @@ def _cmp(got, ref, what):
     assert rel <= REL_16, what
 
 
-def _backward(A, w, dout, window=0):
-    out, lse = gpu_prefill(w, A, window=window)
+def _backward(A, w, dout, window=0, softcap=0.0):
+    out, lse = gpu_prefill(w, A, window=window, softcap=softcap)
     cu_q = A.attn_cu_seqlens(_i32(w.q_lens))
     cu_kv = A.attn_cu_seqlens(_i32(w.kv_lens))
     q_ids = None if w.q_ids is None else _i32(w.q_ids)
@@ -58,26 +58,27 @@ def _backward(A, w, dout, window=0):
     grads = A.attn_varlen_bwd(w.q.to(DEV), w.k_new.to(DEV), w.v_new.to(DEV), out, dout.to(DEV),
                               lse, cu_q, cu_kv, int(w.q_lens.max(initial=0)),
                               int(w.kv_lens.max(initial=0)), scale=w.scale,
-                              mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, window=window)
+                              mask_flags=w.mask_flags, q_ids=q_ids, kv_ids=kv_ids, window=window,
+                              softcap=softcap)
     torch.cuda.synchronize()
     return grads
 
 
-def _oracle(w, dout, window=0):
+def _oracle(w, dout, window=0, softcap=0.0):
     return ORC.attention_varlen_bwd(w.q.double().cpu().numpy(), w.k_new.double().cpu().numpy(),
                                     w.v_new.double().cpu().numpy(),
                                     dout.double().cpu().numpy(), ORC.cu_seqlens(w.q_lens),
                                     ORC.cu_seqlens(w.kv_lens), w.scale, w.mask_flags, w.q_ids,
-                                    w.kv_ids, window)
+                                    w.kv_ids, window, softcap)
 
 
-def _case(A, w, seed, what, window=0):
+def _case(A, w, seed, what, window=0, softcap=0.0):
     banner(f"backward {what}: q={w.q_lens.tolist()} kv={w.kv_lens.tolist()} "
            f"H={w.num_heads}/{w.num_kv_heads} D={w.head_size} mask={w.mask_flags} "
-           f"window={window} {w.dtype}")
+           f"window={window} softcap={softcap} {w.dtype}")
     dout = W.make_dout(seed, w)
-    dq, dk, dv = _backward(A, w, dout, window)
-    rq, rk, rv = _oracle(w, dout, window)
+    dq, dk, dv = _backward(A, w, dout, window, softcap)
+    rq, rk, rv = _oracle(w, dout, window, softcap)
     _cmp(dq, rq, f"{what} dq")
     _cmp(dk, rk, f"{what} dk")
     _cmp(dv, rv, f"{what} dv")
@@ -154,3 +155,17 @@ def test_empty_sequences(A):
     w = W.make_prefill("bw5", 134, "bf16", [0, 50, 30], [20, 0, 30], 8, 2, 128, 16, 0,
                        device=DEV)
     _case(A, w, 135, "empty_sequences")
+
+
+def test_softcap_causal_gqa_bf16(A):
+    """A cap that bends most scores (2.0 at scale 0.5): dS carries 1 - tanh^2."""
+    w = W.make_prefill("bw6", 138, "bf16", [300, 129], [300, 129], 8, 2, 128, 16, W.MASK_CAUSAL,
+                       device=DEV, scale=0.5)
+    _case(A, w, 139, "softcap_causal_gqa_bf16", softcap=2.0)
+
+
+def test_softcap_window_d64_fp16(A):
+    """The pages' cap of 50 with a local window, D = 64, fp16."""
+    w = W.make_prefill("bw7", 140, "f16", [65, 190], [65, 190], 16, 2, 64, 32, W.MASK_CAUSAL,
+                       device=DEV)
+    _case(A, w, 141, "softcap_window_d64_fp16", window=50, softcap=50.0)

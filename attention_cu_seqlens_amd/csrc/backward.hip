@@ -219,9 +219,17 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
     constexpr int TILE = kBwdTile * 2 * D;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][K, V]
     __shared__ int wave_range[2][4];
-    const int b = blockIdx.z, h = blockIdx.y;
+    // XCD-aware order: workgroup i runs on XCD i % 8; every workgroup of a
+    // (sequence, kv head) unit -- its query heads' row tiles, which stream
+    // the same K / V tiles -- lands on one XCD and shares its L2
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int per = p.group * p.n_qt;
+    const int u = xcd + 8 * (j / per), rj = j % per;
+    if (u >= p.batch * p.num_kv_heads) return;
+    const int b = u / p.num_kv_heads;
+    const int h = (u % p.num_kv_heads) * p.group + rj / p.n_qt;
     const int q_start = p.cu_q[b], q_len = p.cu_q[b + 1] - q_start;
-    const int row0 = blockIdx.x * kBwdRows;
+    const int row0 = (rj % p.n_qt) * kBwdRows;
     if (row0 >= q_len) return;
     const int kv_start = p.cu_kv[b], kv_len = p.cu_kv[b + 1] - kv_start;
     const int hk = h / p.group;
@@ -345,9 +353,14 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     __shared__ __attribute__((aligned(16))) int rows_lo[2][kBwdTile];
     __shared__ __attribute__((aligned(16))) int rows_hi[2][kBwdTile];
     __shared__ int tile_ext[2][4];   // per tile: max lo, min hi, min lo, max hi
-    const int b = blockIdx.z, hk = blockIdx.y;
+    // XCD-aware order as in the dQ kernel: a (sequence, kv head) unit's key
+    // tiles, which stream the same Q / dO tiles, share one XCD's L2
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int u = xcd + 8 * (j / p.n_kt);
+    if (u >= p.batch * p.num_kv_heads) return;
+    const int b = u / p.num_kv_heads, hk = u % p.num_kv_heads;
     const int kv_start = p.cu_kv[b], kv_len = p.cu_kv[b + 1] - kv_start;
-    const int k0 = blockIdx.x * kBwdRows;
+    const int k0 = (j % p.n_kt) * kBwdRows;
     if (k0 >= kv_len) return;
     const int q_start = p.cu_q[b], q_len = p.cu_q[b + 1] - q_start;
     const int off = kv_len - q_len;
@@ -504,17 +517,19 @@ hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_k
     hipLaunchKernelGGL((k_bwd_delta<D, BF16>), dim3(dblocks), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned qt = (unsigned)((max_seqlen_q + kBwdRows - 1) / kBwdRows);
-    const unsigned kt = (unsigned)((max_seqlen_kv + kBwdRows - 1) / kBwdRows);
-    if (qt > 0) {
-        hipLaunchKernelGGL((k_bwd_dq<D, BF16, CAP>), dim3(qt, p.num_heads, p.batch), dim3(256), 0,
-                           s, p);
+    BwdParams q = p;
+    q.n_qt = (max_seqlen_q + kBwdRows - 1) / kBwdRows;
+    q.n_kt = (max_seqlen_kv + kBwdRows - 1) / kBwdRows;
+    const int64_t slots = 8 * (((int64_t)p.batch * p.num_kv_heads + 7) / 8);   // units, padded
+    const int64_t gq = slots * p.group * q.n_qt, gk = slots * q.n_kt;
+    if (gq > 0x7fffffff || gk > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (gq > 0) {
+        hipLaunchKernelGGL((k_bwd_dq<D, BF16, CAP>), dim3((unsigned)gq), dim3(256), 0, s, q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (kt > 0) {
-        hipLaunchKernelGGL((k_bwd_dkdv<D, BF16, CAP>), dim3(kt, p.num_kv_heads, p.batch), dim3(256), 0,
-                           s, p);
+    if (gk > 0) {
+        hipLaunchKernelGGL((k_bwd_dkdv<D, BF16, CAP>), dim3((unsigned)gk), dim3(256), 0, s, q);
         e = hipGetLastError();
     }
     return e;

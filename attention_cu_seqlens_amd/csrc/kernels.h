@@ -94,6 +94,7 @@ struct BwdParams {
     float c;                    // scale * log2(e)
     float cap_in2;              // score cap: 2 log2(e) scale / cap (signed)
     float cap_out;              // cap * log2(e); 0: no cap
+    int n_qt, n_kt;             // 128-row query / key tiles per sequence at the max lengths
 };
 
 // Query rows (token x packed head) per prefill workgroup, and the bytes of

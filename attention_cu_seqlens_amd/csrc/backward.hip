@@ -134,6 +134,64 @@ __device__ __forceinline__ void cols_acc(f32x16_t (&y1)[D / 32], const uint8_t* 
     mfma_queue<(TWO ? 2 : 1) * H, kBwdPrefetch>(frag, op);
 }
 
+// 64 rows x D of a [tokens, heads, D] tensor straight into the swizzled LDS
+// tile layout with direct global->LDS loads, shared by the four waves (wave
+// w issues its quarter).  Lane l of a 1 KB load lands at byte 16 l of it:
+// row i*RPI + l/CPR, physical chunk l % CPR, which holds the logical chunk
+// (l % CPR) ^ swz<D>(row).  Rows at or past n read row n - 1 (n >= 1).  The
+// caller waits for the loads (vmcnt) before the barrier that publishes them.
+template <int D>
+__device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, int r0, int n,
+                                         uint32_t tile, int w, int lane) {
+    constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kBwdTile / RPI;
+    static_assert(NI % 4 == 0, "a tile's loads split over the four waves");
+#pragma unroll
+    for (int k = 0; k < NI / 4; ++k) {
+        const int i = w * (NI / 4) + k;
+        const int row = i * RPI + lane / CPR;
+        const int c = (lane % CPR) ^ swz<D>(row);
+        const int rr = min(r0 + row, n - 1);
+        dma16(base + rr * stride + c * 8, tile + i * 1024);
+    }
+}
+
+// One 32-row block kb of rows_dot2: x = tile_x rows kb*32.. . bx, y likewise.
+template <int D, bool BF16>
+__device__ __forceinline__ void rows_dot2_block(f32x16_t& x, f32x16_t& y, const uint8_t* tx,
+                                                const uint8_t* ty, const u32x4_t (&bx)[D / 16],
+                                                const u32x4_t (&by)[D / 16], int kb) {
+    constexpr int ROWB = 2 * D;
+    constexpr int H = D / 16;
+    const int lane = lane_id(), col = lane & 31, g = lane >> 5;
+    uint32_t lok = (uint32_t)(kb * 32 * ROWB + col * ROWB + ((g ^ swz<D>(col)) << 4));
+    asm volatile("" : "+v"(lok));
+    auto frag = [&](int i) {
+        const int t = i % H;
+        return *reinterpret_cast<const u32x4_t*>((i < H ? tx : ty) + (lok ^ (uint32_t)(t << 5)));
+    };
+    auto op = [&](int i, const u32x4_t& a) {
+        const int t = i % H;
+        if (i < H) x = mfma32<BF16>(a, bx[t], t == 0 ? f32x16_t{} : x);
+        else y = mfma32<BF16>(a, by[t], t == 0 ? f32x16_t{} : y);
+    };
+    mfma_queue<2 * H, kBwdPrefetch>(frag, op);
+}
+
+// The block-kb part of a column accumulation: y[db] += tile^T (rows kb*32..) . X.
+template <int D, bool BF16>
+__device__ __forceinline__ void cols_acc_block(f32x16_t (&y)[D / 32], const uint8_t* tile,
+                                               const u32x4_t (&xb)[2], int kb) {
+    constexpr int H = (D / 32) * 2;
+    uint32_t lo0, hi0;
+    pv_offsets<D>(lo0, hi0);
+    asm volatile("" : "+v"(lo0), "+v"(hi0));
+    auto frag = [&](int i) {
+        return pv_frag<D, kBwdTile>(tile, lo0, hi0, (i / 2) * 4 + kb * 2 + i % 2);
+    };
+    auto op = [&](int i, const u32x4_t& a) { y[i / 2] = mfma32<BF16>(a, xb[i % 2], y[i / 2]); };
+    mfma_queue<H, kBwdPrefetch>(frag, op);
+}
+
 // Accumulator values 8tp .. 8tp+7 of block kb packed as the B operand.
 template <bool BF16>
 __device__ __forceinline__ void pack_block(const float (&v)[16], u32x4_t (&xb)[2]) {
@@ -215,7 +273,7 @@ __global__ __launch_bounds__(256) void k_bwd_delta(BwdParams p) {
 }
 
 template <int D, bool BF16, bool CAP>
-__global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_dq(BwdParams p) {
     constexpr int TILE = kBwdTile * 2 * D;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][K, V]
     __shared__ int wave_range[2][4];
@@ -291,53 +349,51 @@ __global__ __launch_bounds__(256) void k_bwd_dq(BwdParams p) {
         const int64_t stride = (int64_t)p.num_kv_heads * D;
         const uint16_t* kbase = p.k + ((int64_t)kv_start * p.num_kv_heads + hk) * D;
         const uint16_t* vbase = p.v + ((int64_t)kv_start * p.num_kv_heads + hk) * D;
-        StageRows<D> sk, sv;
-        sk.load(kbase, stride, kv_begin, kv_len, tid);
-        sv.load(vbase, stride, kv_begin, kv_len, tid);
-        sk.store(lds[0], tid);
-        sv.store(lds[0] + TILE, tid);
+        const uint32_t lds0 = lds_addr(lds);
+        auto fetch = [&](int j0, int bf) {
+            const uint32_t t = lds0 + bf * 2 * TILE;
+            dma_rows<D>(kbase, stride, j0, kv_len, t, w, lane);
+            dma_rows<D>(vbase, stride, j0, kv_len, t + TILE, w, lane);
+        };
+        fetch(kv_begin, 0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         for (int it = 0; it < n_t; ++it) {
             const int j0 = kv_begin + it * kBwdTile;
             const uint8_t* kt = lds[it & 1];
             const uint8_t* vt = kt + TILE;
-            const bool more = it + 1 < n_t;
-            if (more) {
-                sk.load(kbase, stride, j0 + kBwdTile, kv_len, tid);
-                sv.load(vbase, stride, j0 + kBwdTile, kv_len, tid);
-            }
+            if (it + 1 < n_t) fetch(j0 + kBwdTile, (it + 1) & 1);
             // this wave's rows against keys j0 .. j0 + 63: none visible (skip),
             // all visible (no mask), or some
             const bool skip = j0 >= w_hi || j0 + kBwdTile <= w_lo;
             if (!skip) {
                 const bool full = j0 >= w_lo_max && j0 + kBwdTile <= w_hi_min;
-                f32x16_t s[2], dp[2];
-                rows_dot2<D, BF16>(s, dp, kt, vt, qv, dov);
-                u32x4_t xb[2][2];
+                // the tile's two 32-key blocks one after the other, so only one
+                // block's S, dP and dS are live at a time
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
+                    f32x16_t s1, dp1;
+                    rows_dot2_block<D, BF16>(s1, dp1, kt, vt, qv, dov, kb);
                     float ds[16];
                     float pr;
                     if (full) {
 #pragma unroll
                         for (int e = 0; e < 16; ++e)
-                            ds[e] = prob_ds<CAP>(s[kb][e], dp[kb][e], lse2, dlt, p, pr);
+                            ds[e] = prob_ds<CAP>(s1[e], dp1[e], lse2, dlt, p, pr);
                     } else {
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int key = j0 + kb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                            const float d = prob_ds<CAP>(s[kb][e], dp[kb][e], lse2, dlt, p, pr);
+                            const float d = prob_ds<CAP>(s1[e], dp1[e], lse2, dlt, p, pr);
                             ds[e] = (key >= lo && key < hi) ? d : 0.f;
                         }
                     }
-                    pack_block<BF16>(ds, xb[kb]);
+                    u32x4_t xb[2];
+                    pack_block<BF16>(ds, xb);
+                    cols_acc_block<D, BF16>(acc, kt, xb, kb);
                 }
-                cols_acc<D, BF16, false>(acc, kt, xb, acc, kt, xb);
             }
-            if (more) {
-                sk.store(lds[(it + 1) & 1], tid);
-                sv.store(lds[(it + 1) & 1] + TILE, tid);
-            }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             __syncthreads();
         }
     }

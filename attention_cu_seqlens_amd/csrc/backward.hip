@@ -22,8 +22,8 @@
 // Both stream kernels use the two MFMA patterns of the forward: rows of an
 // LDS tile against a register operand (the S^T = K Q^T product), and the
 // transposed LDS read against packed 16-bit accumulators (the P.V product),
-// on tiles in the same swizzled row-major LDS layout.  Tiles are staged
-// through registers and double-buffered: the next tile's global loads are in
+// on tiles in the same swizzled row-major LDS layout.  Tiles arrive by direct
+// global->LDS loads and are double-buffered: the next tile's loads are in
 // flight while the current one is used.
 
 #include "device_common.h"
@@ -36,35 +36,6 @@ namespace {
 
 constexpr int kBwdTile = 64;    // rows of a streamed tile
 constexpr int kBwdRows = 128;   // rows a workgroup owns (4 waves x 32)
-
-// 64 rows x D of a [tokens, heads, D] tensor staged through registers into
-// the swizzled LDS tile layout (row r, chunk c at chunk c ^ swz<D>(r)).
-template <int D>
-struct StageRows {
-    static constexpr int CPR = D / 8;
-    static constexpr int ROWB = 2 * D;
-    static constexpr int PER = kBwdTile * CPR / 256;   // chunks per thread
-    u32x4_t r[PER];
-
-    // Rows r0 .. r0 + 63 of `base` (row stride in elements); rows at or past
-    // n read row n - 1 (n >= 1), which callers give probability 0.
-    __device__ __forceinline__ void load(const uint16_t* base, int64_t stride, int r0, int n,
-                                         int tid) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int ci = tid + 256 * i, row = ci / CPR, c = ci % CPR;
-            const int rr = min(r0 + row, n - 1);
-            r[i] = *reinterpret_cast<const u32x4_t*>(base + rr * stride + c * 8);
-        }
-    }
-    __device__ __forceinline__ void store(uint8_t* tile, int tid) const {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int ci = tid + 256 * i, row = ci / CPR, c = ci % CPR;
-            *reinterpret_cast<u32x4_t*>(tile + row * ROWB + ((c ^ swz<D>(row)) << 4)) = r[i];
-        }
-    }
-};
 
 // MFMA steps 0 .. N-1 with their A operands read PD steps ahead through a
 // small register ring (the forward's prefetch queue): without it the
@@ -450,15 +421,17 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16_t{};
     if (n_t > 0 && q_len > 0) {
         const int64_t stride = (int64_t)p.num_heads * D;
-        StageRows<D> sq, sd;
         // rows of tile it: head hk * G + it / n_qt, queries qlo + (it % n_qt) * 64 ..
         auto head_of = [&](int it) { return hk * p.group + it / n_qt; };
         auto row0_of = [&](int it) { return qlo + (it % n_qt) * kBwdTile; };
-        auto load = [&](int it) {
+        const uint32_t lds0 = lds_addr(lds);
+        // Q and dO rows of tile it into buffer bf, direct to LDS
+        auto load = [&](int it, int bf) {
             const int h = head_of(it), j0 = row0_of(it);
             const int64_t base = (int64_t)q_start * p.num_heads + h;
-            sq.load(p.q + base * D, stride, j0, q_len, tid);
-            sd.load(p.dout + base * D, stride, j0, q_len, tid);
+            const uint32_t t = lds0 + bf * 2 * TILE;
+            dma_rows<D>(p.q + base * D, stride, j0, q_len, t, w, lane);
+            dma_rows<D>(p.dout + base * D, stride, j0, q_len, t + TILE, w, lane);
         };
         // per-row values of tile it into buffer bf (wave 0): LSE, delta and
         // the row's visible keys [lo, hi) as in the forward (empty for rows
@@ -497,10 +470,9 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
                 }
             }
         };
-        load(0);
+        load(0, 0);
         rows(0, 0);
-        sq.store(lds[0], tid);
-        sd.store(lds[0] + TILE, tid);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         for (int it = 0; it < n_t; ++it) {
             const int bf = it & 1;
@@ -508,7 +480,7 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
             const uint8_t* qt = lds[bf];
             const uint8_t* dt = qt + TILE;
             const bool more = it + 1 < n_t;
-            if (more) load(it + 1);
+            if (more) load(it + 1, bf ^ 1);
             // this wave's keys against the tile's rows: none visible (skip),
             // all visible (no mask), or some
             const int lo_max = tile_ext[bf][0], hi_min = tile_ext[bf][1];
@@ -554,9 +526,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
             }
             if (more) {
                 rows(it + 1, bf ^ 1);
-                sq.store(lds[bf ^ 1], tid);
-                sd.store(lds[bf ^ 1] + TILE, tid);
             }
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             __syncthreads();
         }
     }

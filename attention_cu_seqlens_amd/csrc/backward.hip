@@ -14,11 +14,11 @@
 //                one per lane column, Q and dO in registers as the B
 //                operands) and streams 64-key K / V tiles:
 //                S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
-//   k_bwd_dkdv   a workgroup owns 128 keys of one kv head (K and V rows in
-//                registers) and streams 64-row Q / dO tiles of every query
-//                head of the group: S = Q K^T, dP = dO V^T, then
-//                dV^T += dO^T P and dK^T += Q^T dS -- the group's heads sum
-//                in registers.
+//   k_bwd_dkdv16 a workgroup owns 128 keys of one kv head, 16 per wave (K
+//                and V rows in registers), and streams 64-row Q / dO tiles of
+//                every query head of the group: S = Q K^T, dP = dO V^T, then
+//                dV^T += dO^T P and dK^T += Q^T dS on 16x16x32 MFMA tiles --
+//                the group's heads sum in registers.
 // Both stream kernels use the two MFMA patterns of the forward: rows of an
 // LDS tile against a register operand (the S^T = K Q^T product), and the
 // transposed LDS read against packed 16-bit accumulators (the P.V product),
@@ -106,19 +106,19 @@ __device__ __forceinline__ void cols_acc(f32x16_t (&y1)[D / 32], const uint8_t* 
 }
 
 // 64 rows x D of a [tokens, heads, D] tensor straight into the swizzled LDS
-// tile layout with direct global->LDS loads, shared by the four waves (wave
-// w issues its quarter).  Lane l of a 1 KB load lands at byte 16 l of it:
+// tile layout with direct global->LDS loads, shared by the NW waves (wave w
+// issues its share).  Lane l of a 1 KB load lands at byte 16 l of it:
 // row i*RPI + l/CPR, physical chunk l % CPR, which holds the logical chunk
 // (l % CPR) ^ swz<D>(row).  Rows at or past n read row n - 1 (n >= 1).  The
 // caller waits for the loads (vmcnt) before the barrier that publishes them.
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, int r0, int n,
                                          uint32_t tile, int w, int lane) {
     constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kBwdTile / RPI;
-    static_assert(NI % 4 == 0, "a tile's loads split over the four waves");
+    static_assert(NI % NW == 0, "a tile's loads split evenly over the waves");
 #pragma unroll
-    for (int k = 0; k < NI / 4; ++k) {
-        const int i = w * (NI / 4) + k;
+    for (int k = 0; k < NI / NW; ++k) {
+        const int i = w * (NI / NW) + k;
         const int row = i * RPI + lane / CPR;
         const int c = (lane % CPR) ^ swz<D>(row);
         const int rr = min(r0 + row, n - 1);
@@ -371,17 +371,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (valid) store_cols<D, BF16>(acc, p.scale, p.dq + qrow * D);
 }
 
+// 16x16x32 MFMA on 8 packed 16-bit values per lane: lane l holds row (A) or
+// column (B) l % 16 and k-slots 8 (l / 16) .. +7; the 16x16 accumulator
+// gives lane l column l % 16, rows 4 (l / 16) + r in register r.
+template <bool BF16>
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+}
+
+// The dK/dV kernel with 16 keys per wave on 16x16x32 MFMA tiles: eight waves
+// own the workgroup's 128 keys, two per SIMD (the accumulators of a 16-key
+// slice, 2 x D/16 x 4 registers, leave room for a second wave).  Per 64-row
+// Q / dO tile, for each of the four 16-row blocks: S = Q K^T and dP = dO V^T
+// (Q / dO rows from LDS as A, this lane column's K / V row in registers as
+// B); then dV^T += dO^T P and dK^T += Q^T dS over the 64 rows in two 32-row
+// steps, with P and dS packed from the accumulators of blocks 2st, 2st + 1
+// as the B operand (k-slots 0..3: rows 32st + 4g + r, 4..7: rows
+// 32st + 16 + 4g + r for lane group g) and dO^T / Q^T read transposed from
+// LDS in the same row order.
 template <int D, bool BF16, bool CAP>
-__global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
-    constexpr int TILE = kBwdTile * 2 * D;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_dkdv16(
+    BwdParams p) {
+    constexpr int NW = 8;
+    constexpr int ROWB = 2 * D;
+    constexpr int TILE = kBwdTile * ROWB;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * TILE];   // [buffer][Q, dO]
     __shared__ __attribute__((aligned(16))) float rows_lse2[2][kBwdTile];
     __shared__ __attribute__((aligned(16))) float rows_delta[2][kBwdTile];
     __shared__ __attribute__((aligned(16))) int rows_lo[2][kBwdTile];
     __shared__ __attribute__((aligned(16))) int rows_hi[2][kBwdTile];
     __shared__ int tile_ext[2][4];   // per tile: max lo, min hi, min lo, max hi
-    // XCD-aware order as in the dQ kernel: a (sequence, kv head) unit's key
-    // tiles, which stream the same Q / dO tiles, share one XCD's L2
     const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
     const int u = xcd + 8 * (j / p.n_kt);
     if (u >= p.batch * p.num_kv_heads) return;
@@ -392,46 +417,42 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
     const int q_start = p.cu_q[b], q_len = p.cu_q[b + 1] - q_start;
     const int off = kv_len - q_len;
     const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-    const int col = lane & 31, g = lane >> 5;
-    const int key = k0 + w * 32 + col;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int key = k0 + w * 16 + c16;
     const bool kvalid = key < kv_len;
     const int kk = kvalid ? key : kv_len - 1;
     const int64_t krow = (int64_t)(kv_start + kk) * p.num_kv_heads + hk;
 
-    u32x4_t kr[D / 16], vr[D / 16];
+    u32x4_t kr[D / 32], vr[D / 32];
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-        kr[t] = *reinterpret_cast<const u32x4_t*>(p.k + krow * D + 16 * t + 8 * g);
-        vr[t] = *reinterpret_cast<const u32x4_t*>(p.v + krow * D + 16 * t + 8 * g);
+    for (int t = 0; t < D / 32; ++t) {
+        kr[t] = *reinterpret_cast<const u32x4_t*>(p.k + krow * D + 32 * t + 8 * g);
+        vr[t] = *reinterpret_cast<const u32x4_t*>(p.v + krow * D + 32 * t + 8 * g);
     }
     const bool causal = p.mask & kMaskCausal;
-    // this wave's keys
-    const int wk_lo = k0 + w * 32;
-    const int wk_hi = min(wk_lo + 32, kv_len);   // exclusive
+    const int wk_lo = k0 + w * 16;
+    const int wk_hi = min(wk_lo + 16, kv_len);   // exclusive
 
-    // queries that can see any of keys k0 .. k0 + 127
     int qlo = 0, qhi = q_len;
     if (causal) qlo = max(qlo, k0 - off);
     if (p.window > 0) qhi = min(qhi, k0 + kBwdRows - 1 - off + p.window);
     const int n_qt = qhi > qlo ? (qhi - qlo + kBwdTile - 1) / kBwdTile : 0;
     const int n_t = n_qt * p.group;
 
-    f32x16_t dk[D / 32], dv[D / 32];
+    f32x4_t dk[D / 16], dv[D / 16];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16_t{};
+    for (int db = 0; db < D / 16; ++db) dk[db] = dv[db] = f32x4_t{};
     if (n_t > 0 && q_len > 0) {
         const int64_t stride = (int64_t)p.num_heads * D;
-        // rows of tile it: head hk * G + it / n_qt, queries qlo + (it % n_qt) * 64 ..
         auto head_of = [&](int it) { return hk * p.group + it / n_qt; };
         auto row0_of = [&](int it) { return qlo + (it % n_qt) * kBwdTile; };
         const uint32_t lds0 = lds_addr(lds);
-        // Q and dO rows of tile it into buffer bf, direct to LDS
         auto load = [&](int it, int bf) {
             const int h = head_of(it), j0 = row0_of(it);
             const int64_t base = (int64_t)q_start * p.num_heads + h;
             const uint32_t t = lds0 + bf * 2 * TILE;
-            dma_rows<D>(p.q + base * D, stride, j0, q_len, t, w, lane);
-            dma_rows<D>(p.dout + base * D, stride, j0, q_len, t + TILE, w, lane);
+            dma_rows<D, NW>(p.q + base * D, stride, j0, q_len, t, w, lane);
+            dma_rows<D, NW>(p.dout + base * D, stride, j0, q_len, t + TILE, w, lane);
         };
         // per-row values of tile it into buffer bf (wave 0): LSE, delta and
         // the row's visible keys [lo, hi) as in the forward (empty for rows
@@ -470,70 +491,119 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(BwdParams p) {
                 }
             }
         };
+        // A-operand lane offsets.  Rows of an S / dP block: row 16 qb + c16,
+        // logical chunk 4t + g (its swizzle depends on the row mod 16 only).
+        uint32_t arow = (uint32_t)(c16 * ROWB);
+        const int asw = swz<D>(c16);
+        asm volatile("" : "+v"(arow));
         load(0, 0);
         rows(0, 0);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         for (int it = 0; it < n_t; ++it) {
             const int bf = it & 1;
-            const int j0 = row0_of(it);
             const uint8_t* qt = lds[bf];
             const uint8_t* dt = qt + TILE;
             const bool more = it + 1 < n_t;
             if (more) load(it + 1, bf ^ 1);
-            // this wave's keys against the tile's rows: none visible (skip),
-            // all visible (no mask), or some
             const int lo_max = tile_ext[bf][0], hi_min = tile_ext[bf][1];
             const int lo_min = tile_ext[bf][2], hi_max = tile_ext[bf][3];
             const bool skip = wk_hi <= wk_lo || wk_hi <= lo_min || wk_lo >= hi_max;
             if (!skip) {
-                const bool full = lo_max <= wk_lo && hi_min >= wk_hi && wk_hi - wk_lo == 32;
-                f32x16_t s[2], dp[2];
-                rows_dot2<D, BF16>(s, dp, qt, dt, kr, vr);
-                u32x4_t pbp[2][2], pbs[2][2];
+                const bool full = lo_max <= wk_lo && hi_min >= wk_hi && wk_hi - wk_lo == 16;
+                f32x4_t s4[4], dp4[4];
+                {
+                    constexpr int H = 4 * (D / 32);   // steps per product (qb, t)
+                    auto frag = [&](int i) {
+                        const int jj = i % H, qb = jj / (D / 32), t = jj % (D / 32);
+                        const uint8_t* tile = i < H ? qt : dt;
+                        return *reinterpret_cast<const u32x4_t*>(
+                            tile + qb * 16 * ROWB + arow + (((4 * t + g) ^ asw) << 4));
+                    };
+                    auto op = [&](int i, const u32x4_t& a) {
+                        const int jj = i % H, qb = jj / (D / 32), t = jj % (D / 32);
+                        if (i < H) s4[qb] = mfma16<BF16>(a, kr[t], t == 0 ? f32x4_t{} : s4[qb]);
+                        else dp4[qb] = mfma16<BF16>(a, vr[t], t == 0 ? f32x4_t{} : dp4[qb]);
+                    };
+                    mfma_queue<2 * H, kBwdPrefetch>(frag, op);
+                }
+                float pv[4][4], dsv[4][4];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    float pv[16], dsv[16];
+                for (int qb = 0; qb < 4; ++qb) {
+                    const int tr = qb * 16 + 4 * g;   // tile rows tr .. tr+3
+                    const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&rows_lse2[bf][tr]);
+                    const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&rows_delta[bf][tr]);
+                    if (full) {
 #pragma unroll
-                    for (int rq = 0; rq < 4; ++rq) {
-                        const int tr = kb * 32 + 8 * rq + 4 * g;   // tile rows tr .. tr+3
-                        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(&rows_lse2[bf][tr]);
-                        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(&rows_delta[bf][tr]);
-                        if (full) {
+                        for (int r = 0; r < 4; ++r)
+                            dsv[qb][r] = prob_ds<CAP>(s4[qb][r], dp4[qb][r], l4[r], d4[r], p, pv[qb][r]);
+                    } else {
+                        const i32x4_t lo4 = *reinterpret_cast<const i32x4_t*>(&rows_lo[bf][tr]);
+                        const i32x4_t hi4 = *reinterpret_cast<const i32x4_t*>(&rows_hi[bf][tr]);
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int e = 4 * rq + i;
-                                dsv[e] = prob_ds<CAP>(s[kb][e], dp[kb][e], l4[i], d4[i], p, pv[e]);
-                            }
-                        } else {
-                            const i32x4_t lo4 = *reinterpret_cast<const i32x4_t*>(&rows_lo[bf][tr]);
-                            const i32x4_t hi4 = *reinterpret_cast<const i32x4_t*>(&rows_hi[bf][tr]);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int e = 4 * rq + i;
-                                const bool vis = kvalid && key >= lo4[i] && key < hi4[i];
-                                float pr;
-                                const float d = prob_ds<CAP>(s[kb][e], dp[kb][e], l4[i], d4[i], p, pr);
-                                pv[e] = vis ? pr : 0.f;
-                                dsv[e] = vis ? d : 0.f;
-                            }
+                        for (int r = 0; r < 4; ++r) {
+                            const bool vis = kvalid && key >= lo4[r] && key < hi4[r];
+                            float pr;
+                            const float d = prob_ds<CAP>(s4[qb][r], dp4[qb][r], l4[r], d4[r], p, pr);
+                            pv[qb][r] = vis ? pr : 0.f;
+                            dsv[qb][r] = vis ? d : 0.f;
                         }
                     }
-                    pack_block<BF16>(pv, pbp[kb]);
-                    pack_block<BF16>(dsv, pbs[kb]);
                 }
-                cols_acc<D, BF16, true>(dv, dt, pbp, dk, qt, pbs);
+                u32x4_t pbp[2], pbs[2];
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    pbp[st] = u32x4_t{pack2<BF16>(pv[2 * st][0], pv[2 * st][1]),
+                                      pack2<BF16>(pv[2 * st][2], pv[2 * st][3]),
+                                      pack2<BF16>(pv[2 * st + 1][0], pv[2 * st + 1][1]),
+                                      pack2<BF16>(pv[2 * st + 1][2], pv[2 * st + 1][3])};
+                    pbs[st] = u32x4_t{pack2<BF16>(dsv[2 * st][0], dsv[2 * st][1]),
+                                      pack2<BF16>(dsv[2 * st][2], dsv[2 * st][3]),
+                                      pack2<BF16>(dsv[2 * st + 1][0], dsv[2 * st + 1][1]),
+                                      pack2<BF16>(dsv[2 * st + 1][2], dsv[2 * st + 1][3])};
+                }
+                {
+                    // transposed reads: lane 4e + qq of group g points at row
+                    // 32st + 16rd + 4g + e, columns 16db + 4qq .. +3; output
+                    // lane c16 receives that row quad of column 16db + c16
+                    const int e = c16 >> 2, qq = c16 & 3;
+                    constexpr int H = (D / 16) * 2;   // steps per product (db, st)
+                    auto tr8 = [&](const uint8_t* tile, int row, int col) {
+                        return ds_read_tr16(tile + row * ROWB + ((((col >> 3) ^ swz<D>(row))) << 4) +
+                                            (col & 7) * 2);
+                    };
+                    auto frag = [&](int i) {
+                        const int jj = i % H, db = jj / 2, st = jj % 2;
+                        const uint8_t* tile = i < H ? dt : qt;
+                        const int r0 = 32 * st + 4 * g + e, col = 16 * db + 4 * qq;
+                        const u32x2_t x0 = tr8(tile, r0, col);
+                        const u32x2_t x1 = tr8(tile, r0 + 16, col);
+                        return u32x4_t{x0.x, x0.y, x1.x, x1.y};
+                    };
+                    auto op = [&](int i, const u32x4_t& a) {
+                        const int jj = i % H, db = jj / 2, st = jj % 2;
+                        if (i < H) dv[db] = mfma16<BF16>(a, pbp[st], dv[db]);
+                        else dk[db] = mfma16<BF16>(a, pbs[st], dk[db]);
+                    };
+                    mfma_queue<2 * H, kBwdPrefetch>(frag, op);
+                }
             }
-            if (more) {
-                rows(it + 1, bf ^ 1);
-            }
+            if (more) rows(it + 1, bf ^ 1);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             __syncthreads();
         }
     }
     if (kvalid) {
-        store_cols<D, BF16>(dk, p.scale, p.dk + krow * D);
-        store_cols<D, BF16>(dv, 1.f, p.dv + krow * D);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            u32x2_t a, c;
+            a.x = pack2<BF16>(dk[db][0] * p.scale, dk[db][1] * p.scale);
+            a.y = pack2<BF16>(dk[db][2] * p.scale, dk[db][3] * p.scale);
+            c.x = pack2<BF16>(dv[db][0], dv[db][1]);
+            c.y = pack2<BF16>(dv[db][2], dv[db][3]);
+            *reinterpret_cast<u32x2_t*>(p.dk + krow * D + 16 * db + 4 * g) = a;
+            *reinterpret_cast<u32x2_t*>(p.dv + krow * D + 16 * db + 4 * g) = c;
+        }
     }
 }
 
@@ -556,7 +626,7 @@ hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_k
         if (e != hipSuccess) return e;
     }
     if (gk > 0) {
-        hipLaunchKernelGGL((k_bwd_dkdv<D, BF16, CAP>), dim3((unsigned)gk), dim3(256), 0, s, q);
+        hipLaunchKernelGGL((k_bwd_dkdv16<D, BF16, CAP>), dim3((unsigned)gk), dim3(512), 0, s, q);
         e = hipGetLastError();
     }
     return e;

@@ -148,3 +148,12 @@ def test_keys_beyond_one_page_window(A, random_lists):
         out, lse = _case(A, w, bm, "long_kv_causal_lists", cache=cache)
         out_c, lse_c = gpu_prefill(w, A, cache=cache)
         assert torch.equal(out, out_c) and torch.equal(lse, lse_c)
+
+
+def test_every_block_hidden(A):
+    """Empty lists everywhere: every row sees nothing (O = 0, LSE = -inf),
+    whatever the element mask says."""
+    w = W.make_prefill("bsnone", 142, "bf16", [130, 64], [130, 64], 8, 2, 128, 16, W.MASK_CAUSAL)
+    kn, ki, fn, fi = W.causal_block_mask(w.q_lens, w.kv_lens, 64, 64)
+    out, lse = _case(A, w, (64, 64, 0 * kn, ki, 0 * fn, fi), "every_block_hidden")
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))

@@ -92,3 +92,12 @@ def test_full_paged_gqa_decode_fp8kv(A):
     g = torch.as_tensor(q_idx, device=out.device)
     compare(out[g], lse[g], ref_o, ref_l, ATOL_16, REL_16,
             what=f"{w.name} seqs {seqs} x {w.num_heads} heads")
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs", [(32, 1, 128, 16), (12, 4, 64, 64)])
+def test_decode_fp8kv_group_sizes(A, hq, hkv, d, bs):
+    w = _fp8kv_decode(86, "bf16", [1, 0, 257, 4096, 1500], hq, hkv, d, bs)
+    banner(f"decode fp8kv groups hq={hq} hkv={hkv} d={d} bs={bs}")
+    out, lse = gpu_decode_fp8kv(w, A, split_tokens=1024)
+    ref_o, ref_l = oracle_decode_fp8kv(w)
+    compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what=f"decode_fp8kv_g{hq // hkv}_d{d}")

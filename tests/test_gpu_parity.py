@@ -307,3 +307,15 @@ def test_fp8_unaligned_varlen_no_mask(A):
     out, lse = gpu_fp8(w, A)
     ref_o, ref_l = oracle_fp8(w)
     compare(out, lse, ref_o, ref_l, ATOL_FP8, what="fp8_unaligned", lse_atol=LSE_ATOL_FP8)
+
+
+@pytest.mark.parametrize("hq,hkv,d,bs", [(8, 8, 128, 16), (32, 1, 128, 16), (12, 4, 64, 32),
+                                         (64, 2, 128, 64)])
+def test_decode_group_sizes(A, hq, hkv, d, bs):
+    """GQA groups 1, 32 (the largest decode takes), 3 (not a power of two)
+    and 32 at block size 64; ragged lengths incl. 0 and a split boundary."""
+    w = W.make_decode("decg", 34, "bf16", [1, 0, 257, 4096, 1500], hq, hkv, d, bs)
+    banner(f"decode groups hq={hq} hkv={hkv} d={d} bs={bs}")
+    out, lse = gpu_decode(w, A, split_tokens=1024)
+    ref_o, ref_l = oracle_decode(w)
+    compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what=f"decode_g{hq // hkv}_d{d}_bs{bs}")

@@ -262,7 +262,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (row0 >= q_len) return;
     const int kv_start = p.cu_kv[b], kv_len = p.cu_kv[b + 1] - kv_start;
     const int hk = h / p.group;
-    const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+    const int lane = lane_id(), w = wave_id();
     const int col = lane & 31, g = lane >> 5;
     const int r = row0 + w * 32 + col;
     const bool valid = r < q_len;

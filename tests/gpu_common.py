@@ -5,8 +5,6 @@ The oracle side and the HIP side each compute their own cu_seqlens and fill
 their own paged cache from the same generated tokens.
 """
 
-import math
-import os
 import sys
 
 import numpy as np

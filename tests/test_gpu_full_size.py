@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle as ORC
 import workloads as W
 from gpu_common import (ATOL_16, ATOL_FP8, LSE_ATOL_FP8, REL_16, banner, compare, gpu_decode,
                         gpu_fp8, gpu_prefill, lib_module, oracle_decode, oracle_fp8,
@@ -104,3 +105,68 @@ def test_prefill_zero_length_sequences(A):
     out, lse = gpu_prefill(w, A)
     ref_o, ref_l = oracle_prefill(w)
     compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what="zero_length_sequences")
+
+
+def test_prefill_many_sequences(A):
+    """300 short ragged sequences x 8 head groups: 2400 (sequence, head group)
+    units, so each XCD walks its units in several chunks of 64 when it maps
+    workgroups to tiles (the varlen workload has 16 units per XCD)."""
+    rng = np.random.default_rng(143)
+    lens = rng.integers(0, 200, 300)
+    w = W.make_prefill("many", 144, "bf16", lens, lens, 32, 8, 128, 16, W.MASK_CAUSAL, rng=rng)
+    banner(f"many sequences: {len(lens)}, total {int(lens.sum())}")
+    out, lse = gpu_prefill(w, A)
+    ref_o, ref_l = oracle_prefill(w)
+    compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what="many_sequences")
+
+
+def test_fp8_many_sequences(A):
+    """200 short causal sequences (many units per XCD).  The fp8 method
+    rounds P to e4m3 for the fp8 P.V product (relative error up to 2^-4 per
+    weight), which averages out over many visible keys but not over a few:
+    rows with at least 16 visible keys take the fp8 bar, rows with fewer the
+    bound that rounding implies -- each normalised weight within
+    2 * 2^-4 / (1 - 2^-4) relative, so |dO_d| <= that * max_k |v_kd - O_d|,
+    plus the bf16 output rounding."""
+    rng = np.random.default_rng(145)
+    lens = rng.integers(0, 300, 200)
+    w = W.make_fp8("many8", 146, lens, lens, 8, 2, 128, W.MASK_CAUSAL)
+    banner(f"fp8 many sequences: {len(lens)}, total {int(lens.sum())}")
+    out, lse = gpu_fp8(w, A)
+    ref_o, ref_l = oracle_fp8(w)
+    # visible keys of each row (causal, equal lengths: position + 1)
+    n_vis = np.concatenate([np.arange(1, n + 1) for n in lens]) if lens.sum() else np.zeros(0)
+    many = n_vis >= 16
+    compare(out[torch.as_tensor(np.nonzero(many)[0], device=out.device)], lse[torch.as_tensor(
+            np.nonzero(many)[0], device=out.device)], ref_o[many], ref_l[many], ATOL_FP8,
+            what="fp8_many_sequences rows with >= 16 keys", lse_atol=LSE_ATOL_FP8)
+    # rows with fewer keys: the e4m3 weight bound
+    few = np.nonzero(~many)[0]
+    v = ORC.e4m3_decode(w.v8_colmajor.cpu().numpy()) * float(w.descale[2])   # [Hkv, D, total]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    seq_of = np.searchsorted(cu, few, side="right") - 1
+    o = out.float().cpu().double().numpy()
+    group = w.num_heads // w.num_kv_heads
+    rel = 2 * 2.0 ** -4 / (1 - 2.0 ** -4)
+    worst = 0.0
+    for i, b in zip(few, seq_of):
+        keys = np.arange(cu[b], i + 1)                       # causal: keys up to the row
+        for h in range(w.num_heads):
+            vk = v[h // group][:, keys].T                    # [n_keys, D]
+            ref = ref_o[i, h]
+            bound = rel * np.max(np.abs(vk - ref[None, :]), axis=0) + 2.0 ** -8 * np.abs(ref) + 1e-3
+            err = np.abs(o[i, h] - ref)
+            worst = max(worst, float(np.max(err / bound)))
+            assert np.all(err <= bound), (int(i), h)
+    print(f"[parity] fp8_many_sequences rows with < 16 keys: max error {worst:.3f} of the bound",
+          flush=True)
+
+
+def test_decode_many_sequences(A):
+    rng = np.random.default_rng(147)
+    lens = rng.integers(0, 600, 600)
+    w = W.make_decode("manyd", 148, "bf16", lens, 32, 8, 128, 16)
+    banner(f"decode many sequences: {len(lens)}")
+    out, lse = gpu_decode(w, A)
+    ref_o, ref_l = oracle_decode(w)
+    compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what="decode_many_sequences")

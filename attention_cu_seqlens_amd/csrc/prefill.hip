@@ -80,8 +80,13 @@ __device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t 
         for (int db = 0; db < D / 32; ++db) st.o[db] *= st.alpha;
         st.need = false;
     }
+    // The MFMA phase runs at raised wave priority: when both waves of a SIMD
+    // are ready, its LDS reads and MFMAs issue ahead of the other wave's
+    // softmax VALU work (+1.7% on the varlen workload, output unchanged).
+    __builtin_amdgcn_s_setprio(1);
     mfma_stream16<D, BN, BF16, PV, QK, PrefillWave<D, BN>::NPRE>(st.o, st.s, st.pb, q, st.pre,
                                                                 v_tile, k_tile, hook);
+    __builtin_amdgcn_s_setprio(0);
 }
 
 template <int D, int BN, int QB, int NW, bool BF16, bool CAP, bool BSP>

@@ -169,3 +169,16 @@ def test_softcap_window_d64_fp16(A):
     w = W.make_prefill("bw7", 140, "f16", [65, 190], [65, 190], 16, 2, 64, 32, W.MASK_CAUSAL,
                        device=DEV)
     _case(A, w, 141, "softcap_window_d64_fp16", window=50, softcap=50.0)
+
+
+def test_document_window_softcap_together(A):
+    rng = np.random.default_rng(151)
+    lens = [260, 180]
+    docs = []
+    for n in lens:
+        cuts = np.sort(rng.choice(np.arange(1, n), 3, replace=False))
+        docs.append(np.searchsorted(cuts, np.arange(n), side="right").astype(np.int32))
+    ids = np.concatenate(docs)
+    w = W.make_prefill("bw8", 152, "bf16", lens, lens, 8, 2, 128, 16,
+                       W.MASK_DOCUMENT | W.MASK_CAUSAL, q_ids=ids, kv_ids=ids, device=DEV)
+    _case(A, w, 153, "document_window_softcap", window=60, softcap=3.0)

@@ -157,3 +157,20 @@ def test_every_block_hidden(A):
     kn, ki, fn, fi = W.causal_block_mask(w.q_lens, w.kv_lens, 64, 64)
     out, lse = _case(A, w, (64, 64, 0 * kn, ki, 0 * fn, fi), "every_block_hidden")
     assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_everything_at_once_d64_fp16(A):
+    """Random partial / full lists per kv head, with a document mask, a
+    window and a cap inside the partial blocks, fp16, D = 64."""
+    rng = np.random.default_rng(149)
+    lens = [333, 190]
+    docs = []
+    for n in lens:
+        cuts = np.sort(rng.choice(np.arange(1, n), 2, replace=False))
+        docs.append(np.searchsorted(cuts, np.arange(n), side="right").astype(np.int32))
+    ids = np.concatenate(docs)
+    w = W.make_prefill("bsall", 150, "f16", lens, lens, 8, 2, 64, 32,
+                       W.MASK_DOCUMENT | W.MASK_CAUSAL, q_ids=ids, kv_ids=ids)
+    bm = (64, 64) + W.random_block_mask(rng, w.q_lens, w.kv_lens, 64, 64, 2, p_partial=0.5,
+                                        p_full=0.3)
+    _case(A, w, bm, "everything_d64_fp16", window=90, softcap=4.0)

@@ -101,3 +101,12 @@ def test_decode_fp8kv_group_sizes(A, hq, hkv, d, bs):
     out, lse = gpu_decode_fp8kv(w, A, split_tokens=1024)
     ref_o, ref_l = oracle_decode_fp8kv(w)
     compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what=f"decode_fp8kv_g{hq // hkv}_d{d}")
+
+
+def test_decode_fp8kv_d64_fp16_window_softcap(A):
+    w = _fp8kv_decode(87, "f16", [33, 700, 129, 0], 16, 2, 64, 32)
+    w.scale = 0.5
+    banner("decode fp8kv d64 fp16 window 100 softcap 2")
+    out, lse = gpu_decode_fp8kv(w, A, window=100, softcap=2.0)
+    ref_o, ref_l = oracle_decode_fp8kv(w, window=100, softcap=2.0)
+    compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what="decode_fp8kv_d64_fp16_w100_c2")

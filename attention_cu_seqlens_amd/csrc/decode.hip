@@ -16,6 +16,8 @@
 // each sequence's split count from its own length.
 
 #include <algorithm>
+#include <atomic>
+#include <cstdint>
 #include <type_traits>
 
 #include "device_common.h"
@@ -226,15 +228,25 @@ namespace {
 template <int D, int NW, bool BF16, bool CAP, bool KV8>
 hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
     constexpr int lds = DecodeLayout<D, NW, BF16, KV8>::LDS_BYTES;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16, CAP, KV8>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (attr != hipSuccess) return attr;
+    // The dynamic-LDS limit is a per-device function attribute: set it once
+    // on each device this launcher runs on (one bit per device ordinal;
+    // ordinals past 63 set it on every launch).
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit == 0 || (attr_set.load(std::memory_order_acquire) & bit) == 0) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_paged_decode<D, NW, BF16, CAP, KV8>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set.fetch_or(bit, std::memory_order_acq_rel);
+    }
     const int64_t grid = (int64_t)p.batch * p.num_kv_heads * p.max_splits;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((k_paged_decode<D, NW, BF16, CAP, KV8>), dim3((unsigned)grid), dim3(NW * 64),
                        lds, s, p);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_decode_combine<D, BF16>), dim3((unsigned)(p.batch * p.num_heads)),
                        dim3(D), 0, s, p);

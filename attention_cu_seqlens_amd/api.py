@@ -52,7 +52,10 @@ def attn_cu_seqlens(seqlens, out=None):
     _need(seqlens, "seqlens", torch.int32)
     batch = seqlens.numel()
     if out is None:
-        out = torch.zeros(batch + 1, dtype=torch.int32, device=seqlens.device)
+        # the kernel writes every entry; an empty batch launches nothing, so
+        # its single 0 comes from the allocation
+        alloc = torch.zeros if batch == 0 else torch.empty
+        out = alloc(batch + 1, dtype=torch.int32, device=seqlens.device)
     _need(out, "out", torch.int32, seqlens.device)
     if out.numel() != batch + 1:
         raise ValueError("out must hold batch + 1 elements")

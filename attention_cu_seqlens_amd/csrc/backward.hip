@@ -105,13 +105,34 @@ __device__ __forceinline__ void cols_acc(f32x16_t (&y1)[D / 32], const uint8_t* 
     mfma_queue<(TWO ? 2 : 1) * H, kBwdPrefetch>(frag, op);
 }
 
+// Chunk swizzle of the dK/dV kernel's Q and dO tiles.  Its two reads:
+//   * 16-byte operand reads (16 lanes per LDS cycle): 16 aligned rows, one
+//     logical chunk -> the swizzle must be a bijection on each aligned
+//     16 rows (per row parity at D = 64, where a row spans half the banks);
+//   * transposed 8-byte reads: lane quarter q reads rows 4q .. 4q+3 of an
+//     aligned 16, two neighbouring chunks {2m, 2m+1} per row, and the chunk
+//     pair m ^ (s >> 1) must differ between the rows served in one cycle --
+//     whether a cycle pairs quarters {0, 1} or {0, 2}, i.e. s >> 1 distinct
+//     on rows {0..7} and on rows {0..3, 8..11} (and their complements; per
+//     parity at D = 64).
+// With r = b3 b2 b1 b0, s >> 1 takes the low row bits (b1 b0; b1 at D = 64)
+// and b2 ^ b3, and b3 fills the last bit.  swz<D> meets the first condition
+// only (rows r and r + 4 share a pair).
+template <int D>
+__device__ __forceinline__ int swz_dkdv(int r) {
+    const int x23 = ((r >> 2) ^ (r >> 3)) & 1, b3 = (r >> 3) & 1;
+    if constexpr (D == 128) return (((r & 3) | (x23 << 2)) << 1) | b3;
+    else return ((((r >> 1) & 1) | (x23 << 1)) << 1) | b3;
+}
+
 // 64 rows x D of a [tokens, heads, D] tensor straight into the swizzled LDS
 // tile layout with direct global->LDS loads, shared by the NW waves (wave w
 // issues its share).  Lane l of a 1 KB load lands at byte 16 l of it:
 // row i*RPI + l/CPR, physical chunk l % CPR, which holds the logical chunk
-// (l % CPR) ^ swz<D>(row).  Rows at or past n read row n - 1 (n >= 1).  The
-// caller waits for the loads (vmcnt) before the barrier that publishes them.
-template <int D, int NW = 4>
+// (l % CPR) ^ sw(row), sw = swz_dkdv<D> when DKDV, else swz<D>.  Rows at or
+// past n read row n - 1 (n >= 1).  The caller waits for the loads (vmcnt)
+// before the barrier that publishes them.
+template <int D, int NW = 4, bool DKDV = false>
 __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, int r0, int n,
                                          uint32_t tile, int w, int lane) {
     constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kBwdTile / RPI;
@@ -120,7 +141,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, i
     for (int k = 0; k < NI / NW; ++k) {
         const int i = w * (NI / NW) + k;
         const int row = i * RPI + lane / CPR;
-        const int c = (lane % CPR) ^ swz<D>(row);
+        const int c = (lane % CPR) ^ (DKDV ? swz_dkdv<D>(row) : swz<D>(row));
         const int rr = min(r0 + row, n - 1);
         dma16(base + rr * stride + c * 8, tile + i * 1024);
     }
@@ -451,8 +472,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
             const int h = head_of(it), j0 = row0_of(it);
             const int64_t base = (int64_t)q_start * p.num_heads + h;
             const uint32_t t = lds0 + bf * 2 * TILE;
-            dma_rows<D, NW>(p.q + base * D, stride, j0, q_len, t, w, lane);
-            dma_rows<D, NW>(p.dout + base * D, stride, j0, q_len, t + TILE, w, lane);
+            dma_rows<D, NW, true>(p.q + base * D, stride, j0, q_len, t, w, lane);
+            dma_rows<D, NW, true>(p.dout + base * D, stride, j0, q_len, t + TILE, w, lane);
         };
         // per-row values of tile it into buffer bf (wave 0): LSE, delta and
         // the row's visible keys [lo, hi) as in the forward (empty for rows
@@ -494,7 +515,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
         // A-operand lane offsets.  Rows of an S / dP block: row 16 qb + c16,
         // logical chunk 4t + g (its swizzle depends on the row mod 16 only).
         uint32_t arow = (uint32_t)(c16 * ROWB);
-        const int asw = swz<D>(c16);
+        const int asw = swz_dkdv<D>(c16);
         asm volatile("" : "+v"(arow));
         load(0, 0);
         rows(0, 0);
@@ -569,7 +590,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
                     const int e = c16 >> 2, qq = c16 & 3;
                     constexpr int H = (D / 16) * 2;   // steps per product (db, st)
                     auto tr8 = [&](const uint8_t* tile, int row, int col) {
-                        return ds_read_tr16(tile + row * ROWB + ((((col >> 3) ^ swz<D>(row))) << 4) +
+                        return ds_read_tr16(tile + row * ROWB + ((((col >> 3) ^ swz_dkdv<D>(row))) << 4) +
                                             (col & 7) * 2);
                     };
                     auto frag = [&](int i) {

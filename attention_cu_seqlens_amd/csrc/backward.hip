@@ -58,53 +58,6 @@ __device__ __forceinline__ void mfma_queue(const Frag& frag, const Op& op) {
 
 constexpr int kBwdPrefetch = 4;
 
-// Two row products of one tile pair in one queue:
-//   x[kb] = tile_x rows . bx,  y[kb] = tile_y rows . by   (kb = 0, 1)
-// -- the S^T = K Q^T pattern: rows kb*32.. of the LDS tile against this lane
-// column's register row (dims 16t + 8g .. +7 in b[t]).
-template <int D, bool BF16>
-__device__ __forceinline__ void rows_dot2(f32x16_t (&x)[2], f32x16_t (&y)[2], const uint8_t* tx,
-                                          const uint8_t* ty, const u32x4_t (&bx)[D / 16],
-                                          const u32x4_t (&by)[D / 16]) {
-    constexpr int ROWB = 2 * D;
-    constexpr int H = (D / 16) * 2;   // steps per product
-    const int lane = lane_id(), col = lane & 31, g = lane >> 5;
-    uint32_t lok = (uint32_t)(col * ROWB + ((g ^ swz<D>(col)) << 4));
-    asm volatile("" : "+v"(lok));
-    auto frag = [&](int i) {
-        const int j = i % H, t = j / 2, kb = j % 2;
-        const uint8_t* tile = i < H ? tx : ty;
-        return *reinterpret_cast<const u32x4_t*>(tile + kb * 32 * ROWB + (lok ^ (uint32_t)(t << 5)));
-    };
-    auto op = [&](int i, const u32x4_t& a) {
-        const int j = i % H, t = j / 2, kb = j % 2;
-        if (i < H) x[kb] = mfma32<BF16>(a, bx[t], t == 0 ? f32x16_t{} : x[kb]);
-        else y[kb] = mfma32<BF16>(a, by[t], t == 0 ? f32x16_t{} : y[kb]);
-    };
-    mfma_queue<2 * H, kBwdPrefetch>(frag, op);
-}
-
-// Column accumulations of one or two tiles in one queue:
-//   y1[db] += tile1^T . X1  (and y2[db] += tile2^T . X2 when TWO)
-// with X the packed 16-bit accumulators of a row product (rows = tile rows):
-// the P.V pattern with the transposed LDS read.
-template <int D, bool BF16, bool TWO>
-__device__ __forceinline__ void cols_acc(f32x16_t (&y1)[D / 32], const uint8_t* t1,
-                                         const u32x4_t (&x1)[2][2], f32x16_t (&y2)[D / 32],
-                                         const uint8_t* t2, const u32x4_t (&x2)[2][2]) {
-    constexpr int H = (D / 32) * 4;
-    uint32_t lo0, hi0;
-    pv_offsets<D>(lo0, hi0);
-    asm volatile("" : "+v"(lo0), "+v"(hi0));
-    auto frag = [&](int i) { return pv_frag<D, kBwdTile>(i < H ? t1 : t2, lo0, hi0, i % H); };
-    auto op = [&](int i, const u32x4_t& a) {
-        const int j = i % H, db = j / 4, kb = (j / 2) % 2, tp = j % 2;
-        if (i < H) y1[db] = mfma32<BF16>(a, x1[kb][tp], y1[db]);
-        else y2[db] = mfma32<BF16>(a, x2[kb][tp], y2[db]);
-    };
-    mfma_queue<(TWO ? 2 : 1) * H, kBwdPrefetch>(frag, op);
-}
-
 // Chunk swizzle of the dK/dV kernel's Q and dO tiles.  Its two reads:
 //   * 16-byte operand reads (16 lanes per LDS cycle): 16 aligned rows, one
 //     logical chunk -> the swizzle must be a bijection on each aligned
@@ -147,7 +100,10 @@ __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, i
     }
 }
 
-// One 32-row block kb of rows_dot2: x = tile_x rows kb*32.. . bx, y likewise.
+// Two row products of one 32-row block kb in one queue:
+//   x = tile_x rows kb*32.. . bx,  y = tile_y rows kb*32.. . by
+// -- the S^T = K Q^T pattern: rows of the LDS tile against this lane
+// column's register row (dims 16t + 8g .. +7 in b[t]).
 template <int D, bool BF16>
 __device__ __forceinline__ void rows_dot2_block(f32x16_t& x, f32x16_t& y, const uint8_t* tx,
                                                 const uint8_t* ty, const u32x4_t (&bx)[D / 16],
@@ -169,7 +125,9 @@ __device__ __forceinline__ void rows_dot2_block(f32x16_t& x, f32x16_t& y, const 
     mfma_queue<2 * H, kBwdPrefetch>(frag, op);
 }
 
-// The block-kb part of a column accumulation: y[db] += tile^T (rows kb*32..) . X.
+// The block-kb part of a column accumulation: y[db] += tile^T (rows
+// kb*32..) . X, with X the packed 16-bit accumulators of a row product
+// (rows = tile rows) -- the P.V pattern with the transposed LDS read.
 template <int D, bool BF16>
 __device__ __forceinline__ void cols_acc_block(f32x16_t (&y)[D / 32], const uint8_t* tile,
                                                const u32x4_t (&xb)[2], int kb) {

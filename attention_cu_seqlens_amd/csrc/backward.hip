@@ -433,16 +433,30 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
             dma_rows<D, NW, true>(p.q + base * D, stride, j0, q_len, t, w, lane);
             dma_rows<D, NW, true>(p.dout + base * D, stride, j0, q_len, t + TILE, w, lane);
         };
-        // per-row values of tile it into buffer bf (wave 0): LSE, delta and
-        // the row's visible keys [lo, hi) as in the forward (empty for rows
-        // past the sequence), plus the tile's extreme bounds
-        auto rows = [&](int it, int bf) {
+        // per-row values of tile it into buffer bf (wave 0), in two parts:
+        // rows_dma issues the row's LSE and delta as direct global->LDS loads
+        // (one 4-byte load per row; rows past the sequence read its last
+        // row), together with the tile's Q / dO loads, so their latency is
+        // spent under a tile of MFMAs; rows_fin, a tile later, waits for
+        // them, scales the LSE to log2 units, zeroes rows past the sequence
+        // and computes the row's visible keys [lo, hi) as in the forward
+        // (empty past the sequence) and the tile's extreme bounds
+        auto rows_dma = [&](int it, int bf) {
             if (tid < kBwdTile) {
                 const int h = head_of(it), q = row0_of(it) + tid;
+                const int64_t i = (int64_t)(q_start + min(q, q_len - 1)) * p.num_heads + h;
+                dma4(p.lse + i, lds_addr(&rows_lse2[bf][0]));
+                dma4(p.delta + i, lds_addr(&rows_delta[bf][0]));
+            }
+        };
+        auto rows_fin = [&](int it, int bf) {
+            if (tid < kBwdTile) {
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                asm volatile("" ::: "memory");   // LDS reads below stay after the wait
+                const int q = row0_of(it) + tid;
                 const bool in = q < q_len;
-                const int64_t i = (int64_t)(q_start + (in ? q : q_len - 1)) * p.num_heads + h;
-                rows_lse2[bf][tid] = in ? p.lse[i] * kLog2e : 0.f;
-                rows_delta[bf][tid] = in ? p.delta[i] : 0.f;
+                rows_lse2[bf][tid] = in ? rows_lse2[bf][tid] * kLog2e : 0.f;
+                rows_delta[bf][tid] = in ? rows_delta[bf][tid] : 0.f;
                 int lo = 0, hi = 0;
                 if (in) {
                     hi = kv_len;
@@ -476,7 +490,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
         const int asw = swz_dkdv<D>(c16);
         asm volatile("" : "+v"(arow));
         load(0, 0);
-        rows(0, 0);
+        rows_dma(0, 0);
+        rows_fin(0, 0);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         __syncthreads();
         for (int it = 0; it < n_t; ++it) {
@@ -484,7 +499,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
             const uint8_t* qt = lds[bf];
             const uint8_t* dt = qt + TILE;
             const bool more = it + 1 < n_t;
-            if (more) load(it + 1, bf ^ 1);
+            if (more) {
+                load(it + 1, bf ^ 1);
+                rows_dma(it + 1, bf ^ 1);
+            }
             const int lo_max = tile_ext[bf][0], hi_min = tile_ext[bf][1];
             const int lo_min = tile_ext[bf][2], hi_max = tile_ext[bf][3];
             const bool skip = wk_hi <= wk_lo || wk_hi <= lo_min || wk_lo >= hi_max;
@@ -567,7 +585,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
                     mfma_queue<2 * H, kBwdPrefetch>(frag, op);
                 }
             }
-            if (more) rows(it + 1, bf ^ 1);
+            if (more) rows_fin(it + 1, bf ^ 1);
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             __syncthreads();
         }

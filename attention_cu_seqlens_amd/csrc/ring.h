@@ -73,6 +73,15 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds) {
                  : "memory", "m0");
 }
 
+// The 4-byte form: lane i's 4 bytes land at LDS byte address lds + 4*i.
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(m0), "v"(gptr)
+                 : "memory", "m0");
+}
+
 // The same load with a wave-uniform 64-bit base in SGPRs and a 32-bit
 // per-lane byte offset: no per-lane address arithmetic.
 // The base goes through readfirstlane so it is in SGPRs even where the

@@ -226,9 +226,12 @@ attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const v
     if (!std::isfinite(scale) || !window_cap_ok(window_left, softcap)) return ATTN_ERR_BAD_SHAPE;
     const attn_status m = check_mask(mask_flags, q_ids, kv_ids);
     if (m != ATTN_OK) return m;
-    if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr ||
-        lse == nullptr || cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr || dq == nullptr ||
-        dk == nullptr || dv == nullptr)
+    // Query-side tensors are required when there are query rows, key-side
+    // ones when there are keys (an empty tensor may come as NULL).
+    if (cu_seqlens_q == nullptr || cu_seqlens_kv == nullptr ||
+        (total_q > 0 && (q == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+                         dq == nullptr)) ||
+        (total_kv > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)))
         return ATTN_ERR_NULL_ARG;
     for (const void* ptr : {q, k, v, out, dout, static_cast<const void*>(dq),
                             static_cast<const void*>(dk), static_cast<const void*>(dv)})

@@ -200,25 +200,44 @@ __device__ __forceinline__ float prob_ds(float s, float dp, float lse2, float de
     }
 }
 
-// delta[row, h] = sum_d dO * O in fp32, one thread per (row, head).
+// delta[row, h] = sum_d dO * O in fp32.  D/8 consecutive lanes read one
+// (row, head)'s contiguous D 16-bit values (16 bytes each, non-temporal: each
+// byte is read once), so a load instruction covers 64/(D/8) whole rows; a
+// wave keeps kDeltaSteps such row groups in flight per iteration and sums
+// each row across its lanes with shuffles.
+constexpr int kDeltaSteps = 4;
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_bwd_delta(BwdParams p) {
+    constexpr int LPR = D / 8;      // lanes per row
+    constexpr int RPW = 64 / LPR;   // rows per wave and load
     const int64_t n = (int64_t)p.total_q * p.num_heads;
-    for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-        const u32x4_t* o = reinterpret_cast<const u32x4_t*>(p.out + i * D);
-        const u32x4_t* d = reinterpret_cast<const u32x4_t*>(p.dout + i * D);
-        float acc = 0.f;
+    const int lane = lane_id(), sub = lane % LPR;
+    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 64;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t r0 = wave * RPW * kDeltaSteps; r0 < n; r0 += nwaves * RPW * kDeltaSteps) {
+        u32x4_t a[kDeltaSteps], b[kDeltaSteps];
 #pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const u32x4_t a = o[c], b = d[c];
+        for (int k = 0; k < kDeltaSteps; ++k) {
+            // rows past the end read row n - 1 and are not stored
+            const int64_t i = min(r0 + k * RPW + lane / LPR, n - 1);
+            a[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.out + i * D) + sub);
+            b[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.dout + i * D) + sub);
+        }
+#pragma unroll
+        for (int k = 0; k < kDeltaSteps; ++k) {
+            float acc = 0.f;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const f32x2_t fa = unpack16<BF16>(a[w]), fb = unpack16<BF16>(b[w]);
+                const f32x2_t fa = unpack16<BF16>(a[k][w]), fb = unpack16<BF16>(b[k][w]);
                 acc = __builtin_fmaf(fa.x, fb.x, acc);
                 acc = __builtin_fmaf(fa.y, fb.y, acc);
             }
+#pragma unroll
+            for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+            const int64_t i = r0 + k * RPW + lane / LPR;
+            if (sub == 0 && i < n) p.delta[i] = acc;
         }
-        p.delta[i] = acc;
     }
 }
 
@@ -607,10 +626,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 template <int D, bool BF16, bool CAP>
 hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_kv, hipStream_t s) {
     const int64_t n = (int64_t)p.total_q * p.num_heads;
-    const int dblocks = (int)std::min<int64_t>((n + 255) / 256, 16384);
-    hipLaunchKernelGGL((k_bwd_delta<D, BF16>), dim3(dblocks), dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // four waves per block, each covering 64/(D/8) rows per load and
+    // kDeltaSteps loads per iteration
+    const int64_t rows_per_block = 4 * (64 / (D / 8)) * kDeltaSteps;
+    const int dblocks = (int)std::min<int64_t>((n + rows_per_block - 1) / rows_per_block, 8192);
+    hipError_t e = hipSuccess;
+    if (dblocks > 0) {   // no query rows: nothing to reduce (dK, dV come out zero)
+        hipLaunchKernelGGL((k_bwd_delta<D, BF16>), dim3(dblocks), dim3(256), 0, s, p);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     BwdParams q = p;
     q.n_qt = (max_seqlen_q + kBwdRows - 1) / kBwdRows;
     q.n_kt = (max_seqlen_kv + kBwdRows - 1) / kBwdRows;

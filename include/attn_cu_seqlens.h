@@ -286,8 +286,10 @@ size_t attn_varlen_bwd_workspace_bytes(int32_t total_q, int32_t num_heads);
  *                256-byte aligned, owned by the caller, no initialisation;
  *                calls sharing it must not overlap in time
  * dtype ATTN_F16 or ATTN_BF16 for every 16-bit tensor; head_size 64 or 128.
- * All tensors 16-byte aligned device memory.  Errors: as
- * attn_paged_prefill_fwd, plus ATTN_ERR_WORKSPACE.
+ * All tensors 16-byte aligned device memory.  q, out, dout, lse and dq may
+ * be NULL when total_q is 0, k, v, dk and dv when total_kv is 0 (empty
+ * tensors); with no query rows and some keys, dk and dv are written as 0.
+ * Errors: as attn_paged_prefill_fwd, plus ATTN_ERR_WORKSPACE.
  */
 attn_status attn_varlen_bwd(const void* q, const void* k, const void* v, const void* out,
                             const void* dout, const float* lse, const int32_t* cu_seqlens_q,

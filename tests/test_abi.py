@@ -128,6 +128,14 @@ def test_varlen_bwd_host_checks(lib):
     assert call(ws=None) == 6
     assert call(ws=ctypes.c_void_p(128)) == 6     # not 256-byte aligned
     assert call(dq=ctypes.c_void_p(24)) == 2      # misaligned
+    # empty tensors may be NULL: query side when total_q is 0, key side when
+    # total_kv is 0 (both empty: nothing to do); still required otherwise
+    none_q = dict(q=None, out=None, dout=None, lse=None, dq=None)
+    none_kv = dict(k=None, v=None, dk=None, dv=None)
+    assert call(tq=0, tkv=0, msq=0, mskv=0, **none_q, **none_kv) == 0
+    assert call(tq=0, tkv=0, msq=0, mskv=0, **none_q) == 0
+    assert call(tkv=0, **none_q) == 1             # total_q > 0 needs the query side
+    assert call(tq=0, **none_kv) == 1             # total_kv > 0 needs the key side
 
 
 def _prefill_args(**kw):

@@ -182,3 +182,24 @@ def test_document_window_softcap_together(A):
     w = W.make_prefill("bw8", 152, "bf16", lens, lens, 8, 2, 128, 16,
                        W.MASK_DOCUMENT | W.MASK_CAUSAL, q_ids=ids, kv_ids=ids, device=DEV)
     _case(A, w, 153, "document_window_softcap", window=60, softcap=3.0)
+
+
+def test_no_query_rows_gives_zero_dk_dv(A):
+    """Every sequence has keys and no query rows (total_q = 0): the empty
+    query-side tensors come as NULL pointers, and dK, dV (NaN-filled before
+    the call) must come back exactly 0."""
+    w = W.make_prefill("bw0q", 181, "bf16", [0, 0, 0], [40, 7, 129], 8, 2, 128, 16,
+                       W.MASK_CAUSAL, device=DEV)
+    banner(f"backward with no query rows: kv={w.kv_lens.tolist()}")
+    cu_q = A.attn_cu_seqlens(_i32(w.q_lens))
+    cu_kv = A.attn_cu_seqlens(_i32(w.kv_lens))
+    empty = torch.empty((0, w.num_heads, w.head_size), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((0, w.num_heads), dtype=torch.float32, device=DEV)
+    dk = torch.full_like(w.k_new, float("nan"))
+    dv = torch.full_like(w.v_new, float("nan"))
+    dq, dk, dv = A.attn_varlen_bwd(empty, w.k_new, w.v_new, empty, empty, lse, cu_q, cu_kv, 0,
+                                   int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags,
+                                   dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0
+    assert torch.all(dk == 0) and torch.all(dv == 0)

@@ -43,6 +43,17 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _lse_out(lse, return_lse, shape, dev):
+    """The LSE output: the caller's float32 tensor of the given shape, or a new
+    one when return_lse is set, or None."""
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=dev) if return_lse else None
+    _need(lse, "lse", torch.float32, dev)
+    if tuple(lse.shape) != tuple(shape):
+        raise ValueError(f"lse must be {list(shape)}")
+    return lse
+
+
 def _u8(t):
     return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
 
@@ -216,7 +227,7 @@ def attn_rotary_reshape_and_cache(k_cache, v_cache, block_table, cu_seqlens_new,
 
 def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_seqlens_kv,
                            max_seqlen_q, max_seqlen_kv, scale=None, mask_flags=0, q_ids=None,
-                           kv_ids=None, out=None, return_lse=False, window=0, softcap=0.0):
+                           kv_ids=None, out=None, return_lse=False, window=0, softcap=0.0, lse=None):
     """Paged varlen attention; returns out (and lse [total_q, Hq] fp32 if asked).
     window: local window in keys (0 = none); softcap: score cap (0 = none)."""
     dev = q.device
@@ -238,7 +249,7 @@ def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_se
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev)
-    lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lse = _lse_out(lse, return_lse, (total_q, hq), dev)
     batch = cu_seqlens_q.numel() - 1
     lib = _lib.load()
     with torch.cuda.device(dev):
@@ -248,7 +259,7 @@ def attn_paged_prefill_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q, cu_se
             int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale), int(mask_flags), _ptr(q_ids),
             _ptr(kv_ids), int(window), float(softcap), _DT[q.dtype], _ptr(out), _ptr(lse),
             _stream(dev)))
-    return (out, lse) if return_lse else out
+    return (out, lse) if lse is not None else out
 
 
 def attn_paged_prefill_block_sparse_fwd(q, k_cache, v_cache, block_table, cu_seqlens_q,
@@ -256,7 +267,7 @@ def attn_paged_prefill_block_sparse_fwd(q, k_cache, v_cache, block_table, cu_seq
                                         kv_block, kv_num_blocks, kv_indices,
                                         full_kv_num_blocks=None, full_kv_indices=None,
                                         scale=None, mask_flags=0, q_ids=None, kv_ids=None,
-                                        out=None, return_lse=False, window=0, softcap=0.0):
+                                        out=None, return_lse=False, window=0, softcap=0.0, lse=None):
     """Paged varlen attention under a stored block-sparse mask: kv_num_blocks
     int32 [batch, Hm, n_qb], kv_indices int32 [batch, Hm, n_qb, capacity]
     (Hm = 1, num_kv_heads or num_heads); the full pair is optional."""
@@ -293,7 +304,7 @@ def attn_paged_prefill_block_sparse_fwd(q, k_cache, v_cache, block_table, cu_seq
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev)
-    lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lse = _lse_out(lse, return_lse, (total_q, hq), dev)
     lib = _lib.load()
     with torch.cuda.device(dev):
         _lib.check("attn_paged_prefill_block_sparse_fwd", lib.attn_paged_prefill_block_sparse_fwd(
@@ -303,7 +314,7 @@ def attn_paged_prefill_block_sparse_fwd(q, k_cache, v_cache, block_table, cu_seq
             _ptr(kv_ids), int(window), float(softcap), int(q_block), int(kv_block), hm, n_qb, cap,
             _ptr(kv_num_blocks), _ptr(kv_indices), _ptr(full_kv_num_blocks),
             _ptr(full_kv_indices), _DT[q.dtype], _ptr(out), _ptr(lse), _stream(dev)))
-    return (out, lse) if return_lse else out
+    return (out, lse) if lse is not None else out
 
 
 def attn_paged_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_size, max_seqlen_kv,
@@ -315,7 +326,7 @@ def attn_paged_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_size,
 
 def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_seqlen_kv,
                           scale=None, split_tokens=0, out=None, return_lse=False, workspace=None,
-                          window=0, softcap=0.0):
+                          window=0, softcap=0.0, lse=None):
     """One query per sequence (q [batch, Hq, D]) against the paged cache.
     window: keep each sequence's last `window` keys (0 = all); softcap: score cap."""
     dev = q.device
@@ -335,7 +346,7 @@ def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_s
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev)
-    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lse = _lse_out(lse, return_lse, (batch, hq), dev)
     lib = _lib.load()
     with torch.cuda.device(dev):
         _lib.check("attn_paged_decode_fwd", lib.attn_paged_decode_fwd(
@@ -343,12 +354,12 @@ def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_s
             _ptr(cu_seqlens_kv), batch, int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale),
             int(window), float(softcap), int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse),
             _ptr(workspace), workspace.numel(), _stream(dev)))
-    return (out, lse) if return_lse else out
+    return (out, lse) if lse is not None else out
 
 
 def attn_paged_decode_fp8kv_fwd(q, k_cache8, v_cache8, kv_descale, block_table, cu_seqlens_kv,
                                 max_seqlen_kv, scale=None, split_tokens=0, out=None,
-                                return_lse=False, workspace=None, window=0, softcap=0.0):
+                                return_lse=False, workspace=None, window=0, softcap=0.0, lse=None):
     """Decode against an fp8 e4m3 paged cache: k_cache8 / v_cache8 uint8 (or
     float8_e4m3fn) [num_blocks, block_size, Hkv, D], kv_descale fp32 [2]
     (dk, dv); q [batch, Hq, D] fp16 or bf16."""
@@ -375,7 +386,7 @@ def attn_paged_decode_fp8kv_fwd(q, k_cache8, v_cache8, kv_descale, block_table, 
     if out is None:
         out = torch.empty_like(q)
     _need(out, "out", q.dtype, dev)
-    lse = torch.empty((batch, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lse = _lse_out(lse, return_lse, (batch, hq), dev)
     lib = _lib.load()
     with torch.cuda.device(dev):
         _lib.check("attn_paged_decode_fp8kv_fwd", lib.attn_paged_decode_fp8kv_fwd(
@@ -383,12 +394,12 @@ def attn_paged_decode_fp8kv_fwd(q, k_cache8, v_cache8, kv_descale, block_table, 
             _ptr(cu_seqlens_kv), batch, int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale),
             int(window), float(softcap), int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse),
             _ptr(workspace), workspace.numel(), _stream(dev)))
-    return (out, lse) if return_lse else out
+    return (out, lse) if lse is not None else out
 
 
 def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                  max_seqlen_kv, scale=None, mask_flags=0, q_ids=None, kv_ids=None, out=None,
-                 return_lse=False, window=0, softcap=0.0):
+                 return_lse=False, window=0, softcap=0.0, lse=None):
     """fp8 e4m3 attention: q8 [total_q, Hq, D], k8 [total_kv, Hkv, D],
     v8_colmajor [Hkv, D, total_kv] (uint8 codes or float8_e4m3fn), descale fp32 [3]."""
     dev = q8.device
@@ -410,7 +421,7 @@ def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_
     if out is None:
         out = torch.empty((total_q, hq, d), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, dev)
-    lse = torch.empty((total_q, hq), dtype=torch.float32, device=dev) if return_lse else None
+    lse = _lse_out(lse, return_lse, (total_q, hq), dev)
     batch = cu_seqlens_q.numel() - 1
     lib = _lib.load()
     with torch.cuda.device(dev):
@@ -419,4 +430,4 @@ def attn_fp8_fwd(q8, k8, v8_colmajor, descale, cu_seqlens_q, cu_seqlens_kv, max_
             batch, total_q, total_kv, int(max_seqlen_q), int(max_seqlen_kv), hq, hkv, d,
             float(scale), int(mask_flags), _ptr(q_ids), _ptr(kv_ids), int(window),
             float(softcap), _ptr(out), _ptr(lse), _stream(dev)))
-    return (out, lse) if return_lse else out
+    return (out, lse) if lse is not None else out

@@ -26,6 +26,15 @@
 // is a convex combination of V rows.  The sum is one more MFMA per 64-key
 // group with an all-ones operand: every partial sum of at most 64 e4m3
 // values in [2^-9, 2^8] is exact in fp32, so this equals the plain sum.
+//
+// A weight rounded to e4m3 is off by up to 2^-4 of itself.  Over the many
+// keys of a fully visible tile these errors average out, but a row whose
+// visible keys are few (the first rows of a causal sequence or of a document,
+// a narrow window) sees them all in masked tiles.  There P is carried as two
+// e4m3 terms, P8 = e4m3(P) and e4m3(P - P8), both multiplied with the same V
+// operand and both summed into l: the weight error drops to about 2^-8 of
+// the weight, as with 16-bit probabilities, for twice the P.V MFMAs on
+// those tiles only.
 
 #include "device_common.h"
 #include "kernels.h"
@@ -70,8 +79,15 @@ struct Ring8 {
     static constexpr int IPW = 4;                  // loads per wave per tensor
     static constexpr int LOADS_PER_TILE = 2 * IPW;
 
-    uint32_t koff[IPW];   // lane's byte offset from the wave's first K row
-    uint32_t voff[IPW];   // lane's byte offset from the wave's first V^T row
+    // Lane byte offsets from the wave's first K row and V^T row.  The K
+    // swizzle of the lane's row does not change between the wave's loads
+    // (rows 32 wl + 8 i + lane / 8 share bits 1, 2 and 5), and the V^T one
+    // depends on i only through i & 1, so load i adds a wave-uniform row
+    // offset (8 i K rows, 16 (i >> 1) V^T rows) to the scalar base instead of
+    // holding one register per load.
+    uint32_t koff;
+    uint32_t voff[2];
+    int k_stride, total_kv;
 
     __device__ __forceinline__ static int row(int lane, int wl, int i) {
         return 32 * wl + 8 * i + (lane >> 3);
@@ -83,13 +99,15 @@ struct Ring8 {
         return (lane & 7) ^ vswz(row(lane, wl, i));
     }
 
-    __device__ __forceinline__ void init(int lane, int wl, int k_stride, int total_kv) {
+    __device__ __forceinline__ void init(int lane, int wl, int k_stride_, int total_kv_) {
+        k_stride = k_stride_;
+        total_kv = total_kv_;
+        const int rr = lane >> 3;
+        koff = (uint32_t)(rr * k_stride + kchunk(lane, wl, 0) * 16);
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int rr = 8 * i + (lane >> 3);
-            koff[i] = (uint32_t)(rr * k_stride + kchunk(lane, wl, i) * 16);
-            voff[i] = (uint32_t)rr * (uint32_t)total_kv + (uint32_t)(vchunk(lane, wl, i) * 16);
-        }
+        for (int i = 0; i < 2; ++i)
+            voff[i] = (uint32_t)(8 * i + rr) * (uint32_t)total_kv +
+                      (uint32_t)(vchunk(lane, wl, i) * 16);
     }
 
     struct Src {
@@ -101,8 +119,11 @@ struct Ring8 {
     // wave-uniform bases.  stage: LDS byte address of the ring stage.
     __device__ __forceinline__ void dma(int k, const Src& sr, uint32_t stage, int wl) const {
         const int i = k % IPW;
-        if (k < IPW) dma16_s(sr.k, koff[i], stage + (wl * IPW + i) * 1024);
-        else dma16_s(sr.v, voff[i], stage + TILE + (wl * IPW + i) * 1024);
+        if (k < IPW)
+            dma16_s(sr.k + (int64_t)(8 * i) * k_stride, koff, stage + (wl * IPW + i) * 1024);
+        else
+            dma16_s(sr.v + (int64_t)(16 * (i >> 1)) * total_kv, voff[i & 1],
+                    stage + TILE + (wl * IPW + i) * 1024);
     }
 };
 
@@ -110,16 +131,19 @@ struct Ring8 {
 struct Fp8Wave {
     f32x16_t s[4];       // scores of the tile waiting for its softmax
     i32x8_t pb[2];       // e4m3 probabilities of the tile waiting for its P.V
+    i32x8_t plo[2];      // e4m3 remainders P - pb (masked tiles only)
     f32x16_t o[4];       // O^T accumulators (P8 . V8, unscaled)
     f32x16_t l;          // row sums of P8 (every row of a column holds it)
     float m, alpha;
     bool need;
+    bool split;          // the tile waiting for its P.V carries plo
 };
 
 // Online softmax of one tile (VALU): mask when partial, cap the scores with
 // CAP (in log2 units, scale factor 1 after that), new running max (lazy:
 // moved only when some row's tile max exceeds it by more than
-// kRescaleSlack), probabilities rounded to e4m3 into pb.
+// kRescaleSlack), probabilities rounded to e4m3 into pb; a masked tile also
+// gets the e4m3 remainders P - pb into plo.
 template <bool MASKED, bool CAP>
 __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, int hi,
                                          float cap_in2, float cap_out) {
@@ -145,9 +169,11 @@ __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, i
     if constexpr (CAP) c = 1.f;
     mx = fmaxf(mx, xor32(mx));
     mx = (mx == kNegInf) ? kNegInf : mx * c;
+    // per-row running max, as in the 16-bit kernels: a row's result does not
+    // depend on the rows that share its wave
     const bool up = mx > st.m + kRescaleSlack;
     st.need = __any(up);
-    const float mnew = st.need ? fmaxf(st.m, mx) : st.m;
+    const float mnew = up ? mx : st.m;
     st.alpha = (mnew == kNegInf) ? 1.f : fast_exp2(st.m - mnew);
     st.m = mnew;
     const float nm = (mnew == kNegInf) ? 0.f : -mnew;
@@ -167,7 +193,22 @@ __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, i
             int packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
             packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], packed, true);
             st.pb[gp][wd] = packed;
+            if constexpr (MASKED) {
+                // the rounded values back in fp32 (exact), and what they miss
+                const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(packed, false);
+                const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(packed, true);
+                int rest = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0] - h01.x, pv[1] - h01.y, 0, false);
+                rest = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2] - h23.x, pv[3] - h23.y, rest, true);
+                st.plo[gp][wd] = rest;
+            }
         }
+    if constexpr (!MASKED) {
+        // plo is read only after a masked tile; an empty definition here ends
+        // the old remainders' life, so their registers are not held across
+        // unmasked tiles (no instruction is emitted)
+        asm volatile("" : "=v"(st.plo[0]), "=v"(st.plo[1]));
+    }
+    st.split = MASKED;
 }
 
 __device__ __forceinline__ i32x8_t frag8(const uint8_t* p, uint32_t off) {
@@ -208,14 +249,16 @@ constexpr int kStream8Prefetch = 3;
 //   PV: the row sums of P8 (two MFMAs with an all-ones operand, no LDS
 //       operand: they cover the first operand reads), then
 //       O^T[db] += V^T_tile(db, gp) . P^T(gp), 8 MFMAs (step db*2 + gp,
-//       `hook` after each);
+//       `hook` after each); with LO the remainders plo take two more row-sum
+//       MFMAs and one more product per step, on the same V operand;
 //   QK: S^T[kb] = K_tile(kb) . Q^T, 8 MFMAs (step t*4 + kb).
 // QK runs for every tile, visible keys or not, so the scores are always
 // overwritten and the previous tile's are never live across the P.V.
-template <bool PV, bool QK, class Hook>
+template <bool PV, bool QK, bool LO, class Hook>
 __device__ __forceinline__ void mfma_stream8(Fp8Wave& st, const uint8_t* vt, const uint8_t* kt,
                                              const i32x8_t (&q)[2], const Hook& hook) {
     static_assert(PV || QK, "empty stream");
+    static_assert(PV || !LO, "remainders belong to a P.V");
     if (PV && st.need) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) st.o[db] *= st.alpha;
@@ -251,6 +294,10 @@ __device__ __forceinline__ void mfma_stream8(Fp8Wave& st, const uint8_t* vt, con
         const i32x8_t ones = {one4, one4, one4, one4, one4, one4, one4, one4};
         st.l = mfma_fp8(ones, st.pb[0], st.l);
         st.l = mfma_fp8(ones, st.pb[1], st.l);
+        if constexpr (LO) {
+            st.l = mfma_fp8(ones, st.plo[0], st.l);
+            st.l = mfma_fp8(ones, st.plo[1], st.l);
+        }
     }
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -258,6 +305,7 @@ __device__ __forceinline__ void mfma_stream8(Fp8Wave& st, const uint8_t* vt, con
         __builtin_amdgcn_sched_barrier(0);
         if (i < NPV) {
             st.o[i >> 1] = mfma_fp8(a[i % (PD + 1)], st.pb[i & 1], st.o[i >> 1]);
+            if constexpr (LO) st.o[i >> 1] = mfma_fp8(a[i % (PD + 1)], st.plo[i & 1], st.o[i >> 1]);
             hook(i);
         } else {
             const int j = i - NPV;
@@ -443,9 +491,12 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     st.l = f32x16_t{};
     st.pb[0] = i32x8_t{};
     st.pb[1] = i32x8_t{};
+    st.plo[0] = i32x8_t{};
+    st.plo[1] = i32x8_t{};
     st.m = kNegInf;
     st.alpha = 1.f;
     st.need = false;
+    st.split = false;
 
     // Every wave runs every tile: a tile with no visible key for this wave
     // (a causal diagonal) gives P = 0 and leaves m, l and O unchanged.
@@ -471,7 +522,7 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
         block_barrier();
-        if (lead) mfma_stream8<false, true>(st, ring, ring, q, NoHook{});
+        if (lead) mfma_stream8<false, true, false>(st, ring, ring, q, NoHook{});
 
         for (int jt = 0; jt < n; ++jt) {
             const int j0 = kv_begin + jt * BN8;
@@ -484,7 +535,10 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
             } else {
                 // (at jt == 0 this P.V multiplies P8 = 0 by the zeroed V^T of
                 // the last stage: it adds nothing)
-                mfma_stream8<true, true>(st, st_prev + R::TILE, st_cur, q, NoHook{});
+                if (st.split)
+                    mfma_stream8<true, true, true>(st, st_prev + R::TILE, st_cur, q, NoHook{});
+                else
+                    mfma_stream8<true, true, false>(st, st_prev + R::TILE, st_cur, q, NoHook{});
             }
             // tile jt+1 must have landed; tile jt+2, issued after it, may stay
             // in flight
@@ -503,16 +557,21 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
                 if (load3 && !spread) issue_all(j3, st3);
                 R::Src sr{p.k, p.vt};
                 if (spread) sr = src(j3);
-                mfma_stream8<true, true>(st, st_cur + R::TILE, st_next, q,
-                                         Dma8Hook<R>{ld, sr, st3, wl, spread});
+                const Dma8Hook<R> hook{ld, sr, st3, wl, spread};
+                if (st.split)
+                    mfma_stream8<true, true, true>(st, st_cur + R::TILE, st_next, q, hook);
+                else
+                    mfma_stream8<true, true, false>(st, st_cur + R::TILE, st_next, q, hook);
             } else {
                 softmax(j0);
             }
             block_barrier();
         }
-        if (!lead)
-            mfma_stream8<true, false>(st, ring + ((n - 1) % kStages8) * R::STAGE + R::TILE, ring, q,
-                                      NoHook{});
+        if (!lead) {
+            const uint8_t* vt_last = ring + ((n - 1) % kStages8) * R::STAGE + R::TILE;
+            if (st.split) mfma_stream8<true, false, true>(st, vt_last, ring, q, NoHook{});
+            else mfma_stream8<true, false, false>(st, vt_last, ring, q, NoHook{});
+        }
     }
 
     if (valid) {

@@ -380,9 +380,13 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], float c, fl
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = fmaxf(mx, xor32(mx));
     mx = (mx == kNegInf) ? kNegInf : mx * c;
+    // Each row moves its own running max (only the rescale branch is
+    // wave-uniform), so a row's arithmetic does not depend on which rows
+    // share its wave: a query head gives the same bits whether or not it is
+    // packed with the other heads of its GQA group.
     const bool up = mx > m + kRescaleSlack;
     need = __any(up);
-    const float mnew = need ? fmaxf(m, mx) : m;
+    const float mnew = up ? mx : m;
     alpha = (mnew == kNegInf) ? 1.f : fast_exp2(m - mnew);
     m = mnew;
     const float nm = (mnew == kNegInf) ? 0.f : -mnew;

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     ATTN_F16,
     ATTN_BF16,
     ATTN_FP8_E4M3,
+    ATTN_DECODE_SCRATCH_BYTES,
     MASK_NONE,
     MASK_CAUSAL,
     MASK_DOCUMENT,
@@ -24,6 +25,7 @@ from .api import (  # noqa: F401
     attn_paged_prefill_block_sparse_fwd,
     attn_paged_decode_workspace_bytes,
     attn_paged_decode_fwd,
+    attn_paged_decode_fwd_noalloc,
     attn_paged_decode_fp8kv_fwd,
     attn_fp8_fwd,
     attn_varlen_bwd,

@@ -19,6 +19,7 @@ STATUS_NAMES = {
     6: "ATTN_ERR_WORKSPACE",
 }
 ATTN_F16, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+ATTN_DECODE_SCRATCH_BYTES = 16 << 20   # attn_paged_decode_fwd_noalloc's scratch per GPU
 MASK_NONE, MASK_CAUSAL, MASK_DOCUMENT, MASK_PATCH = 0, 1, 2, 4
 
 _p = ctypes.c_void_p
@@ -52,6 +53,9 @@ SIGNATURES = {
     "attn_paged_decode_fwd": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _f32, _i32, _f32, _i32, ctypes.c_int,
                                              _p, _p, _p, _size, _p]),
+    "attn_paged_decode_fwd_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _i32, _p, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, _f32, _i32, _f32, _i32,
+                                                     ctypes.c_int, _p, _p, _p]),
     "attn_paged_decode_fp8kv_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32,
                                                    _i32, _i32, _i32, _i32, _f32, _i32, _f32, _i32,
                                                    ctypes.c_int, _p, _p, _p, _size, _p]),

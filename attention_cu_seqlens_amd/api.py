@@ -357,6 +357,37 @@ def attn_paged_decode_fwd(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_s
     return (out, lse) if lse is not None else out
 
 
+def attn_paged_decode_fwd_noalloc(q, k_cache, v_cache, block_table, cu_seqlens_kv, max_seqlen_kv,
+                                  scale=None, split_tokens=0, out=None, return_lse=False,
+                                  window=0, softcap=0.0, lse=None):
+    """attn_paged_decode_fwd without a workspace: the split partials live in
+    the library's per-GPU scratch array, so the C call allocates nothing
+    (pass `out` / `lse` to keep this wrapper from allocating them).  Calls
+    that overlap in time on one GPU race on that scratch."""
+    dev = q.device
+    _need(q, "q", (torch.float16, torch.bfloat16))
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, name, q.dtype, dev)
+    for name, t in (("block_table", block_table), ("cu_seqlens_kv", cu_seqlens_kv)):
+        _need(t, name, torch.int32, dev)
+    batch, hq, d = q.shape
+    nb, bs, hkv, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, dev)
+    lse = _lse_out(lse, return_lse, (batch, hq), dev)
+    lib = _lib.load()
+    with torch.cuda.device(dev):
+        _lib.check("attn_paged_decode_fwd_noalloc", lib.attn_paged_decode_fwd_noalloc(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+            _ptr(cu_seqlens_kv), batch, int(max_seqlen_kv), hq, hkv, d, bs, nb, float(scale),
+            int(window), float(softcap), int(split_tokens), _DT[q.dtype], _ptr(out), _ptr(lse),
+            _stream(dev)))
+    return (out, lse) if lse is not None else out
+
+
 def attn_paged_decode_fp8kv_fwd(q, k_cache8, v_cache8, kv_descale, block_table, cu_seqlens_kv,
                                 max_seqlen_kv, scale=None, split_tokens=0, out=None,
                                 return_lse=False, workspace=None, window=0, softcap=0.0, lse=None):

@@ -435,7 +435,7 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
                         int32_t head_size, int32_t block_size, int32_t num_blocks, float scale,
                         int32_t window_left, float softcap, int32_t split_tokens, attn_dtype dtype,
                         void* out, float* lse, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        void* stream, bool use_scratch = false) {
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
     if (head_size != 64 && head_size != 128) return ATTN_ERR_UNSUPPORTED;
     if (block_size != 16 && block_size != 32 && block_size != 64) return ATTN_ERR_UNSUPPORTED;
@@ -457,11 +457,20 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     const int span = attn::decode_span(max_seqlen_kv, window_left);
     const int st = attn::decode_split_tokens(batch, num_kv_heads, span, split_tokens);
     const size_t need = attn::decode_workspace_bytes(batch, num_heads, head_size, span, st);
-    if (workspace == nullptr || workspace_bytes < need ||
-        (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    if (use_scratch) {
+        // the library's own scratch array (no allocation): size checked here,
+        // on the host, before any HIP call
+        if (need > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE;
+    } else if (workspace == nullptr || workspace_bytes < need ||
+               (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) {
         return ATTN_ERR_WORKSPACE;
+    }
     const attn_status d = check_device();
     if (d != ATTN_OK) return d;
+    if (use_scratch) {
+        if (attn::decode_scratch(&workspace) != hipSuccess) return ATTN_ERR_DEVICE;
+        workspace_bytes = attn::kDecodeScratchBytes;
+    }
 
     attn::DecodeParams p{};
     p.q = static_cast<const uint16_t*>(q);
@@ -512,6 +521,22 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
                        cu_seqlens_kv, batch, max_seqlen_kv, num_heads, num_kv_heads, head_size,
                        block_size, num_blocks, scale, window_left, softcap, split_tokens, dtype,
                        out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_paged_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* cu_seqlens_kv, int32_t batch,
+                                          int32_t max_seqlen_kv, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t num_blocks, float scale,
+                                          int32_t window_left, float softcap,
+                                          int32_t split_tokens, attn_dtype dtype, void* out,
+                                          float* lse, void* stream) {
+    static_assert(ATTN_DECODE_SCRATCH_BYTES == attn::kDecodeScratchBytes, "scratch size");
+    return decode_impl(q, k_cache, v_cache, false, nullptr, block_table, max_blocks_per_seq,
+                       cu_seqlens_kv, batch, max_seqlen_kv, num_heads, num_kv_heads, head_size,
+                       block_size, num_blocks, scale, window_left, softcap, split_tokens, dtype,
+                       out, lse, nullptr, 0, stream, /*use_scratch=*/true);
 }
 
 attn_status attn_paged_decode_fp8kv_fwd(const void* q, const void* k_cache8, const void* v_cache8,

@@ -223,6 +223,35 @@ size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_s
     return (size_t)(o_bytes + rows * 2 * 4);
 }
 
+// Split partials of the allocation-free decode entry point: one array per
+// GPU, created with the code object on each device and held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept per device ordinal.
+static __device__ __align__(256) uint8_t scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+    constexpr int kSlots = 64;
+    static std::atomic<void*> addr[kSlots];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kSlots) {
+        void* known = addr[dev].load(std::memory_order_acquire);
+        if (known != nullptr) {
+            *ptr = known;
+            return hipSuccess;
+        }
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    if (dev >= 0 && dev < kSlots) addr[dev].store(p, std::memory_order_release);
+    *ptr = p;
+    return hipSuccess;
+}
+
 namespace {
 
 template <int D, int NW, bool BF16, bool CAP, bool KV8>

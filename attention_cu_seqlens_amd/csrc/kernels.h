@@ -169,6 +169,12 @@ hipError_t launch_paged_prefill(const PrefillParams& p, int head_size, bool bf16
 hipError_t launch_paged_decode(const DecodeParams& p, int head_size, bool bf16, hipStream_t s);
 hipError_t launch_fp8_prefill(const Fp8Params& p, int head_size, int max_seqlen_q, hipStream_t s);
 
+// Scratch of the allocation-free decode entry point (one array per GPU).
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+// Device address of this GPU's scratch array (the current device), looked up
+// once per device.
+hipError_t decode_scratch(void** ptr);
+
 // Decode planning shared by the workspace query and the launch.
 int decode_span(int max_seqlen_kv, int window);
 int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested);

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum attn_status {
     ATTN_OK = 0,
@@ -339,6 +339,34 @@ attn_status attn_paged_decode_fwd(const void* q, const void* k_cache, const void
                                   float scale, int32_t window_left, float softcap,
                                   int32_t split_tokens, attn_dtype dtype, void* out, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_paged_decode_fwd_noalloc -- attn_paged_decode_fwd for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation and
+ * arguments without the workspace pair.  The split partials live in a
+ * library-owned scratch array of ATTN_DECODE_SCRATCH_BYTES bytes on each GPU
+ * (held from the library's first use of that GPU until the process ends).
+ * No allocation or free of any kind happens inside the call.
+ *   Errors: as attn_paged_decode_fwd; ATTN_ERR_WORKSPACE when these sizes
+ *   need more than ATTN_DECODE_SCRATCH_BYTES (the need is
+ *   attn_paged_decode_workspace_bytes with the same arguments), checked on
+ *   the host before any HIP call.
+ *   Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (two streams, two threads) race and give undefined
+ *   results; calls on one stream are ordered and safe.  The scratch keeps
+ *   the last call's partials; nothing in it needs to start at zero.
+ */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+attn_status attn_paged_decode_fwd_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* cu_seqlens_kv, int32_t batch,
+                                          int32_t max_seqlen_kv, int32_t num_heads,
+                                          int32_t num_kv_heads, int32_t head_size,
+                                          int32_t block_size, int32_t num_blocks, float scale,
+                                          int32_t window_left, float softcap,
+                                          int32_t split_tokens, attn_dtype dtype, void* out,
+                                          float* lse, void* stream);
 
 /*
  * attn_paged_decode_fp8kv_fwd -- attn_paged_decode_fwd over an fp8 e4m3

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.attn_abi_version() == 3
+    assert lib.attn_abi_version() == 4
     for code in range(7):
         assert lib.attn_status_string(code)
     assert lib.attn_status_string(99) == b"unknown status"
@@ -234,6 +234,30 @@ def test_decode_host_checks(lib):
     assert call(window=-5) == 2
     assert call(softcap=float("nan")) == 2
     assert call(batch=0) == 0
+
+
+def test_decode_noalloc_host_checks(lib):
+    """The allocation-free decode takes the decode checks and refuses, on the
+    host, sizes whose split partials exceed its fixed scratch."""
+    ws = lib.attn_paged_decode_workspace_bytes
+
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, bt=P, mbps=4096, cukv=P, batch=4, mskv=1000, hq=8, hkv=2, d=128,
+                 bs=16, nb=300, scale=0.1, window=0, softcap=0.0, split=256, dtype=1, out=P,
+                 lse=None, stream=None)
+        a.update(kw)
+        return lib.attn_paged_decode_fwd_noalloc(*a.values())
+
+    assert call(q=None) == 1
+    assert call(split=300) == 2
+    assert call(hq=66, hkv=1) == 3
+    assert call(batch=0) == 0
+    # 256 sequences x 64 heads x 64 splits of 256 keys: 256 MiB of partials
+    big = dict(batch=256, hq=64, hkv=8, mskv=16384, split=256)
+    assert ws(256, 64, 8, 128, 16384, 0, 256) > _lib.ATTN_DECODE_SCRATCH_BYTES
+    assert call(**big) == 6
+    # the decode workload's shape fits
+    assert ws(64, 32, 8, 128, 32768, 0, 0) <= _lib.ATTN_DECODE_SCRATCH_BYTES
 
 
 def test_decode_fp8kv_host_checks(lib):

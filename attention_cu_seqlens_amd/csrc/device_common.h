@@ -85,6 +85,30 @@ __device__ __forceinline__ float cap_score(float s, float in2, float out) {
 // Exchange with lane ^ 32 (the other half of a 32-wide MFMA column).
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Both halves of x: v_permlane32_swap (a VALU op, no LDS round trip unlike
+// a ds_bpermute shuffle) exchanges lanes 32-63 of its first register with
+// lanes 0-31 of its second.  Given two copies of x, the first then holds
+// lanes 0-31 of x in both halves and the second lanes 32-63, so
+// op(first, second) pairs each lane with lane ^ 32; max and + commute, so
+// both lanes of a pair get the same bits.  Written as asm (both registers
+// are outputs): the compiler's builtin for it merged the two results into
+// one.  The s_nop gives the two wait states a permlane needs after a VALU
+// write of its operands.
+__device__ __forceinline__ f32x2_t pair_halves(float x) {
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    return f32x2_t{a, b};
+}
+// max / sum of x over the lane pair (l, l ^ 32), the same value in both lanes
+__device__ __forceinline__ float pair_max(float x) {
+    const f32x2_t h = pair_halves(x);
+    return fmaxf(h.x, h.y);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const f32x2_t h = pair_halves(x);
+    return h.x + h.y;
+}
+
 __device__ __forceinline__ int wave_min(int x) {
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s, 64));
@@ -558,7 +582,7 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
     bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = fmaxf(mx[qb], xor32(mx[qb]));
+        mx[qb] = pair_max(mx[qb]);
         mx[qb] = (mx[qb] == kNegInf) ? kNegInf : mx[qb] * c;
         need |= mx[qb] > st.m[qb] + kRescaleSlack;
     }
@@ -601,7 +625,7 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
                 pb[kb][tp][qb] = w;
             }
         }
-        st.l[qb] += rs[qb] + xor32(rs[qb]);
+        st.l[qb] += pair_sum(rs[qb]);
     }
 
     // O^T += V^T P^T

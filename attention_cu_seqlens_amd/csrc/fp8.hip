@@ -167,7 +167,7 @@ __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, i
             mx = fmaxf(mx, st.s[kb][r]);
         }
     if constexpr (CAP) c = 1.f;
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair_max(mx);
     mx = (mx == kNegInf) ? kNegInf : mx * c;
     // per-row running max, as in the 16-bit kernels: a row's result does not
     // depend on the rows that share its wave

@@ -295,6 +295,14 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     for (int i = tid; i < R::TILE / 16; i += NW * 64)
         *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
             u32x4_t{0u, 0u, 0u, 0u};
+    // Q has landed on every path into the key loop.  The compiler cannot see
+    // the ring's direct-to-LDS loads (inline asm), so a Q register it still
+    // counts as in flight inside the loop makes it wait on the vector-memory
+    // counter before each QK MFMA -- and that wait would drain the ring loads
+    // the lead waves just issued.  Consuming Q here, on the common path,
+    // settles its loads once, before any ring load exists.
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) asm volatile("" : "+v"(q[t]));
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
         int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
@@ -409,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         block_barrier();   // the next chunk's window and ring refill start after all reads
     }
 
-    const float l = st.lpart + xor32(st.lpart);
+    const float l = pair_sum(st.lpart);
     if (valid) {
         const int64_t rowi = (int64_t)(q_start + tok) * p.num_heads + head;
         store_row<D, BF16>(st.o, l, p.out + rowi * D);

@@ -378,7 +378,7 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], float c, fl
     for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = pair_max(mx);
     mx = (mx == kNegInf) ? kNegInf : mx * c;
     // Each row moves its own running max (only the rescale branch is
     // wave-uniform), so a row's arithmetic does not depend on which rows

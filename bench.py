@@ -10,15 +10,22 @@ TFLOP/s of the whole step: 4 * D * Hq * sum_b L_b (L_b + 1) / 2 flops (the
 visible query-key pairs, each needing a D-long dot product and a D-long
 weighted sum) divided by the step time.
 
-The same JSON line carries the prefill kernel's roofline figure, the fp64 CPU
-oracle timed on a bounded sample of the same workload, and more single-GPU
+The same JSON line carries the prefill kernel's roofline figure (mean and
+median launch time from HIP events on the launching stream), the fp64 CPU
+oracle timed on a bounded sample of the same workload (with the host's CPU
+count, the cores this process may use and numpy's BLAS threads) and on
+bounded samples of the decode, cross-attention and fp8 workloads, and more
+single-GPU
 measurements: paged decode (HBM GB/s, with its own roofline figure), the same
 decode over an fp8 e4m3 cache (one byte per element), the varlen prefill
 under 128x128 causal block lists through the block-sparse entry point, the
 fused rotary + packed-QKV unpack + cache write of its tokens (HBM GB/s), a plain
 device-to-device copy (the practical HBM ceiling, and the calibration kernel
 for the traffic counters), byte->patch cross attention, dense causal fp8 and
-the varlen backward on the same workload (TFLOP/s).
+the varlen backward on the same workload (TFLOP/s).  The two exp-heavy lines
+(cross attention at head size 64, dense fp8) carry a roofline object with
+both of their bounds: the MFMA floor and the softmax VALU floor (see
+VALU_CYCLES_PER_64), the binding one on top.
 
 `roofline.traffic` is the HBM bytes one prefill launch moves, from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters recorded in profiles/traffic.json;
@@ -44,6 +51,17 @@ import numpy as np  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 / fp16 MFMA
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Softmax VALU floor (the "alu" bound of the exp-heavy workloads).  From the
+# chip's unit counts: 256 CUs x 4 SIMDs at 2.4 GHz; per SIMD a wave-wide
+# (64-lane) VALU instruction issues every 4 cycles and v_exp_f32 every 8
+# (measured on the box).  Each score needs, per 64 scores: one FMA (scale and
+# max shift, 4 cycles), one exp (8), half a v_max3 (2), half a two-value pack
+# to the product's type (2), and for the 16-bit kernels one add into the row
+# sum (4): 20 cycles, or 16 where the row sum runs on the MFMA (fp8).
+SIMDS = 256 * 4
+CLOCK_HZ = 2.4e9
+EXP_PER_S = 64 / 8 * SIMDS * CLOCK_HZ                    # 19.7 T exp/s
+VALU_CYCLES_PER_64 = {"bf16": 20.0, "fp8": 16.0}
 CSRC = os.path.join(ROOT, "attention_cu_seqlens_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources that define each measured kernel; a change to any of them voids its
@@ -75,6 +93,30 @@ def patch_pairs(w):
         pid = w.q_ids[cu[b]:cu[b + 1]].astype(np.int64)
         tot += int(np.minimum(pid + 1, int(w.kv_lens[b])).sum())
     return tot
+
+
+def two_bounds(flops, scores, kind, ms, mfma_peak_tflops):
+    """Roofline object of an exp-heavy kernel with both of its bounds: the
+    MFMA floor (flops at the dense MFMA peak) and the softmax VALU floor
+    (scores at the VALU_CYCLES_PER_64 cost), plus the exp floor alone; the
+    binding one is the longer floor."""
+    mfma_us = flops / (mfma_peak_tflops * 1e12) * 1e6
+    valu_per_s = 64 / VALU_CYCLES_PER_64[kind] * SIMDS * CLOCK_HZ
+    valu_us = scores / valu_per_s * 1e6
+    exp_us = scores / EXP_PER_S * 1e6
+    us = ms * 1e3
+    tf = flops / (ms * 1e-3) / 1e12
+    sc = scores / (ms * 1e-3)
+    mfma = {"achieved": round(tf, 2), "peak": mfma_peak_tflops, "unit": "TFLOP/s",
+            "frac": round(tf / mfma_peak_tflops, 4), "floor_us": round(mfma_us, 2)}
+    valu = {"achieved": round(sc / 1e12, 4), "peak": round(valu_per_s / 1e12, 4),
+            "unit": "T scores/s", "frac": round(sc / valu_per_s, 4), "floor_us": round(valu_us, 2),
+            "exp_floor_us": round(exp_us, 2), "scores": scores}
+    bound = "alu" if valu_us > mfma_us else "mfma"
+    top = valu if bound == "alu" else mfma
+    return {"bound": bound, "achieved": top["achieved"], "peak": top["peak"],
+            "unit": top["unit"], "frac": top["frac"], "kernel_us": round(us, 2),
+            "mfma": mfma, "valu": valu}
 
 
 def timed(fn, iters, torch):
@@ -125,40 +167,122 @@ def paged_inputs(w, A, torch, dev):
     return lens_q, lens_kv, kc, vc, bt
 
 
-def cpu_baseline(w, n_seqs):
-    """The fp64 oracle on the first n_seqs sequences of the workload, all heads:
-    cache fill through reshape_and_cache, then paged causal attention."""
-    import oracle as ORC
+def host_threads():
+    """Host CPU counts on this machine: (os.cpu_count, cores this process may
+    run on, numpy's BLAS thread count -- the threads the oracle's products use)."""
+    cpu = os.cpu_count()
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = cpu
     try:
         from threadpoolctl import threadpool_info
         blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
-        cores = int(max(blas)) if blas else 1
+        blas_threads = int(max(blas)) if blas else 1
     except Exception:
-        cores = 1
-    lens = [int(x) for x in w.q_lens[:n_seqs]]
-    tot = sum(lens)
-    q = w.q[:tot].double().cpu().numpy()
-    k = w.k_new[:tot].double().cpu().numpy()
-    v = w.v_new[:tot].double().cpu().numpy()
-    bs = w.block_size
-    nblk = [(n + bs - 1) // bs for n in lens]
-    table = np.zeros((len(lens), max(nblk)), dtype=np.int32)
+        blas_threads = 1
+    return cpu, aff, blas_threads
+
+
+def _contiguous_table(lens, bs):
+    """Block table placing the given sequences' pages one after another."""
+    nblk = [(int(n) + bs - 1) // bs for n in lens]
+    table = np.zeros((len(lens), max(1, max(nblk, default=1))), dtype=np.int32)
     base = 0
     for i, n in enumerate(nblk):
         table[i, :n] = np.arange(base, base + n)
         base += n
-    kc = np.zeros((base, bs) + k.shape[1:])
+    return table, max(1, base)
+
+
+def _oracle_paged(w, n_seqs, rows_fn=None):
+    """The fp64 oracle on the first n_seqs sequences of a paged workload (all
+    heads): cache fill through reshape_and_cache, then paged attention (the
+    decode form when q_len is 1).  rows_fn(q_lens) may pick sampled rows.
+    Returns (seconds, lens_q, lens_kv, rows or None)."""
+    import oracle as ORC
+    lq = [int(x) for x in w.q_lens[:n_seqs]]
+    lk = [int(x) for x in w.kv_lens[:n_seqs]]
+    tq, tk = sum(lq), sum(lk)
+    q = w.q[:tq].double().cpu().numpy()
+    k = w.k_new[:tk].double().cpu().numpy()
+    v = w.v_new[:tk].double().cpu().numpy()
+    bs = w.block_size
+    table, nb = _contiguous_table(lk, bs)
+    kc = np.zeros((nb, bs) + k.shape[1:])
     vc = np.zeros_like(kc)
-    cu = ORC.cu_seqlens(lens)
+    cu_q, cu_kv = ORC.cu_seqlens(lq), ORC.cu_seqlens(lk)
+    rows = None if rows_fn is None else rows_fn(lq)
+    ids = None if w.q_ids is None else np.asarray(w.q_ids)[:tq]
     t0 = time.perf_counter()
-    kc, vc = ORC.reshape_and_cache(k, v, kc, vc, table, cu, cu, bs)
-    ORC.paged_attention(q, kc, vc, table, cu, cu, bs, w.scale, w.mask_flags)
-    dt = time.perf_counter() - t0
+    kc, vc = ORC.reshape_and_cache(k, v, kc, vc, table, cu_kv, cu_kv, bs)
+    ORC.paged_attention(q, kc, vc, table, cu_q, cu_kv, bs, w.scale, w.mask_flags, q_ids=ids,
+                        rows=rows)
+    return time.perf_counter() - t0, lq, lk, rows
+
+
+def cpu_baseline(w, n_seqs):
+    """The fp64 oracle on the first n_seqs sequences of the varlen prefill
+    workload, all heads: cache fill through reshape_and_cache, then paged
+    causal attention."""
+    cpu, aff, blas = host_threads()
+    dt, lens, _, _ = _oracle_paged(w, n_seqs)
     flops = 4.0 * w.head_size * w.num_heads * sum(n * (n + 1) / 2 for n in lens)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas, "kind": "oracle",
+            "os_cpu_count": cpu, "affinity_cores": aff, "blas_threads": blas,
+            "seconds": round(dt, 2),
             "sample": f"sequences 0-{len(lens) - 1} (lengths {lens}) x all {w.num_heads} query "
                       f"heads of the same workload: cache fill + paged causal attention in fp64 "
-                      f"numpy, {dt:.1f} s; BLAS threads = cores"}
+                      f"numpy, {dt:.1f} s; cores = numpy's BLAS threads (the oracle's products "
+                      f"run on them, everything else on one thread)"}
+
+
+def cpu_baseline_more(W, dev):
+    """The fp64 oracle on bounded samples of the decode, cross-attention and
+    dense fp8 workloads (CPU only), each reported in its workload's unit."""
+    import oracle as ORC
+    import torch
+    cpu, aff, blas = host_threads()
+    res = {}
+    log("  oracle: decode sample")
+    wd = W.paged_gqa_decode_bf16(device=dev)
+    dt, _, lk, _ = _oracle_paged(wd, 6)
+    kv_bytes = 2 * sum(lk) * wd.num_kv_heads * wd.head_size * 2
+    res["decode"] = {"value": kv_bytes / dt / 1e9, "unit": "GB/s of bf16 K/V", "seconds": round(dt, 2),
+                     "sample": f"sequences 0-5 (kv lengths {lk}) x all {wd.num_heads} heads: cache "
+                               f"fill + decode in fp64 numpy"}
+    del wd
+    torch.cuda.empty_cache()
+    log(f"  oracle: decode {dt:.1f} s; cross-attention sample")
+    wc = W.byte_patch_cross_bf16(device="cpu")
+    dt, lq, _, _ = _oracle_paged(wc, 1)
+    pid = np.asarray(wc.q_ids)[:lq[0]].astype(np.int64)
+    pairs = int(np.minimum(pid + 1, int(wc.kv_lens[0])).sum())
+    res["cross_attention"] = {
+        "value": 4.0 * wc.head_size * wc.num_heads * pairs / dt / 1e12, "unit": "TFLOP/s",
+        "seconds": round(dt, 2), "sample": f"sequence 0 (8192 bytes x 1024 patch keys) x all "
+                                           f"{wc.num_heads} heads"}
+    del wc
+    log(f"  oracle: cross {dt:.1f} s; fp8 sample")
+    w8 = W.dense_causal_fp8(device="cpu", batch=1)
+    stride = 512
+    rows = np.arange(0, int(w8.q_lens[0]), stride)
+    cu = ORC.cu_seqlens(w8.q_lens)
+    t0 = time.perf_counter()
+    ORC.fp8_attention(w8.q.numpy(), w8.k_new.numpy(), w8.v8_colmajor.numpy(), w8.descale, cu, cu,
+                      w8.scale, w8.mask_flags, rows=rows)
+    dt = time.perf_counter() - t0
+    pairs = int((rows + 1).sum())
+    res["fp8"] = {"value": 4.0 * w8.head_size * w8.num_heads * pairs / dt / 1e12,
+                  "unit": "TFLOP/s", "seconds": round(dt, 2),
+                  "sample": f"every {stride}th query row of sequence 0 (of 8192) x all "
+                            f"{w8.num_heads} heads, causal"}
+    del w8
+    log(f"  oracle: fp8 {dt:.1f} s")
+    for r in res.values():
+        r.update({"kind": "oracle", "cores": blas})
+    res["host"] = {"os_cpu_count": cpu, "affinity_cores": aff, "blas_threads": blas}
+    return res
 
 
 def bench_copy(torch, dev, nbytes=2 << 30, iters=10):
@@ -334,8 +458,10 @@ def bench_fp8(A, W, torch, dev, iters=20):
         run()
     ms = timed(run, iters, torch)
     tf = flops / (ms * 1e-3) / 1e12
+    scores = causal_pairs(w.q_lens, w.kv_lens) * w.num_heads
     return {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
-            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "flops": flops}
+            "frac_of_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4), "flops": flops,
+            "roofline": two_bounds(flops, scores, "fp8", ms, PEAK_FP8_TFLOPS)}
 
 
 def main():
@@ -400,7 +526,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = ev0.elapsed_time(ev1) / args.steps
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in k_ev]))
+    k_all = [a.elapsed_time(b) for a, b in k_ev]
+    k_ms = float(np.mean(k_all))
+    k_med = float(np.median(k_all))
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (k_ms * 1e-3) / 1e12
     log(f"step {ms_step:.4f} ms (wall {wall * 1e3 / args.steps:.4f} ms), prefill kernel {k_ms:.4f} ms")
@@ -428,7 +556,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("k_paged_prefill", w.name),
-                     "kernel_ms": round(k_ms, 5), "flops_per_launch": flops},
+                     "kernel_ms": round(k_ms, 5), "kernel_ms_median": round(k_med, 5),
+                     "flops_per_launch": flops},
     }
     del kc, vc, out
     torch.cuda.empty_cache()
@@ -444,8 +573,12 @@ def main():
         torch.cuda.empty_cache()
         log("byte->patch cross attention")
         wc = W.byte_patch_cross_bf16(device=dev)
+        pp = patch_pairs(wc)
         line["cross_attention"] = bench_prefill_generic(
-            A, W, torch, dev, wc, 4.0 * wc.head_size * wc.num_heads * patch_pairs(wc))
+            A, W, torch, dev, wc, 4.0 * wc.head_size * wc.num_heads * pp)
+        line["cross_attention"]["roofline"] = two_bounds(
+            line["cross_attention"]["flops"], pp * wc.num_heads, "bf16",
+            line["cross_attention"]["ms"], PEAK_BF16_TFLOPS)
         del wc
         torch.cuda.empty_cache()
         log("rotary + packed-QKV unpack + cache write")
@@ -467,6 +600,9 @@ def main():
     if not args.no_cpu:
         log("cpu oracle baseline")
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+        if not args.no_extra:
+            log("cpu oracle baselines of the decode, cross and fp8 workloads")
+            line["cpu_baseline_other_workloads"] = cpu_baseline_more(W, dev)
 
     print(json.dumps(line), flush=True)
 

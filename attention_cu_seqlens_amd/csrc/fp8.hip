@@ -149,13 +149,16 @@ __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, i
                                          float cap_in2, float cap_out) {
     const int g = lane_id() >> 5;
     if constexpr (MASKED) {
+        // key k held by register r of block kb is visible iff the unsigned
+        // k - lo is below hi - lo (hi >= lo)
+        const uint32_t off = (uint32_t)(j0 + 32 * g - lo);
+        const uint32_t width = (uint32_t)(hi - lo);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                // key held by register r of block kb for this lane
-                const int key = j0 + 64 * (kb >> 1) + 32 * g + 16 * (kb & 1) + r;
-                if (!(key >= lo && key < hi)) st.s[kb][r] = kNegInf;
+                const uint32_t k = off + (uint32_t)(64 * (kb >> 1) + 16 * (kb & 1) + r);
+                if (!(k < width)) st.s[kb][r] = kNegInf;
             }
     }
     float mx = kNegInf;
@@ -187,8 +190,7 @@ __device__ __forceinline__ void softmax8(Fp8Wave& st, float c, int j0, int lo, i
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float sv = st.s[kb][r0 + e];
-                pv[e] = fast_exp2(__builtin_fmaf(sv, c, nm));
-                if constexpr (MASKED) pv[e] = (sv == kNegInf) ? 0.f : pv[e];
+                pv[e] = fast_exp2(__builtin_fmaf(sv, c, nm));   // c > 0: masked -> 0
             }
             int packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[0], pv[1], 0, false);
             packed = __builtin_amdgcn_cvt_pk_fp8_f32(pv[2], pv[3], packed, true);
@@ -352,7 +354,9 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     const float dq = p.descale[0], dk = p.descale[1], dv = p.descale[2];
     const float c_signed = p.scale * dq * dk * kLog2e;
     const bool neg = c_signed < 0.f;
-    const float c = fabsf(c_signed);
+    // at least 1e-30: a masked score (-inf) always gives exp2(-inf) = 0, and
+    // a zero scale still weighs every visible key exactly 1
+    const float c = fmaxf(fabsf(c_signed), 1e-30f);
     // score cap in log2 units (cap_score), on the descaled score
     const float cap_in2 = CAP ? 2.f * c / p.softcap : 0.f;
     const float cap_out = CAP ? p.softcap * kLog2e : 0.f;

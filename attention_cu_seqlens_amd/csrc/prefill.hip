@@ -51,20 +51,21 @@ __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool parti
                                               int hi, float c, const uint8_t* v_tile,
                                               float cap_in2, float cap_out) {
     if (partial) {
-        const int g = lane_id() >> 5;
+        // key k of register r is visible iff lo <= k < hi, i.e. the unsigned
+        // k - lo is below hi - lo (hi >= lo): one add, one compare and one
+        // select per score
+        const uint32_t off = (uint32_t)(j0 + 4 * (lane_id() >> 5) - lo);
+        const uint32_t width = (uint32_t)(hi - lo);
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = j0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                if (!(key >= lo && key < hi)) st.s[kb][r] = kNegInf;
+                const uint32_t k = off + (uint32_t)(kb * 32 + 8 * (r >> 2) + (r & 3));
+                if (!(k < width)) st.s[kb][r] = kNegInf;
             }
-        softmax_tile<BN, BF16, true, CAP>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need,
-                                          cap_in2, cap_out);
-    } else {
-        softmax_tile<BN, BF16, false, CAP>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need,
-                                           cap_in2, cap_out);
     }
+    softmax_tile<BN, BF16, CAP>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need, cap_in2,
+                                cap_out);
     preload_pv<D, BN, PrefillWave<D, BN>::NPRE>(st.pre, v_tile);
 }
 
@@ -121,7 +122,10 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int h0 = hg << p.pack_log2;
     const int hk = h0 / p.group;
     const bool neg = p.c < 0.f;
-    const float c = fabsf(p.c);
+    // |scale| log2(e), at least 1e-30: a masked score (-inf) then always
+    // gives exp2(-inf) = 0, and a zero scale still gives every visible key
+    // weight exactly 1 (scores times 1e-30 are far below half an ulp of 1)
+    const float c = fmaxf(fabsf(p.c), 1e-30f);
 
     const int tid = threadIdx.x;
     // Block-sparse set-up, first half: the list counts of the query blocks

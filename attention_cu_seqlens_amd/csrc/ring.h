@@ -355,13 +355,15 @@ __device__ __forceinline__ void mfma_stream16(f32x16_t (&o)[D / 32], f32x16_t (&
 }
 
 // Online softmax of one tile's scores for one 32-row block (QB = 1).
-// s: raw S^T accumulators (masked entries already -inf when MASKED);
+// s: raw S^T accumulators (masked entries already -inf); c > 0, so a masked
+// score gives exp2(-inf) = 0 with no further test (a zero scale is passed
+// as a tiny positive c, which leaves every visible weight exactly 1);
 // on return pb holds the packed probabilities, m may have moved (then *need
 // is set and alpha holds exp2(m_old - m_new)), and lpart accumulated this
 // lane's partial row sum (relative to the final m after any rescale).  CAP
 // first replaces every score by its capped value in log2 units (cap_score),
 // after which the scale factor is 1.
-template <int BN, bool BF16, bool MASKED, bool CAP = false>
+template <int BN, bool BF16, bool CAP = false>
 __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], float c, float& m,
                                              float& lpart, u32x4_t (&pb)[BN / 32][2],
                                              float& alpha, bool& need, float cap_in2 = 0.f,
@@ -397,7 +399,6 @@ __device__ __forceinline__ void softmax_tile(f32x16_t (&s)[BN / 32], float c, fl
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             p[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, nm));
-            if constexpr (MASKED) p[r] = (s[kb][r] == kNegInf) ? 0.f : p[r];
             rs += p[r];
         }
 #pragma unroll

@@ -109,42 +109,74 @@ __device__ __forceinline__ float pair_sum(float x) {
     return h.x + h.y;
 }
 
-__device__ __forceinline__ int wave_min(int x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = min(x, __shfl_xor(x, s, 64));
-    return x;
-}
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int s = 1; s < 64; s <<= 1) {
-        const int t = __shfl_up(x, s, 64);
-        if (lane >= s) x += t;
-    }
-    return x;
+// Lane moves within rows of 16 lanes (DPP, GFX9 encodings): quad_perm
+// [1,0,3,2] and [2,3,0,1], the half-row and row mirrors, and row_shr:s
+// (0x110 + s; lanes with no source lane in their row read 0).  A DPP move
+// runs on the VALU, with no LDS round trip as a lane shuffle has.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
 }
 
+// Reductions over the 64 lanes (every lane active); the result is
+// wave-uniform.  Within a row the moves pair lanes i^1, i^2, the two
+// halves and the two 8-lane halves' mirrors, so every lane ends with its
+// row's extreme; the four rows are combined on the scalar unit.
+__device__ __forceinline__ int wave_min(int x) {
+    x = min(x, dpp_move<kDppXor1>(x));
+    x = min(x, dpp_move<kDppXor2>(x));
+    x = min(x, dpp_move<kDppHalfMirror>(x));
+    x = min(x, dpp_move<kDppMirror>(x));
+    return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+// Inclusive prefix sum over the 64 lanes: a Hillis-Steele scan inside each
+// row (shifts 1, 2, 4, 8), then each row adds the totals of the rows below.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += dpp_move<0x111>(x);
+    x += dpp_move<0x112>(x);
+    x += dpp_move<0x114>(x);
+    x += dpp_move<0x118>(x);
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = lane_id() >> 4;
+    return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// The token ranges of one sequence in the packed query and key arrays.
+struct SeqSpan {
+    int q_start, q_len, kv_start, kv_len;
+};
+
 // Work item k of XCD `xcd` (workgroup i runs on XCD i % 8, k = i / 8) ->
-// (sequence b, head group hg, query tile qt), for query tiles of `tt` tokens.
-// Units u = b * n_hg + hg are dealt to XCDs round-robin (XCD x owns units
-// x, x + 8, ...); an XCD walks its units in order and each unit's query
-// tiles longest first, so the tiles that share one K/V stream run together
-// on one XCD and its L2.  Only existing tiles get a work item, so short
-// sequences leave no idle workgroups behind; returns false past the XCD's
-// last tile.  Wave-uniform; every wave of a workgroup computes the same.
-__device__ __forceinline__ bool map_tile(const int32_t* cu_q, int batch, int n_hg, int tt, int xcd,
-                                         int k, int& b, int& hg, int& qt) {
+// (sequence b, head group hg, query tile qt), for query tiles of `tt` tokens,
+// and the sequence's spans.  Units u = b * n_hg + hg are dealt to XCDs
+// round-robin (XCD x owns units x, x + 8, ...); an XCD walks its units in
+// order and each unit's query tiles longest first, so the tiles that share
+// one K/V stream run together on one XCD and its L2.  Only existing tiles get
+// a work item, so short sequences leave no idle workgroups behind; returns
+// false past the XCD's last tile.  The cu_seqlens entries of both sides are
+// read in one round trip.  Wave-uniform; every wave of a workgroup computes
+// the same.
+__device__ __forceinline__ bool map_tile(const int32_t* cu_q, const int32_t* cu_kv, int batch,
+                                         int n_hg, int tt, int xcd, int k, int& b, int& hg,
+                                         int& qt, SeqSpan& sp) {
     const int units = batch * n_hg;
     const int lane = lane_id();
     int base = 0;   // tiles of the chunks before this one
     for (int m0 = 0; xcd + 8 * m0 < units; m0 += 64) {
         const int u = xcd + 8 * (m0 + lane);
-        int t = 0;
+        int q0 = 0, q1 = 0, k0 = 0, k1 = 0;
         if (u < units) {
             const int bb = u / n_hg;
-            t = (cu_q[bb + 1] - cu_q[bb] + tt - 1) / tt;
+            q0 = cu_q[bb];
+            q1 = cu_q[bb + 1];
+            k0 = cu_kv[bb];
+            k1 = cu_kv[bb + 1];
         }
+        const int t = (q1 - q0 + tt - 1) / tt;
         const int incl = wave_incl_scan(t);
         const int total = __builtin_amdgcn_readlane(incl, 63);
         if (k < base + total) {
@@ -157,6 +189,10 @@ __device__ __forceinline__ bool map_tile(const int32_t* cu_q, int batch, int n_h
             b = uu / n_hg;
             hg = uu - b * n_hg;
             qt = tu - 1 - (k - base - first);
+            sp.q_start = __builtin_amdgcn_readlane(q0, src);
+            sp.q_len = __builtin_amdgcn_readlane(q1, src) - sp.q_start;
+            sp.kv_start = __builtin_amdgcn_readlane(k0, src);
+            sp.kv_len = __builtin_amdgcn_readlane(k1, src) - sp.kv_start;
             return true;
         }
         base += total;
@@ -194,9 +230,12 @@ __device__ __forceinline__ int upper_bound_i32(const int32_t* a, int n, int x) {
 }
 
 __device__ __forceinline__ int wave_max(int x) {
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) x = max(x, __shfl_xor(x, s, 64));
-    return x;
+    x = max(x, dpp_move<kDppXor1>(x));
+    x = max(x, dpp_move<kDppXor2>(x));
+    x = max(x, dpp_move<kDppHalfMirror>(x));
+    x = max(x, dpp_move<kDppMirror>(x));
+    return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+               max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 // Bits 2 and 3 of a key index swapped.  The accumulator rows a lane feeds to

@@ -341,14 +341,15 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     __shared__ int wave_range[2][NW];
 
     int b, hg, qt;
-    if (!map_tile(p.cu_q, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
-                  blockIdx.x >> 3, b, hg, qt))
+    SeqSpan sp;
+    if (!map_tile(p.cu_q, p.cu_kv, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
+                  blockIdx.x >> 3, b, hg, qt, sp))
         return;
-    const int q_start = p.cu_q[b];
-    const int q_len = p.cu_q[b + 1] - q_start;
+    const int q_start = sp.q_start;
+    const int q_len = sp.q_len;
     const int tok0 = qt * (BM >> p.pack_log2);
-    const int kv_start = p.cu_kv[b];
-    const int kv_len = p.cu_kv[b + 1] - kv_start;
+    const int kv_start = sp.kv_start;
+    const int kv_len = sp.kv_len;
     const int h0 = hg << p.pack_log2;
     const int hk = h0 / p.group;
     const float dq = p.descale[0], dk = p.descale[1], dv = p.descale[2];

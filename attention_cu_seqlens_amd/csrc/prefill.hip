@@ -110,15 +110,16 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const uint8_t* bstate8 = reinterpret_cast<const uint8_t*>(bstate);
 
     int b, hg, qt;
-    if (!map_tile(p.cu_q, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
-                  blockIdx.x >> 3, b, hg, qt))
+    SeqSpan sp;
+    if (!map_tile(p.cu_q, p.cu_kv, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
+                  blockIdx.x >> 3, b, hg, qt, sp))
         return;
 
-    const int q_start = p.cu_q[b];
-    const int q_len = p.cu_q[b + 1] - q_start;
+    const int q_start = sp.q_start;
+    const int q_len = sp.q_len;
     const int tok0 = qt * (BM >> p.pack_log2);
-    const int kv_start = p.cu_kv[b];
-    const int kv_len = p.cu_kv[b + 1] - kv_start;
+    const int kv_start = sp.kv_start;
+    const int kv_len = sp.kv_len;
     const int h0 = hg << p.pack_log2;
     const int hk = h0 / p.group;
     const bool neg = p.c < 0.f;
@@ -299,18 +300,20 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     for (int i = tid; i < R::TILE / 16; i += NW * 64)
         *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
             u32x4_t{0u, 0u, 0u, 0u};
-    // Q has landed on every path into the key loop.  The compiler cannot see
-    // the ring's direct-to-LDS loads (inline asm), so a Q register it still
-    // counts as in flight inside the loop makes it wait on the vector-memory
-    // counter before each QK MFMA -- and that wait would drain the ring loads
-    // the lead waves just issued.  Consuming Q here, on the common path,
-    // settles its loads once, before any ring load exists.
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) asm volatile("" : "+v"(q[t]));
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
         int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
         fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+        // Q has landed before any ring load is issued.  The compiler cannot
+        // see the ring's direct-to-LDS loads (inline asm), so a Q register it
+        // still counts as in flight inside the tile loop makes it wait on the
+        // vector-memory counter before each QK MFMA -- and that wait would
+        // drain the ring loads the lead waves just issued.  Consuming Q here
+        // settles its loads on every path into the tile loop; the block ids
+        // above were loaded after Q, so waiting for them already waited for
+        // Q, and the two round trips overlap.
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) asm volatile("" : "+v"(q[t]));
         if constexpr (BSP) {
             // compact the chunk's listed tiles (thread t looks at tile t)
             bool on = false;

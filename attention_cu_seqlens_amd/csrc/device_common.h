@@ -682,11 +682,31 @@ __device__ __forceinline__ void tile_step(RowsState<D, QB>& st, const uint8_t* l
             }
 }
 
-// Write the normalised O^T of one 32-row block to a token-major output row
-// (`orow` points at the row's first element) and return 1/l (0 if l == 0).
-template <int D, bool BF16>
-__device__ __forceinline__ void store_row(const f32x16_t* o_db, float l, uint16_t* orow) {
-    const int g = lane_id() >> 5;
+// Bytes of LDS one wave needs for store_rows_lds: 32 rows of D 16-bit
+// values, each row padded by 16 bytes so the lanes' 8-byte writes of one
+// register group spread over all banks.
+template <int D>
+constexpr int kStoreRowPitch = 2 * D + 16;
+template <int D>
+constexpr int kStoreSliceBytes = 32 * kStoreRowPitch<D>;
+
+// Write the normalised O (O^T accumulators / l, 0 when l == 0) of a wave's
+// 32 query rows to their token-major output rows, through LDS: each lane
+// first puts its half row (the accumulator rows it holds) into `slice` (row
+// = its column), then the wave stores whole rows, 16 contiguous bytes per
+// lane, so one store instruction covers 64 / (D / 8) complete rows instead
+// of 16 bytes in each of 32 rows.  row_ptr(rr) gives the output row of local row
+// rr (0..31), or null for a row that is not stored.  `slice` must be this
+// wave's alone; the wave's LDS operations complete in order, so its reads
+// see its writes without a barrier.
+template <int D, bool BF16, class RowPtr>
+__device__ __forceinline__ void store_rows_lds(const f32x16_t* o_db, float l, uint8_t* slice,
+                                               const RowPtr& row_ptr) {
+    constexpr int PITCH = kStoreRowPitch<D>;
+    constexpr int CPR = D / 8;      // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;   // rows per store instruction
+    const int lane = lane_id();
+    const int col = lane & 31, g = lane >> 5;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -696,8 +716,16 @@ __device__ __forceinline__ void store_row(const f32x16_t* o_db, float l, uint16_
             u32x2_t w;
             w.x = pack2<BF16>(o_db[db][4 * rq + 0] * inv, o_db[db][4 * rq + 1] * inv);
             w.y = pack2<BF16>(o_db[db][4 * rq + 2] * inv, o_db[db][4 * rq + 3] * inv);
-            *reinterpret_cast<u32x2_t*>(orow + d) = w;
+            *reinterpret_cast<u32x2_t*>(slice + col * PITCH + 2 * d) = w;
         }
+    const int ch = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+        const int rr = i * RPI + lane / CPR;
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(slice + rr * PITCH + 16 * ch);
+        uint16_t* dst = row_ptr(rr);
+        if (dst != nullptr) *reinterpret_cast<u32x4_t*>(dst + 8 * ch) = v;
+    }
 }
 
 }  // namespace attn

@@ -374,21 +374,7 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
     const int tok = tok0 + (r >> p.pack_log2);
     const int head = h0 + (r & ((1 << p.pack_log2) - 1));
     const bool valid = tok < q_len;
-    // Q^T operand (dims 64t + 32g .. +31); a row past the sequence end reads
-    // row tok0 (its keys are all masked and it is never stored).
     i32x8_t q[2];
-    {
-        const uint8_t* qp =
-            p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D8 + 32 * g;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t);
-            const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t + 16);
-            q[t] = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
-                           (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
-            if (neg) q[t] ^= (int)0x80808080u;   // a negative scale applied to -q
-        }
-    }
     int lo = 0, hi = 0;
     if (valid) {
         hi = kv_len;
@@ -521,11 +507,29 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
 #pragma unroll
             for (int k = 0; k < kStages8 - 1; ++k)
                 if (k < n) issue_all(kv_begin + k * BN8, ring_lds + k * R::STAGE);
-            static_assert(kStages8 == 4, "wait counts below");
-            if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
-            else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
+        // Q^T operand (dims 64t + 32g .. +31); a row past the sequence end
+        // reads row tok0 (its keys are all masked and it is never stored).
+        // Loaded after the ring's first tiles, so the two round trips
+        // overlap: the wait for Q below also waits for those tiles, and it
+        // leaves no Q load in flight inside the tile loop (where the compiler,
+        // which cannot see the ring's direct-to-LDS loads, would wait for it
+        // with a count that drains them).
+        {
+            const uint8_t* qp =
+                p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D8 + 32 * g;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t);
+                const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(qp + 64 * t + 16);
+                q[t] = i32x8_t{(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                               (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                if (neg) q[t] ^= (int)0x80808080u;   // a negative scale applied to -q
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) asm volatile("" : "+v"(q[t]));
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         block_barrier();
         if (lead) mfma_stream8<false, true, false>(st, ring, ring, q, NoHook{});
 
@@ -579,15 +583,26 @@ __global__ __launch_bounds__(NW * 64) void k_fp8_prefill(Fp8Params p) {
         }
     }
 
-    if (valid) {
-        const float l = st.l[0];
-        const int64_t row = (int64_t)(q_start + tok) * p.num_heads + head;
-        f32x16_t o_db[4];
+    const float l = st.l[0];
+    f32x16_t o_db[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) o_db[db] = st.o[db] * dv;
-        store_row<D8, true>(o_db, l, p.out + row * D8);
-        if (p.lse != nullptr && g == 0)
-            p.lse[row] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
+    for (int db = 0; db < 4; ++db) o_db[db] = st.o[db] * dv;
+    // O goes out through this wave's slice of the ring, once the trailing
+    // waves' last P.V has read its V^T tile; the slices lie below the last
+    // stage's V^T half, which was zeroed before the key loop (with no barrier
+    // after it when the loop is empty).
+    static_assert(NW * kStoreSliceBytes<D8> <= (kStages8 - 1) * R::STAGE + R::TILE,
+                  "output slices clear of the zeroed V^T half");
+    block_barrier();
+    store_rows_lds<D8, true>(o_db, l, ring + w * kStoreSliceBytes<D8>, [&](int rr) -> uint16_t* {
+        const int rw = w * 32 + rr;
+        const int tk = tok0 + (rw >> p.pack_log2);
+        const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+        return tk < q_len ? p.out + ((int64_t)(q_start + tk) * p.num_heads + hd) * D8 : nullptr;
+    });
+    if (valid && p.lse != nullptr && g == 0) {
+        const int64_t row = (int64_t)(q_start + tok) * p.num_heads + head;
+        p.lse[row] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
     }
 }
 

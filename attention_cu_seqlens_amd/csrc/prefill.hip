@@ -165,20 +165,6 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int tok = tok0 + (r >> p.pack_log2);
     const int head = h0 + (r & ((1 << p.pack_log2) - 1));
     const bool valid = tok < q_len;
-    // Q operand; a row past the sequence end reads row tok0 instead (its keys
-    // are all masked and it is never stored), so the loads issue back to back
-    // with no branch and their latency overlaps the set-up below.
-    u32x4_t q[D / 16];
-    {
-        const uint16_t* qp =
-            p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D + 8 * g;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) q[t] = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-        if (neg) {
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t) q[t] = neg16x8(q[t]);
-        }
-    }
     int lo = 0, hi = 0;
     if (valid) {
         hi = kv_len;
@@ -192,6 +178,23 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         // local window: keys after the query's own position minus the window
         if (p.window > 0) lo = max(lo, tok + (kv_len - q_len) - p.window + 1);
         if (hi < lo) hi = lo;
+    }
+    // Q operand; a row past the sequence end reads row tok0 instead (its keys
+    // are all masked and it is never stored), so the loads issue back to back
+    // with no branch and their latency overlaps the set-up below.  They are
+    // issued after the row intervals: a mask whose interval needs loads
+    // (patch, document) waits for them, and a wait for a load issued after
+    // Q would also wait for Q.
+    u32x4_t q[D / 16];
+    {
+        const uint16_t* qp =
+            p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D + 8 * g;
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) q[t] = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
+        if (neg) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) q[t] = neg16x8(q[t]);
+        }
     }
     // Wave extremes over valid rows; an all-invalid wave gets an empty range.
     const int w_lo = wave_min(valid ? lo : 0x7fffffff);
@@ -425,11 +428,21 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     }
 
     const float l = pair_sum(st.lpart);
-    if (valid) {
+    // O goes out through this wave's slice of the ring: every wave has passed
+    // the last chunk's closing barrier (nothing reads the ring any more), and
+    // the slices lie below the last stage's V half, which was zeroed before
+    // the key loop without a barrier after it.
+    static_assert(NW * kStoreSliceBytes<D> <= (kStages - 1) * R::STAGE + R::TILE,
+                  "output slices clear of the zeroed V half");
+    store_rows_lds<D, BF16>(st.o, l, ring + w * kStoreSliceBytes<D>, [&](int rr) -> uint16_t* {
+        const int rw = w * 32 + rr;
+        const int tk = tok0 + (rw >> p.pack_log2);
+        const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+        return tk < q_len ? p.out + ((int64_t)(q_start + tk) * p.num_heads + hd) * D : nullptr;
+    });
+    if (valid && p.lse != nullptr && g == 0) {
         const int64_t rowi = (int64_t)(q_start + tok) * p.num_heads + head;
-        store_row<D, BF16>(st.o, l, p.out + rowi * D);
-        if (p.lse != nullptr && g == 0)
-            p.lse[rowi] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
+        p.lse[rowi] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
     }
 }
 

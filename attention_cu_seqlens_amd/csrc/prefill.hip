@@ -109,6 +109,15 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     __shared__ int bcnt[BSP ? 16 : 1];
     const uint8_t* bstate8 = reinterpret_cast<const uint8_t*>(bstate);
 
+    // Kernel arguments the set-up reads, fetched together up front (left to
+    // itself the compiler reloads each one where it is used, one dependent
+    // scalar round trip after another).
+    int a_group = p.group, a_heads = p.num_heads, a_window = p.window;
+    uint32_t a_mask = p.mask;
+    float a_c = p.c;
+    const uint16_t* a_q = p.q;
+    asm volatile("" : "+s"(a_group), "+s"(a_heads), "+s"(a_window), "+s"(a_mask), "+s"(a_c),
+                 "+s"(a_q));
     int b, hg, qt;
     SeqSpan sp;
     if (!map_tile(p.cu_q, p.cu_kv, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
@@ -121,12 +130,12 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int kv_start = sp.kv_start;
     const int kv_len = sp.kv_len;
     const int h0 = hg << p.pack_log2;
-    const int hk = h0 / p.group;
-    const bool neg = p.c < 0.f;
+    const int hk = h0 / a_group;
+    const bool neg = a_c < 0.f;
     // |scale| log2(e), at least 1e-30: a masked score (-inf) then always
     // gives exp2(-inf) = 0, and a zero scale still gives every visible key
     // weight exactly 1 (scores times 1e-30 are far below half an ulp of 1)
-    const float c = fmaxf(fabsf(p.c), 1e-30f);
+    const float c = fmaxf(fabsf(a_c), 1e-30f);
 
     const int tid = threadIdx.x;
     // Block-sparse set-up, first half: the list counts of the query blocks
@@ -168,32 +177,41 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     int lo = 0, hi = 0;
     if (valid) {
         hi = kv_len;
-        if (p.mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
-        if (p.mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
-        if (p.mask & kMaskDocument) {
+        if (a_mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
+        if (a_mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
+        if (a_mask & kMaskDocument) {
             const int doc = p.q_ids[q_start + tok];
             lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
             hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
         }
         // local window: keys after the query's own position minus the window
-        if (p.window > 0) lo = max(lo, tok + (kv_len - q_len) - p.window + 1);
+        if (a_window > 0) lo = max(lo, tok + (kv_len - q_len) - a_window + 1);
         if (hi < lo) hi = lo;
     }
-    // Q operand; a row past the sequence end reads row tok0 instead (its keys
-    // are all masked and it is never stored), so the loads issue back to back
-    // with no branch and their latency overlaps the set-up below.  They are
-    // issued after the row intervals: a mask whose interval needs loads
-    // (patch, document) waits for them, and a wait for a load issued after
-    // Q would also wait for Q.
-    u32x4_t q[D / 16];
+    // Q into this wave's slice of the ring (stages 0 and 1, free until the
+    // first key chunk's loads), laid out like a K tile: row rr (the wave's
+    // rows in order) holds 16-byte chunk c at c ^ swz(rr).  One direct load
+    // moves 64 / (D / 8) whole rows -- with GQA packing, consecutive heads of
+    // one token, contiguous in memory -- where loading the operand layout
+    // straight into registers touched 32 rows per instruction.  A row past
+    // the sequence end reads row tok0 instead (its keys are all masked and it
+    // is never stored).  Issued after the row intervals: a mask whose interval
+    // needs loads (patch, document) waits for them, and such a wait would
+    // also wait for any load issued before.
+    static_assert(NW * 32 * 2 * D <= 2 * R::STAGE, "Q slices fit stages 0 and 1");
+    uint8_t* const q_slice = ring + w * 32 * 2 * D;
     {
-        const uint16_t* qp =
-            p.q + ((int64_t)(q_start + (valid ? tok : tok0)) * p.num_heads + head) * D + 8 * g;
+        constexpr int CPR = D / 8, RPI = 64 / CPR;
+        const int ch = lane % CPR;
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) q[t] = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-        if (neg) {
-#pragma unroll
-            for (int t = 0; t < D / 16; ++t) q[t] = neg16x8(q[t]);
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int rr = i * RPI + lane / CPR;
+            const int rw = w * 32 + rr;
+            const int tk = tok0 + (rw >> p.pack_log2);
+            const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+            const uint16_t* src = a_q + ((int64_t)(q_start + (tk < q_len ? tk : tok0)) * a_heads + hd) * D +
+                                  8 * (ch ^ swz<D>(rr));
+            dma16(src, lds_addr(q_slice + i * 1024));
         }
     }
     // Wave extremes over valid rows; an all-invalid wave gets an empty range.
@@ -261,6 +279,21 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     kv_begin = __builtin_amdgcn_readfirstlane(kv_begin);
     kv_end = __builtin_amdgcn_readfirstlane(kv_end);
 
+    // Q operand from the wave's slice (its direct loads have landed after
+    // the wait; each wave reads only its own slice): lane (col, g) takes
+    // chunks 2t + g of row col.  Every wave's reads complete before the
+    // barrier that precedes the first ring load into these stages.
+    u32x4_t q[D / 16];
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    {
+        const uint32_t lq = (uint32_t)(col * 2 * D + ((g ^ swz<D>(col)) << 4));
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            q[t] = *reinterpret_cast<const u32x4_t*>(q_slice + (lq ^ (uint32_t)(t << 5)));
+            if (neg) q[t] = neg16x8(q[t]);
+        }
+    }
+
     const int32_t* table = p.block_table + (int64_t)b * p.mbps;
     const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
     const int tok_stride = p.num_kv_heads * D;
@@ -307,16 +340,6 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
         fill_page_window(win, table, first, n_blocks, tid, NW * 64);
-        // Q has landed before any ring load is issued.  The compiler cannot
-        // see the ring's direct-to-LDS loads (inline asm), so a Q register it
-        // still counts as in flight inside the tile loop makes it wait on the
-        // vector-memory counter before each QK MFMA -- and that wait would
-        // drain the ring loads the lead waves just issued.  Consuming Q here
-        // settles its loads on every path into the tile loop; the block ids
-        // above were loaded after Q, so waiting for them already waited for
-        // Q, and the two round trips overlap.
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) asm volatile("" : "+v"(q[t]));
         if constexpr (BSP) {
             // compact the chunk's listed tiles (thread t looks at tile t)
             bool on = false;
@@ -428,6 +451,9 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     }
 
     const float l = pair_sum(st.lpart);
+    // With no key tile the output slices below could overlap another wave's
+    // Q slice still being read: wait for every wave first.
+    if (kv_begin >= kv_end) block_barrier();
     // O goes out through this wave's slice of the ring: every wave has passed
     // the last chunk's closing barrier (nothing reads the ring any more), and
     // the slices lie below the last stage's V half, which was zeroed before

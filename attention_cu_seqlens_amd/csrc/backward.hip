@@ -95,7 +95,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* base, int64_t stride, i
         const int i = w * (NI / NW) + k;
         const int row = i * RPI + lane / CPR;
         const int c = (lane % CPR) ^ (DKDV ? swz_dkdv<D>(row) : swz<D>(row));
-        const int rr = min(r0 + row, n - 1);
+        const int rr = min(max(r0 + row, 0), n - 1);
         dma16(base + rr * stride + c * 8, tile + i * 1024);
     }
 }
@@ -442,8 +442,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     for (int db = 0; db < D / 16; ++db) dk[db] = dv[db] = f32x4_t{};
     if (n_t > 0 && q_len > 0) {
         const int64_t stride = (int64_t)p.num_heads * D;
-        auto head_of = [&](int it) { return hk * p.group + it / n_qt; };
-        auto row0_of = [&](int it) { return qlo + (it % n_qt) * kBwdTile; };
+        // Query tiles are aligned to qhi and taken from the top down, with
+        // the group's heads innermost: the workgroups of one kv head, which
+        // run together on one XCD, then read the same Q / dO tiles at about
+        // the same time, and all but the first find them in the L2.  The
+        // bottom tile may reach below qlo (rows that see none of these keys)
+        // or below row 0 (rows that do not exist: loads clamped, masked).
+        auto head_of = [&](int it) { return hk * p.group + it % p.group; };
+        auto row0_of = [&](int it) { return qhi - kBwdTile * (it / p.group + 1); };
         const uint32_t lds0 = lds_addr(lds);
         auto load = [&](int it, int bf) {
             const int h = head_of(it), j0 = row0_of(it);
@@ -463,7 +469,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
         auto rows_dma = [&](int it, int bf) {
             if (tid < kBwdTile) {
                 const int h = head_of(it), q = row0_of(it) + tid;
-                const int64_t i = (int64_t)(q_start + min(q, q_len - 1)) * p.num_heads + h;
+                const int64_t i = (int64_t)(q_start + min(max(q, 0), q_len - 1)) * p.num_heads + h;
                 dma4(p.lse + i, lds_addr(&rows_lse2[bf][0]));
                 dma4(p.delta + i, lds_addr(&rows_delta[bf][0]));
             }
@@ -473,7 +479,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
                 asm volatile("" ::: "memory");   // LDS reads below stay after the wait
                 const int q = row0_of(it) + tid;
-                const bool in = q < q_len;
+                const bool in = q >= 0 && q < q_len;
                 rows_lse2[bf][tid] = in ? rows_lse2[bf][tid] * kLog2e : 0.f;
                 rows_delta[bf][tid] = in ? rows_delta[bf][tid] : 0.f;
                 int lo = 0, hi = 0;

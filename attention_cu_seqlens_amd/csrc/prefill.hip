@@ -165,8 +165,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int col = lane & 31, g = lane >> 5;
     // Waves 0-3 and 4-7 each hold one wave per SIMD; the second group runs
     // half a tile behind the first, so on every SIMD one wave issues MFMAs
-    // while the other computes a softmax.  The first group alone loads the
-    // K/V ring, between the MFMAs of its MFMA phase.
+    // while the other computes a softmax.  The second group alone loads the
+    // K/V ring, at the start of its softmax phase.
     const bool lead = w < NW / 2;
 
     // this lane's query row
@@ -300,7 +300,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int head_off = hk * D;
     const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
     R ld;
-    ld.init(lane, w & (NW / 2 - 1), tok_stride);
+    const int wl = w & (NW / 2 - 1);   // this wave's index within its group
+    ld.init(lane, wl, tok_stride);
     const uint32_t ring_lds = lds_addr(ring);
 
     PrefillWave<D, BN> st;
@@ -318,16 +319,16 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     // of a SIMD are offset by half a tile, so that one issues MFMAs (and their
     // LDS operand reads) while the other runs the softmax on the VALU:
     //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
-    //   phase 2 of tile j: lead PV(j), QK(j+1), loads    trail softmax(j)
-    // The lead waves alone load the ring: tile j+3 goes into the stage of
-    // tile j-1 (free once phase 1 of tile j is over), one load after every
-    // other MFMA of the lead's P.V.
+    //   phase 2 of tile j: lead PV(j), QK(j+1)           trail loads, softmax(j)
+    // The trailing waves alone load the ring: tile j+3 goes into the stage of
+    // tile j-1 (free once phase 1 of tile j is over), all of its loads at the
+    // start of their softmax phase.  Per tile the lead waves' work (softmax,
+    // then the MFMA phase) is on the critical path in both phases; the
+    // trailing waves' softmax phase is the one with slack, so the load issue
+    // goes there (issued from the lead's MFMA phase it lengthened every tile).
     // The trailing waves' first P.V of a chunk multiplies P = 0 (pb zeroed
     // here and after each chunk) by the V tile of the last stage: zeroed here
     // (uninitialised LDS could hold NaN codes), later a finite cache tile.
-    constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
-    static_assert(kPvSteps % R::LOADS_PER_TILE == 0, "loads spread evenly over the MFMAs");
-    using Hook = DmaHook<R, kPvSteps / R::LOADS_PER_TILE>;
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -368,14 +369,14 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             if constexpr (BSP) return cs + (int)tlist[max(0, min(k, n - 1))] * BN;
             else return cs + k * BN;
         };
-        if (lead) {
+        if (!lead) {
 #pragma unroll
             for (int k = 0; k < kStages - 1; ++k)
                 if (k < n) {
                     const int jk = tile_key(k);
                     ld.issue(ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first, jk,
-                             kv_len, p.bs_log2, tok_stride, head_off, w,
-                             win[R::slot(jk, first, p.bs_log2, w)]);
+                             kv_len, p.bs_log2, tok_stride, head_off, wl,
+                             win[R::slot(jk, first, p.bs_log2, wl)]);
                 }
             // tile 0 must have landed; tiles 1 and 2 may stay in flight
             static_assert(kStages == 4, "wait counts below");
@@ -412,12 +413,12 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                                                 p.cap_in2, p.cap_out);
             else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
             const int j3 = tile_key(jt + kStages - 1);
-            const bool load3 = lead && jt + kStages - 1 < n;
+            const bool load3 = !lead && jt + kStages - 1 < n;
             int page = 0;
-            if (load3) page = win[R::slot(j3, first, p.bs_log2, w)];
+            if (load3) page = win[R::slot(j3, first, p.bs_log2, wl)];
             // tile jt+1 must have landed; tile jt+2, issued after it, may stay in
             // flight
-            if (lead && jt + 1 < n) {
+            if (!lead && jt + 1 < n) {
                 if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
@@ -425,17 +426,14 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             // phase 2 (after the last tile the lead's QK reads a stale stage;
             // those scores are never used)
             if (lead) {
-                const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
-                const bool spread = load3 && R::whole(j3, kv_len, w);
-                if (load3 && !spread)
-                    ld.issue(st3, p.k_cache, p.v_cache, win, first, j3, kv_len, p.bs_log2,
-                             tok_stride, head_off, w, page);
-                typename R::Src sr{p.k_cache, p.v_cache};
-                if (spread)
-                    sr = R::src(p.k_cache, p.v_cache, page, j3, w, p.bs_log2, tok_stride, head_off);
-                step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next,
-                                                   Hook{ld, sr, st3, w, spread});
+                step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next);
             } else {
+                // tile jt+3 into the stage of tile jt-1, whose last reader (this
+                // group's P.V(jt-1)) ran in phase 1, then the softmax
+                if (load3)
+                    ld.issue(ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE, p.k_cache,
+                             p.v_cache, win, first, j3, kv_len, p.bs_log2, tok_stride, head_off,
+                             wl, page);
                 phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
                                                 p.cap_in2, p.cap_out);
             }

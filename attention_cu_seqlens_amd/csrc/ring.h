@@ -210,26 +210,10 @@ struct Ring16 {
     }
 };
 
-// Callbacks run after each MFMA of a tile product (step = MFMA index within
-// the product): NoHook does nothing; DmaHook issues one load of a ring tile
-// after every EVERY-th MFMA, so a tile's loads go out between the MFMAs
-// instead of arriving at the load unit as one burst.
+// Callback run after each MFMA of a tile product (step = MFMA index within
+// the product) when the caller has nothing to interleave.
 struct NoHook {
     __device__ __forceinline__ void operator()(int) const {}
-};
-
-template <class R, int EVERY>
-struct DmaHook {
-    const R& ld;
-    typename R::Src sr;
-    uint32_t stage;
-    int wl;
-    bool on;
-    __device__ __forceinline__ void operator()(int step) const {
-        if (step % EVERY == EVERY - 1 && step / EVERY < R::LOADS_PER_TILE) {
-            if (on) ld.dma(step / EVERY, sr, stage, wl);
-        }
-    }
 };
 
 // Operand prefetch depth of the MFMA stream, in MFMA steps: the LDS reads of

@@ -319,13 +319,14 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     // of a SIMD are offset by half a tile, so that one issues MFMAs (and their
     // LDS operand reads) while the other runs the softmax on the VALU:
     //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
-    //   phase 2 of tile j: lead PV(j), QK(j+1)           trail loads, softmax(j)
-    // The trailing waves alone load the ring: tile j+3 goes into the stage of
-    // tile j-1 (free once phase 1 of tile j is over), all of its loads at the
-    // start of their softmax phase.  Per tile the lead waves' work (softmax,
-    // then the MFMA phase) is on the critical path in both phases; the
-    // trailing waves' softmax phase is the one with slack, so the load issue
-    // goes there (issued from the lead's MFMA phase it lengthened every tile).
+    //   phase 2 of tile j: lead PV(j), QK(j+1), V loads  trail K loads, softmax(j)
+    // Tile j+3 goes into the stage of tile j-1 (free once phase 1 of tile j is
+    // over) in phase 2: the lead waves issue its V rows between the MFMAs of
+    // their P.V, the trailing waves its K rows at the start of their softmax.
+    // Per-phase timing: issued from the lead's MFMA phase alone, the loads
+    // lengthened it by about 565 cycles per tile (that wave is bound by its
+    // LDS operand reads, and the loads write LDS too); from the trailing
+    // softmax alone by about 325; half in each balances phase 2.
     // The trailing waves' first P.V of a chunk multiplies P = 0 (pb zeroed
     // here and after each chunk) by the V tile of the last stage: zeroed here
     // (uninitialised LDS could hold NaN codes), later a finite cache tile.
@@ -369,19 +370,22 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
             if constexpr (BSP) return cs + (int)tlist[max(0, min(k, n - 1))] * BN;
             else return cs + k * BN;
         };
-        if (!lead) {
+        {
+            // the lead waves load the V rows of each tile, the trailing waves
+            // the K rows
 #pragma unroll
             for (int k = 0; k < kStages - 1; ++k)
                 if (k < n) {
                     const int jk = tile_key(k);
-                    ld.issue(ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first, jk,
-                             kv_len, p.bs_log2, tok_stride, head_off, wl,
-                             win[R::slot(jk, first, p.bs_log2, wl)]);
+                    ld.issue_half(lead, ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first,
+                                  jk, kv_len, p.bs_log2, tok_stride, head_off, wl,
+                                  win[R::slot(jk, first, p.bs_log2, wl)]);
                 }
-            // tile 0 must have landed; tiles 1 and 2 may stay in flight
+            // this wave's half of tile 0 must have landed; tiles 1 and 2 may
+            // stay in flight
             static_assert(kStages == 4, "wait counts below");
-            if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::LOADS_PER_TILE));
-            else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+            if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
+            else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
             else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
         block_barrier();
@@ -413,27 +417,39 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                                                 p.cap_in2, p.cap_out);
             else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
             const int j3 = tile_key(jt + kStages - 1);
-            const bool load3 = !lead && jt + kStages - 1 < n;
+            const bool load3 = jt + kStages - 1 < n;
             int page = 0;
             if (load3) page = win[R::slot(j3, first, p.bs_log2, wl)];
             // tile jt+1 must have landed; tile jt+2, issued after it, may stay in
             // flight
-            if (!lead && jt + 1 < n) {
-                if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::LOADS_PER_TILE));
+            if (jt + 1 < n) {
+                if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             block_barrier();
             // phase 2 (after the last tile the lead's QK reads a stale stage;
             // those scores are never used)
+            const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
             if (lead) {
-                step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next);
+                // V rows of tile jt+3 between the MFMAs of the P.V
+                const bool spread = load3 && R::whole(j3, kv_len, wl);
+                if (load3 && !spread)
+                    ld.issue_half(true, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
+                                  p.bs_log2, tok_stride, head_off, wl, page);
+                typename R::Src sr{p.k_cache, p.v_cache};
+                if (spread)
+                    sr = R::src(p.k_cache, p.v_cache, page, j3, wl, p.bs_log2, tok_stride, head_off);
+                constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
+                static_assert(kPvSteps % R::IPW == 0, "loads spread evenly over the MFMAs");
+                step_mfma<D, BN, BF16, true, true>(
+                    st, q, st_cur + R::TILE, st_next,
+                    DmaHalfHook<R, kPvSteps / R::IPW>{ld, sr, st3, wl, true, spread});
             } else {
-                // tile jt+3 into the stage of tile jt-1, whose last reader (this
-                // group's P.V(jt-1)) ran in phase 1, then the softmax
+                // K rows of tile jt+3 into the stage of tile jt-1 (its last
+                // reader, this group's P.V(jt-1), ran in phase 1), then the softmax
                 if (load3)
-                    ld.issue(ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE, p.k_cache,
-                             p.v_cache, win, first, j3, kv_len, p.bs_log2, tok_stride, head_off,
-                             wl, page);
+                    ld.issue_half(false, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
+                                  p.bs_log2, tok_stride, head_off, wl, page);
                 phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
                                                 p.cap_in2, p.cap_out);
             }

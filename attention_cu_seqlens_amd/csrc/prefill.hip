@@ -132,6 +132,14 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const int h0 = hg << p.pack_log2;
     const int hk = h0 / a_group;
     const bool neg = a_c < 0.f;
+    const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
+    // Without a document mask, a local window or block lists every row's
+    // visible keys start at key 0, so the first key chunk starts there: its
+    // block ids are requested now, and their round trip overlaps the row
+    // intervals and the set-up barrier instead of following them.
+    const bool win_early = !BSP && !(a_mask & kMaskDocument) && a_window <= 0;
+    if (win_early) fill_page_window(win, table, 0, n_blocks, threadIdx.x, NW * 64);
     // |scale| log2(e), at least 1e-30: a masked score (-inf) then always
     // gives exp2(-inf) = 0, and a zero scale still gives every visible key
     // weight exactly 1 (scores times 1e-30 are far below half an ulp of 1)
@@ -294,8 +302,6 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         }
     }
 
-    const int32_t* table = p.block_table + (int64_t)b * p.mbps;
-    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
     const int tok_stride = p.num_kv_heads * D;
     const int head_off = hk * D;
     const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
         int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
         const int first = cs >> p.bs_log2;
-        fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+        if (!(win_early && cs == 0)) fill_page_window(win, table, first, n_blocks, tid, NW * 64);
         if constexpr (BSP) {
             // compact the chunk's listed tiles (thread t looks at tile t)
             bool on = false;

@@ -48,6 +48,7 @@ struct PrefillParams {
     int bm_cap;                 // list capacity
     int bm_n_kb;                // ceil(max_seqlen_kv / kv block): state row length
     int bm_qbs_log2, bm_kvbs_log2;
+    int wg_per_xcd;             // persistent launch: workgroups per XCD
 };
 
 // Rotary + packed-QKV unpack + reshape_and_cache, one pass over the new

@@ -14,13 +14,19 @@
 // Work decomposition needs no device->host sync: the host bounds the grid by
 // max_seqlen_q and total_q, and each workgroup finds its (sequence, head
 // group, query tile) from cu_seqlens_q (map_tile); the few workgroups past
-// the last tile exit at once.
+// the last tile exit at once.  When every sequence has the same length
+// (total_q = batch * max_seqlen_q) at head size 64, one workgroup per CU
+// instead walks a fixed snake of its XCD's tiles (no dispatch between
+// tiles; at head size 128 the loop made the compiler spill).
 //
 // Masks reduce to one visible key interval [lo, hi) per query row: causal
 // (bottom-right) and patch bound hi, document ids (non-decreasing within a
 // sequence) bound both.  Each wave classifies every key tile as empty (skip),
 // full (no per-element test) or partial from the extreme intervals of its
 // rows.
+
+#include <algorithm>
+#include <atomic>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -90,7 +96,7 @@ __device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t 
     __builtin_amdgcn_s_setprio(0);
 }
 
-template <int D, int BN, int QB, int NW, bool BF16, bool CAP, bool BSP>
+template <int D, int BN, int QB, int NW, bool BF16, bool CAP, bool BSP, bool PERSIST>
 __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     static_assert(QB == 1 && NW == 8, "two groups of four single-block waves");
     constexpr int BM = NW * 32;
@@ -118,381 +124,417 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     const uint16_t* a_q = p.q;
     asm volatile("" : "+s"(a_group), "+s"(a_heads), "+s"(a_window), "+s"(a_mask), "+s"(a_c),
                  "+s"(a_q));
-    int b, hg, qt;
-    SeqSpan sp;
-    if (!map_tile(p.cu_q, p.cu_kv, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
-                  blockIdx.x >> 3, b, hg, qt, sp))
-        return;
-
-    const int q_start = sp.q_start;
-    const int q_len = sp.q_len;
-    const int tok0 = qt * (BM >> p.pack_log2);
-    const int kv_start = sp.kv_start;
-    const int kv_len = sp.kv_len;
-    const int h0 = hg << p.pack_log2;
-    const int hk = h0 / a_group;
-    const bool neg = a_c < 0.f;
-    const int32_t* table = p.block_table + (int64_t)b * p.mbps;
-    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
-    // Without a document mask, a local window or block lists every row's
-    // visible keys start at key 0, so the first key chunk starts there: its
-    // block ids are requested now, and their round trip overlaps the row
-    // intervals and the set-up barrier instead of following them.
-    const bool win_early = !BSP && !(a_mask & kMaskDocument) && a_window <= 0;
-    if (win_early) fill_page_window(win, table, 0, n_blocks, threadIdx.x, NW * 64);
-    // |scale| log2(e), at least 1e-30: a masked score (-inf) then always
-    // gives exp2(-inf) = 0, and a zero scale still gives every visible key
-    // weight exactly 1 (scores times 1e-30 are far below half an ulp of 1)
-    const float c = fmaxf(fabsf(a_c), 1e-30f);
-
-    const int tid = threadIdx.x;
-    // Block-sparse set-up, first half: the list counts of the query blocks
-    // this workgroup touches are loaded here, so their latency overlaps the
-    // Q loads and interval searches below; the state words are cleared.
-    int bm_cnt = 0;
-    int n_lq = 1, qb0 = 0, mh = 0;
-    if constexpr (BSP) {
-        n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);   // at most 8
-        qb0 = tok0 >> p.bm_qbs_log2;
-        mh = p.bm_heads == 1 ? 0 : (p.bm_heads == p.num_heads ? h0 : hk);
-        const int qb_last = q_len > 0 ? (q_len - 1) >> p.bm_qbs_log2 : -1;
-        if (tid < 2 * n_lq) {
-            const int pass = tid >= n_lq, qb = qb0 + tid - pass * n_lq;
-            const int32_t* num = pass ? p.bm_full_num : p.bm_kv_num;
-            if (num != nullptr && qb <= qb_last && qb < p.bm_nqb)
-                bm_cnt = min(max(num[((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb], 0), p.bm_cap);
-        }
-        for (int i = tid; i < (n_lq * p.bm_n_kb + 3) / 4; i += NW * 64) bstate[i] = 0u;
-        if (tid == 0) {
-            bsum[NW] = 0x7fffffff;
-            bsum[NW + 1] = -1;
-        }
-    }
-    const int lane = lane_id();
-    const int w = wave_id();
-    const int col = lane & 31, g = lane >> 5;
-    // Waves 0-3 and 4-7 each hold one wave per SIMD; the second group runs
-    // half a tile behind the first, so on every SIMD one wave issues MFMAs
-    // while the other computes a softmax.  The second group alone loads the
-    // K/V ring, at the start of its softmax phase.
-    const bool lead = w < NW / 2;
-
-    // this lane's query row
-    const int r = w * 32 + col;
-    const int tok = tok0 + (r >> p.pack_log2);
-    const int head = h0 + (r & ((1 << p.pack_log2) - 1));
-    const bool valid = tok < q_len;
-    int lo = 0, hi = 0;
-    if (valid) {
-        hi = kv_len;
-        if (a_mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
-        if (a_mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
-        if (a_mask & kMaskDocument) {
-            const int doc = p.q_ids[q_start + tok];
-            lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
-            hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
-        }
-        // local window: keys after the query's own position minus the window
-        if (a_window > 0) lo = max(lo, tok + (kv_len - q_len) - a_window + 1);
-        if (hi < lo) hi = lo;
-    }
-    // Q into this wave's slice of the ring (stages 0 and 1, free until the
-    // first key chunk's loads), laid out like a K tile: row rr (the wave's
-    // rows in order) holds 16-byte chunk c at c ^ swz(rr).  One direct load
-    // moves 64 / (D / 8) whole rows -- with GQA packing, consecutive heads of
-    // one token, contiguous in memory -- where loading the operand layout
-    // straight into registers touched 32 rows per instruction.  A row past
-    // the sequence end reads row tok0 instead (its keys are all masked and it
-    // is never stored).  Issued after the row intervals: a mask whose interval
-    // needs loads (patch, document) waits for them, and such a wait would
-    // also wait for any load issued before.
-    static_assert(NW * 32 * 2 * D <= 2 * R::STAGE, "Q slices fit stages 0 and 1");
-    uint8_t* const q_slice = ring + w * 32 * 2 * D;
-    {
-        constexpr int CPR = D / 8, RPI = 64 / CPR;
-        const int ch = lane % CPR;
-#pragma unroll
-        for (int i = 0; i < 32 / RPI; ++i) {
-            const int rr = i * RPI + lane / CPR;
-            const int rw = w * 32 + rr;
-            const int tk = tok0 + (rw >> p.pack_log2);
-            const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
-            const uint16_t* src = a_q + ((int64_t)(q_start + (tk < q_len ? tk : tok0)) * a_heads + hd) * D +
-                                  8 * (ch ^ swz<D>(rr));
-            dma16(src, lds_addr(q_slice + i * 1024));
-        }
-    }
-    // Wave extremes over valid rows; an all-invalid wave gets an empty range.
-    const int w_lo = wave_min(valid ? lo : 0x7fffffff);
-    const int w_hi = wave_max(valid ? hi : -0x7fffffff);
-    const int w_lo_max = wave_max(valid ? lo : -0x7fffffff);
-    const int w_hi_min = wave_min(valid ? hi : 0x7fffffff);
-    const bool w_any = w_hi > w_lo;
-    if (lane == 0) {
-        wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
-        wave_range[1][w] = w_any ? w_hi : -0x7fffffff;
-    }
-    if (BSP && tid < 2 * n_lq) bcnt[tid] = bm_cnt;
-    __syncthreads();
-    int kv_begin = 0x7fffffff, kv_end = -0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-        kv_begin = min(kv_begin, wave_range[0][i]);
-        kv_end = max(kv_end, wave_range[1][i]);
-    }
-    kv_begin &= ~15;
-
-    // The element mask's key range, [el_lo, el_hi): a partial block's tiles
-    // outside it hold no visible key for any row of the workgroup.
-    const int el_lo = kv_begin, el_hi = kv_end;
-
-    // Block-sparse set-up, second half: read the listed block ids (flattened
-    // over the 2 * n_lq lists) and set their state bits, bit 0 partial and
-    // bit 1 full, one byte per (local query block, key block); a block in
-    // both lists reads as full.  This wave's rows lie in one query block
-    // (its 32 >> pack tokens are aligned and a query block holds at least
-    // 32 tokens).  The key range becomes that of the listed blocks.
-    int lq_w = 0;
-    if constexpr (BSP) {
-        const int n_kb = p.bm_n_kb;
-        lq_w = ((tok0 + ((w * 32) >> p.pack_log2)) >> p.bm_qbs_log2) - qb0;
-        // key blocks of this sequence that have a state byte (a kv_len above
-        // max_seqlen_kv would otherwise run past the row)
-        const int n_kb_seq = min(n_kb, kv_len > 0 ? ((kv_len - 1) >> p.bm_kvbs_log2) + 1 : 0);
-        int total = 0;
-        for (int k = 0; k < 2 * n_lq; ++k) total += bcnt[k];
-        for (int e = tid; e < total; e += NW * 64) {
-            int k = 0, base = 0;
-            while (e >= base + bcnt[k]) base += bcnt[k++];
-            const int pass = k >= n_lq, lq = k - pass * n_lq;
-            const int32_t* idx = pass ? p.bm_full_idx : p.bm_kv_idx;
-            const int64_t row = ((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb0 + lq;
-            const int kb = idx[row * p.bm_cap + (e - base)];
-            if (kb >= 0 && kb < n_kb_seq) {
-                const int at = lq * n_kb + kb;
-                atomicOr(&bstate[at >> 2], (pass ? 2u : 1u) << (8 * (at & 3)));
-                atomicMin(&bsum[NW], kb);
-                atomicMax(&bsum[NW + 1], kb);
-            }
-        }
-        __syncthreads();
-        const int kb_lo = bsum[NW], kb_hi = bsum[NW + 1];
-        if (kb_hi < kb_lo) {
-            kv_begin = kv_end = 0;
+    // Persistent form: workgroup g of an XCD takes items g, then 2G-1-g,
+    // then 2G+g, ... of the XCD's list (G workgroups per XCD; a snake, so
+    // the longest-first order of each unit's tiles pairs long with short).
+    const int g_wg = blockIdx.x >> 3;
+    for (int j = 0;; ++j) {
+        int k_item = g_wg;
+        if constexpr (PERSIST) {
+            k_item = j * p.wg_per_xcd + ((j & 1) ? p.wg_per_xcd - 1 - g_wg : g_wg);
         } else {
-            kv_begin = kb_lo << p.bm_kvbs_log2;
-            kv_end = (int)min((int64_t)kv_len, (int64_t)(kb_hi + 1) << p.bm_kvbs_log2);
+            if (j > 0) break;
         }
-    }
-    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin);
-    kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+        int b, hg, qt;
+        SeqSpan sp;
+        if (!map_tile(p.cu_q, p.cu_kv, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
+                      k_item, b, hg, qt, sp))
+            break;
 
-    // Q operand from the wave's slice (its direct loads have landed after
-    // the wait; each wave reads only its own slice): lane (col, g) takes
-    // chunks 2t + g of row col.  Every wave's reads complete before the
-    // barrier that precedes the first ring load into these stages.
-    u32x4_t q[D / 16];
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    {
-        const uint32_t lq = (uint32_t)(col * 2 * D + ((g ^ swz<D>(col)) << 4));
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            q[t] = *reinterpret_cast<const u32x4_t*>(q_slice + (lq ^ (uint32_t)(t << 5)));
-            if (neg) q[t] = neg16x8(q[t]);
-        }
-    }
+        const int q_start = sp.q_start;
+        const int q_len = sp.q_len;
+        const int tok0 = qt * (BM >> p.pack_log2);
+        const int kv_start = sp.kv_start;
+        const int kv_len = sp.kv_len;
+        const int h0 = hg << p.pack_log2;
+        const int hk = h0 / a_group;
+        const bool neg = a_c < 0.f;
+        const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+        const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
+        // Without a document mask, a local window or block lists every row's
+        // visible keys start at key 0, so the first key chunk starts there: its
+        // block ids are requested now, and their round trip overlaps the row
+        // intervals and the set-up barrier instead of following them.
+        const bool win_early = !BSP && !(a_mask & kMaskDocument) && a_window <= 0;
+        if (win_early) fill_page_window(win, table, 0, n_blocks, threadIdx.x, NW * 64);
+        // |scale| log2(e), at least 1e-30: a masked score (-inf) then always
+        // gives exp2(-inf) = 0, and a zero scale still gives every visible key
+        // weight exactly 1 (scores times 1e-30 are far below half an ulp of 1)
+        const float c = fmaxf(fabsf(a_c), 1e-30f);
 
-    const int tok_stride = p.num_kv_heads * D;
-    const int head_off = hk * D;
-    const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
-    R ld;
-    const int wl = w & (NW / 2 - 1);   // this wave's index within its group
-    ld.init(lane, wl, tok_stride);
-    const uint32_t ring_lds = lds_addr(ring);
-
-    PrefillWave<D, BN> st;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
-    st.m = kNegInf;
-    st.lpart = 0.f;
-    st.alpha = 1.f;
-    st.need = false;
-
-    // Key chunks of PAGE_WIN blocks: stage the chunk's block ids, then stream
-    // its tiles through the ring.
-    //
-    // Per tile j each wave runs QK(j) -> softmax(j) -> PV(j).  The two waves
-    // of a SIMD are offset by half a tile, so that one issues MFMAs (and their
-    // LDS operand reads) while the other runs the softmax on the VALU:
-    //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
-    //   phase 2 of tile j: lead PV(j), QK(j+1), V loads  trail K loads, softmax(j)
-    // Tile j+3 goes into the stage of tile j-1 (free once phase 1 of tile j is
-    // over) in phase 2: the lead waves issue its V rows between the MFMAs of
-    // their P.V, the trailing waves its K rows at the start of their softmax.
-    // Per-phase timing: issued from the lead's MFMA phase alone, the loads
-    // lengthened it by about 565 cycles per tile (that wave is bound by its
-    // LDS operand reads, and the loads write LDS too); from the trailing
-    // softmax alone by about 325; half in each balances phase 2.
-    // The trailing waves' first P.V of a chunk multiplies P = 0 (pb zeroed
-    // here and after each chunk) by the V tile of the last stage: zeroed here
-    // (uninitialised LDS could hold NaN codes), later a finite cache tile.
-#pragma unroll
-    for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < (PrefillWave<D, BN>::NPRE > 0 ? PrefillWave<D, BN>::NPRE : 1); ++i)
-        st.pre[i] = u32x4_t{0u, 0u, 0u, 0u};
-    for (int i = tid; i < R::TILE / 16; i += NW * 64)
-        *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
-            u32x4_t{0u, 0u, 0u, 0u};
-    for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
-        int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
-        const int first = cs >> p.bs_log2;
-        if (!(win_early && cs == 0)) fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+        const int tid = threadIdx.x;
+        // Block-sparse set-up, first half: the list counts of the query blocks
+        // this workgroup touches are loaded here, so their latency overlaps the
+        // Q loads and interval searches below; the state words are cleared.
+        int bm_cnt = 0;
+        int n_lq = 1, qb0 = 0, mh = 0;
         if constexpr (BSP) {
-            // compact the chunk's listed tiles (thread t looks at tile t)
-            bool on = false;
-            if (tid < n) {
-                const int jt = cs + tid * BN;
-                const int kb = jt >> p.bm_kvbs_log2;
-                int v = 0;
-                for (int lq = 0; lq < n_lq; ++lq) v |= bstate8[lq * p.bm_n_kb + kb];
-                on = (v & 2) || ((v & 1) && jt < el_hi && jt + BN > el_lo);
+            n_lq = max(1, (BM >> p.pack_log2) >> p.bm_qbs_log2);   // at most 8
+            qb0 = tok0 >> p.bm_qbs_log2;
+            mh = p.bm_heads == 1 ? 0 : (p.bm_heads == p.num_heads ? h0 : hk);
+            const int qb_last = q_len > 0 ? (q_len - 1) >> p.bm_qbs_log2 : -1;
+            if (tid < 2 * n_lq) {
+                const int pass = tid >= n_lq, qb = qb0 + tid - pass * n_lq;
+                const int32_t* num = pass ? p.bm_full_num : p.bm_kv_num;
+                if (num != nullptr && qb <= qb_last && qb < p.bm_nqb)
+                    bm_cnt = min(max(num[((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb], 0), p.bm_cap);
             }
-            const uint64_t bal = __ballot(on);
-            if (lane == 0) bsum[w] = __popcll(bal);
-            __syncthreads();
-            int off = 0, tot = 0;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
-                off += i < w ? bsum[i] : 0;
-                tot += bsum[i];
+            for (int i = tid; i < (n_lq * p.bm_n_kb + 3) / 4; i += NW * 64) bstate[i] = 0u;
+            if (tid == 0) {
+                bsum[NW] = 0x7fffffff;
+                bsum[NW + 1] = -1;
             }
-            if (on) tlist[off + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)tid;
-            n = tot;
         }
-        __syncthreads();
-        // key offset of the chunk's k-th tile (listed tiles only when sparse)
-        auto tile_key = [&](int k) {
-            if constexpr (BSP) return cs + (int)tlist[max(0, min(k, n - 1))] * BN;
-            else return cs + k * BN;
-        };
-        {
-            // the lead waves load the V rows of each tile, the trailing waves
-            // the K rows
-#pragma unroll
-            for (int k = 0; k < kStages - 1; ++k)
-                if (k < n) {
-                    const int jk = tile_key(k);
-                    ld.issue_half(lead, ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first,
-                                  jk, kv_len, p.bs_log2, tok_stride, head_off, wl,
-                                  win[R::slot(jk, first, p.bs_log2, wl)]);
-                }
-            // this wave's half of tile 0 must have landed; tiles 1 and 2 may
-            // stay in flight
-            static_assert(kStages == 4, "wait counts below");
-            if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
-            else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
-            else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        }
-        block_barrier();
-        if (lead) step_mfma<D, BN, BF16, false, true>(st, q, ring, ring);
+        const int lane = lane_id();
+        const int w = wave_id();
+        const int col = lane & 31, g = lane >> 5;
+        // Waves 0-3 and 4-7 each hold one wave per SIMD; the second group runs
+        // half a tile behind the first, so on every SIMD one wave issues MFMAs
+        // while the other computes a softmax.  The second group alone loads the
+        // K/V ring, at the start of its softmax phase.
+        const bool lead = w < NW / 2;
 
-        for (int jt = 0; jt < n; ++jt) {
-            const int j0 = tile_key(jt);
-            bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
-            int lo_t = lo, hi_t = hi;   // this tile's visible interval per row
-            if constexpr (BSP) {
-                const int v = __builtin_amdgcn_readfirstlane(
-                    bstate8[lq_w * p.bm_n_kb + (j0 >> p.bm_kvbs_log2)]);
-                const int stt = v >= 2 ? 2 : v;
-                if (stt == 2) {          // full block: every existing key
-                    lo_t = 0;
-                    hi_t = valid ? kv_len : 0;
-                    partial = j0 + BN > kv_len;
-                } else if (stt == 0) {   // not listed for this wave's rows
-                    lo_t = hi_t = 0;
-                    partial = true;
+        // this lane's query row
+        const int r = w * 32 + col;
+        const int tok = tok0 + (r >> p.pack_log2);
+        const int head = h0 + (r & ((1 << p.pack_log2) - 1));
+        const bool valid = tok < q_len;
+        int lo = 0, hi = 0;
+        if (valid) {
+            hi = kv_len;
+            if (a_mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
+            if (a_mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
+            if (a_mask & kMaskDocument) {
+                const int doc = p.q_ids[q_start + tok];
+                lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
+                hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
+            }
+            // local window: keys after the query's own position minus the window
+            if (a_window > 0) lo = max(lo, tok + (kv_len - q_len) - a_window + 1);
+            if (hi < lo) hi = lo;
+        }
+        // Q into this wave's slice of the ring (stages 0 and 1, free until the
+        // first key chunk's loads), laid out like a K tile: row rr (the wave's
+        // rows in order) holds 16-byte chunk c at c ^ swz(rr).  One direct load
+        // moves 64 / (D / 8) whole rows -- with GQA packing, consecutive heads of
+        // one token, contiguous in memory -- where loading the operand layout
+        // straight into registers touched 32 rows per instruction.  A row past
+        // the sequence end reads row tok0 instead (its keys are all masked and it
+        // is never stored).  Issued after the row intervals: a mask whose interval
+        // needs loads (patch, document) waits for them, and such a wait would
+        // also wait for any load issued before.
+        static_assert(NW * 32 * 2 * D <= 2 * R::STAGE, "Q slices fit stages 0 and 1");
+        uint8_t* const q_slice = ring + w * 32 * 2 * D;
+        {
+            constexpr int CPR = D / 8, RPI = 64 / CPR;
+            const int ch = lane % CPR;
+#pragma unroll
+            for (int i = 0; i < 32 / RPI; ++i) {
+                const int rr = i * RPI + lane / CPR;
+                const int rw = w * 32 + rr;
+                const int tk = tok0 + (rw >> p.pack_log2);
+                const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+                const uint16_t* src = a_q + ((int64_t)(q_start + (tk < q_len ? tk : tok0)) * a_heads + hd) * D +
+                                      8 * (ch ^ swz<D>(rr));
+                dma16(src, lds_addr(q_slice + i * 1024));
+            }
+        }
+        // Wave extremes over valid rows; an all-invalid wave gets an empty range.
+        const int w_lo = wave_min(valid ? lo : 0x7fffffff);
+        const int w_hi = wave_max(valid ? hi : -0x7fffffff);
+        const int w_lo_max = wave_max(valid ? lo : -0x7fffffff);
+        const int w_hi_min = wave_min(valid ? hi : 0x7fffffff);
+        const bool w_any = w_hi > w_lo;
+        if (lane == 0) {
+            wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
+            wave_range[1][w] = w_any ? w_hi : -0x7fffffff;
+        }
+        if (BSP && tid < 2 * n_lq) bcnt[tid] = bm_cnt;
+        __syncthreads();
+        int kv_begin = 0x7fffffff, kv_end = -0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            kv_begin = min(kv_begin, wave_range[0][i]);
+            kv_end = max(kv_end, wave_range[1][i]);
+        }
+        kv_begin &= ~15;
+
+        // The element mask's key range, [el_lo, el_hi): a partial block's tiles
+        // outside it hold no visible key for any row of the workgroup.
+        const int el_lo = kv_begin, el_hi = kv_end;
+
+        // Block-sparse set-up, second half: read the listed block ids (flattened
+        // over the 2 * n_lq lists) and set their state bits, bit 0 partial and
+        // bit 1 full, one byte per (local query block, key block); a block in
+        // both lists reads as full.  This wave's rows lie in one query block
+        // (its 32 >> pack tokens are aligned and a query block holds at least
+        // 32 tokens).  The key range becomes that of the listed blocks.
+        int lq_w = 0;
+        if constexpr (BSP) {
+            const int n_kb = p.bm_n_kb;
+            lq_w = ((tok0 + ((w * 32) >> p.pack_log2)) >> p.bm_qbs_log2) - qb0;
+            // key blocks of this sequence that have a state byte (a kv_len above
+            // max_seqlen_kv would otherwise run past the row)
+            const int n_kb_seq = min(n_kb, kv_len > 0 ? ((kv_len - 1) >> p.bm_kvbs_log2) + 1 : 0);
+            int total = 0;
+            for (int k = 0; k < 2 * n_lq; ++k) total += bcnt[k];
+            for (int e = tid; e < total; e += NW * 64) {
+                int k = 0, base = 0;
+                while (e >= base + bcnt[k]) base += bcnt[k++];
+                const int pass = k >= n_lq, lq = k - pass * n_lq;
+                const int32_t* idx = pass ? p.bm_full_idx : p.bm_kv_idx;
+                const int64_t row = ((int64_t)b * p.bm_heads + mh) * p.bm_nqb + qb0 + lq;
+                const int kb = idx[row * p.bm_cap + (e - base)];
+                if (kb >= 0 && kb < n_kb_seq) {
+                    const int at = lq * n_kb + kb;
+                    atomicOr(&bstate[at >> 2], (pass ? 2u : 1u) << (8 * (at & 3)));
+                    atomicMin(&bsum[NW], kb);
+                    atomicMax(&bsum[NW + 1], kb);
                 }
             }
-            const uint8_t* st_cur = ring + (jt % kStages) * R::STAGE;
-            const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
-            const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
-            // phase 1
-            if (lead)
-                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
-                                                p.cap_in2, p.cap_out);
-            else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
-            const int j3 = tile_key(jt + kStages - 1);
-            const bool load3 = jt + kStages - 1 < n;
-            int page = 0;
-            if (load3) page = win[R::slot(j3, first, p.bs_log2, wl)];
-            // tile jt+1 must have landed; tile jt+2, issued after it, may stay in
-            // flight
-            if (jt + 1 < n) {
-                if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
+            __syncthreads();
+            const int kb_lo = bsum[NW], kb_hi = bsum[NW + 1];
+            if (kb_hi < kb_lo) {
+                kv_begin = kv_end = 0;
+            } else {
+                kv_begin = kb_lo << p.bm_kvbs_log2;
+                kv_end = (int)min((int64_t)kv_len, (int64_t)(kb_hi + 1) << p.bm_kvbs_log2);
+            }
+        }
+        kv_begin = __builtin_amdgcn_readfirstlane(kv_begin);
+        kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+
+        // Q operand from the wave's slice (its direct loads have landed after
+        // the wait; each wave reads only its own slice): lane (col, g) takes
+        // chunks 2t + g of row col.  Every wave's reads complete before the
+        // barrier that precedes the first ring load into these stages.
+        u32x4_t q[D / 16];
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        {
+            const uint32_t lq = (uint32_t)(col * 2 * D + ((g ^ swz<D>(col)) << 4));
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) {
+                q[t] = *reinterpret_cast<const u32x4_t*>(q_slice + (lq ^ (uint32_t)(t << 5)));
+                if (neg) q[t] = neg16x8(q[t]);
+            }
+        }
+
+        const int tok_stride = p.num_kv_heads * D;
+        const int head_off = hk * D;
+        const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
+        R ld;
+        const int wl = w & (NW / 2 - 1);   // this wave's index within its group
+        ld.init(lane, wl, tok_stride);
+        const uint32_t ring_lds = lds_addr(ring);
+
+        PrefillWave<D, BN> st;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
+        st.m = kNegInf;
+        st.lpart = 0.f;
+        st.alpha = 1.f;
+        st.need = false;
+
+        // Key chunks of PAGE_WIN blocks: stage the chunk's block ids, then stream
+        // its tiles through the ring.
+        //
+        // Per tile j each wave runs QK(j) -> softmax(j) -> PV(j).  The two waves
+        // of a SIMD are offset by half a tile, so that one issues MFMAs (and their
+        // LDS operand reads) while the other runs the softmax on the VALU:
+        //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
+        //   phase 2 of tile j: lead PV(j), QK(j+1), V loads  trail K loads, softmax(j)
+        // Tile j+3 goes into the stage of tile j-1 (free once phase 1 of tile j is
+        // over) in phase 2: the lead waves issue its V rows between the MFMAs of
+        // their P.V, the trailing waves its K rows at the start of their softmax.
+        // Per-phase timing: issued from the lead's MFMA phase alone, the loads
+        // lengthened it by about 565 cycles per tile (that wave is bound by its
+        // LDS operand reads, and the loads write LDS too); from the trailing
+        // softmax alone by about 325; half in each balances phase 2.
+        // The trailing waves' first P.V of a chunk multiplies P = 0 (pb zeroed
+        // here and after each chunk) by the V tile of the last stage: zeroed here
+        // (uninitialised LDS could hold NaN codes), later a finite cache tile.
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < (PrefillWave<D, BN>::NPRE > 0 ? PrefillWave<D, BN>::NPRE : 1); ++i)
+            st.pre[i] = u32x4_t{0u, 0u, 0u, 0u};
+        for (int i = tid; i < R::TILE / 16; i += NW * 64)
+            *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
+                u32x4_t{0u, 0u, 0u, 0u};
+        for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
+            int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
+            const int first = cs >> p.bs_log2;
+            if (!(win_early && cs == 0)) fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+            if constexpr (BSP) {
+                // compact the chunk's listed tiles (thread t looks at tile t)
+                bool on = false;
+                if (tid < n) {
+                    const int jt = cs + tid * BN;
+                    const int kb = jt >> p.bm_kvbs_log2;
+                    int v = 0;
+                    for (int lq = 0; lq < n_lq; ++lq) v |= bstate8[lq * p.bm_n_kb + kb];
+                    on = (v & 2) || ((v & 1) && jt < el_hi && jt + BN > el_lo);
+                }
+                const uint64_t bal = __ballot(on);
+                if (lane == 0) bsum[w] = __popcll(bal);
+                __syncthreads();
+                int off = 0, tot = 0;
+#pragma unroll
+                for (int i = 0; i < NW; ++i) {
+                    off += i < w ? bsum[i] : 0;
+                    tot += bsum[i];
+                }
+                if (on) tlist[off + __popcll(bal & ((1ull << lane) - 1))] = (uint16_t)tid;
+                n = tot;
+            }
+            __syncthreads();
+            // key offset of the chunk's k-th tile (listed tiles only when sparse)
+            auto tile_key = [&](int k) {
+                if constexpr (BSP) return cs + (int)tlist[max(0, min(k, n - 1))] * BN;
+                else return cs + k * BN;
+            };
+            {
+                // the lead waves load the V rows of each tile, the trailing waves
+                // the K rows
+#pragma unroll
+                for (int k = 0; k < kStages - 1; ++k)
+                    if (k < n) {
+                        const int jk = tile_key(k);
+                        ld.issue_half(lead, ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first,
+                                      jk, kv_len, p.bs_log2, tok_stride, head_off, wl,
+                                      win[R::slot(jk, first, p.bs_log2, wl)]);
+                    }
+                // this wave's half of tile 0 must have landed; tiles 1 and 2 may
+                // stay in flight
+                static_assert(kStages == 4, "wait counts below");
+                if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
+                else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
                 else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
             }
             block_barrier();
-            // phase 2 (after the last tile the lead's QK reads a stale stage;
-            // those scores are never used)
-            const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
-            if (lead) {
-                // V rows of tile jt+3 between the MFMAs of the P.V
-                const bool spread = load3 && R::whole(j3, kv_len, wl);
-                if (load3 && !spread)
-                    ld.issue_half(true, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
-                                  p.bs_log2, tok_stride, head_off, wl, page);
-                typename R::Src sr{p.k_cache, p.v_cache};
-                if (spread)
-                    sr = R::src(p.k_cache, p.v_cache, page, j3, wl, p.bs_log2, tok_stride, head_off);
-                constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
-                static_assert(kPvSteps % R::IPW == 0, "loads spread evenly over the MFMAs");
-                step_mfma<D, BN, BF16, true, true>(
-                    st, q, st_cur + R::TILE, st_next,
-                    DmaHalfHook<R, kPvSteps / R::IPW>{ld, sr, st3, wl, true, spread});
-            } else {
-                // K rows of tile jt+3 into the stage of tile jt-1 (its last
-                // reader, this group's P.V(jt-1), ran in phase 1), then the softmax
-                if (load3)
-                    ld.issue_half(false, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
-                                  p.bs_log2, tok_stride, head_off, wl, page);
-                phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
-                                                p.cap_in2, p.cap_out);
-            }
-            block_barrier();
-        }
-        if (!lead && n > 0) {
-            step_mfma<D, BN, BF16, true, false>(st, q, ring + ((n - 1) % kStages) * R::STAGE + R::TILE,
-                                                ring);
-#pragma unroll
-            for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-        block_barrier();   // the next chunk's window and ring refill start after all reads
-    }
+            if (lead) step_mfma<D, BN, BF16, false, true>(st, q, ring, ring);
 
-    const float l = pair_sum(st.lpart);
-    // With no key tile the output slices below could overlap another wave's
-    // Q slice still being read: wait for every wave first.
-    if (kv_begin >= kv_end) block_barrier();
-    // O goes out through this wave's slice of the ring: every wave has passed
-    // the last chunk's closing barrier (nothing reads the ring any more), and
-    // the slices lie below the last stage's V half, which was zeroed before
-    // the key loop without a barrier after it.
-    static_assert(NW * kStoreSliceBytes<D> <= (kStages - 1) * R::STAGE + R::TILE,
-                  "output slices clear of the zeroed V half");
-    store_rows_lds<D, BF16>(st.o, l, ring + w * kStoreSliceBytes<D>, [&](int rr) -> uint16_t* {
-        const int rw = w * 32 + rr;
-        const int tk = tok0 + (rw >> p.pack_log2);
-        const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
-        return tk < q_len ? p.out + ((int64_t)(q_start + tk) * p.num_heads + hd) * D : nullptr;
-    });
-    if (valid && p.lse != nullptr && g == 0) {
-        const int64_t rowi = (int64_t)(q_start + tok) * p.num_heads + head;
-        p.lse[rowi] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
+            for (int jt = 0; jt < n; ++jt) {
+                const int j0 = tile_key(jt);
+                bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
+                int lo_t = lo, hi_t = hi;   // this tile's visible interval per row
+                if constexpr (BSP) {
+                    const int v = __builtin_amdgcn_readfirstlane(
+                        bstate8[lq_w * p.bm_n_kb + (j0 >> p.bm_kvbs_log2)]);
+                    const int stt = v >= 2 ? 2 : v;
+                    if (stt == 2) {          // full block: every existing key
+                        lo_t = 0;
+                        hi_t = valid ? kv_len : 0;
+                        partial = j0 + BN > kv_len;
+                    } else if (stt == 0) {   // not listed for this wave's rows
+                        lo_t = hi_t = 0;
+                        partial = true;
+                    }
+                }
+                const uint8_t* st_cur = ring + (jt % kStages) * R::STAGE;
+                const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
+                const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
+                // phase 1
+                if (lead)
+                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
+                                                    p.cap_in2, p.cap_out);
+                else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
+                const int j3 = tile_key(jt + kStages - 1);
+                const bool load3 = jt + kStages - 1 < n;
+                int page = 0;
+                if (load3) page = win[R::slot(j3, first, p.bs_log2, wl)];
+                // tile jt+1 must have landed; tile jt+2, issued after it, may stay in
+                // flight
+                if (jt + 1 < n) {
+                    if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
+                    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                }
+                block_barrier();
+                // phase 2 (after the last tile the lead's QK reads a stale stage;
+                // those scores are never used)
+                const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
+                if (lead) {
+                    // V rows of tile jt+3 between the MFMAs of the P.V
+                    const bool spread = load3 && R::whole(j3, kv_len, wl);
+                    if (load3 && !spread)
+                        ld.issue_half(true, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
+                                      p.bs_log2, tok_stride, head_off, wl, page);
+                    typename R::Src sr{p.k_cache, p.v_cache};
+                    if (spread)
+                        sr = R::src(p.k_cache, p.v_cache, page, j3, wl, p.bs_log2, tok_stride, head_off);
+                    constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
+                    static_assert(kPvSteps % R::IPW == 0, "loads spread evenly over the MFMAs");
+                    step_mfma<D, BN, BF16, true, true>(
+                        st, q, st_cur + R::TILE, st_next,
+                        DmaHalfHook<R, kPvSteps / R::IPW>{ld, sr, st3, wl, true, spread});
+                } else {
+                    // K rows of tile jt+3 into the stage of tile jt-1 (its last
+                    // reader, this group's P.V(jt-1), ran in phase 1), then the softmax
+                    if (load3)
+                        ld.issue_half(false, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
+                                      p.bs_log2, tok_stride, head_off, wl, page);
+                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
+                                                    p.cap_in2, p.cap_out);
+                }
+                block_barrier();
+            }
+            if (!lead && n > 0) {
+                step_mfma<D, BN, BF16, true, false>(st, q, ring + ((n - 1) % kStages) * R::STAGE + R::TILE,
+                                                    ring);
+#pragma unroll
+                for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+            block_barrier();   // the next chunk's window and ring refill start after all reads
+        }
+
+        const float l = pair_sum(st.lpart);
+        // With no key tile the output slices below could overlap another wave's
+        // Q slice still being read: wait for every wave first.
+        if (kv_begin >= kv_end) block_barrier();
+        // O goes out through this wave's slice of the ring: every wave has passed
+        // the last chunk's closing barrier (nothing reads the ring any more), and
+        // the slices lie below the last stage's V half, which was zeroed before
+        // the key loop without a barrier after it.
+        static_assert(NW * kStoreSliceBytes<D> <= (kStages - 1) * R::STAGE + R::TILE,
+                      "output slices clear of the zeroed V half");
+        store_rows_lds<D, BF16>(st.o, l, ring + w * kStoreSliceBytes<D>, [&](int rr) -> uint16_t* {
+            const int rw = w * 32 + rr;
+            const int tk = tok0 + (rw >> p.pack_log2);
+            const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+            return tk < q_len ? p.out + ((int64_t)(q_start + tk) * p.num_heads + hd) * D : nullptr;
+        });
+        if (valid && p.lse != nullptr && g == 0) {
+            const int64_t rowi = (int64_t)(q_start + tok) * p.num_heads + head;
+            p.lse[rowi] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
+        }
+        // the next item's loads overwrite LDS this item's waves may still read
+        if constexpr (PERSIST) __syncthreads();
     }
 }
 
 namespace {
+
+// Compute units per XCD of the current device (looked up once per device).
+hipError_t cus_per_xcd(int* out) {
+    static std::atomic<int> known[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int v = known[dev].load(std::memory_order_acquire);
+        if (v > 0) {
+            *out = v;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    n = std::max(1, n / 8);
+    if (dev >= 0 && dev < 64) known[dev].store(n, std::memory_order_release);
+    *out = n;
+    return hipSuccess;
+}
 
 template <int D, int BN, int QB, int NW, bool BF16, bool CAP, bool BSP>
 hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) {
@@ -500,12 +542,29 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
     PrefillParams p = p0;
     const int tokens_per_tile = BM >> p.pack_log2;
     p.n_qtiles = (max_seqlen_q + tokens_per_tile - 1) / tokens_per_tile;
-    const int64_t grid = 8 * tiles_per_xcd(p.batch, p.n_head_groups, p.total_q, max_seqlen_q,
-                                           tokens_per_tile);
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP, BSP>), dim3((unsigned)grid),
-                       dim3(NW * 64), 0, s, p);
+    const int64_t per_xcd = tiles_per_xcd(p.batch, p.n_head_groups, p.total_q, max_seqlen_q,
+                                          tokens_per_tile);
+    if (per_xcd <= 0) return hipSuccess;
+    if (8 * per_xcd > 0x7fffffff) return hipErrorInvalidConfiguration;
+    // Equal-length sequences (every query tile of a unit count is known, the
+    // tiles' key ranges vary only along each unit): one workgroup per CU runs
+    // a fixed snake of the XCD's items, with no dispatch between items.
+    // Ragged batches keep one workgroup per item (the dispatcher balances
+    // their unequal lengths).
+    const bool uniform = (int64_t)p.total_q == (int64_t)p.batch * max_seqlen_q;
+    if constexpr (D == 64) {
+        if (uniform) {
+            int cu = 0;
+            hipError_t e = cus_per_xcd(&cu);
+            if (e != hipSuccess) return e;
+            p.wg_per_xcd = (int)std::min<int64_t>(per_xcd, cu);
+            hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP, BSP, true>),
+                               dim3((unsigned)(8 * p.wg_per_xcd)), dim3(NW * 64), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP, BSP, false>),
+                       dim3((unsigned)(8 * per_xcd)), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
 

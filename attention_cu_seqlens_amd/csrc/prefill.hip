@@ -341,15 +341,16 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         // Per tile j each wave runs QK(j) -> softmax(j) -> PV(j).  The two waves
         // of a SIMD are offset by half a tile, so that one issues MFMAs (and their
         // LDS operand reads) while the other runs the softmax on the VALU:
-        //   phase 1 of tile j: lead softmax(j)               trail PV(j-1), QK(j)
-        //   phase 2 of tile j: lead PV(j), QK(j+1), V loads  trail K loads, softmax(j)
-        // Tile j+3 goes into the stage of tile j-1 (free once phase 1 of tile j is
-        // over) in phase 2: the lead waves issue its V rows between the MFMAs of
-        // their P.V, the trailing waves its K rows at the start of their softmax.
-        // Per-phase timing: issued from the lead's MFMA phase alone, the loads
-        // lengthened it by about 565 cycles per tile (that wave is bound by its
-        // LDS operand reads, and the loads write LDS too); from the trailing
-        // softmax alone by about 325; half in each balances phase 2.
+        //   lead:  softmax(j), then P.V(j) and QK(j+1)
+        //   trail: P.V(j-1) and QK(j), then the ring loads, then softmax(j)
+        // with one workgroup barrier per tile.  A tile then takes the longer of
+        // the two waves' totals rather than the sum of the longer side of each
+        // half (two barriers per tile measured 4% slower on the varlen workload,
+        // 8% on byte->patch cross attention).  The trailing waves alone load the
+        // ring, V rows of tile j+2 and K rows of tile j+3: the lead waves' MFMA
+        // stream is bound by its LDS operand reads, and loads issued from it
+        // (which write LDS too) cost it about 70 cycles each, against about 40
+        // from the trailing side.
         // The trailing waves' first P.V of a chunk multiplies P = 0 (pb zeroed
         // here and after each chunk) by the V tile of the last stage: zeroed here
         // (uninitialised LDS could hold NaN codes), later a finite cache tile.
@@ -393,23 +394,36 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 if constexpr (BSP) return cs + (int)tlist[max(0, min(k, n - 1))] * BN;
                 else return cs + k * BN;
             };
+            // Tile jt, between barriers:
+            //   lead:  softmax(jt); P.V(jt), QK(jt+1)
+            //   trail: P.V(jt-1), QK(jt); V rows of tile jt+2, K rows of tile
+            //          jt+3; softmax(jt)
+            // V(jt+2) goes into the stage of tile jt-2, whose V was last read by
+            // P.V(jt-2) in tile jt-1; K(jt+3) into the stage of tile jt-1, whose K
+            // was last read by QK(jt-1) in tile jt-1.  Before the barrier the
+            // trailing waves wait for V(jt+1) and K(jt+2), which the next tile
+            // reads (softmax read-ahead and P.V; the lead's QK(jt+2)).
             {
-                // the lead waves load the V rows of each tile, the trailing waves
-                // the K rows
+                // trailing waves: K(0), V(0), K(1), V(1), K(2); then K(0), V(0),
+                // K(1) must have landed (the lead's QK(0), softmax(0), QK(1))
+                if (!lead) {
 #pragma unroll
-                for (int k = 0; k < kStages - 1; ++k)
-                    if (k < n) {
-                        const int jk = tile_key(k);
-                        ld.issue_half(lead, ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win, first,
-                                      jk, kv_len, p.bs_log2, tok_stride, head_off, wl,
-                                      win[R::slot(jk, first, p.bs_log2, wl)]);
-                    }
-                // this wave's half of tile 0 must have landed; tiles 1 and 2 may
-                // stay in flight
-                static_assert(kStages == 4, "wait counts below");
-                if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
-                else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
-                else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    for (int k = 0; k < kStages - 1; ++k)
+                        if (k < n) {
+                            const int jk = tile_key(k);
+                            const int pg = win[R::slot(jk, first, p.bs_log2, wl)];
+                            ld.issue_half(false, ring_lds + k * R::STAGE, p.k_cache, p.v_cache, win,
+                                          first, jk, kv_len, p.bs_log2, tok_stride, head_off, wl, pg);
+                            if (k < kStages - 2)
+                                ld.issue_half(true, ring_lds + k * R::STAGE, p.k_cache, p.v_cache,
+                                              win, first, jk, kv_len, p.bs_log2, tok_stride,
+                                              head_off, wl, pg);
+                        }
+                    static_assert(kStages == 4, "wait counts below");
+                    if (n > 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
+                    else if (n > 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
+                    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                }
             }
             block_barrier();
             if (lead) step_mfma<D, BN, BF16, false, true>(st, q, ring, ring);
@@ -434,47 +448,35 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 const uint8_t* st_cur = ring + (jt % kStages) * R::STAGE;
                 const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
                 const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
-                // phase 1
-                if (lead)
-                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
-                                                    p.cap_in2, p.cap_out);
-                else step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
-                const int j3 = tile_key(jt + kStages - 1);
-                const bool load3 = jt + kStages - 1 < n;
-                int page = 0;
-                if (load3) page = win[R::slot(j3, first, p.bs_log2, wl)];
-                // tile jt+1 must have landed; tile jt+2, issued after it, may stay in
-                // flight
-                if (jt + 1 < n) {
-                    if (jt + 2 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
-                    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-                }
-                block_barrier();
-                // phase 2 (after the last tile the lead's QK reads a stale stage;
-                // those scores are never used)
-                const uint32_t st3 = ring_lds + ((jt + kStages - 1) % kStages) * R::STAGE;
                 if (lead) {
-                    // V rows of tile jt+3 between the MFMAs of the P.V
-                    const bool spread = load3 && R::whole(j3, kv_len, wl);
-                    if (load3 && !spread)
-                        ld.issue_half(true, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
-                                      p.bs_log2, tok_stride, head_off, wl, page);
-                    typename R::Src sr{p.k_cache, p.v_cache};
-                    if (spread)
-                        sr = R::src(p.k_cache, p.v_cache, page, j3, wl, p.bs_log2, tok_stride, head_off);
-                    constexpr int kPvSteps = (D / 32) * (BN / 32) * 2;
-                    static_assert(kPvSteps % R::IPW == 0, "loads spread evenly over the MFMAs");
-                    step_mfma<D, BN, BF16, true, true>(
-                        st, q, st_cur + R::TILE, st_next,
-                        DmaHalfHook<R, kPvSteps / R::IPW>{ld, sr, st3, wl, true, spread});
-                } else {
-                    // K rows of tile jt+3 into the stage of tile jt-1 (its last
-                    // reader, this group's P.V(jt-1), ran in phase 1), then the softmax
-                    if (load3)
-                        ld.issue_half(false, st3, p.k_cache, p.v_cache, win, first, j3, kv_len,
-                                      p.bs_log2, tok_stride, head_off, wl, page);
                     phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
                                                     p.cap_in2, p.cap_out);
+                    step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next);
+                } else {
+                    step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
+                    // issue order V(jt+2), K(jt+3): waiting for V(jt+1) and K(jt+2)
+                    // leaves only the loads of this tile in flight
+                    if (jt + 2 < n) {
+                        const int j2 = tile_key(jt + 2);
+                        ld.issue_half(true, ring_lds + ((jt + 2) % kStages) * R::STAGE, p.k_cache,
+                                      p.v_cache, win, first, j2, kv_len, p.bs_log2, tok_stride,
+                                      head_off, wl, win[R::slot(j2, first, p.bs_log2, wl)]);
+                    }
+                    if (jt + 3 < n) {
+                        const int j3 = tile_key(jt + 3);
+                        ld.issue_half(false, ring_lds + ((jt + 3) % kStages) * R::STAGE, p.k_cache,
+                                      p.v_cache, win, first, j3, kv_len, p.bs_log2, tok_stride,
+                                      head_off, wl, win[R::slot(j3, first, p.bs_log2, wl)]);
+                    }
+                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
+                                                    p.cap_in2, p.cap_out);
+                    // this wave's V(jt+1) and K(jt+2) landed: only V(jt+2), K(jt+3) may stay
+                    {
+                        const int inflight = (jt + 2 < n ? R::IPW : 0) + (jt + 3 < n ? R::IPW : 0);
+                        if (inflight == 2 * R::IPW) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
+                        else if (inflight == R::IPW) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
+                        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    }
                 }
                 block_barrier();
             }

@@ -121,7 +121,6 @@ struct Ring16 {
     static constexpr int RPI = 64 / CPR;        // rows per 1 KB load instruction
     static constexpr int IPW = TILE / 1024 / NL;  // load instructions per wave per tensor
     static_assert(TILE % (1024 * NL) == 0, "tile does not divide over the waves");
-    static constexpr int LOADS_PER_TILE = 2 * IPW;  // per loading wave: K and V
     static constexpr int RW = IPW * RPI;
     static_assert(RW == 16, "a loading wave's rows must be one aligned 16-key group");
 
@@ -171,14 +170,6 @@ struct Ring16 {
         return Src{cache_k + off, cache_v + off};
     }
 
-    // Load number k (< LOADS_PER_TILE: K rows first, then V) of a whole() tile.
-    // stage: LDS byte address of the ring stage.
-    __device__ __forceinline__ void dma(int k, const Src& sr, uint32_t stage, int wl) const {
-        const int i = k % IPW;
-        const bool isv = k >= IPW;
-        dma16_s(isv ? sr.v : sr.k, voff[i], stage + (isv ? TILE : 0) + (wl * IPW + i) * 1024);
-    }
-
     // Load i (< IPW) of this wave's K rows (v false) or V rows (v true) of a
     // whole() tile.
     __device__ __forceinline__ void dma_half(int i, bool v, const Src& sr, uint32_t stage,
@@ -187,7 +178,10 @@ struct Ring16 {
     }
 
     // This wave's K rows (v false) or V rows (v true) of the tile at j0 at
-    // once (kv_len >= 1); rows past kv_len read row kv_len - 1, as in issue().
+    // once (kv_len >= 1).  Rows past kv_len read row kv_len - 1: they hold
+    // finite values and every key past kv_len is masked to probability 0 by
+    // the caller.  `page` is win[slot()], read by the caller ahead of time
+    // (any value when the tile is not whole()).
     __device__ __forceinline__ void issue_half(bool v, uint32_t stage, const uint16_t* cache_k,
                                                const uint16_t* cache_v, const int* win, int first,
                                                int j0, int kv_len, int bs_log2, int tok_stride,
@@ -211,59 +205,12 @@ struct Ring16 {
             dma16(base + off, stage + (v ? TILE : 0) + (wl * IPW + i) * 1024);
         }
     }
-
-    // All of this wave's loads of the tile at j0 at once (kv_len >= 1).  Rows
-    // past kv_len read row kv_len - 1: they hold finite values and every key
-    // past kv_len is masked to probability 0 by the caller.  `page` is
-    // win[slot()], read by the caller ahead of time (any value when the tile
-    // is not whole()).
-    __device__ __forceinline__ void issue(uint32_t stage, const uint16_t* cache_k,
-                                          const uint16_t* cache_v, const int* win, int first,
-                                          int j0, int kv_len, int bs_log2, int tok_stride,
-                                          int head_off, int wl, int page) const {
-        if (whole(j0, kv_len, wl)) {
-            const Src sr = src(cache_k, cache_v, page, j0, wl, bs_log2, tok_stride, head_off);
-#pragma unroll
-            for (int k = 0; k < LOADS_PER_TILE; ++k) dma(k, sr, stage, wl);
-            return;
-        }
-        const int bs_mask = (1 << bs_log2) - 1;
-        const int64_t page_stride = (int64_t)tok_stride << bs_log2;
-        const int lane = lane_id();
-#pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int tok = min(j0 + row(lane, wl, i), kv_len - 1);
-            const int pg = win[(tok >> bs_log2) - first];
-            const int64_t off = pg * page_stride +
-                                ((tok & bs_mask) * tok_stride + head_off + chunk(lane, wl, i) * 8);
-            const uint32_t dst = stage + (wl * IPW + i) * 1024;
-            dma16(cache_k + off, dst);
-            dma16(cache_v + off, dst + TILE);
-        }
-    }
 };
 
 // Callback run after each MFMA of a tile product (step = MFMA index within
 // the product) when the caller has nothing to interleave.
 struct NoHook {
     __device__ __forceinline__ void operator()(int) const {}
-};
-
-// The IPW loads of one half (K rows or V rows) of a whole() ring tile, one
-// after every EVERY-th MFMA of a P.V.
-template <class R, int EVERY>
-struct DmaHalfHook {
-    const R& ld;
-    typename R::Src sr;
-    uint32_t stage;
-    int wl;
-    bool v;
-    bool on;
-    __device__ __forceinline__ void operator()(int step) const {
-        if (step % EVERY == EVERY - 1 && step / EVERY < R::IPW) {
-            if (on) ld.dma_half(step / EVERY, v, sr, stage, wl);
-        }
-    }
 };
 
 // Operand prefetch depth of the MFMA stream, in MFMA steps: the LDS reads of

@@ -62,6 +62,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # sum (4): 20 cycles, or 16 where the row sum runs on the MFMA (fp8).
 # Launches of the prefill alone behind the kernel's roofline figure (median).
 KERNEL_LAUNCHES = 50
+# Wall time each extra line runs its kernel before it is timed.
+WARM_MS = 100.0
 SIMDS = 256 * 4
 CLOCK_HZ = 2.4e9
 EXP_PER_S = 64 / 8 * SIMDS * CLOCK_HZ                    # 19.7 T exp/s
@@ -121,6 +123,23 @@ def two_bounds(flops, scores, kind, ms, mfma_peak_tflops):
     return {"bound": bound, "achieved": top["achieved"], "peak": top["peak"],
             "unit": top["unit"], "frac": top["frac"], "kernel_us": round(us, 2),
             "mfma": mfma, "valu": valu}
+
+
+def warm_up(fn, torch, ms=WARM_MS, max_calls=5000):
+    """Runs fn back to back for at least `ms` of wall time before a line is
+    timed, so the clocks settle at this kernel's own load: each line follows
+    kernels of another kind (an HBM-bound decode before the compute-bound cross
+    attention), and a few launches are over before the clocks have moved."""
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in range(1, max_calls + 1):
+        fn()
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms:
+                break
+    torch.cuda.synchronize()
 
 
 def timed(fn, iters, torch):
@@ -295,8 +314,7 @@ def bench_copy(torch, dev, nbytes=2 << 30, iters=20):
     """Device-to-device copy: the practical HBM ceiling (read + write bytes)."""
     x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
-    for _ in range(2):
-        y.copy_(x)
+    warm_up(lambda: y.copy_(x), torch)
     ms = timed(lambda: y.copy_(x), iters, torch)
     del x, y
     torch.cuda.empty_cache()
@@ -330,8 +348,7 @@ def bench_decode(A, W, torch, dev, iters=50, fp8kv=False):
             A.attn_paged_decode_fwd(w.q, kc, vc, bt, cu_kv, maxkv, scale=w.scale, out=out,
                                     workspace=ws)
 
-    for _ in range(3):
-        run()
+    warm_up(run, torch)
     ms = timed(run, iters, torch)
     tokens = int(w.kv_lens.sum())
     used_blocks = int(sum(math.ceil(int(n) / w.block_size) for n in w.kv_lens))
@@ -368,8 +385,7 @@ def bench_rotary_cache(A, W, torch, dev, iters=50):
         A.attn_rotary_reshape_and_cache(kc, vc, bt, cu, cu, maxkv, qkv=qkv, num_heads=hq,
                                         cos_table=cos, sin_table=sin, q_out=q_out)
 
-    for _ in range(3):
-        run()
+    warm_up(run, torch)
     ms = timed(run, iters, torch)
     nbytes = 2 * qkv.numel() * 2 + total * d * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
@@ -403,8 +419,7 @@ def bench_prefill_generic(A, W, torch, dev, w, flops, iters=50, block_mask=None)
                                      int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags,
                                      q_ids=q_ids, out=out)
 
-    for _ in range(3):
-        run()
+    warm_up(run, torch)
     ms = timed(run, iters, torch)
     tf = flops / (ms * 1e-3) / 1e12
     return {"workload": w.name, "ms": round(ms, 4), "TFLOP/s": round(tf, 2),
@@ -436,8 +451,7 @@ def bench_backward(A, W, torch, dev, iters=20):
                           scale=w.scale, mask_flags=w.mask_flags, dq=dq, dk=dk, dv=dv,
                           workspace=ws)
 
-    for _ in range(2):
-        run()
+    warm_up(run, torch)
     ms = timed(run, iters, torch)
     flops = 2.5 * 4.0 * w.head_size * w.num_heads * causal_pairs(w.q_lens, w.kv_lens)
     tf = flops / (ms * 1e-3) / 1e12
@@ -460,8 +474,7 @@ def bench_fp8(A, W, torch, dev, iters=50):
         A.attn_fp8_fwd(w.q, w.k_new, w.v8_colmajor, ds, cu_q, cu_q, int(w.q_lens.max()),
                        int(w.kv_lens.max()), scale=w.scale, mask_flags=w.mask_flags, out=out)
 
-    for _ in range(3):
-        run()
+    warm_up(run, torch)
     ms = timed(run, iters, torch)
     tf = flops / (ms * 1e-3) / 1e12
     scores = causal_pairs(w.q_lens, w.kv_lens) * w.num_heads

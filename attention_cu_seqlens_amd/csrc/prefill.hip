@@ -40,22 +40,18 @@ constexpr int kStages = 4;
 // Per-wave pipeline state of one 32-row block.
 template <int D, int BN>
 struct PrefillWave {
-    static constexpr int NPRE = pv_preload<D, BN>();
     f32x16_t s[BN / 32];      // scores of the tile waiting for its softmax
     u32x4_t pb[BN / 32][2];   // probabilities of the tile waiting for its P.V
-    u32x4_t pre[NPRE > 0 ? NPRE : 1];   // first V^T operands of that P.V, read ahead
     f32x16_t o[D / 32];
     float m, lpart, alpha;
     bool need;
 };
 
 // Softmax phase (VALU): mask the scores of the tile at key j0 when partial,
-// then probabilities into pb (scores capped first with CAP); finally read
-// the first operands of the tile's P.V from its V tile v_tile.
+// then probabilities into pb (scores capped first with CAP).
 template <int D, int BN, bool BF16, bool CAP>
 __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool partial, int j0, int lo,
-                                              int hi, float c, const uint8_t* v_tile,
-                                              float cap_in2, float cap_out) {
+                                              int hi, float c, float cap_in2, float cap_out) {
     if (partial) {
         // key k of register r is visible iff lo <= k < hi, i.e. the unsigned
         // k - lo is below hi - lo (hi >= lo): one add, one compare and one
@@ -72,7 +68,6 @@ __device__ __forceinline__ void phase_softmax(PrefillWave<D, BN>& st, bool parti
     }
     softmax_tile<BN, BF16, CAP>(st.s, c, st.m, st.lpart, st.pb, st.alpha, st.need, cap_in2,
                                 cap_out);
-    preload_pv<D, BN, PrefillWave<D, BN>::NPRE>(st.pre, v_tile);
 }
 
 // The MFMA work of a phase: P.V of the softmaxed tile (after the rare
@@ -91,8 +86,7 @@ __device__ __forceinline__ void step_mfma(PrefillWave<D, BN>& st, const u32x4_t 
     // are ready, its LDS reads and MFMAs issue ahead of the other wave's
     // softmax VALU work (+1.7% on the varlen workload, output unchanged).
     __builtin_amdgcn_s_setprio(1);
-    mfma_stream16<D, BN, BF16, PV, QK, PrefillWave<D, BN>::NPRE>(st.o, st.s, st.pb, q, st.pre,
-                                                                v_tile, k_tile, hook);
+    mfma_stream16<D, BN, BF16, PV, QK>(st.o, st.s, st.pb, q, v_tile, k_tile, hook);
     __builtin_amdgcn_s_setprio(0);
 }
 
@@ -356,9 +350,6 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
         // (uninitialised LDS could hold NaN codes), later a finite cache tile.
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) st.pb[kb][0] = st.pb[kb][1] = u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < (PrefillWave<D, BN>::NPRE > 0 ? PrefillWave<D, BN>::NPRE : 1); ++i)
-            st.pre[i] = u32x4_t{0u, 0u, 0u, 0u};
         for (int i = tid; i < R::TILE / 16; i += NW * 64)
             *reinterpret_cast<u32x4_t*>(ring + (kStages - 1) * R::STAGE + R::TILE + 16 * i) =
                 u32x4_t{0u, 0u, 0u, 0u};
@@ -449,8 +440,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 const uint8_t* st_prev = ring + ((jt + kStages - 1) % kStages) * R::STAGE;
                 const uint8_t* st_next = ring + ((jt + 1) % kStages) * R::STAGE;
                 if (lead) {
-                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
-                                                    p.cap_in2, p.cap_out);
+                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, p.cap_in2,
+                                                    p.cap_out);
                     step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next);
                 } else {
                     step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
@@ -468,8 +459,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                                       p.v_cache, win, first, j3, kv_len, p.bs_log2, tok_stride,
                                       head_off, wl, win[R::slot(j3, first, p.bs_log2, wl)]);
                     }
-                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, st_cur + R::TILE,
-                                                    p.cap_in2, p.cap_out);
+                    phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, p.cap_in2,
+                                                    p.cap_out);
                     // this wave's V(jt+1) and K(jt+2) landed: only V(jt+2), K(jt+3) may stay
                     {
                         const int inflight = (jt + 2 < n ? R::IPW : 0) + (jt + 3 < n ? R::IPW : 0);

@@ -251,53 +251,25 @@ __device__ __forceinline__ u32x4_t pv_frag(const uint8_t* vt, uint32_t lo0, uint
     return u32x4_t{l2.x, l2.y, h2.x, h2.y};
 }
 
-// Number of P.V operands a wave reads ahead, at the end of its softmax phase
-// (the LDS issue slots of that phase are otherwise idle and the tile's scores
-// are dead by then, so their registers hold the operands).  D = 128 only: at
-// D = 64 the softmax phase is the longer one and the extra reads slow it.
-template <int D, int BN>
-constexpr int pv_preload() {
-    constexpr int steps = (D / 32) * (BN / 32) * 2;
-    constexpr int by_regs = (BN / 32) * 16 / 4;   // the scores' registers, 4 per operand
-    return D < 128 ? 0 : steps < by_regs ? steps : by_regs;
-}
-
-// pre holds max(NPRE, 1) operands; nothing is read when NPRE == 0.
-template <int D, int BN, int NPRE, int N>
-__device__ __forceinline__ void preload_pv(u32x4_t (&pre)[N], const uint8_t* vt) {
-    static_assert(N == (NPRE > 0 ? NPRE : 1), "preload array size");
-    if constexpr (NPRE > 0) {
-        uint32_t lo0, hi0;
-        pv_offsets<D>(lo0, hi0);
-#pragma unroll
-        for (int i = 0; i < NPRE; ++i) pre[i] = pv_frag<D, BN>(vt, lo0, hi0, i);
-    }
-}
-
 // The MFMA work of one pipeline phase as a single stream, so the operand
 // prefetch runs on across the boundary between the two products instead of
 // refilling at the start of each:
 //   PV: O^T[db] += V_tile^T(db) . P^T, P^T packed per (key block, 16-key
 //       step): (D/32) * (BN/32) * 2 MFMAs (steps db, kb, tp; `hook` after
-//       each); the first NPRE operands (NPRE may be 0) come read already in
-//       `pre`, which holds max(NPRE, 1);
+//       each);
 //   QK: S^T[kb] = K_tile(kb) . Q^T for the BN/32 key blocks: (D/16) * (BN/32)
 //       MFMAs (steps t, kb).
-template <int D, int BN, bool BF16, bool PV, bool QK, int NPRE, int NP, class Hook>
+template <int D, int BN, bool BF16, bool PV, bool QK, class Hook>
 __device__ __forceinline__ void mfma_stream16(f32x16_t (&o)[D / 32], f32x16_t (&s)[BN / 32],
                                               const u32x4_t (&pb)[BN / 32][2],
-                                              const u32x4_t (&q)[D / 16],
-                                              const u32x4_t (&pre)[NP], const uint8_t* vt,
+                                              const u32x4_t (&q)[D / 16], const uint8_t* vt,
                                               const uint8_t* kt, const Hook& hook) {
     static_assert(PV || QK, "empty stream");
-    static_assert(NPRE >= 0 && NPRE <= (D / 32) * (BN / 32) * 2, "preload count");
-    static_assert(NP == (NPRE > 0 ? NPRE : 1), "preload array size");
     constexpr int ROWB = D * 2;
     constexpr int NKB = BN / 32;
     constexpr int NPV = PV ? (D / 32) * NKB * 2 : 0;
     constexpr int N = NPV + (QK ? (D / 16) * NKB : 0);
-    constexpr int P0 = PV ? NPRE : 0;             // steps whose operand is preloaded
-    constexpr int PD = kStreamPrefetch < N - P0 ? kStreamPrefetch : N - P0;
+    constexpr int PD = kStreamPrefetch < N ? kStreamPrefetch : N;
     uint32_t lo0, hi0;
     pv_offsets<D>(lo0, hi0);
     // K: lane offset of chunk g of row col (rows kb*32 + col share their low
@@ -316,13 +288,13 @@ __device__ __forceinline__ void mfma_stream16(f32x16_t (&o)[D / 32], f32x16_t (&
     };
     u32x4_t a[PD + 1];
 #pragma unroll
-    for (int i = 0; i < PD; ++i) a[i] = frag(P0 + i);
+    for (int i = 0; i < PD; ++i) a[i] = frag(i);
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-        // buffer slot of step k >= P0: (k - P0) % (PD + 1)
-        if (i >= P0 && i + PD < N) a[(i - P0 + PD) % (PD + 1)] = frag(i + PD);
+        // buffer slot of step k: k % (PD + 1)
+        if (i + PD < N) a[(i + PD) % (PD + 1)] = frag(i + PD);
         __builtin_amdgcn_sched_barrier(0);
-        const u32x4_t op = i < P0 ? pre[i < P0 ? i : 0] : a[(i - P0) % (PD + 1)];
+        const u32x4_t op = a[i % (PD + 1)];
         if (i < NPV) {
             const int db = i / (NKB * 2), kb = (i / 2) % NKB, tp = i % 2;
             o[db] = mfma32<BF16>(op, pb[kb][tp], o[db]);

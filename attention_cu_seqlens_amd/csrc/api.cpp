@@ -15,6 +15,9 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
+// Longest decode tile list accepted (keeps the split kernel's tile
+// positions, and a workgroup's share past them, within int).
+constexpr int64_t kDecodeMaxTiles = int64_t{1} << 30;
 std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
 
 attn_status check_device() {
@@ -418,9 +421,11 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
         return 0;
     if (split_tokens < 0 || split_tokens % 256 != 0 || split_tokens > 8192) return 0;
     if (window_left < 0) return 0;
-    const int span = attn::decode_span(max_seqlen_kv, window_left);
-    const int st = attn::decode_split_tokens(batch, num_kv_heads, span, split_tokens);
-    return attn::decode_workspace_bytes(batch, num_heads, head_size, span, st);
+    if (attn::decode_tile_bound(batch, num_kv_heads, max_seqlen_kv, window_left) > kDecodeMaxTiles)
+        return 0;
+    return attn::decode_workspace(batch, num_heads, num_kv_heads, head_size, max_seqlen_kv,
+                                  window_left, split_tokens)
+        .bytes;
 }
 
 }  // extern "C"
@@ -454,9 +459,11 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
         return ATTN_ERR_NULL_ARG;
     if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al16(out)) return ATTN_ERR_BAD_SHAPE;
     if (batch == 0) return ATTN_OK;
-    const int span = attn::decode_span(max_seqlen_kv, window_left);
-    const int st = attn::decode_split_tokens(batch, num_kv_heads, span, split_tokens);
-    const size_t need = attn::decode_workspace_bytes(batch, num_heads, head_size, span, st);
+    if (attn::decode_tile_bound(batch, num_kv_heads, max_seqlen_kv, window_left) > kDecodeMaxTiles)
+        return ATTN_ERR_BAD_SHAPE;
+    const attn::DecodeWorkspace lay = attn::decode_workspace(
+        batch, num_heads, num_kv_heads, head_size, max_seqlen_kv, window_left, split_tokens);
+    const size_t need = lay.bytes;
     if (use_scratch) {
         // the library's own scratch array (no allocation): size checked here,
         // on the host, before any HIP call
@@ -484,11 +491,14 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     }
     p.block_table = block_table;
     p.cu_kv = cu_seqlens_kv;
-    p.max_splits = span > 0 ? (span + st - 1) / st : 1;
-    const int64_t rows = (int64_t)batch * num_heads * p.max_splits;
-    const int64_t o_bytes = ((rows * head_size * 4 + 255) / 256) * 256;
+    int cus = 0;
+    if (attn::cu_count(&cus) != hipSuccess) return ATTN_ERR_DEVICE;
+    p.grid = attn::decode_grid(batch, num_kv_heads, max_seqlen_kv, window_left, split_tokens,
+                               2 * cus);
+    p.split_tiles = split_tokens / 32;
     p.part_o = static_cast<float*>(workspace);
-    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);
+    p.seg_meta = reinterpret_cast<int*>(static_cast<char*>(workspace) + lay.meta_off);
     p.out = static_cast<uint16_t*>(out);
     p.lse = lse;
     p.mbps = max_blocks_per_seq;
@@ -497,7 +507,6 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     p.num_kv_heads = num_kv_heads;
     p.group = num_heads / num_kv_heads;
     p.bs_log2 = ilog2(block_size);
-    p.split_tokens = st;
     p.c = scale * 1.4426950408889634f;
     p.window = window_left;
     set_cap(scale, softcap, p.cap_in2, p.cap_out);

@@ -1,19 +1,28 @@
 // Paged GQA decode (one query token per sequence) for 16-bit dtypes on gfx950.
 //
-// Split-KV: workgroup (sequence b, kv head hk, split s) streams keys
-// [s*split_tokens, (s+1)*split_tokens) of the paged cache.  Its NW waves take
-// interleaved 32-key blocks of each BN = 32*NW key tile, each with its own
-// online-softmax state for the G = Hq/Hkv query heads of the group (the 32
-// query columns of the MFMA, G of them live).  The waves merge in LDS at the
-// end and the workgroup writes one partial (unnormalised O, running max m,
-// sum l) per query head.  A second kernel merges the splits with the same
-// logsumexp rule; its LSE output is the "OUTPUT_LOGSUMEXP" quantity of the
-// FlexAttention kernel options shown in the blt issue "Cross Attention does
-// not work on CPU and older GPUs".
+// Split-KV with a balanced schedule: every (sequence b, kv head hk) unit's
+// visible keys form a run of 32-key tiles; the runs are laid end to end in
+// (b, hk) order and workgroup w takes tiles [w*C, (w+1)*C) of that list, so
+// every workgroup streams the same number of tiles (the last one fewer)
+// whatever the mix of lengths.  By default the grid is two workgroups per CU,
+// all resident at once: no tail of long splits running alone and no
+// workgroup turnover.  A workgroup's share is cut at unit boundaries into
+// segments; each segment's NW waves take interleaved 32-key tiles, each with
+// its own online-softmax state for the G = Hq/Hkv query heads of the group
+// (the 32 query columns of the MFMA, G of them live), merge in LDS and write
+// one partial (unnormalised O, running max m, sum l) per query head.  A
+// second kernel merges each unit's segments with the same logsumexp rule;
+// its LSE output is the "OUTPUT_LOGSUMEXP" quantity of the FlexAttention
+// kernel options shown in the blt issue "Cross Attention does not work on
+// CPU and older GPUs".
 //
-// The grid is sized from max_seqlen_kv on the host (no device->host sync);
-// splits past a sequence's end exit at once and the merge kernel derives
-// each sequence's split count from its own length.
+// Segment (unit u, workgroup w) writes partial slot u + w: along the list
+// either the unit or the workgroup index grows from one segment to the next,
+// so the slots are distinct, and a unit's segments hold consecutive slots.
+// The workgroup that runs a unit's first tile records the unit's first slot
+// and segment count for the merge.  No device->host sync: the tile counts
+// come from cu_seqlens_kv on the device; the host sizes the grid and the
+// workspace from max_seqlen_kv.
 
 #include <algorithm>
 #include <atomic>
@@ -35,33 +44,67 @@ struct DecodeLayout {
     static constexpr int LDS_BYTES = TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES;
 };
 
+// First key of the tiles a sequence of kv_len keys runs: 0, or with a local
+// window of W keys the start of its last W keys rounded down to 32 (tiles
+// stay 32-key aligned; the keys before the window are masked).
+__device__ __forceinline__ int decode_klo(int kv_len, int window) {
+    return (window > 0 ? max(0, kv_len - window) : 0) & ~31;
+}
+__device__ __forceinline__ int decode_tiles(int kv_len, int window) {
+    return kv_len > 0 ? (kv_len - decode_klo(kv_len, window) + 31) >> 5 : 0;
+}
+
 template <int D, int NW, bool BF16, bool CAP, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_decode(DecodeParams p) {
     using L = DecodeLayout<D, NW, BF16, KV8>;
     using Tile = typename L::Tile;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int* win = reinterpret_cast<int*>(smem + L::WIN_OFF);
+    const int tid = threadIdx.x;
+    const int lane = lane_id(), w = wave_id();
+    const int Hkv = p.num_kv_heads;
+    const int wg = blockIdx.x;
 
-    // Split index outermost: workgroup i runs on XCD i % 8, so consecutive
-    // workgroups are different (sequence, kv head) units of the same split
-    // and every XCD gets an equal share of each split index.  (Split-fastest
-    // order piles the low split indices, which every sequence has, onto the
-    // XCDs they map to whenever the split count is a multiple of 8.)
-    const int units = p.batch * p.num_kv_heads;
-    const int s = blockIdx.x / units;
-    const int unit = blockIdx.x - s * units;
-    const int hk = unit % p.num_kv_heads;
-    const int b = unit / p.num_kv_heads;
-    const int kv_start = p.cu_kv[b];
-    const int kv_len = p.cu_kv[b + 1] - kv_start;
-    // The splits tile the keys from window_base (0 without a local window):
-    // a window keeps the sequence's last p.window keys, lo_w on; the grid
-    // starts at lo_w rounded down to 32 keys (tiles stay 32-key aligned) and
-    // the keys before lo_w are masked.
-    const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
-    const int k0 = (lo_w & ~31) + s * p.split_tokens;
-    if (k0 >= kv_len) return;
-    const int k1 = min(kv_len, k0 + p.split_tokens);
+    // The tile list: total length, this workgroup's share [start, end) and
+    // the unit holding its first tile.  Wave-uniform, computed by every wave.
+    int total = 0;
+    for (int base = 0; base < p.batch; base += 64) {
+        const int bb = base + lane;
+        const int t = bb < p.batch ? decode_tiles(p.cu_kv[bb + 1] - p.cu_kv[bb], p.window) : 0;
+        total += __builtin_amdgcn_readlane(wave_incl_scan(t), 63);
+    }
+    total *= Hkv;
+    const int C = p.split_tiles > 0
+                      ? p.split_tiles
+                      : max(kDecodeMinSegTiles, (total + (int)gridDim.x - 1) / (int)gridDim.x);
+    if ((int64_t)wg * C >= total) return;
+    const int start = wg * C;
+    const int end = min(total, start + C);
+    int b = 0, hk = 0, t0 = 0;
+    {
+        int acc = 0;   // tiles per kv head of the sequences before `base`
+        for (int base = 0; base < p.batch; base += 64) {
+            const int bb = base + lane;
+            const int t = bb < p.batch ? decode_tiles(p.cu_kv[bb + 1] - p.cu_kv[bb], p.window) : 0;
+            const int incl = wave_incl_scan(t);
+            const int tot = __builtin_amdgcn_readlane(incl, 63);
+            if (start < (acc + tot) * Hkv) {
+                const bool mine = t > 0 && start >= (acc + incl - t) * Hkv && start < (acc + incl) * Hkv;
+                const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(mine)));
+                b = base + src;
+                const int tb = __builtin_amdgcn_readlane(t, src);
+                const int off = start - (acc + __builtin_amdgcn_readlane(incl - t, src)) * Hkv;
+                hk = off / tb;
+                t0 = off - hk * tb;
+                break;
+            }
+            acc += tot;
+        }
+    }
+
+    const int G = p.group;
+    const int col = lane & 31, g = lane >> 5;
+    const bool valid = col < G;
     const bool neg = p.c < 0.f;
     // fp8 cache: the K descale joins the score scale (and the cap's input
     // factor), the V descale multiplies the partial O
@@ -69,100 +112,129 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const float dv = KV8 ? p.kv_descale[1] : 1.f;
     const float c = fabsf(p.c) * dk;
     const float cap_in2 = p.cap_in2 * dk;
-
-    const int tid = threadIdx.x;
-    const int lane = lane_id(), w = wave_id();
-    const int col = lane & 31, g = lane >> 5;
-    const int G = p.group;
-    const bool valid = col < G;
-    const int head = hk * G + col;
-
-    RowsState<D, 1> st;
-    st.init();
-    {
-        const uint16_t* qp = p.q + ((int64_t)b * p.num_heads + head) * D + 8 * g;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (valid) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
-            st.q[0][t] = neg ? neg16x8(v) : v;
-        }
-    }
-    st.lo[0] = lo_w;   // keys before the window are masked
-    st.hi[0] = k1;
-
-    const int32_t* table = p.block_table + (int64_t)b * p.mbps;
-    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
-    const int first = k0 >> p.bs_log2;
-    fill_page_window(win, table, first, n_blocks, tid, NW * 64);
-    __syncthreads();
-
-    // Each wave streams 32-key tiles w, w + NW, ... of the split through its
-    // own LDS slot, with its next tile's loads in flight while it computes.
-    const int tok_stride = p.num_kv_heads * D;
-    const int head_off = hk * D;
-    const int n_t = (k1 - k0 + 31) >> 5;
-    // tiles wholly below the window hold no visible key: start past them
-    const int t_first = lo_w > k0 ? (lo_w - k0) >> 5 : 0;
+    const int tok_stride = Hkv * D;
+    // keys per page window: a range this long starting anywhere fits one
+    const int chunk_keys = PAGE_WIN << p.bs_log2;
     uint8_t* mine = smem + w * Tile::BYTES;
-    Tile ld;
-    auto load = [&](int j) {
-        if constexpr (KV8)
-            ld.load(p.k8, p.v8, win, first, j, k1, p.bs_log2, tok_stride, head_off, lane);
-        else
-            ld.load(p.k_cache, p.v_cache, win, first, j, k1, p.bs_log2, tok_stride, head_off, lane);
-    };
-    if (t_first + w < n_t) load(k0 + 32 * (t_first + w));
-    for (int t = t_first + w; t < n_t; t += NW) {
-        const int j = k0 + 32 * t;
-        ld.store(mine, j, k1, lane);
-        __builtin_amdgcn_wave_barrier();
-        if (t + NW < n_t) load(j + 32 * NW);
-        if (j >= lo_w && j + 32 <= k1)
-            tile_step<D, 32, 1, 1, BF16, false, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
-        else
-            tile_step<D, 32, 1, 1, BF16, true, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
-        __builtin_amdgcn_wave_barrier();
-    }
-    __syncthreads();
 
-    // merge the NW wave states of this split
-    float* red_o = reinterpret_cast<float*>(smem);   // [NW][G][D]
-    float* red_m = red_o + NW * G * D;               // [NW][G]
-    float* red_l = red_m + NW * G;
-    if (valid) {
+    for (int pos = start;;) {
+        const int kv_start = p.cu_kv[b];
+        const int kv_len = p.cu_kv[b + 1] - kv_start;
+        const int klo = decode_klo(kv_len, p.window);
+        const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
+        const int nt = (kv_len - klo + 31) >> 5;
+        const int t1 = min(nt, t0 + (end - pos));
+        const int u = b * Hkv + hk;
+        const int seg = u + wg;
+        if (t0 == 0 && tid == 0) {
+            // the unit's last tile lies in workgroup (pos + nt - 1) / C
+            p.seg_meta[2 * u] = seg;
+            p.seg_meta[2 * u + 1] = (pos + nt - 1) / C - wg + 1;
+        }
+        const int k0 = klo + 32 * t0;
+        const int k1 = min(kv_len, klo + 32 * t1);
+        const int head = hk * G + col;
+
+        RowsState<D, 1> st;
+        st.init();
+        {
+            const uint16_t* qp = p.q + ((int64_t)b * p.num_heads + head) * D + 8 * g;
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int d = db * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                red_o[(w * G + col) * D + d] = st.o[db][0][r];
+            for (int t = 0; t < D / 16; ++t) {
+                u32x4_t v = {0u, 0u, 0u, 0u};
+                if (valid) v = *reinterpret_cast<const u32x4_t*>(qp + 16 * t);
+                st.q[0][t] = neg ? neg16x8(v) : v;
             }
-        if (g == 0) {
-            red_m[w * G + col] = st.m[0];
-            red_l[w * G + col] = st.l[0];
         }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += NW * 64) {
-        const int cc = idx / D, d = idx % D;
-        float mstar = kNegInf;
+        st.lo[0] = lo_w;   // keys before the window are masked
+        st.hi[0] = k1;
+
+        const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+        const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
+        const int head_off = hk * D;
+        for (int cs = k0; cs < k1; cs += chunk_keys) {
+            const int ce = min(k1, cs + chunk_keys);
+            const int first = cs >> p.bs_log2;
+            fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+            __syncthreads();
+            // Each wave streams 32-key tiles w, w + NW, ... of the chunk through
+            // its own LDS slot, with its next tile's loads in flight while it
+            // computes.  Chunks are whole tiles except the segment's last, so
+            // k1 bounds every tile's rows.
+            const int n_t = (ce - cs + 31) >> 5;
+            Tile ld;
+            auto load = [&](int j) {
+                if constexpr (KV8)
+                    ld.load(p.k8, p.v8, win, first, j, k1, p.bs_log2, tok_stride, head_off, lane);
+                else
+                    ld.load(p.k_cache, p.v_cache, win, first, j, k1, p.bs_log2, tok_stride, head_off,
+                            lane);
+            };
+            if (w < n_t) load(cs + 32 * w);
+            for (int t = w; t < n_t; t += NW) {
+                const int j = cs + 32 * t;
+                ld.store(mine, j, k1, lane);
+                __builtin_amdgcn_wave_barrier();
+                if (t + NW < n_t) load(j + 32 * NW);
+                if (j >= lo_w && j + 32 <= k1)
+                    tile_step<D, 32, 1, 1, BF16, false, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
+                else
+                    tile_step<D, 32, 1, 1, BF16, true, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
+                __builtin_amdgcn_wave_barrier();
+            }
+            __syncthreads();   // the window and the tile slots are free again
+        }
+
+        // merge the NW wave states of this segment
+        float* red_o = reinterpret_cast<float*>(smem);   // [NW][G][D]
+        float* red_m = red_o + NW * G * D;               // [NW][G]
+        float* red_l = red_m + NW * G;
+        if (valid) {
 #pragma unroll
-        for (int i = 0; i < NW; ++i) mstar = fmaxf(mstar, red_m[i * G + cc]);
-        float lsum = 0.f, osum = 0.f;
+            for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const float mi = red_m[i * G + cc];
-            const float wgt = (mi == kNegInf) ? 0.f : fast_exp2(mi - mstar);
-            lsum += red_l[i * G + cc] * wgt;
-            osum += red_o[(i * G + cc) * D + d] * wgt;
+                for (int r = 0; r < 16; ++r) {
+                    const int d = db * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                    red_o[(w * G + col) * D + d] = st.o[db][0][r];
+                }
+            if (g == 0) {
+                red_m[w * G + col] = st.m[0];
+                red_l[w * G + col] = st.l[0];
+            }
         }
-        const int64_t slot = ((int64_t)b * p.num_heads + hk * G + cc) * p.max_splits + s;
-        p.part_o[slot * D + d] = osum * dv;
-        if (d == 0) {
-            p.part_ml[slot * 2 + 0] = mstar;
-            p.part_ml[slot * 2 + 1] = lsum;
+        __syncthreads();
+        for (int idx = tid; idx < G * D; idx += NW * 64) {
+            const int cc = idx / D, d = idx % D;
+            float mstar = kNegInf;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) mstar = fmaxf(mstar, red_m[i * G + cc]);
+            float lsum = 0.f, osum = 0.f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const float mi = red_m[i * G + cc];
+                const float wgt = (mi == kNegInf) ? 0.f : fast_exp2(mi - mstar);
+                lsum += red_l[i * G + cc] * wgt;
+                osum += red_o[(i * G + cc) * D + d] * wgt;
+            }
+            const int64_t slot = (int64_t)seg * G + cc;
+            p.part_o[slot * D + d] = osum * dv;
+            if (d == 0) {
+                p.part_ml[slot * 2 + 0] = mstar;
+                p.part_ml[slot * 2 + 1] = lsum;
+            }
         }
+
+        pos += t1 - t0;
+        if (pos >= end) break;
+        // next unit with tiles (one exists: pos < end <= total)
+        t0 = 0;
+        if (++hk == Hkv) {
+            hk = 0;
+            do {
+                ++b;
+            } while (decode_tiles(p.cu_kv[b + 1] - p.cu_kv[b], p.window) == 0);
+        }
+        __syncthreads();   // the merge's LDS reads precede the next window fill
     }
 }
 
@@ -170,19 +242,27 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.num_heads;
+    const int h = bh - b * p.num_heads;
+    const int hk = h / p.group;
+    const int cc = h - hk * p.group;
     const int kv_len = p.cu_kv[b + 1] - p.cu_kv[b];
-    const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
-    const int n_s = (kv_len - (lo_w & ~31) + p.split_tokens - 1) / p.split_tokens;
+    int first = 0, n_s = 0;
+    if (decode_tiles(kv_len, p.window) > 0) {
+        const int u = b * p.num_kv_heads + hk;
+        first = p.seg_meta[2 * u];
+        n_s = p.seg_meta[2 * u + 1];
+    }
     const int d = threadIdx.x;
-    const int64_t base = (int64_t)bh * p.max_splits;
     float mstar = kNegInf;
-    for (int s = 0; s < n_s; ++s) mstar = fmaxf(mstar, p.part_ml[(base + s) * 2]);
+    for (int s = 0; s < n_s; ++s)
+        mstar = fmaxf(mstar, p.part_ml[((int64_t)(first + s) * p.group + cc) * 2]);
     float lsum = 0.f, osum = 0.f;
     for (int s = 0; s < n_s; ++s) {
-        const float ms = p.part_ml[(base + s) * 2];
+        const int64_t slot = (int64_t)(first + s) * p.group + cc;
+        const float ms = p.part_ml[slot * 2];
         const float wgt = (ms == kNegInf) ? 0.f : fast_exp2(ms - mstar);
-        lsum += p.part_ml[(base + s) * 2 + 1] * wgt;
-        osum += p.part_o[(base + s) * D + d] * wgt;
+        lsum += p.part_ml[slot * 2 + 1] * wgt;
+        osum += p.part_o[slot * D + d] * wgt;
     }
     const float val = lsum > 0.f ? osum / lsum : 0.f;
     f32x2_t v2 = {val, 0.f};
@@ -194,33 +274,70 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
         p.lse[bh] = lsum > 0.f ? (mstar + __builtin_log2f(lsum)) * kLn2 : kNegInf;
 }
 
-// Automatic split size: the smallest power of two (>= 256 keys) that keeps the
-// grid at no more than 4096 workgroups, i.e. about 8 rounds of the two
-// resident workgroups per CU.  Fewer, longer workgroups pay the per-workgroup
-// start (block ids, first tile from HBM) less often; the paged GQA decode
-// workload (64 sequences, kv 1024-32768, 8 kv heads) measured 5.8-6.0 TB/s at
-// 4096 keys per split against 5.1 at 512 and 5.5 at 1024.
-// Keys a split grid must cover for kv lengths up to max_seqlen_kv: with a
-// local window W, at most W keys plus up to 31 before them (the grid starts
+// Keys a unit's tiles can span for kv lengths up to max_seqlen_kv: with a
+// local window W, at most W keys plus up to 31 before them (the tiles start
 // 32-key aligned).
 int decode_span(int max_seqlen_kv, int window) {
     return window > 0 ? (int)std::min<int64_t>(max_seqlen_kv, (int64_t)window + 31) : max_seqlen_kv;
 }
 
-int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested) {
-    if (requested > 0) return requested;
-    const int64_t units = (int64_t)batch * num_kv_heads;
-    int st = 256;
-    while (st < 8192 && units * ((max_seqlen_kv + st - 1) / st) > 4096) st *= 2;
-    return st;
+// Upper bound of the tile list's length (every sequence at max_seqlen_kv).
+int64_t decode_tile_bound(int batch, int num_kv_heads, int max_seqlen_kv, int window) {
+    const int64_t span = decode_span(max_seqlen_kv, window);
+    return (int64_t)batch * num_kv_heads * ((span + 31) / 32);
 }
 
-size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_seqlen_kv,
-                              int split_tokens) {
-    const int64_t splits = max_seqlen_kv > 0 ? (max_seqlen_kv + split_tokens - 1) / split_tokens : 1;
-    const int64_t rows = (int64_t)batch * num_heads * splits;
-    const int64_t o_bytes = ((rows * head_size * 4 + 255) / 256) * 256;
-    return (size_t)(o_bytes + rows * 2 * 4);
+// Workgroups of the split kernel: with split_tokens the list is cut every
+// split_tokens keys (enough workgroups for the longest possible list; the
+// ones past its end return at once); by default the grid is `resident`
+// workgroups (two per CU), fewer when segments of kDecodeMinSegTiles tiles
+// already cover the bound, and at most kDecodeMaxGrid.
+int decode_grid(int batch, int num_kv_heads, int max_seqlen_kv, int window, int split_tokens,
+                int resident) {
+    const int64_t bound = decode_tile_bound(batch, num_kv_heads, max_seqlen_kv, window);
+    if (bound <= 0) return 1;
+    if (split_tokens > 0) return (int)((bound + split_tokens / 32 - 1) / (split_tokens / 32));
+    const int64_t by_min = (bound + kDecodeMinSegTiles - 1) / kDecodeMinSegTiles;
+    return (int)std::max<int64_t>(1, std::min<int64_t>({by_min, (int64_t)resident,
+                                                         (int64_t)kDecodeMaxGrid}));
+}
+
+// Workspace layout: partial slots, one per (unit, workgroup) segment, at
+// most units + grid of them (part_o, then part_ml), then the per-unit
+// segment records.
+DecodeWorkspace decode_workspace(int batch, int num_heads, int num_kv_heads, int head_size,
+                                 int max_seqlen_kv, int window, int split_tokens) {
+    const int64_t units = (int64_t)batch * num_kv_heads;
+    const int64_t grid = decode_grid(batch, num_kv_heads, max_seqlen_kv, window, split_tokens,
+                                     kDecodeMaxGrid);
+    const int64_t rows = (units + grid) * (num_heads / num_kv_heads);
+    DecodeWorkspace ws;
+    ws.ml_off = (size_t)(((rows * head_size * 4 + 255) / 256) * 256);
+    ws.meta_off = ws.ml_off + (size_t)(((rows * 2 * 4 + 255) / 256) * 256);
+    ws.bytes = ws.meta_off + (size_t)(units * 2 * 4);
+    return ws;
+}
+
+// Compute units of the current device (looked up once per device).
+hipError_t cu_count(int* out) {
+    static std::atomic<int> known[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int v = known[dev].load(std::memory_order_acquire);
+        if (v > 0) {
+            *out = v;
+            return hipSuccess;
+        }
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    n = std::max(1, n);
+    if (dev >= 0 && dev < 64) known[dev].store(n, std::memory_order_release);
+    *out = n;
+    return hipSuccess;
 }
 
 // Split partials of the allocation-free decode entry point: one array per
@@ -271,9 +388,8 @@ hipError_t launch_decode_cfg(const DecodeParams& p, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_acq_rel);
     }
-    const int64_t grid = (int64_t)p.batch * p.num_kv_heads * p.max_splits;
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16, CAP, KV8>), dim3((unsigned)grid), dim3(NW * 64),
+    if (p.grid <= 0) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_paged_decode<D, NW, BF16, CAP, KV8>), dim3((unsigned)p.grid), dim3(NW * 64),
                        lds, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -113,8 +113,9 @@ struct DecodeParams {
     const float* kv_descale;    // [2] device (dk, dv) with k8
     const int32_t* block_table;
     const int32_t* cu_kv;
-    float* part_o;              // [batch*Hq, max_splits, D]
-    float* part_ml;             // [batch*Hq, max_splits, 2]
+    float* part_o;              // [slots, G, D] segment partials (slot = unit + workgroup)
+    float* part_ml;             // [slots, G, 2] their running max and sum
+    int* seg_meta;              // [batch*Hkv, 2] first slot and segment count per unit
     uint16_t* out;              // [batch, Hq, D]
     float* lse;                 // [batch, Hq] or null
     int mbps;
@@ -123,8 +124,8 @@ struct DecodeParams {
     int num_kv_heads;
     int group;
     int bs_log2;
-    int split_tokens;
-    int max_splits;
+    int split_tiles;            // tiles per workgroup, 0: balanced over the grid
+    int grid;                   // workgroups of the split kernel
     float c;
     int window;                 // local window (keys), 0 = none
     float cap_in2, cap_out;     // score cap constants (SoftCap), cap_out == 0: none
@@ -176,10 +177,22 @@ constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
 // once per device.
 hipError_t decode_scratch(void** ptr);
 
+// Compute units of the current device (looked up once per device).
+hipError_t cu_count(int* out);
+
 // Decode planning shared by the workspace query and the launch.
+// Shortest share of the tile list a workgroup takes by default (512 keys),
+// and the most workgroups the default grid uses (two per CU up to 512 CUs).
+constexpr int kDecodeMinSegTiles = 16;
+constexpr int kDecodeMaxGrid = 1024;
 int decode_span(int max_seqlen_kv, int window);
-int decode_split_tokens(int batch, int num_kv_heads, int max_seqlen_kv, int requested);
-size_t decode_workspace_bytes(int batch, int num_heads, int head_size, int max_seqlen_kv,
-                              int split_tokens);
+int64_t decode_tile_bound(int batch, int num_kv_heads, int max_seqlen_kv, int window);
+int decode_grid(int batch, int num_kv_heads, int max_seqlen_kv, int window, int split_tokens,
+                int resident);
+struct DecodeWorkspace {
+    size_t ml_off, meta_off, bytes;   // byte offsets of part_ml and seg_meta; total size
+};
+DecodeWorkspace decode_workspace(int batch, int num_heads, int num_kv_heads, int head_size,
+                                 int max_seqlen_kv, int window, int split_tokens);
 
 }  // namespace attn

@@ -507,25 +507,12 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 
 namespace {
 
-// Compute units per XCD of the current device (looked up once per device).
+// Compute units per XCD of the current device.
 hipError_t cus_per_xcd(int* out) {
-    static std::atomic<int> known[64];
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < 64) {
-        const int v = known[dev].load(std::memory_order_acquire);
-        if (v > 0) {
-            *out = v;
-            return hipSuccess;
-        }
-    }
     int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    const hipError_t e = cu_count(&n);
     if (e != hipSuccess) return e;
-    n = std::max(1, n / 8);
-    if (dev >= 0 && dev < 64) known[dev].store(n, std::memory_order_release);
-    *out = n;
+    *out = std::max(1, n / 8);
     return hipSuccess;
 }
 

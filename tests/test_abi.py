@@ -212,10 +212,23 @@ def test_decode_host_checks(lib):
     assert ws(64, 32, 8, 128, 32768, 0, 8448) == 0      # split above 8192
     assert ws(64, 32, 8, 128, 32768, -1, 0) == 0        # negative window
     assert ws(0, 32, 8, 128, 1, 0, 0) == 0
+    def layout(units, group, d, grid):
+        # partial slots (units + grid) x group: O rows, then (m, l), each
+        # rounded up to 256 bytes; then two ints per unit
+        rows = (units + grid) * group
+        up = lambda n: (n + 255) // 256 * 256
+        return up(rows * d * 4) + up(rows * 2 * 4) + units * 2 * 4
+
     need = ws(4, 8, 2, 128, 1000, 0, 256)
-    assert need == 4 * 8 * 4 * 128 * 4 + 4 * 8 * 4 * 2 * 4
-    # a window of 300 keys: the splits cover at most 300 + 31 keys -> 2 of 256
-    assert ws(4, 8, 2, 128, 1000, 300, 256) == 4 * 8 * 2 * 128 * 4 + 4 * 8 * 2 * 2 * 4
+    # 8 units of at most 32 tiles, 8 tiles (256 keys) per workgroup: 32 workgroups
+    assert need == layout(8, 4, 128, 32)
+    # a window of 300 keys: a unit spans at most 300 + 31 keys -> 11 tiles
+    assert ws(4, 8, 2, 128, 1000, 300, 256) == layout(8, 4, 128, 11)
+    # by default: segments of at least 16 tiles over at most 1024 workgroups
+    assert ws(4, 8, 2, 128, 1000, 0, 0) == layout(8, 4, 128, 16)
+    assert ws(64, 32, 8, 128, 32768, 0, 0) == layout(512, 4, 128, 1024)
+    # tile lists longer than 2^30 are refused
+    assert ws(1 << 14, 64, 64, 128, 1 << 20, 0, 0) == 0
 
     def call(**kw):
         a = dict(q=P, kc=P, vc=P, bt=P, mbps=64, cukv=P, batch=4, mskv=1000, hq=8, hkv=2, d=128,

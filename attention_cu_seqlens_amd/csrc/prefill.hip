@@ -97,6 +97,11 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     static_assert(BM == kPrefillRows, "rows per workgroup as the host assumes");
     static_assert(PAGE_WIN * 64 / BN <= NW * 64, "a chunk's tiles fit one per thread");
     using R = Ring16<D, BN, NW / 2>;
+    // Head size 64: the lead waves issue the K rows of tile jt + 3 after their
+    // MFMA phase, the trailing waves only the V rows of tile jt + 2 (byte ->
+    // patch cross attention 0.122 against 0.130 ms).  At 128 the lead waves'
+    // loads lengthen the varlen prefill (0.887 against 0.833 ms).
+    constexpr bool kLeadK = D == 64;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * R::STAGE];
     __shared__ int wave_range[2][NW];
     __shared__ int win[PAGE_WIN + 1];
@@ -386,14 +391,16 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                 else return cs + k * BN;
             };
             // Tile jt, between barriers:
-            //   lead:  softmax(jt); P.V(jt), QK(jt+1)
-            //   trail: P.V(jt-1), QK(jt); V rows of tile jt+2, K rows of tile
-            //          jt+3; softmax(jt)
-            // V(jt+2) goes into the stage of tile jt-2, whose V was last read by
-            // P.V(jt-2) in tile jt-1; K(jt+3) into the stage of tile jt-1, whose K
-            // was last read by QK(jt-1) in tile jt-1.  Before the barrier the
-            // trailing waves wait for V(jt+1) and K(jt+2), which the next tile
-            // reads (softmax read-ahead and P.V; the lead's QK(jt+2)).
+            //   lead:  softmax(jt); P.V(jt), QK(jt+1) [; K rows of tile jt+3]
+            //   trail: P.V(jt-1), QK(jt); V rows of tile jt+2 [, K rows of tile
+            //          jt+3]; softmax(jt)
+            // (the K rows of tile jt+3 from the lead waves at head size 64, from
+            // the trailing waves at 128).  V(jt+2) goes into the stage of tile
+            // jt-2, whose V was last read by P.V(jt-2) in tile jt-1; K(jt+3) into
+            // the stage of tile jt-1, whose K was last read by QK(jt-1) in tile
+            // jt-1.  Before the barrier each wave waits for its own loads among
+            // V(jt+1) and K(jt+2), which the next tile reads (P.V; the lead's
+            // QK(jt+2)).
             {
                 // trailing waves: K(0), V(0), K(1), V(1), K(2); then K(0), V(0),
                 // K(1) must have landed (the lead's QK(0), softmax(0), QK(1))
@@ -443,6 +450,18 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                     phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, p.cap_in2,
                                                     p.cap_out);
                     step_mfma<D, BN, BF16, true, true>(st, q, st_cur + R::TILE, st_next);
+                    if constexpr (kLeadK) {
+                        if (jt + 3 < n) {
+                            const int j3 = tile_key(jt + 3);
+                            ld.issue_half(false, ring_lds + ((jt + 3) % kStages) * R::STAGE,
+                                          p.k_cache, p.v_cache, win, first, j3, kv_len, p.bs_log2,
+                                          tok_stride, head_off, wl,
+                                          win[R::slot(j3, first, p.bs_log2, wl)]);
+                        }
+                        // this wave's K(jt+2) landed: only K(jt+3) may stay
+                        if (jt + 3 < n) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
+                        else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+                    }
                 } else {
                     step_mfma<D, BN, BF16, true, true>(st, q, st_prev + R::TILE, st_cur);
                     // issue order V(jt+2), K(jt+3): waiting for V(jt+1) and K(jt+2)
@@ -453,7 +472,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                                       p.v_cache, win, first, j2, kv_len, p.bs_log2, tok_stride,
                                       head_off, wl, win[R::slot(j2, first, p.bs_log2, wl)]);
                     }
-                    if (jt + 3 < n) {
+                    if (!kLeadK && jt + 3 < n) {
                         const int j3 = tile_key(jt + 3);
                         ld.issue_half(false, ring_lds + ((jt + 3) % kStages) * R::STAGE, p.k_cache,
                                       p.v_cache, win, first, j3, kv_len, p.bs_log2, tok_stride,
@@ -463,7 +482,8 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                                                     p.cap_out);
                     // this wave's V(jt+1) and K(jt+2) landed: only V(jt+2), K(jt+3) may stay
                     {
-                        const int inflight = (jt + 2 < n ? R::IPW : 0) + (jt + 3 < n ? R::IPW : 0);
+                        const int inflight =
+                            (jt + 2 < n ? R::IPW : 0) + (!kLeadK && jt + 3 < n ? R::IPW : 0);
                         if (inflight == 2 * R::IPW) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * R::IPW));
                         else if (inflight == R::IPW) __builtin_amdgcn_s_waitcnt(vmcnt_imm(R::IPW));
                         else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

@@ -480,6 +480,10 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
                     }
                     phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo_t, hi_t, c, p.cap_in2,
                                                     p.cap_out);
+                    // the probabilities are computed before the wait below (left to
+                    // itself the compiler sinks the exponentials after it)
+                    asm volatile("" ::"v"(st.pb[0][0]), "v"(st.pb[0][1]), "v"(st.pb[BN / 32 - 1][0]),
+                                 "v"(st.pb[BN / 32 - 1][1]), "v"(st.lpart));
                     // this wave's V(jt+1) and K(jt+2) landed: only V(jt+2), K(jt+3) may stay
                     {
                         const int inflight =

@@ -8,12 +8,12 @@
 // delta = rowsum(dO * O) = rowsum(dP * P):
 //     dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),
 //     dQ = scale dS K,  dK = scale dS^T Q.
-// Three kernels, no atomics:
-//   k_bwd_delta  delta per (query row, head);
+// Two kernels, no atomics:
 //   k_bwd_dq     a workgroup owns 128 query rows of one head (32 per wave,
 //                one per lane column, Q and dO in registers as the B
-//                operands) and streams 64-key K / V tiles:
-//                S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
+//                operands); it computes each row's delta from its dO and O
+//                (stored for the second kernel) and streams 64-key K / V
+//                tiles: S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T;
 //   k_bwd_dkdv16 a workgroup owns 128 keys of one kv head, 16 per wave (K
 //                and V rows in registers), and streams 64-row Q / dO tiles of
 //                every query head of the group: S = Q K^T, dP = dO V^T, then
@@ -200,47 +200,6 @@ __device__ __forceinline__ float prob_ds(float s, float dp, float lse2, float de
     }
 }
 
-// delta[row, h] = sum_d dO * O in fp32.  D/8 consecutive lanes read one
-// (row, head)'s contiguous D 16-bit values (16 bytes each, non-temporal: each
-// byte is read once), so a load instruction covers 64/(D/8) whole rows; a
-// wave keeps kDeltaSteps such row groups in flight per iteration and sums
-// each row across its lanes with shuffles.
-constexpr int kDeltaSteps = 4;
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_bwd_delta(BwdParams p) {
-    constexpr int LPR = D / 8;      // lanes per row
-    constexpr int RPW = 64 / LPR;   // rows per wave and load
-    const int64_t n = (int64_t)p.total_q * p.num_heads;
-    const int lane = lane_id(), sub = lane % LPR;
-    const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 64;
-    const int64_t nwaves = (int64_t)gridDim.x * 4;
-    for (int64_t r0 = wave * RPW * kDeltaSteps; r0 < n; r0 += nwaves * RPW * kDeltaSteps) {
-        u32x4_t a[kDeltaSteps], b[kDeltaSteps];
-#pragma unroll
-        for (int k = 0; k < kDeltaSteps; ++k) {
-            // rows past the end read row n - 1 and are not stored
-            const int64_t i = min(r0 + k * RPW + lane / LPR, n - 1);
-            a[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.out + i * D) + sub);
-            b[k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.dout + i * D) + sub);
-        }
-#pragma unroll
-        for (int k = 0; k < kDeltaSteps; ++k) {
-            float acc = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const f32x2_t fa = unpack16<BF16>(a[k][w]), fb = unpack16<BF16>(b[k][w]);
-                acc = __builtin_fmaf(fa.x, fb.x, acc);
-                acc = __builtin_fmaf(fa.y, fb.y, acc);
-            }
-#pragma unroll
-            for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-            const int64_t i = r0 + k * RPW + lane / LPR;
-            if (sub == 0 && i < n) p.delta[i] = acc;
-        }
-    }
-}
-
 template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_dq(BwdParams p) {
     constexpr int TILE = kBwdTile * 2 * D;
@@ -267,14 +226,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int rr = valid ? r : q_len - 1;
     const int64_t qrow = (int64_t)(q_start + rr) * p.num_heads + h;
 
-    u32x4_t qv[D / 16], dov[D / 16];
+    u32x4_t qv[D / 16], dov[D / 16], ov[D / 16];
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
         qv[t] = *reinterpret_cast<const u32x4_t*>(p.q + qrow * D + 16 * t + 8 * g);
         dov[t] = *reinterpret_cast<const u32x4_t*>(p.dout + qrow * D + 16 * t + 8 * g);
+        ov[t] = *reinterpret_cast<const u32x4_t*>(p.out + qrow * D + 16 * t + 8 * g);
     }
     const float lse2 = p.lse[qrow] * kLog2e;
-    const float dlt = p.delta[qrow];
+    // delta = sum_d dO * O in fp32: this lane's half row (dims 16t + 8g ..
+    // + 7), then the other half from lane l ^ 32; stored for the dK/dV kernel
+    float dpart = 0.f;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x2_t fo = unpack16<BF16>(ov[t][e]), fd = unpack16<BF16>(dov[t][e]);
+            dpart = __builtin_fmaf(fo.x, fd.x, dpart);
+            dpart = __builtin_fmaf(fo.y, fd.y, dpart);
+        }
+    const float dlt = pair_sum(dpart);
+    if (valid && g == 0) p.delta[qrow] = dlt;
     // this row's visible keys [lo, hi), as in the forward
     int lo = 0, hi = 0;
     if (valid) {
@@ -631,17 +603,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 template <int D, bool BF16, bool CAP>
 hipError_t launch_bwd_cfg(const BwdParams& p, int max_seqlen_q, int max_seqlen_kv, hipStream_t s) {
-    const int64_t n = (int64_t)p.total_q * p.num_heads;
-    // four waves per block, each covering 64/(D/8) rows per load and
-    // kDeltaSteps loads per iteration
-    const int64_t rows_per_block = 4 * (64 / (D / 8)) * kDeltaSteps;
-    const int dblocks = (int)std::min<int64_t>((n + rows_per_block - 1) / rows_per_block, 8192);
     hipError_t e = hipSuccess;
-    if (dblocks > 0) {   // no query rows: nothing to reduce (dK, dV come out zero)
-        hipLaunchKernelGGL((k_bwd_delta<D, BF16>), dim3(dblocks), dim3(256), 0, s, p);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     BwdParams q = p;
     q.n_qt = (max_seqlen_q + kBwdRows - 1) / kBwdRows;
     q.n_kt = (max_seqlen_kv + kBwdRows - 1) / kBwdRows;

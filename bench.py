@@ -427,7 +427,7 @@ def bench_prefill_generic(A, W, torch, dev, w, flops, iters=50, block_mask=None)
 
 
 def bench_backward(A, W, torch, dev, iters=20):
-    """Varlen backward (delta + dQ + dK/dV kernels) on the varlen causal
+    """Varlen backward (dQ with the row sums delta, then dK/dV) on the varlen causal
     workload, packed K / V; O and the LSE from the paged forward.  Work is
     counted the usual way, 2.5x the forward's causal flops (five products
     per visible pair: S, dP, dV, dK, dQ); the kernels recompute S and dP in

@@ -6,7 +6,7 @@ replayed with new inputs copied in (eagerly) between replays:
     paged causal prefill with LSE;
   * a split-KV decode (decode and combine kernels) with the caller's
     workspace;
-  * a varlen backward (delta, dQ and dK/dV kernels) with the caller's
+  * a varlen backward (the dQ kernel with its row sums, then dK/dV) with the caller's
     workspace and gradient buffers.
 Every replay must equal an eager call on the same inputs bit for bit: the
 kernels, launch shapes and reduction orders are the same, and the library

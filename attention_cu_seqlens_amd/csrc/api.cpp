@@ -506,6 +506,7 @@ attn_status decode_impl(const void* q, const void* k_cache, const void* v_cache,
     p.num_heads = num_heads;
     p.num_kv_heads = num_kv_heads;
     p.group = num_heads / num_kv_heads;
+    p.head_pack = attn::decode_head_pack(num_kv_heads);
     p.bs_log2 = ilog2(block_size);
     p.c = scale * 1.4426950408889634f;
     p.window = window_left;

@@ -1,20 +1,27 @@
 // Paged GQA decode (one query token per sequence) for 16-bit dtypes on gfx950.
 //
-// Split-KV with a balanced schedule: every (sequence b, kv head hk) unit's
-// visible keys form a run of 32-key tiles; the runs are laid end to end in
-// (b, hk) order and workgroup w takes tiles [w*C, (w+1)*C) of that list, so
-// every workgroup streams the same number of tiles (the last one fewer)
-// whatever the mix of lengths.  By default the grid is two workgroups per CU,
-// all resident at once: no tail of long splits running alone and no
-// workgroup turnover.  A workgroup's share is cut at unit boundaries into
-// segments; each segment's NW waves take interleaved 32-key tiles, each with
-// its own online-softmax state for the G = Hq/Hkv query heads of the group
-// (the 32 query columns of the MFMA, G of them live), merge in LDS and write
-// one partial (unnormalised O, running max m, sum l) per query head.  A
-// second kernel merges each unit's segments with the same logsumexp rule;
-// its LSE output is the "OUTPUT_LOGSUMEXP" quantity of the FlexAttention
-// kernel options shown in the blt issue "Cross Attention does not work on
-// CPU and older GPUs".
+// Split-KV with a balanced schedule.  A unit is (sequence b, group hg of HP
+// adjacent kv heads), HP = 4, 2 or 1, the largest that divides Hkv: the
+// cache stores a key's kv heads side by side, so the HP heads' rows of one
+// key are HP * D contiguous elements, and the unit's loads of a key cover
+// them at once instead of one head's D elements at a stride of Hkv * D (an
+// fp8 cache with 8 kv heads streamed one head at a time reads 128-byte
+// pieces 1 KiB apart and runs about 15% below the same bytes read as whole
+// rows).  Every unit's visible keys form a run of 32-key tiles; the runs are
+// laid end to end in (b, hg) order and workgroup w takes tiles
+// [w*C, (w+1)*C) of that list, so every workgroup streams the same number of
+// tiles (the last one fewer) whatever the mix of lengths.  By default the
+// grid is two workgroups per CU, all resident at once: no tail of long
+// splits running alone and no workgroup turnover.  A workgroup's share is
+// cut at unit boundaries into segments; in each, NW / HP waves serve each
+// head of the group, taking interleaved 32-key tiles of its keys, each wave
+// with its own online-softmax state for the G = Hq/Hkv query heads of its
+// kv head (the 32 query columns of the MFMA, G of them live); the waves of a
+// head merge in LDS and write one partial (unnormalised O, running max m,
+// sum l) per query head: HP * G rows per segment.  A second kernel merges
+// each unit's segments with the same logsumexp rule; its LSE output is the
+// "OUTPUT_LOGSUMEXP" quantity of the FlexAttention kernel options shown in
+// the blt issue "Cross Attention does not work on CPU and older GPUs".
 //
 // Segment (unit u, workgroup w) writes partial slot u + w: along the list
 // either the unit or the workgroup index grows from one segment to the next,
@@ -63,6 +70,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
     const int Hkv = p.num_kv_heads;
+    const int HP = p.head_pack;   // kv heads per unit
+    const int Hu = Hkv / HP;      // units per sequence
+    const int WPH = NW / HP;      // waves per kv head
+    const int hsub = w / WPH;     // this wave's head within the unit
+    const int wt = w - hsub * WPH;
     const int wg = blockIdx.x;
 
     // The tile list: total length, this workgroup's share [start, end) and
@@ -73,14 +85,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int t = bb < p.batch ? decode_tiles(p.cu_kv[bb + 1] - p.cu_kv[bb], p.window) : 0;
         total += __builtin_amdgcn_readlane(wave_incl_scan(t), 63);
     }
-    total *= Hkv;
+    total *= Hu;
     const int C = p.split_tiles > 0
                       ? p.split_tiles
                       : max(kDecodeMinSegTiles, (total + (int)gridDim.x - 1) / (int)gridDim.x);
     if ((int64_t)wg * C >= total) return;
     const int start = wg * C;
     const int end = min(total, start + C);
-    int b = 0, hk = 0, t0 = 0;
+    int b = 0, hg = 0, t0 = 0;
     {
         int acc = 0;   // tiles per kv head of the sequences before `base`
         for (int base = 0; base < p.batch; base += 64) {
@@ -88,14 +100,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             const int t = bb < p.batch ? decode_tiles(p.cu_kv[bb + 1] - p.cu_kv[bb], p.window) : 0;
             const int incl = wave_incl_scan(t);
             const int tot = __builtin_amdgcn_readlane(incl, 63);
-            if (start < (acc + tot) * Hkv) {
-                const bool mine = t > 0 && start >= (acc + incl - t) * Hkv && start < (acc + incl) * Hkv;
+            if (start < (acc + tot) * Hu) {
+                const bool mine = t > 0 && start >= (acc + incl - t) * Hu && start < (acc + incl) * Hu;
                 const int src = __builtin_amdgcn_readfirstlane(__builtin_ctzll(__ballot(mine)));
                 b = base + src;
                 const int tb = __builtin_amdgcn_readlane(t, src);
-                const int off = start - (acc + __builtin_amdgcn_readlane(incl - t, src)) * Hkv;
-                hk = off / tb;
-                t0 = off - hk * tb;
+                const int off = start - (acc + __builtin_amdgcn_readlane(incl - t, src)) * Hu;
+                hg = off / tb;
+                t0 = off - hg * tb;
                 break;
             }
             acc += tot;
@@ -124,7 +136,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const int lo_w = p.window > 0 ? max(0, kv_len - p.window) : 0;
         const int nt = (kv_len - klo + 31) >> 5;
         const int t1 = min(nt, t0 + (end - pos));
-        const int u = b * Hkv + hk;
+        const int u = b * Hu + hg;
         const int seg = u + wg;
         if (t0 == 0 && tid == 0) {
             // the unit's last tile lies in workgroup (pos + nt - 1) / C
@@ -133,6 +145,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         }
         const int k0 = klo + 32 * t0;
         const int k1 = min(kv_len, klo + 32 * t1);
+        const int hk = hg * HP + hsub;
         const int head = hk * G + col;
 
         RowsState<D, 1> st;
@@ -157,10 +170,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             const int first = cs >> p.bs_log2;
             fill_page_window(win, table, first, n_blocks, tid, NW * 64);
             __syncthreads();
-            // Each wave streams 32-key tiles w, w + NW, ... of the chunk through
-            // its own LDS slot, with its next tile's loads in flight while it
-            // computes.  Chunks are whole tiles except the segment's last, so
-            // k1 bounds every tile's rows.
+            // Each wave streams 32-key tiles wt, wt + WPH, ... of the chunk for
+            // its kv head through its own LDS slot, with its next tile's loads in
+            // flight while it computes.  Chunks are whole tiles except the
+            // segment's last, so k1 bounds every tile's rows.
             const int n_t = (ce - cs + 31) >> 5;
             Tile ld;
             auto load = [&](int j) {
@@ -170,12 +183,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
                     ld.load(p.k_cache, p.v_cache, win, first, j, k1, p.bs_log2, tok_stride, head_off,
                             lane);
             };
-            if (w < n_t) load(cs + 32 * w);
-            for (int t = w; t < n_t; t += NW) {
+            if (wt < n_t) load(cs + 32 * wt);
+            for (int t = wt; t < n_t; t += WPH) {
                 const int j = cs + 32 * t;
                 ld.store(mine, j, k1, lane);
                 __builtin_amdgcn_wave_barrier();
-                if (t + NW < n_t) load(j + 32 * NW);
+                if (t + WPH < n_t) load(j + 32 * WPH);
                 if (j >= lo_w && j + 32 <= k1)
                     tile_step<D, 32, 1, 1, BF16, false, CAP>(st, mine, j, 0, c, cap_in2, p.cap_out);
                 else
@@ -185,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             __syncthreads();   // the window and the tile slots are free again
         }
 
-        // merge the NW wave states of this segment
+        // merge the wave states of each kv head of this segment
         float* red_o = reinterpret_cast<float*>(smem);   // [NW][G][D]
         float* red_m = red_o + NW * G * D;               // [NW][G]
         float* red_l = red_m + NW * G;
@@ -203,20 +216,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             }
         }
         __syncthreads();
-        for (int idx = tid; idx < G * D; idx += NW * 64) {
-            const int cc = idx / D, d = idx % D;
+        for (int idx = tid; idx < HP * G * D; idx += NW * 64) {
+            const int row = idx / D, d = idx % D;   // row = head-in-unit * G + query column
+            const int hh = row / G, cc = row - hh * G;
+            const int i0 = hh * WPH;                // the head's waves i0 .. i0 + WPH - 1
             float mstar = kNegInf;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) mstar = fmaxf(mstar, red_m[i * G + cc]);
+            for (int i = i0; i < i0 + WPH; ++i) mstar = fmaxf(mstar, red_m[i * G + cc]);
             float lsum = 0.f, osum = 0.f;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
+            for (int i = i0; i < i0 + WPH; ++i) {
                 const float mi = red_m[i * G + cc];
                 const float wgt = (mi == kNegInf) ? 0.f : fast_exp2(mi - mstar);
                 lsum += red_l[i * G + cc] * wgt;
                 osum += red_o[(i * G + cc) * D + d] * wgt;
             }
-            const int64_t slot = (int64_t)seg * G + cc;
+            const int64_t slot = (int64_t)seg * (HP * G) + row;
             p.part_o[slot * D + d] = osum * dv;
             if (d == 0) {
                 p.part_ml[slot * 2 + 0] = mstar;
@@ -228,8 +241,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (pos >= end) break;
         // next unit with tiles (one exists: pos < end <= total)
         t0 = 0;
-        if (++hk == Hkv) {
-            hk = 0;
+        if (++hg == Hu) {
+            hg = 0;
             do {
                 ++b;
             } while (decode_tiles(p.cu_kv[b + 1] - p.cu_kv[b], p.window) == 0);
@@ -243,22 +256,23 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.num_heads;
     const int h = bh - b * p.num_heads;
-    const int hk = h / p.group;
-    const int cc = h - hk * p.group;
+    const int GP = p.group * p.head_pack;   // partial rows per segment
+    const int hg = h / GP;
+    const int cc = h - hg * GP;
     const int kv_len = p.cu_kv[b + 1] - p.cu_kv[b];
     int first = 0, n_s = 0;
     if (decode_tiles(kv_len, p.window) > 0) {
-        const int u = b * p.num_kv_heads + hk;
+        const int u = b * (p.num_kv_heads / p.head_pack) + hg;
         first = p.seg_meta[2 * u];
         n_s = p.seg_meta[2 * u + 1];
     }
     const int d = threadIdx.x;
     float mstar = kNegInf;
     for (int s = 0; s < n_s; ++s)
-        mstar = fmaxf(mstar, p.part_ml[((int64_t)(first + s) * p.group + cc) * 2]);
+        mstar = fmaxf(mstar, p.part_ml[((int64_t)(first + s) * GP + cc) * 2]);
     float lsum = 0.f, osum = 0.f;
     for (int s = 0; s < n_s; ++s) {
-        const int64_t slot = (int64_t)(first + s) * p.group + cc;
+        const int64_t slot = (int64_t)(first + s) * GP + cc;
         const float ms = p.part_ml[slot * 2];
         const float wgt = (ms == kNegInf) ? 0.f : fast_exp2(ms - mstar);
         lsum += p.part_ml[slot * 2 + 1] * wgt;
@@ -274,6 +288,11 @@ __global__ __launch_bounds__(D) void k_decode_combine(DecodeParams p) {
         p.lse[bh] = lsum > 0.f ? (mstar + __builtin_log2f(lsum)) * kLn2 : kNegInf;
 }
 
+// kv heads per decode unit: 4, 2 or 1, the largest dividing num_kv_heads.
+int decode_head_pack(int num_kv_heads) {
+    return num_kv_heads % 4 == 0 ? 4 : num_kv_heads % 2 == 0 ? 2 : 1;
+}
+
 // Keys a unit's tiles can span for kv lengths up to max_seqlen_kv: with a
 // local window W, at most W keys plus up to 31 before them (the tiles start
 // 32-key aligned).
@@ -281,10 +300,12 @@ int decode_span(int max_seqlen_kv, int window) {
     return window > 0 ? (int)std::min<int64_t>(max_seqlen_kv, (int64_t)window + 31) : max_seqlen_kv;
 }
 
-// Upper bound of the tile list's length (every sequence at max_seqlen_kv).
+// Upper bound of the tile list's length (every sequence at max_seqlen_kv;
+// one tile covers the unit's kv heads).
 int64_t decode_tile_bound(int batch, int num_kv_heads, int max_seqlen_kv, int window) {
     const int64_t span = decode_span(max_seqlen_kv, window);
-    return (int64_t)batch * num_kv_heads * ((span + 31) / 32);
+    const int64_t units = (int64_t)batch * (num_kv_heads / decode_head_pack(num_kv_heads));
+    return units * ((span + 31) / 32);
 }
 
 // Workgroups of the split kernel: with split_tokens the list is cut every
@@ -302,15 +323,16 @@ int decode_grid(int batch, int num_kv_heads, int max_seqlen_kv, int window, int 
                                                          (int64_t)kDecodeMaxGrid}));
 }
 
-// Workspace layout: partial slots, one per (unit, workgroup) segment, at
-// most units + grid of them (part_o, then part_ml), then the per-unit
-// segment records.
+// Workspace layout: partial slots of one row per query head of the unit,
+// one slot per (unit, workgroup) segment, at most units + grid of them
+// (part_o, then part_ml), then the per-unit segment records.
 DecodeWorkspace decode_workspace(int batch, int num_heads, int num_kv_heads, int head_size,
                                  int max_seqlen_kv, int window, int split_tokens) {
-    const int64_t units = (int64_t)batch * num_kv_heads;
+    const int head_units = num_kv_heads / decode_head_pack(num_kv_heads);
+    const int64_t units = (int64_t)batch * head_units;
     const int64_t grid = decode_grid(batch, num_kv_heads, max_seqlen_kv, window, split_tokens,
                                      kDecodeMaxGrid);
-    const int64_t rows = (units + grid) * (num_heads / num_kv_heads);
+    const int64_t rows = (units + grid) * (num_heads / head_units);
     DecodeWorkspace ws;
     ws.ml_off = (size_t)(((rows * head_size * 4 + 255) / 256) * 256);
     ws.meta_off = ws.ml_off + (size_t)(((rows * 2 * 4 + 255) / 256) * 256);

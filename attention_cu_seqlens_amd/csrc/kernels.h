@@ -113,9 +113,9 @@ struct DecodeParams {
     const float* kv_descale;    // [2] device (dk, dv) with k8
     const int32_t* block_table;
     const int32_t* cu_kv;
-    float* part_o;              // [slots, G, D] segment partials (slot = unit + workgroup)
-    float* part_ml;             // [slots, G, 2] their running max and sum
-    int* seg_meta;              // [batch*Hkv, 2] first slot and segment count per unit
+    float* part_o;              // [slots, HP*G, D] segment partials (slot = unit + workgroup)
+    float* part_ml;             // [slots, HP*G, 2] their running max and sum
+    int* seg_meta;              // [batch*Hkv/HP, 2] first slot and segment count per unit
     uint16_t* out;              // [batch, Hq, D]
     float* lse;                 // [batch, Hq] or null
     int mbps;
@@ -123,6 +123,7 @@ struct DecodeParams {
     int num_heads;
     int num_kv_heads;
     int group;
+    int head_pack;              // HP: kv heads per unit (decode_head_pack)
     int bs_log2;
     int split_tiles;            // tiles per workgroup, 0: balanced over the grid
     int grid;                   // workgroups of the split kernel
@@ -185,6 +186,7 @@ hipError_t cu_count(int* out);
 // and the most workgroups the default grid uses (two per CU up to 512 CUs).
 constexpr int kDecodeMinSegTiles = 16;
 constexpr int kDecodeMaxGrid = 1024;
+int decode_head_pack(int num_kv_heads);
 int decode_span(int max_seqlen_kv, int window);
 int64_t decode_tile_bound(int batch, int num_kv_heads, int max_seqlen_kv, int window);
 int decode_grid(int batch, int num_kv_heads, int max_seqlen_kv, int window, int split_tokens,

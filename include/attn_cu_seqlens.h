@@ -313,11 +313,11 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
 /*
  * attn_paged_decode_fwd -- one query token per sequence against its paged
  * cache (q_len = 1; under bottom-right alignment the query sees all kv_len
- * keys).  Split-KV: the 32-key tiles of every (sequence, kv head) pair are
- * laid end to end and each workgroup takes an equal share of that list,
- * cut into pieces at the pairs' ends; a second kernel merges each pair's
- * partial results with their logsumexp (the LSE output of the blt issue's
- * kernel options).
+ * keys).  Split-KV: the 32-key tiles of every (sequence, group of up to 4
+ * adjacent kv heads) unit are laid end to end and each workgroup takes an
+ * equal share of that list, cut into pieces at the units' ends; a second
+ * kernel merges each query head's partial results with their logsumexp (the
+ * LSE output of the blt issue's kernel options).
  *   q            [batch, num_heads, head_size], ATTN_F16 or ATTN_BF16
  *   cu_seqlens_kv int32 [batch + 1]; max_seqlen_kv bounds every kv length
  *   window_left, softcap  as prefill: the window keeps a sequence's last
@@ -325,7 +325,7 @@ size_t attn_paged_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32
  *   split_tokens keys per workgroup share: a multiple of 256 no larger than
  *                8192, or 0 for equal shares over two workgroups per CU
  *                (at least 512 keys each); the tile list (batch x
- *                num_kv_heads x tiles of max_seqlen_kv) must stay within 2^30
+ *                kv-head groups x tiles of max_seqlen_kv) must stay within 2^30
  *   out          [batch, num_heads, head_size], same dtype as q
  *   lse          float32 [batch, num_heads] or NULL
  *   workspace    device scratch of at least

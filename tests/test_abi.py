@@ -212,21 +212,25 @@ def test_decode_host_checks(lib):
     assert ws(64, 32, 8, 128, 32768, 0, 8448) == 0      # split above 8192
     assert ws(64, 32, 8, 128, 32768, -1, 0) == 0        # negative window
     assert ws(0, 32, 8, 128, 1, 0, 0) == 0
-    def layout(units, group, d, grid):
-        # partial slots (units + grid) x group: O rows, then (m, l), each
-        # rounded up to 256 bytes; then two ints per unit
-        rows = (units + grid) * group
+    def layout(units, rows_per_slot, d, grid):
+        # partial slots (units + grid), one row per query head of a unit: O
+        # rows, then (m, l), each rounded up to 256 bytes; then two ints per unit
+        rows = (units + grid) * rows_per_slot
         up = lambda n: (n + 255) // 256 * 256
         return up(rows * d * 4) + up(rows * 2 * 4) + units * 2 * 4
 
     need = ws(4, 8, 2, 128, 1000, 0, 256)
-    # 8 units of at most 32 tiles, 8 tiles (256 keys) per workgroup: 32 workgroups
-    assert need == layout(8, 4, 128, 32)
+    # 2 kv heads form one unit per sequence (8 query rows): 4 units of at most
+    # 32 tiles, 8 tiles (256 keys) per workgroup -> 16 workgroups
+    assert need == layout(4, 8, 128, 16)
     # a window of 300 keys: a unit spans at most 300 + 31 keys -> 11 tiles
-    assert ws(4, 8, 2, 128, 1000, 300, 256) == layout(8, 4, 128, 11)
+    assert ws(4, 8, 2, 128, 1000, 300, 256) == layout(4, 8, 128, 6)
     # by default: segments of at least 16 tiles over at most 1024 workgroups
-    assert ws(4, 8, 2, 128, 1000, 0, 0) == layout(8, 4, 128, 16)
-    assert ws(64, 32, 8, 128, 32768, 0, 0) == layout(512, 4, 128, 1024)
+    assert ws(4, 8, 2, 128, 1000, 0, 0) == layout(4, 8, 128, 8)
+    # 8 kv heads: units of 4 heads (16 query rows), 2 per sequence
+    assert ws(64, 32, 8, 128, 32768, 0, 0) == layout(128, 16, 128, 1024)
+    # 3 kv heads: one head per unit
+    assert ws(4, 6, 3, 64, 1000, 0, 256) == layout(12, 2, 64, 48)
     # tile lists longer than 2^30 are refused
     assert ws(1 << 14, 64, 64, 128, 1 << 20, 0, 0) == 0
 
@@ -265,7 +269,7 @@ def test_decode_noalloc_host_checks(lib):
     assert call(split=300) == 2
     assert call(hq=66, hkv=1) == 3
     assert call(batch=0) == 0
-    # 256 sequences x 64 heads x 64 splits of 256 keys: 256 MiB of partials
+    # 256 sequences x 64 heads in splits of 256 keys: over 500 MiB of partials
     big = dict(batch=256, hq=64, hkv=8, mskv=16384, split=256)
     assert ws(256, 64, 8, 128, 16384, 0, 256) > _lib.ATTN_DECODE_SCRATCH_BYTES
     assert call(**big) == 6

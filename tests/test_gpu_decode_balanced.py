@@ -1,11 +1,13 @@
 """The decode's balanced split schedule against the fp64 oracle.
 
-The (sequence, kv head) units' tile runs are laid end to end and cut into
-equal workgroup shares, so a share may hold many short units, a long unit
-may be cut into many shares, and a share may begin in the middle of a unit.
-Each case is built so that one of these happens, with empty sequences
-between the units, and is held to the oracle with the default schedule and
-with forced shares of split_tokens keys.
+The (sequence, group of 4, 2 or 1 adjacent kv heads) units' tile runs are
+laid end to end and cut into equal workgroup shares, so a share may hold many
+short units, a long unit may be cut into many shares, and a share may begin
+in the middle of a unit.  Each case is built so that one of these happens,
+with empty sequences between the units, and is held to the oracle with the
+default schedule and with forced shares of split_tokens keys; the kv head
+counts cover every grouping (8, 4, 12: four heads per unit; 2, 6: two; 3:
+one).
 """
 
 import numpy as np
@@ -67,3 +69,13 @@ def test_fp8_cache_balanced(A):
     w = W.to_fp8_cache(W.make_decode("bal_fp8", 606, "bf16", [20000, 1, 0, 333, 9000], 32, 8,
                                      128, 64))
     _check(A, w, "fp8_cache", (0, 512, 8192), fp8=True)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 4), (24, 6), (12, 12)])
+def test_head_groups(A, hq, hkv):
+    """Four kv heads (one unit of 4 per sequence), six (three units of 2) and
+    twelve with one query head each (three units of 4, G = 1), ragged lengths
+    with an empty sequence, forced shares cutting units mid-way."""
+    w = W.make_decode(f"bal_groups_{hkv}", 607 + hkv, "bf16", [700, 0, 2500, 33, 4100], hq, hkv,
+                      128, 16)
+    _check(A, w, f"head_groups_{hq}_{hkv}", (0, 256, 1280))

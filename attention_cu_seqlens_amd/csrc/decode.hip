@@ -63,6 +63,7 @@ __device__ __forceinline__ int decode_tiles(int kv_len, int window) {
 
 template <int D, int NW, bool BF16, bool CAP, bool KV8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_decode(DecodeParams p) {
+    static_assert(NW % 4 == 0, "every head pack (1, 2, 4) divides the waves");
     using L = DecodeLayout<D, NW, BF16, KV8>;
     using Tile = typename L::Tile;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int tid = threadIdx.x;
     const int lane = lane_id(), w = wave_id();
     const int Hkv = p.num_kv_heads;
-    const int HP = p.head_pack;   // kv heads per unit
+    const int HP = p.head_pack;   // kv heads per unit: 1, 2 or 4, divides NW
     const int Hu = Hkv / HP;      // units per sequence
     const int WPH = NW / HP;      // waves per kv head
     const int hsub = w / WPH;     // this wave's head within the unit
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     const int end = min(total, start + C);
     int b = 0, hg = 0, t0 = 0;
     {
-        int acc = 0;   // tiles per kv head of the sequences before `base`
+        int acc = 0;   // tiles per unit of the sequences before `base`
         for (int base = 0; base < p.batch; base += 64) {
             const int bb = base + lane;
             const int t = bb < p.batch ? decode_tiles(p.cu_kv[bb + 1] - p.cu_kv[bb], p.window) : 0;

@@ -187,6 +187,38 @@ def gpu_fp8(w, A, window=0, softcap=0.0):
     return out, lse
 
 
+# ------------------------------------------------------------ random draws
+
+def draw_masked_lengths(rng, batch, max_kv, max_q, masks):
+    """One random varlen layout: kv lengths in [1, max_kv) with some empty
+    sequences, a mask from `masks` and query lengths and ids that fit it --
+    document ids cut each sequence at a few points (queries = keys), patch ids
+    are non-decreasing indices below the key count, causal query blocks end at
+    each key range's end (bottom-right), no mask takes any query lengths.
+    Returns (mask, q_lens, kv_lens, q_ids, kv_ids)."""
+    import workloads as W
+    mask = int(rng.choice(masks))
+    kv_lens = rng.integers(1, max_kv, batch)
+    kv_lens[rng.random(batch) < 0.15] = 0
+    q_ids = kv_ids = None
+    if mask & W.MASK_DOCUMENT:
+        q_lens = kv_lens.copy()
+        docs = []
+        for n in kv_lens:
+            cuts = np.sort(rng.integers(1, max(2, int(n)), int(rng.integers(0, 4))))
+            docs.append(np.searchsorted(cuts, np.arange(n), side="right").astype(np.int32))
+        q_ids = kv_ids = np.concatenate(docs).astype(np.int32)
+    elif mask & W.MASK_PATCH:
+        q_lens = rng.integers(0, max_q, batch)
+        q_ids = np.concatenate([np.sort(rng.integers(0, max(1, int(k)), int(n)))
+                                for n, k in zip(q_lens, kv_lens)]).astype(np.int32)
+    elif mask & W.MASK_CAUSAL:
+        q_lens = np.array([int(rng.integers(0, int(k) + 1)) for k in kv_lens])
+    else:
+        q_lens = rng.integers(0, max_q, batch)
+    return mask, np.asarray(q_lens), kv_lens, q_ids, kv_ids
+
+
 # ----------------------------------------------------------------- comparison
 
 def compare(out_gpu, lse_gpu, out_ref, lse_ref, atol, rel=None, rows=None, what="",

@@ -18,8 +18,8 @@ import torch
 
 import oracle as ORC
 import workloads as W
-from gpu_common import (DEV, REL_16, banner, gpu_prefill, lib_module, requires_gpu,
-                        sub_workload)
+from gpu_common import (DEV, REL_16, banner, draw_masked_lengths, gpu_prefill, lib_module,
+                        requires_gpu, sub_workload)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
@@ -121,6 +121,29 @@ def test_document_causal_with_empty_rows(A):
 def test_patch_cross_d64(A):
     w = W.byte_patch_cross_bf16(device=DEV, batch=2, n_bytes=700, n_keys=96, seed=130)
     _case(A, w, 131, "byte_patch_cross")
+
+
+@pytest.mark.parametrize("i", range(10))
+def test_random_configs(A, i):
+    """Seeded random layouts: heads and GQA group, head size, dtype, ragged and
+    empty sequences, mask (none, causal, document, document + causal, patch),
+    window and cap drawn per case."""
+    rng = np.random.default_rng(7700 + i)
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4]))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f16"]))
+    batch = int(rng.integers(1, 4))
+    masks = [W.MASK_NONE, W.MASK_CAUSAL, W.MASK_CAUSAL, W.MASK_DOCUMENT,
+             W.MASK_DOCUMENT | W.MASK_CAUSAL, W.MASK_PATCH]
+    mask, q_lens, kv_lens, q_ids, kv_ids = draw_masked_lengths(rng, batch, 300, 300, masks)
+    window = int(rng.choice([0, 0, 1, 60]))
+    softcap = float(rng.choice([0.0, 0.0, 15.0]))
+    if int(np.sum(q_lens)) == 0:
+        pytest.skip("the draw has no query token")
+    w = W.make_prefill(f"bwr{i}", 7800 + i, dtype, q_lens, kv_lens, hkv * g, hkv, d, 16, mask,
+                       q_ids=q_ids, kv_ids=kv_ids, device=DEV)
+    _case(A, w, 7900 + i, f"random_{i}", window=window, softcap=softcap)
 
 
 def test_full_varlen_causal_sampled(A):

@@ -5,7 +5,8 @@ Each case draws its own head counts (GQA group sizes 1-16, kv head counts
 that give every decode head grouping), head size, 16-bit type, block size,
 ragged lengths with empty sequences, mask, local window, score cap and forced
 split size, so that combinations no hand-written case names are held to the
-same bars as the others.  The draws are fixed by their seeds: a failure names
+same bars as the others; the dense fp8 prefill draws its heads, layout, mask,
+window, cap and the sign of its scale the same way.  The draws are fixed by their seeds: a failure names
 its case and reruns identically.
 """
 
@@ -13,13 +14,16 @@ import numpy as np
 import pytest
 
 import workloads as W
-from gpu_common import (ATOL_16, REL_16, banner, compare, gpu_cache, gpu_decode,
-                        gpu_decode_fp8kv, gpu_prefill, lib_module, oracle_decode,
-                        oracle_decode_fp8kv, oracle_prefill, requires_gpu)
+from gpu_common import (ATOL_16, ATOL_FP8, LSE_ATOL_FP8, REL_16, banner, compare,
+                        draw_masked_lengths, gpu_cache, gpu_decode, gpu_decode_fp8kv, gpu_fp8,
+                        gpu_prefill, lib_module, oracle_decode, oracle_decode_fp8kv, oracle_fp8,
+                        oracle_prefill, requires_gpu)
 
 pytestmark = [pytest.mark.gpu, requires_gpu]
 
 N_CASES = 24
+MASKS = [W.MASK_NONE, W.MASK_CAUSAL, W.MASK_CAUSAL, W.MASK_DOCUMENT,
+         W.MASK_DOCUMENT | W.MASK_CAUSAL, W.MASK_PATCH]
 
 
 @pytest.fixture(scope="module")
@@ -76,29 +80,7 @@ def _draw_prefill(i):
     dtype = str(rng.choice(["bf16", "f16"]))
     bs = int(rng.choice([16, 32, 64]))
     batch = int(rng.integers(1, 5))
-    mask = int(rng.choice([W.MASK_NONE, W.MASK_CAUSAL, W.MASK_CAUSAL, W.MASK_DOCUMENT,
-                           W.MASK_DOCUMENT | W.MASK_CAUSAL, W.MASK_PATCH]))
-    kv_lens = rng.integers(1, 420, batch)
-    kv_lens[rng.random(batch) < 0.15] = 0
-    q_ids = kv_ids = None
-    if mask & W.MASK_DOCUMENT:
-        # documents: every sequence cut at a few random points; q and kv alike
-        q_lens = kv_lens.copy()
-        docs = []
-        for n in kv_lens:
-            cuts = np.sort(rng.integers(1, max(2, int(n)), int(rng.integers(0, 4))))
-            docs.append(np.searchsorted(cuts, np.arange(n), side="right").astype(np.int32))
-        q_ids = kv_ids = np.concatenate(docs).astype(np.int32) if docs else None
-    elif mask == W.MASK_PATCH:
-        # byte queries with non-decreasing patch indices below their key count
-        q_lens = rng.integers(0, 500, batch)
-        q_ids = np.concatenate([np.sort(rng.integers(0, max(1, int(k)), int(n)))
-                                for n, k in zip(q_lens, kv_lens)]).astype(np.int32)
-    elif mask == W.MASK_CAUSAL:
-        # bottom-right alignment: a query block at the end of each key range
-        q_lens = np.array([int(rng.integers(0, int(k) + 1)) for k in kv_lens])
-    else:
-        q_lens = rng.integers(0, 420, batch)
+    mask, q_lens, kv_lens, q_ids, kv_ids = draw_masked_lengths(rng, batch, 420, 500, MASKS)
     window = int(rng.choice([0, 0, 0, 1, 50, 300]))
     softcap = float(rng.choice([0.0, 0.0, 0.0, 20.0]))
     return dict(seed=7400 + i, hq=hkv * g, hkv=hkv, d=d, dtype=dtype, bs=bs, q_lens=q_lens,
@@ -120,3 +102,35 @@ def test_random_prefill(A, i):
     out, lse = gpu_prefill(w, A, window=c["window"], softcap=c["softcap"])
     ref_o, ref_l = oracle_prefill(w, window=c["window"], softcap=c["softcap"])
     compare(out, lse, ref_o, ref_l, ATOL_16, REL_16, what=f"random_prefill_{i}")
+
+
+def _draw_fp8(i):
+    rng = np.random.default_rng(7500 + i)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4]))
+    batch = int(rng.integers(1, 5))
+    mask, q_lens, kv_lens, q_ids, kv_ids = draw_masked_lengths(rng, batch, 500, 500, MASKS)
+    window = int(rng.choice([0, 0, 0, 1, 70, 260]))
+    softcap = float(rng.choice([0.0, 0.0, 0.0, 20.0]))
+    # scales of the default magnitude 1/sqrt(D) (the workloads' and the bar's),
+    # either sign: a sharper softmax (a causal draw at 0.2 reached 0.083)
+    # weighs a few keys whose single e4m3 rounding no longer averages out
+    scale = rng.choice([None, None, -0.07, 0.09])
+    return dict(seed=7600 + i, hq=hkv * g, hkv=hkv, q_lens=q_lens, kv_lens=kv_lens, mask=mask,
+                q_ids=q_ids, kv_ids=kv_ids, window=window, softcap=softcap,
+                scale=None if scale is None else float(scale))
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_fp8(A, i):
+    c = _draw_fp8(i)
+    banner(f"random fp8 {i}: {c['hq']}/{c['hkv']} heads, q {c['q_lens'].tolist()} "
+           f"kv {c['kv_lens'].tolist()}, mask {c['mask']}, window {c['window']}, "
+           f"cap {c['softcap']}, scale {c['scale']}")
+    if int(np.sum(c["q_lens"])) == 0 or int(np.sum(c["kv_lens"])) == 0:
+        pytest.skip("the draw has no query token or no key")
+    w = W.make_fp8(f"r8_{i}", c["seed"], c["q_lens"], c["kv_lens"], c["hq"], c["hkv"], 128,
+                   c["mask"], q_ids=c["q_ids"], kv_ids=c["kv_ids"], scale=c["scale"])
+    out, lse = gpu_fp8(w, A, window=c["window"], softcap=c["softcap"])
+    ref_o, ref_l = oracle_fp8(w, window=c["window"], softcap=c["softcap"])
+    compare(out, lse, ref_o, ref_l, ATOL_FP8, what=f"random_fp8_{i}", lse_atol=LSE_ATOL_FP8)

@@ -195,7 +195,9 @@ def draw_masked_lengths(rng, batch, max_kv, max_q, masks):
     document ids cut each sequence at a few points (queries = keys), patch ids
     are non-decreasing indices below the key count, causal query blocks end at
     each key range's end (bottom-right), no mask takes any query lengths.
-    Returns (mask, q_lens, kv_lens, q_ids, kv_ids)."""
+    A draw with no query token or no key at all is drawn again from the same
+    generator (whole-batch empty inputs have tests of their own), so every
+    random case runs.  Returns (mask, q_lens, kv_lens, q_ids, kv_ids)."""
     import workloads as W
     mask = int(rng.choice(masks))
     kv_lens = rng.integers(1, max_kv, batch)
@@ -216,6 +218,8 @@ def draw_masked_lengths(rng, batch, max_kv, max_q, masks):
         q_lens = np.array([int(rng.integers(0, int(k) + 1)) for k in kv_lens])
     else:
         q_lens = rng.integers(0, max_q, batch)
+    if int(np.sum(q_lens)) == 0 or int(np.sum(kv_lens)) == 0:
+        return draw_masked_lengths(rng, batch, max_kv, max_q, masks)
     return mask, np.asarray(q_lens), kv_lens, q_ids, kv_ids
 
 

@@ -139,8 +139,6 @@ def test_random_configs(A, i):
     mask, q_lens, kv_lens, q_ids, kv_ids = draw_masked_lengths(rng, batch, 300, 300, masks)
     window = int(rng.choice([0, 0, 1, 60]))
     softcap = float(rng.choice([0.0, 0.0, 15.0]))
-    if int(np.sum(q_lens)) == 0:
-        pytest.skip("the draw has no query token")
     w = W.make_prefill(f"bwr{i}", 7800 + i, dtype, q_lens, kv_lens, hkv * g, hkv, d, 16, mask,
                        q_ids=q_ids, kv_ids=kv_ids, device=DEV)
     _case(A, w, 7900 + i, f"random_{i}", window=window, softcap=softcap)

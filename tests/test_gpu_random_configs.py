@@ -94,8 +94,6 @@ def test_random_prefill(A, i):
     banner(f"random prefill {i}: {c['hq']}/{c['hkv']} heads, D {c['d']} {c['dtype']}, block "
            f"{c['bs']}, q {c['q_lens'].tolist()} kv {c['kv_lens'].tolist()}, mask {c['mask']}, "
            f"window {c['window']}, cap {c['softcap']}")
-    if int(np.sum(c["q_lens"])) == 0:
-        pytest.skip("the draw has no query token")
     w = W.make_prefill(f"rpre{i}", c["seed"], c["dtype"], c["q_lens"], c["kv_lens"], c["hq"],
                        c["hkv"], c["d"], c["bs"], c["mask"], q_ids=c["q_ids"],
                        kv_ids=c["kv_ids"])
@@ -127,8 +125,6 @@ def test_random_fp8(A, i):
     banner(f"random fp8 {i}: {c['hq']}/{c['hkv']} heads, q {c['q_lens'].tolist()} "
            f"kv {c['kv_lens'].tolist()}, mask {c['mask']}, window {c['window']}, "
            f"cap {c['softcap']}, scale {c['scale']}")
-    if int(np.sum(c["q_lens"])) == 0 or int(np.sum(c["kv_lens"])) == 0:
-        pytest.skip("the draw has no query token or no key")
     w = W.make_fp8(f"r8_{i}", c["seed"], c["q_lens"], c["kv_lens"], c["hq"], c["hkv"], 128,
                    c["mask"], q_ids=c["q_ids"], kv_ids=c["kv_ids"], scale=c["scale"])
     out, lse = gpu_fp8(w, A, window=c["window"], softcap=c["softcap"])

@@ -14,10 +14,13 @@
 // Work decomposition needs no device->host sync: the host bounds the grid by
 // max_seqlen_q and total_q, and each workgroup finds its (sequence, head
 // group, query tile) from cu_seqlens_q (map_tile); the few workgroups past
-// the last tile exit at once.  When every sequence has the same length
-// (total_q = batch * max_seqlen_q) at head size 64, one workgroup per CU
-// instead walks a fixed snake of its XCD's tiles (no dispatch between
-// tiles; at head size 128 the loop made the compiler spill).
+// the last tile exit at once.  Head size 128 runs the eight-wave kernel
+// below, one workgroup per CU.  Head size 64 runs four-wave workgroups,
+// several per CU (k_paged_prefill_pair), except under stored block lists,
+// where it keeps the eight-wave kernel; there, when every sequence has the
+// same length (total_q = batch * max_seqlen_q), one workgroup per CU walks a
+// fixed snake of its XCD's tiles (no dispatch between tiles; at head size
+// 128 that loop made the compiler spill).
 //
 // Masks reduce to one visible key interval [lo, hi) per query row: causal
 // (bottom-right) and patch bound hi, document ids (non-decreasing within a
@@ -529,6 +532,195 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
     }
 }
 
+
+// Head size 64, dense or masked (no stored block lists): several small
+// workgroups per CU instead of one.  A workgroup is four waves (one per
+// SIMD) holding 128 packed query rows, and its K/V ring has two stages
+// (35 KB of LDS, 136 registers), so three fit on a CU and each SIMD runs one
+// wave of each.  The workgroups are not in step: while one is in its set-up,
+// epilogue or a barrier, the others' MFMA and softmax work keeps the SIMD
+// busy.  Byte -> patch cross attention's workgroups see short key ranges, so
+// set-up and epilogue are a large share of each, which the eight-wave
+// kernel (one workgroup per CU) cannot overlap.  At head size 128 (66 KB,
+// 193 registers: two per CU) the form measured even with the eight-wave
+// kernel, which stays there.
+// Per key tile each wave waits for its own loads of the tile, meets the
+// others at the barrier (after which the other stage is free: its last
+// reads were the previous tile's), runs QK on the current stage, issues its
+// 16 key rows of the next tile into the other stage, then runs the softmax
+// and P.V.  (Loads issued ahead of QK measured 2.6% slower than the
+// one-workgroup kernel, between QK and the softmax 0.8-2% faster, between
+// the softmax and P.V even.)
+template <int D, bool BF16, bool CAP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_prefill_pair(
+    PrefillParams p) {
+    constexpr int NW = 4, BN = 64, BM = NW * 32;
+    using R = Ring16<D, BN, NW>;
+    static_assert(NW * 32 * 2 * D <= R::STAGE, "Q slices fit stage 0");
+    static_assert(NW * kStoreSliceBytes<D> <= 2 * R::STAGE, "output slices fit the ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * R::STAGE];
+    __shared__ int wave_range[2][NW];
+    __shared__ int win[PAGE_WIN + 1];
+
+    int a_group = p.group, a_heads = p.num_heads, a_window = p.window;
+    uint32_t a_mask = p.mask;
+    float a_c = p.c;
+    const uint16_t* a_q = p.q;
+    asm volatile("" : "+s"(a_group), "+s"(a_heads), "+s"(a_window), "+s"(a_mask), "+s"(a_c),
+                 "+s"(a_q));
+    int b, hg, qt;
+    SeqSpan sp;
+    if (!map_tile(p.cu_q, p.cu_kv, p.batch, p.n_head_groups, BM >> p.pack_log2, blockIdx.x & 7,
+                  blockIdx.x >> 3, b, hg, qt, sp))
+        return;
+    const int q_start = sp.q_start, q_len = sp.q_len;
+    const int tok0 = qt * (BM >> p.pack_log2);
+    const int kv_start = sp.kv_start, kv_len = sp.kv_len;
+    const int h0 = hg << p.pack_log2;
+    const int hk = h0 / a_group;
+    const bool neg = a_c < 0.f;
+    const int32_t* table = p.block_table + (int64_t)b * p.mbps;
+    const int n_blocks = (kv_len + (1 << p.bs_log2) - 1) >> p.bs_log2;
+    const bool win_early = !(a_mask & kMaskDocument) && a_window <= 0;
+    if (win_early) fill_page_window(win, table, 0, n_blocks, threadIdx.x, NW * 64);
+    const float c = fmaxf(fabsf(a_c), 1e-30f);
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int w = wave_id();
+    const int col = lane & 31, g = lane >> 5;
+    const int r = w * 32 + col;
+    const int tok = tok0 + (r >> p.pack_log2);
+    const int head = h0 + (r & ((1 << p.pack_log2) - 1));
+    const bool valid = tok < q_len;
+    int lo = 0, hi = 0;
+    if (valid) {
+        hi = kv_len;
+        if (a_mask & kMaskCausal) hi = min(hi, tok + (kv_len - q_len) + 1);
+        if (a_mask & kMaskPatch) hi = min(hi, p.q_ids[q_start + tok] + 1);
+        if (a_mask & kMaskDocument) {
+            const int doc = p.q_ids[q_start + tok];
+            lo = lower_bound_i32(p.kv_ids + kv_start, kv_len, doc);
+            hi = min(hi, upper_bound_i32(p.kv_ids + kv_start, kv_len, doc));
+        }
+        if (a_window > 0) lo = max(lo, tok + (kv_len - q_len) - a_window + 1);
+        if (hi < lo) hi = lo;
+    }
+    // Q of this wave's rows into its slice of stage 0 by direct loads of whole
+    // rows (a row past the sequence end reads row tok0; never stored)
+    uint8_t* const q_slice = ring + w * 32 * 2 * D;
+    {
+        constexpr int CPR = D / 8, RPI = 64 / CPR;
+        const int ch = lane % CPR;
+#pragma unroll
+        for (int i = 0; i < 32 / RPI; ++i) {
+            const int rr = i * RPI + lane / CPR;
+            const int rw = w * 32 + rr;
+            const int tk = tok0 + (rw >> p.pack_log2);
+            const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+            const uint16_t* src = a_q + ((int64_t)(q_start + (tk < q_len ? tk : tok0)) * a_heads + hd) * D +
+                                  8 * (ch ^ swz<D>(rr));
+            dma16(src, lds_addr(q_slice + i * 1024));
+        }
+    }
+    const int w_lo = wave_min(valid ? lo : 0x7fffffff);
+    const int w_hi = wave_max(valid ? hi : -0x7fffffff);
+    const int w_lo_max = wave_max(valid ? lo : -0x7fffffff);
+    const int w_hi_min = wave_min(valid ? hi : 0x7fffffff);
+    const bool w_any = w_hi > w_lo;
+    if (lane == 0) {
+        wave_range[0][w] = w_any ? w_lo : 0x7fffffff;
+        wave_range[1][w] = w_any ? w_hi : -0x7fffffff;
+    }
+    __syncthreads();
+    int kv_begin = 0x7fffffff, kv_end = -0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        kv_begin = min(kv_begin, wave_range[0][i]);
+        kv_end = max(kv_end, wave_range[1][i]);
+    }
+    kv_begin = __builtin_amdgcn_readfirstlane(kv_begin & ~15);
+    kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+
+    // Q operand from the wave's own slice; every wave's reads complete before
+    // the first key chunk's barrier, after which the ring loads refill stage 0
+    u32x4_t q[D / 16];
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    {
+        const uint32_t lq = (uint32_t)(col * 2 * D + ((g ^ swz<D>(col)) << 4));
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+            q[t] = *reinterpret_cast<const u32x4_t*>(q_slice + (lq ^ (uint32_t)(t << 5)));
+            if (neg) q[t] = neg16x8(q[t]);
+        }
+    }
+
+    const int tok_stride = p.num_kv_heads * D;
+    const int head_off = hk * D;
+    const int chunk_keys = PAGE_WIN << p.bs_log2;   // a multiple of BN
+    R ld;
+    ld.init(lane, w, tok_stride);
+    const uint32_t ring_lds = lds_addr(ring);
+
+    PrefillWave<D, BN> st;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
+    st.m = kNegInf;
+    st.lpart = 0.f;
+    st.alpha = 1.f;
+    st.need = false;
+
+    for (int cs = kv_begin; cs < kv_end; cs += chunk_keys) {
+        const int n = (min(kv_end, cs + chunk_keys) - cs + BN - 1) / BN;
+        const int first = cs >> p.bs_log2;
+        if (!(win_early && cs == 0)) fill_page_window(win, table, first, n_blocks, tid, NW * 64);
+        // the window is in place and every wave is done with the ring (its Q
+        // reads, or the previous chunk's last tile): its LDS operations have
+        // completed before it reaches the barrier
+        __builtin_amdgcn_s_waitcnt(0xC07Fu);   // lgkmcnt(0)
+        __syncthreads();
+        auto issue = [&](int k) {
+            const int jk = cs + k * BN;
+            const int pg = win[R::slot(jk, first, p.bs_log2, w)];
+            const uint32_t stage = ring_lds + (k & 1) * R::STAGE;
+            ld.issue_half(false, stage, p.k_cache, p.v_cache, win, first, jk, kv_len, p.bs_log2,
+                          tok_stride, head_off, w, pg);
+            ld.issue_half(true, stage, p.k_cache, p.v_cache, win, first, jk, kv_len, p.bs_log2,
+                          tok_stride, head_off, w, pg);
+        };
+        issue(0);
+        for (int jt = 0; jt < n; ++jt) {
+            const int j0 = cs + jt * BN;
+            // this wave's rows of tile jt have landed; after the barrier every
+            // wave's have, and nobody reads the other stage any more
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+            block_barrier();
+            const uint8_t* cur = ring + (jt & 1) * R::STAGE;
+            const bool partial = !(w_any && j0 >= w_lo_max && j0 + BN <= w_hi_min);
+            step_mfma<D, BN, BF16, false, true>(st, q, cur, cur);
+            if (jt + 1 < n) issue(jt + 1);
+            phase_softmax<D, BN, BF16, CAP>(st, partial, j0, lo, hi, c, p.cap_in2, p.cap_out);
+            step_mfma<D, BN, BF16, true, false>(st, q, cur + R::TILE, cur);
+        }
+        block_barrier();   // the last tile's reads are done before the ring is reused
+    }
+
+    const float l = pair_sum(st.lpart);
+    // with no key tile the output slices could overlap another wave's Q slice
+    // still being read
+    if (kv_begin >= kv_end) block_barrier();
+    store_rows_lds<D, BF16>(st.o, l, ring + w * kStoreSliceBytes<D>, [&](int rr) -> uint16_t* {
+        const int rw = w * 32 + rr;
+        const int tk = tok0 + (rw >> p.pack_log2);
+        const int hd = h0 + (rw & ((1 << p.pack_log2) - 1));
+        return tk < q_len ? p.out + ((int64_t)(q_start + tk) * p.num_heads + hd) * D : nullptr;
+    });
+    if (valid && p.lse != nullptr && g == 0) {
+        const int64_t rowi = (int64_t)(q_start + tok) * p.num_heads + head;
+        p.lse[rowi] = l > 0.f ? (st.m + __builtin_log2f(l)) * kLn2 : kNegInf;
+    }
+}
+
 namespace {
 
 // Compute units per XCD of the current device.
@@ -550,13 +742,13 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
                                           tokens_per_tile);
     if (per_xcd <= 0) return hipSuccess;
     if (8 * per_xcd > 0x7fffffff) return hipErrorInvalidConfiguration;
-    // Equal-length sequences (every query tile of a unit count is known, the
-    // tiles' key ranges vary only along each unit): one workgroup per CU runs
-    // a fixed snake of the XCD's items, with no dispatch between items.
-    // Ragged batches keep one workgroup per item (the dispatcher balances
-    // their unequal lengths).
+    // Block lists at head size 64 with equal-length sequences (every query
+    // tile of a unit count is known, the tiles' key ranges vary only along
+    // each unit): one workgroup per CU runs a fixed snake of the XCD's items,
+    // with no dispatch between items.  Ragged batches keep one workgroup per
+    // item (the dispatcher balances their unequal lengths).
     const bool uniform = (int64_t)p.total_q == (int64_t)p.batch * max_seqlen_q;
-    if constexpr (D == 64) {
+    if constexpr (D == 64 && BSP) {
         if (uniform) {
             int cu = 0;
             hipError_t e = cus_per_xcd(&cu);
@@ -567,9 +759,21 @@ hipError_t launch_cfg(const PrefillParams& p0, int max_seqlen_q, hipStream_t s) 
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP, BSP, false>),
-                       dim3((unsigned)(8 * per_xcd)), dim3(NW * 64), 0, s, p);
-    return hipGetLastError();
+    if constexpr (D == 64 && !BSP) {
+        // four-wave workgroups, 128 rows each, several per CU
+        constexpr int BM2 = 128;
+        const int tt2 = BM2 >> p.pack_log2;
+        p.n_qtiles = (max_seqlen_q + tt2 - 1) / tt2;
+        const int64_t per_xcd2 = tiles_per_xcd(p.batch, p.n_head_groups, p.total_q, max_seqlen_q, tt2);
+        if (8 * per_xcd2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((k_paged_prefill_pair<D, BF16, CAP>), dim3((unsigned)(8 * per_xcd2)),
+                           dim3(256), 0, s, p);
+        return hipGetLastError();
+    } else {
+        hipLaunchKernelGGL((k_paged_prefill<D, BN, QB, NW, BF16, CAP, BSP, false>),
+                           dim3((unsigned)(8 * per_xcd)), dim3(NW * 64), 0, s, p);
+        return hipGetLastError();
+    }
 }
 
 }  // namespace

@@ -1,9 +1,10 @@
-"""The persistent prefill path: at head size 64, a batch whose sequences all
-have the same length runs one workgroup per CU over a fixed snake of tiles.
+"""Equal-length batches at head size 64.  Under stored block lists such a
+batch runs the persistent path (one workgroup per CU over a fixed snake of
+tiles); without them it runs the four-wave workgroups like any other batch.
 
-Each case is held to the oracle and, bit for bit, to the dispatched path:
-the same call with one more, empty, sequence appended (total_q then differs
-from batch * max_seqlen_q, so the launcher dispatches one workgroup per
+Each case is held to the oracle and, bit for bit, to the same call with one
+more, empty, sequence appended (total_q then differs from batch *
+max_seqlen_q, so the launcher takes its ragged-batch path: one workgroup per
 tile).  A query row's arithmetic does not depend on which workgroup runs
 it, so the two outputs must be identical.
 """

@@ -536,8 +536,10 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 // Head size 64, dense or masked (no stored block lists): several small
 // workgroups per CU instead of one.  A workgroup is four waves (one per
 // SIMD) holding 128 packed query rows, and its K/V ring has two stages
-// (35 KB of LDS, 136 registers), so three fit on a CU and each SIMD runs one
-// wave of each.  The workgroups are not in step: while one is in its set-up,
+// (35 KB of LDS; built for four waves per SIMD, 128 registers), so four fit
+// on a CU and each SIMD runs one wave of each (three at the 136 registers
+// the compiler picks unbounded: 1.1% slower on byte -> patch cross
+// attention).  The workgroups are not in step: while one is in its set-up,
 // epilogue or a barrier, the others' MFMA and softmax work keeps the SIMD
 // busy.  Byte -> patch cross attention's workgroups see short key ranges, so
 // set-up and epilogue are a large share of each, which the eight-wave
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 // one-workgroup kernel, between QK and the softmax 0.8-2% faster, between
 // the softmax and P.V even.)
 template <int D, bool BF16, bool CAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_paged_prefill_pair(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_paged_prefill_pair(
     PrefillParams p) {
     constexpr int NW = 4, BN = 64, BM = NW * 32;
     using R = Ring16<D, BN, NW>;

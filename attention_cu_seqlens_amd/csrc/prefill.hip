@@ -550,9 +550,9 @@ __global__ __launch_bounds__(NW * 64) void k_paged_prefill(PrefillParams p) {
 // others at the barrier (after which the other stage is free: its last
 // reads were the previous tile's), runs QK on the current stage, issues its
 // 16 key rows of the next tile into the other stage, then runs the softmax
-// and P.V.  (Loads issued ahead of QK measured 2.6% slower than the
-// one-workgroup kernel, between QK and the softmax 0.8-2% faster, between
-// the softmax and P.V even.)
+// and P.V.  (Measured in the head-size-128 form against the eight-wave
+// kernel: loads issued ahead of QK 2.6% slower, between QK and the softmax
+// 0.8-2% faster, between the softmax and P.V even.)
 template <int D, bool BF16, bool CAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_paged_prefill_pair(
     PrefillParams p) {
